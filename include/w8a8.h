@@ -1,0 +1,206 @@
+/*
+ * libw8a8 - online INT8 W8A8 linear layers, the routed int8 MoE layer and the
+ * Hadamard-domain (fwht128, g256) variant, as hand-written HIP kernels for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; titles abbreviated):
+ *   [ATOM]  "[gfx1151] Online INT8 W8A8 for Qwen3.6 27B / 35B-A3B on RDNA3.5,
+ *            with working MTP" (ATOM pull request), "Changes" section.
+ *   [QUARK] "Qwen3.6-27B-Quark-W8A8-INT8" model card, "Quantization Scheme".
+ *   [IQ8R]  "Qwen3.6-35B-A3B IQ8R - radiance container", file table and the
+ *            recipe under "How this file was made".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library keeps no reference after a call returns, never allocates device
+ *    memory and never synchronises: work is enqueued on `stream` (a
+ *    hipStream_t passed as void*; NULL = the legacy default stream) and the
+ *    call returns at once, so the calls can be captured into a HIP graph.
+ *  - Matrices are row-major with the last dimension contiguous; ld* is the
+ *    row stride in elements.  Weights are [N, K]: one row per output channel.
+ *    bf16 values are passed as uint16_t bit patterns.
+ *  - Scratch memory comes from a caller-provided workspace `ws` of
+ *    `ws_bytes` bytes, sized by the matching *_workspace_bytes() function.
+ *    Its contents need no initialisation and are undefined after the call.
+ *  - A size of zero (M == 0 or T == 0) is a no-op that returns W8A8_OK.
+ *  - Arguments are validated before anything is enqueued: a rejected call
+ *    launches nothing and leaves every output untouched.
+ *  - Return value: W8A8_OK (0) or a negative w8a8_status.  Launch failures
+ *    return W8A8_HIP_ERROR; the HIP error code is kept per thread and read
+ *    with w8a8_last_hip_error().  Faults inside a kernel surface at the
+ *    caller's next synchronisation, as in any HIP program.
+ *  - Calls are re-entrant and thread-safe.  Calls that share a workspace
+ *    must be ordered on one stream.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w8a8_status {
+    W8A8_OK = 0,
+    W8A8_INVALID_ARG = -1,         /* null pointer, negative size, ld < row length */
+    W8A8_UNSUPPORTED_SHAPE = -2,   /* a size the kernels do not handle (see each call) */
+    W8A8_MISALIGNED = -3,          /* pointer or row stride not 16-byte aligned */
+    W8A8_WORKSPACE_TOO_SMALL = -4, /* ws_bytes below the *_workspace_bytes() value */
+    W8A8_HIP_ERROR = -5,           /* a HIP call or kernel launch failed */
+    W8A8_UNSUPPORTED_DEVICE = -6   /* the current device is not gfx950 */
+} w8a8_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *w8a8_status_string(int status);
+
+/* The hipError_t of the last W8A8_HIP_ERROR returned on this thread (0 if none). */
+int w8a8_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int w8a8_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Per-row dynamic int8 quantisation.                                        */
+/* [QUARK] Quantization Scheme: activations INT8 per token (ch_axis=1) and   */
+/* weights INT8 per channel (ch_axis=0), both symmetric.  [IQ8R] Trunk row:  */
+/* codes -127..127, round to nearest.                                        */
+/*   s[m] = max_k |x[m,k]| / 127            (fp32, IEEE division)            */
+/*   q[m,k] = clamp(round_half_even(x[m,k] / s[m]), -127, 127)               */
+/* An all-zero row gets s = 0 and q = 0.  Inputs must be finite.             */
+/* x: [M, K], x_dtype 0 = bf16 (uint16 bits), 1 = fp32 (weight preparation  */
+/*    uses the same arithmetic on fp32 rows); row stride ldx elements.       */
+/* q: int8 [M, K], row stride ldq; s: fp32 [M].                              */
+/* Requires K % 16 == 0 and 1 <= K <= 65536; x, q 16-byte aligned and ldx,   */
+/* ldq multiples of 16 elements.                                             */
+/* ------------------------------------------------------------------------ */
+int quant_per_token_i8(const void *x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                       int8_t *q, int64_t ldq, float *s, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* W8A8 GEMM with the per-token x per-channel epilogue.                      */
+/* [ATOM] Changes, linear.py bullet: int8 activations (per token) times int8 */
+/* weights (per channel, fp32 scales), bf16 out.                             */
+/*   acc[m,n] = sum_k qa[m,k] * qw[n,k]                     (exact int32)    */
+/*   y[m,n]   = bf16_rne( (float(acc[m,n]) * sa[m]) * sw[n] )  (fp32)        */
+/* qa: int8 [M, K] (lda), sa: fp32 [M]; qw: int8 [N, K] (ldw), sw: fp32 [N]; */
+/* y: bf16 [M, N] (ldy).  M <= 16 runs the weight-streaming decode kernel,   */
+/* larger M the LDS-tiled MFMA kernel.                                       */
+/* Requires K % 64 == 0, K <= 131072, N % 16 == 0; qa, qw 16-byte aligned;   */
+/* lda, ldw multiples of 16; y 4-byte aligned and ldy even.                  */
+/* ------------------------------------------------------------------------ */
+size_t gemm_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int gemm_w8a8(const int8_t *qa, const float *sa, int64_t M, int64_t K, int64_t lda,
+              const int8_t *qw, const float *sw, int64_t N, int64_t ldw, uint16_t *y,
+              int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+
+/* The same kernels as gemm_w8a8 with the epilogue replaced by a store of the */
+/* exact int32 sums acc[m,n] (int32 [M, N], row stride ldacc).  For tests.   */
+int gemm_w8a8_i32acc(const int8_t *qa, int64_t M, int64_t K, int64_t lda, const int8_t *qw,
+                     int64_t N, int64_t ldw, int32_t *acc, int64_t ldacc, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* The whole online W8A8 linear: bf16 x -> per-token int8 (as               */
+/* quant_per_token_i8) -> GEMM and epilogue (as gemm_w8a8) -> bf16 y.        */
+/* The codes and scales live in the workspace.  Same shape rules as          */
+/* gemm_w8a8; x 16-byte aligned with ldx a multiple of 16.                   */
+/* ------------------------------------------------------------------------ */
+size_t linear_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int linear_w8a8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const int8_t *qw,
+                const float *sw, int64_t N, int64_t ldw, uint16_t *y, int64_t ldy, void *ws,
+                size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Routed int8 MoE layer.                                                    */
+/* [ATOM] Changes, fused_moe_triton.py bullet: routing -> per-token int8     */
+/* quant -> gemm1 with fused gated SiLU over interleaved w13 -> per-token    */
+/* int8 quant -> gemm2 with scatter/combine; moe.py bullet: int8 w13/w2 with */
+/* per-channel fp32 scales.                                                  */
+/*   routing (if logits != NULL): softmax over E, keep the top-k (slot j =   */
+/*     j-th largest logit, ties to the lower expert index), renormalise the  */
+/*     kept probabilities; ids/weights are written to topk_ids/topk_w.       */
+/*     If logits == NULL, topk_ids/topk_w are inputs (ids in [0, E)).        */
+/*   qx, sx = per-token quant of x (once per token, shared by its k pairs)   */
+/*   for pair r = t*k + j, e = topk_ids[t,j]:                                */
+/*     h[c]   = (float(sum_h qx[t,h] w13[e,c,h]) * sx[t]) * s13[e,c], c<2I   */
+/*     act[i] = silu(h[2i]) * h[2i+1]     (row 2i = gate, 2i+1 = up)         */
+/*     qa, sa2 = per-row quant of act (one scale per pair)                   */
+/*     y2[c]  = (float(sum_i qa[i] w2[e,c,i]) * sa2) * s2[e,c], c<H          */
+/*   out[t,c] = bf16_rne( sum_j topk_w[t,j] * y2[(t,j), c] )   (fp32)        */
+/* x: bf16 [T, H]; logits: fp32 [T, E]; w13: int8 [E, 2I, H], s13: fp32      */
+/* [E, 2I]; w2: int8 [E, H, I], s2: fp32 [E, H]; topk_ids: int32 [T, k];     */
+/* topk_w: fp32 [T, k]; out: bf16 [T, H].  All contiguous.                   */
+/* Requires H % 64 == 0, I % 64 == 0, H <= 16384, I <= 4096, 1 <= k <= 16,   */
+/* k <= E <= 1024, T*k <= 2^24; pointers 16-byte aligned.                    */
+/* dbg (nullable; each member nullable): extra copies of the intermediates,  */
+/* in pair order r = t*k + j.                                                */
+/* ------------------------------------------------------------------------ */
+typedef struct moe_w8a8_debug {
+    int8_t *qx;    /* [T, H] */
+    float *sx;     /* [T] */
+    int32_t *acc1; /* [T*k, 2I] */
+    float *act;    /* [T*k, I] */
+    int8_t *qa;    /* [T*k, I] */
+    float *sa2;    /* [T*k] */
+    int32_t *acc2; /* [T*k, H] */
+} moe_w8a8_debug;
+
+size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int topk);
+int moe_w8a8_forward(const uint16_t *x, const float *logits, int64_t T, int64_t H, int64_t E,
+                     int64_t I, int topk, const int8_t *w13, const float *s13,
+                     const int8_t *w2, const float *s2, int32_t *topk_ids, float *topk_w,
+                     uint16_t *out, void *ws, size_t ws_bytes, const moe_w8a8_debug *dbg,
+                     void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Hadamard-domain activations.  [IQ8R] Trunk and Activations rows: each 128 */
+/* of K rotated by the unnormalised Hadamard, int8 activations under the     */
+/* same rotation.  Per row: every 128-block goes through the fp32 fast       */
+/* Walsh-Hadamard butterfly in natural (Sylvester) order, stages h = 1, 2,   */
+/* ..., 64, pair (i, i+h) -> (a + b, a - b); then the whole rotated row is   */
+/* quantised as in quant_per_token_i8.                                       */
+/* x: bf16 [M, K] (ldx); q: int8 [M, K] (ldq); s: fp32 [M].                  */
+/* Requires K % 128 == 0, K <= 16384; 16-byte alignment as above.            */
+/* ------------------------------------------------------------------------ */
+int fwht128_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *q,
+                  int64_t ldq, float *s, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Hadamard-domain weight preparation (done once, at load).  [IQ8R] Trunk    */
+/* row and recipe "rtn codes=i8 group=256 scale=u8 scale2=bf16 block2=1x*    */
+/* transform=fwht128 clamp=sym".  Per row n of W (fp32 [N, K], contiguous):  */
+/*   w' = fwht128 of each 128-block (as above);                              */
+/*   a_g = max |w'| over group g of 256, s_g = a_g / 127;                    */
+/*   s2[n] = bf16_rne(max_g s_g / 255);                                      */
+/*   su8[n,g] = a_g == 0 ? 0 : clamp(round_half_even(s_g / s2[n]), 1, 255);  */
+/*   qw[n,k] = clamp(round_half_even(w' / (s2[n] * su8[n,g])), -127, 127)    */
+/*   (codes 0 where the effective scale is 0).                               */
+/* qw: int8 [N, K]; su8: uint8 [N, K/256]; s2: bf16 [N].                     */
+/* Requires K % 256 == 0, K <= 16384.                                        */
+/* ------------------------------------------------------------------------ */
+int fwht128_weight_prep_g256(const float *W, int64_t N, int64_t K, int8_t *qw, uint8_t *su8,
+                             uint16_t *s2, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Hadamard-domain GEMM with u8 group scales.  [IQ8R] Trunk row.             */
+/*   acc_g[m,n] = sum over the 256 k of group g of qa[m,k] * qw[n,k]         */
+/*   T[m,n]     = sum_g su8[n,g] * acc_g[m,n]                 (exact int64)  */
+/*   y[m,n]     = bf16_rne( float( T * sa[m] * s2[n] * 2^-7 ) )  (fp64)      */
+/* The 2^-7 undoes <Hx, Hw> = 128 <x, w> of the unnormalised transform.      */
+/* qa: int8 [M, K] contiguous, sa: fp32 [M]; qw: int8 [N, K] contiguous;     */
+/* su8: uint8 [N, K/256]; s2: bf16 [N]; y: bf16 [M, N] (ldy).                */
+/* Requires K % 256 == 0, K <= 16384, N % 16 == 0.                           */
+/* ------------------------------------------------------------------------ */
+size_t gemm_w8a8_g256_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int gemm_w8a8_g256(const int8_t *qa, const float *sa, int64_t M, int64_t K, const int8_t *qw,
+                   const uint8_t *su8, const uint16_t *s2, int64_t N, uint16_t *y, int64_t ldy,
+                   void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

@@ -1,0 +1,268 @@
+"""Online INT8 W8A8 (dense, routed MoE, fwht128 / g256) on MI355X.
+
+Thin ctypes binding of ``libw8a8.so`` (hand-written gfx950 HIP kernels behind
+the C ABI of ``include/w8a8.h``).  The functions here only marshal torch
+tensors (device memory) and the current HIP stream into the C calls; every
+step of the computation runs in the library's kernels.  There is no CPU or
+PyTorch fallback: if the library is missing or the device is not gfx950 the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw8a8.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "w8a8.h")
+
+_lib = None
+
+W8A8_OK = 0
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "misaligned",
+          -4: "workspace too small", -5: "HIP error", -6: "unsupported device"}
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, fn: str, status: int, hip_err: int = 0):
+        self.status = status
+        msg = f"{fn} failed: {STATUS.get(status, status)}"
+        if status == -5:
+            msg += f" (hipError {hip_err})"
+        super().__init__(msg)
+
+
+_i64, _i32, _sz, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+
+
+class MoeDebug(ctypes.Structure):
+    _fields_ = [("qx", _vp), ("sx", _vp), ("acc1", _vp), ("act", _vp), ("qa", _vp),
+                ("sa2", _vp), ("acc2", _vp)]
+
+
+_SIGS = {
+    "w8a8_status_string": ([_i32], ctypes.c_char_p),
+    "w8a8_last_hip_error": ([], _i32),
+    "w8a8_version": ([], _i32),
+    "quant_per_token_i8": ([_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _vp], _i32),
+    "gemm_w8a8_workspace_bytes": ([_i64, _i64, _i64], _sz),
+    "gemm_w8a8": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp],
+                  _i32),
+    "gemm_w8a8_i32acc": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp],
+                         _i32),
+    "linear_w8a8_workspace_bytes": ([_i64, _i64, _i64], _sz),
+    "linear_w8a8": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp],
+                    _i32),
+    "moe_w8a8_workspace_bytes": ([_i64, _i64, _i64, _i64, _i32], _sz),
+    "moe_w8a8_forward": ([_vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                          _vp, _vp, _sz, ctypes.POINTER(MoeDebug), _vp], _i32),
+    "fwht128_quant": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp], _i32),
+    "fwht128_weight_prep_g256": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp], _i32),
+    "gemm_w8a8_g256_workspace_bytes": ([_i64, _i64, _i64], _sz),
+    "gemm_w8a8_g256": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp],
+                       _i32),
+}
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/w8a8.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw8a8.so (built by ``moe_quant_token_amd.build``); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run moe_quant_token_amd/build.py "
+                               "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != W8A8_OK:
+        raise W8A8Error(fn, status, lib().w8a8_last_hip_error())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _req(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name}: expected a device tensor")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: last dimension must be contiguous")
+
+
+def _workspace(nbytes: int, device, ws: torch.Tensor | None):
+    if nbytes == 0:
+        return ws, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+# --------------------------------------------------------------------------
+def quant_per_token_i8(x: torch.Tensor, q: torch.Tensor | None = None,
+                       s: torch.Tensor | None = None):
+    """Per-row symmetric int8 quantisation of bf16 or fp32 rows -> (q int8, s fp32)."""
+    dt = {torch.bfloat16: 0, torch.float32: 1}.get(x.dtype)
+    if dt is None:
+        raise TypeError("quant_per_token_i8: x must be bfloat16 or float32")
+    _req(x, x.dtype, "x")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device) if q is None else q
+    s = torch.empty((M,), dtype=torch.float32, device=x.device) if s is None else s
+    _check("quant_per_token_i8",
+           lib().quant_per_token_i8(_ptr(x), dt, M, K, x.stride(0), _ptr(q), q.stride(0),
+                                    _ptr(s), _stream(x.device)))
+    return q, s
+
+
+def gemm_w8a8(qa, sa, qw, sw, y: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """y[m, n] = bf16((float(sum_k qa[m,k] qw[n,k]) * sa[m]) * sw[n])."""
+    _req(qa, torch.int8, "qa")
+    _req(qw, torch.int8, "qw")
+    M, K = qa.shape
+    N = qw.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device) if y is None else y
+    ws, wsb = _workspace(lib().gemm_w8a8_workspace_bytes(M, N, K), qa.device, ws)
+    _check("gemm_w8a8",
+           lib().gemm_w8a8(_ptr(qa), _ptr(sa), M, K, qa.stride(0), _ptr(qw), _ptr(sw), N,
+                           qw.stride(0), _ptr(y), y.stride(0), _ptr(ws), wsb,
+                           _stream(qa.device)))
+    return y
+
+
+def gemm_w8a8_i32acc(qa, qw, acc: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """The exact int32 sums of gemm_w8a8 (same kernels, int32 store)."""
+    _req(qa, torch.int8, "qa")
+    _req(qw, torch.int8, "qw")
+    M, K = qa.shape
+    N = qw.shape[0]
+    acc = torch.empty((M, N), dtype=torch.int32, device=qa.device) if acc is None else acc
+    ws, wsb = _workspace(lib().gemm_w8a8_workspace_bytes(M, N, K), qa.device, ws)
+    _check("gemm_w8a8_i32acc",
+           lib().gemm_w8a8_i32acc(_ptr(qa), M, K, qa.stride(0), _ptr(qw), N, qw.stride(0),
+                                  _ptr(acc), acc.stride(0), _ptr(ws), wsb, _stream(qa.device)))
+    return acc
+
+
+def linear_w8a8_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().linear_w8a8_workspace_bytes(M, N, K))
+
+
+def linear_w8a8(x, qw, sw, y: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """bf16 x -> per-token int8 -> W8A8 GEMM + epilogue -> bf16 y."""
+    _req(x, torch.bfloat16, "x")
+    _req(qw, torch.int8, "qw")
+    M, K = x.shape
+    N = qw.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    ws, wsb = _workspace(linear_w8a8_workspace_bytes(M, N, K), x.device, ws)
+    _check("linear_w8a8",
+           lib().linear_w8a8(_ptr(x), M, K, x.stride(0), _ptr(qw), _ptr(sw), N, qw.stride(0),
+                             _ptr(y), y.stride(0), _ptr(ws), wsb, _stream(x.device)))
+    return y
+
+
+def moe_w8a8_workspace_bytes(T: int, H: int, E: int, I: int, topk: int) -> int:
+    return int(lib().moe_w8a8_workspace_bytes(T, H, E, I, topk))
+
+
+def moe_w8a8_forward(x, logits, w13, s13, w2, s2, topk: int, topk_ids=None, topk_w=None,
+                     out=None, ws=None, debug: bool = False):
+    """Routed int8 MoE layer.  ``logits`` None -> ``topk_ids``/``topk_w`` are inputs.
+
+    Returns ``out`` (bf16 [T, H]) and, with ``debug``, a dict of intermediates.
+    """
+    _req(x, torch.bfloat16, "x")
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    dev = x.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    ws, wsb = _workspace(moe_w8a8_workspace_bytes(T, H, E, I, topk), dev, ws)
+    dbg_t = None
+    dbg_p = None
+    if debug:
+        R = T * topk
+        dbg_t = dict(qx=torch.empty((T, H), dtype=torch.int8, device=dev),
+                     sx=torch.empty((T,), dtype=torch.float32, device=dev),
+                     acc1=torch.empty((R, I2), dtype=torch.int32, device=dev),
+                     act=torch.empty((R, I), dtype=torch.float32, device=dev),
+                     qa=torch.empty((R, I), dtype=torch.int8, device=dev),
+                     sa2=torch.empty((R,), dtype=torch.float32, device=dev),
+                     acc2=torch.empty((R, H), dtype=torch.int32, device=dev))
+        dbg_p = ctypes.pointer(MoeDebug(**{k: v.data_ptr() for k, v in dbg_t.items()}))
+    _check("moe_w8a8_forward",
+           lib().moe_w8a8_forward(_ptr(x), _ptr(logits), T, H, E, I, topk, _ptr(w13), _ptr(s13),
+                                  _ptr(w2), _ptr(s2), _ptr(topk_ids), _ptr(topk_w), _ptr(out),
+                                  _ptr(ws), wsb, dbg_p, _stream(dev)))
+    if debug:
+        return out, topk_ids, topk_w, dbg_t
+    return out, topk_ids, topk_w
+
+
+def fwht128_quant(x, q: torch.Tensor | None = None, s: torch.Tensor | None = None):
+    """fwht128 of each 128-block of every bf16 row, then per-row int8 quant."""
+    _req(x, torch.bfloat16, "x")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device) if q is None else q
+    s = torch.empty((M,), dtype=torch.float32, device=x.device) if s is None else s
+    _check("fwht128_quant",
+           lib().fwht128_quant(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(s),
+                               _stream(x.device)))
+    return q, s
+
+
+def fwht128_weight_prep_g256(W):
+    """Rotated int8 weights with u8 scales per 256 of K under a bf16 row scale."""
+    _req(W, torch.float32, "W")
+    W = W.contiguous()
+    N, K = W.shape
+    qw = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    su8 = torch.empty((N, K // 256), dtype=torch.uint8, device=W.device)
+    s2 = torch.empty((N,), dtype=torch.bfloat16, device=W.device)
+    _check("fwht128_weight_prep_g256",
+           lib().fwht128_weight_prep_g256(_ptr(W), N, K, _ptr(qw), _ptr(su8), _ptr(s2),
+                                          _stream(W.device)))
+    return qw, su8, s2
+
+
+def gemm_w8a8_g256(qa, sa, qw, su8, s2, y: torch.Tensor | None = None,
+                   ws: torch.Tensor | None = None):
+    """Hadamard-domain GEMM with per-256 u8 group scales and a bf16 row scale."""
+    _req(qa, torch.int8, "qa")
+    _req(qw, torch.int8, "qw")
+    M, K = qa.shape
+    N = qw.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device) if y is None else y
+    ws, wsb = _workspace(lib().gemm_w8a8_g256_workspace_bytes(M, N, K), qa.device, ws)
+    _check("gemm_w8a8_g256",
+           lib().gemm_w8a8_g256(_ptr(qa), _ptr(sa), M, K, _ptr(qw), _ptr(su8), _ptr(s2), N,
+                                _ptr(y), y.stride(0), _ptr(ws), wsb, _stream(qa.device)))
+    return y

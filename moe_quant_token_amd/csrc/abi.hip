@@ -1,0 +1,261 @@
+// C-ABI entry points of libw8a8 (declared in include/w8a8.h): argument
+// validation, device check, workspace carving and kernel dispatch.  Nothing
+// here allocates, synchronises or reads device memory on the host.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/w8a8.h"
+#include "kernels.h"
+
+using namespace w8a8;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return W8A8_HIP_ERROR;
+}
+
+// Device check, cached per device id (gfx950 only).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return W8A8_UNSUPPORTED_DEVICE;
+  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? W8A8_OK : W8A8_UNSUPPORTED_DEVICE;
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Shape rules shared by gemm_w8a8, gemm_w8a8_i32acc and linear_w8a8.
+int check_gemm_shape(int64_t M, int64_t K, int64_t lda, int64_t N, int64_t ldw, int64_t ldo) {
+  if (M < 0 || K <= 0 || N <= 0) return W8A8_INVALID_ARG;
+  if (lda < K || ldw < K || ldo < N) return W8A8_INVALID_ARG;
+  if (K % 64 != 0 || K > 131072 || N % 16 != 0 || N > (int64_t)1 << 30 ||
+      M > (int64_t)1 << 30)
+    return W8A8_UNSUPPORTED_SHAPE;
+  if (lda % 16 != 0 || ldw % 16 != 0) return W8A8_MISALIGNED;
+  return W8A8_OK;
+}
+
+int dispatch_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t lda,
+                  const int8_t* qw, const float* sw, int64_t N, int64_t ldw, uint16_t* y,
+                  int64_t ldy, hipStream_t st) {
+  hipError_t e = (M <= 16) ? launch_gemm_skinny(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy, st)
+                           : launch_gemm_tile(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy, st);
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w8a8_status_string(int status) {
+  switch (status) {
+    case W8A8_OK: return "ok";
+    case W8A8_INVALID_ARG: return "invalid argument";
+    case W8A8_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case W8A8_MISALIGNED: return "misaligned pointer or row stride";
+    case W8A8_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case W8A8_HIP_ERROR: return "HIP error";
+    case W8A8_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+    default: return "unknown status";
+  }
+}
+
+int w8a8_last_hip_error(void) { return g_last_hip_error; }
+
+int w8a8_version(void) { return 100; }
+
+int quant_per_token_i8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                       int64_t ldq, float* s, void* stream) {
+  if (M < 0 || K <= 0 || ldx < K || ldq < K) return W8A8_INVALID_ARG;
+  if (x_dtype != 0 && x_dtype != 1) return W8A8_INVALID_ARG;
+  if (K % 16 != 0 || K > 65536 || M > (int64_t)1 << 31) return W8A8_UNSUPPORTED_SHAPE;
+  if (M == 0) return W8A8_OK;
+  if (!x || !q || !s) return W8A8_INVALID_ARG;
+  if (!al16(x) || !al16(q) || !al4(s) || ldx % 16 != 0 || ldq % 16 != 0) return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  hipError_t e = launch_quant_rows(x, x_dtype, M, K, ldx, q, ldq, s, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+size_t gemm_w8a8_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+int gemm_w8a8(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t lda,
+              const int8_t* qw, const float* sw, int64_t N, int64_t ldw, uint16_t* y,
+              int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  int r = check_gemm_shape(M, K, lda, N, ldw, ldy);
+  if (r != W8A8_OK) return r;
+  if (M == 0) return W8A8_OK;
+  if (!qa || !sa || !qw || !sw || !y) return W8A8_INVALID_ARG;
+  if (!al16(qa) || !al16(qw) || !al4(sa) || !al4(sw) || !al4(y) || ldy % 2 != 0)
+    return W8A8_MISALIGNED;
+  if (ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  if ((r = check_device()) != W8A8_OK) return r;
+  return dispatch_gemm(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy, as_stream(stream));
+}
+
+int gemm_w8a8_i32acc(const int8_t* qa, int64_t M, int64_t K, int64_t lda, const int8_t* qw,
+                     int64_t N, int64_t ldw, int32_t* acc, int64_t ldacc, void* ws,
+                     size_t ws_bytes, void* stream) {
+  (void)ws;
+  int r = check_gemm_shape(M, K, lda, N, ldw, ldacc);
+  if (r != W8A8_OK) return r;
+  if (M == 0) return W8A8_OK;
+  if (!qa || !qw || !acc) return W8A8_INVALID_ARG;
+  if (!al16(qa) || !al16(qw) || !al4(acc)) return W8A8_MISALIGNED;
+  if (ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  if ((r = check_device()) != W8A8_OK) return r;
+  hipStream_t st = as_stream(stream);
+  hipError_t e = (M <= 16) ? launch_gemm_skinny_i32(qa, M, K, lda, qw, N, ldw, acc, ldacc, st)
+                           : launch_gemm_tile_i32(qa, M, K, lda, qw, N, ldw, acc, ldacc, st);
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+size_t linear_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
+  return align_up((size_t)M * (size_t)K) + align_up((size_t)M * 4) +
+         gemm_w8a8_workspace_bytes(M, N, K);
+}
+
+int linear_w8a8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* qw,
+                const float* sw, int64_t N, int64_t ldw, uint16_t* y, int64_t ldy, void* ws,
+                size_t ws_bytes, void* stream) {
+  int r = check_gemm_shape(M, K, ldx, N, ldw, ldy);
+  if (r != W8A8_OK) return r;
+  if (M == 0) return W8A8_OK;
+  if (!x || !qw || !sw || !y) return W8A8_INVALID_ARG;
+  if (!al16(x) || !al16(qw) || !al4(sw) || !al4(y) || ldy % 2 != 0) return W8A8_MISALIGNED;
+  if (ws_bytes < linear_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  if (!ws || !al16(ws)) return ws ? W8A8_MISALIGNED : W8A8_INVALID_ARG;
+  if ((r = check_device()) != W8A8_OK) return r;
+  hipStream_t st = as_stream(stream);
+  int8_t* q = static_cast<int8_t*>(ws);
+  float* s = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * (size_t)K));
+  hipError_t e = launch_quant_rows(x, 0, M, K, ldx, q, K, s, st);
+  if (e != hipSuccess) return hip_fail(e);
+  return dispatch_gemm(q, s, M, K, K, qw, sw, N, ldw, y, ldy, st);
+}
+
+size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int topk) {
+  if (T <= 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0) return 0;
+  return moe_workspace_bytes(T, H, E, I, topk);
+}
+
+int moe_w8a8_forward(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t E,
+                     int64_t I, int topk, const int8_t* w13, const float* s13, const int8_t* w2,
+                     const float* s2, int32_t* topk_ids, float* topk_w, uint16_t* out, void* ws,
+                     size_t ws_bytes, const moe_w8a8_debug* dbg, void* stream) {
+  if (T < 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0) return W8A8_INVALID_ARG;
+  if (H % 64 != 0 || I % 64 != 0 || H > 16384 || I > 4096 || topk > 16 || topk > E ||
+      E > 1024 || T * topk > ((int64_t)1 << 24))
+    return W8A8_UNSUPPORTED_SHAPE;
+  if (T == 0) return W8A8_OK;
+  if (!x || !w13 || !s13 || !w2 || !s2 || !topk_ids || !topk_w || !out)
+    return W8A8_INVALID_ARG;
+  if (!al16(x) || !al16(w13) || !al16(w2) || !al4(s13) || !al4(s2) || !al4(topk_ids) ||
+      !al4(topk_w) || !al16(out) || (logits && !al4(logits)))
+    return W8A8_MISALIGNED;
+  if (ws_bytes < moe_w8a8_workspace_bytes(T, H, E, I, topk)) return W8A8_WORKSPACE_TOO_SMALL;
+  if (!ws) return W8A8_INVALID_ARG;
+  if (!al16(ws)) return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  MoeArgs a{};
+  a.x = x;
+  a.logits = logits;
+  a.T = (int)T;
+  a.H = (int)H;
+  a.E = (int)E;
+  a.I = (int)I;
+  a.k = topk;
+  a.w13 = w13;
+  a.s13 = s13;
+  a.w2 = w2;
+  a.s2 = s2;
+  a.topk_ids = topk_ids;
+  a.topk_w = topk_w;
+  a.out = out;
+  a.ws = ws;
+  if (dbg) {
+    a.dbg_qx = dbg->qx;
+    a.dbg_sx = dbg->sx;
+    a.dbg_acc1 = dbg->acc1;
+    a.dbg_act = dbg->act;
+    a.dbg_qa = dbg->qa;
+    a.dbg_sa2 = dbg->sa2;
+    a.dbg_acc2 = dbg->acc2;
+  }
+  hipError_t e = launch_moe_forward(a, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+int fwht128_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
+                  float* s, void* stream) {
+  if (M < 0 || K <= 0 || ldx < K || ldq < K) return W8A8_INVALID_ARG;
+  if (K % 128 != 0 || K > 16384 || M > (int64_t)1 << 31) return W8A8_UNSUPPORTED_SHAPE;
+  if (M == 0) return W8A8_OK;
+  if (!x || !q || !s) return W8A8_INVALID_ARG;
+  if (!al16(x) || !al16(q) || !al4(s) || ldx % 16 != 0 || ldq % 16 != 0) return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  hipError_t e = launch_fwht128_quant(x, M, K, ldx, q, ldq, s, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+int fwht128_weight_prep_g256(const float* W, int64_t N, int64_t K, int8_t* qw, uint8_t* su8,
+                             uint16_t* s2, void* stream) {
+  if (N < 0 || K <= 0) return W8A8_INVALID_ARG;
+  if (K % 256 != 0 || K > 16384 || N > (int64_t)1 << 31) return W8A8_UNSUPPORTED_SHAPE;
+  if (N == 0) return W8A8_OK;
+  if (!W || !qw || !su8 || !s2) return W8A8_INVALID_ARG;
+  if (!al16(W) || !al16(qw)) return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  hipError_t e = launch_fwht128_weight_prep(W, N, K, qw, su8, s2, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+size_t gemm_w8a8_g256_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return g256_workspace_bytes(M, N, K);
+}
+
+int gemm_w8a8_g256(const int8_t* qa, const float* sa, int64_t M, int64_t K, const int8_t* qw,
+                   const uint8_t* su8, const uint16_t* s2, int64_t N, uint16_t* y, int64_t ldy,
+                   void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || K <= 0 || N <= 0 || ldy < N) return W8A8_INVALID_ARG;
+  if (K % 256 != 0 || K > 16384 || N % 16 != 0 || N > (int64_t)1 << 30 || M > (int64_t)1 << 30)
+    return W8A8_UNSUPPORTED_SHAPE;
+  if (M == 0) return W8A8_OK;
+  if (!qa || !sa || !qw || !su8 || !s2 || !y) return W8A8_INVALID_ARG;
+  if (!al16(qa) || !al16(qw) || !al4(sa) || !al4(y) || ldy % 2 != 0) return W8A8_MISALIGNED;
+  if (ws_bytes < gemm_w8a8_g256_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  hipError_t e = launch_gemm_g256(qa, sa, M, K, qw, su8, s2, N, y, ldy, ws, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+}  // extern "C"

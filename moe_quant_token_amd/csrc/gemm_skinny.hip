@@ -1,0 +1,116 @@
+// Weight-streaming W8A8 GEMM for decode-shaped inputs (M <= 16 tokens).
+//
+// Source: "[gfx1151] Online INT8 W8A8 for Qwen3.6 27B / 35B-A3B on RDNA3.5,
+// with working MTP" (ATOM pull request): halving weight bytes matters because
+// they are the decode bottleneck (intro, precision split); Changes, linear.py
+// bullet: per-token int8 activations x per-channel int8 weights, bf16 out.
+//
+// At M <= 16 every weight byte is used once, so the kernel is bound by HBM
+// reads of the [N, K] int8 weights.  Each workgroup owns 16 output channels
+// (one 16x16x64 MFMA column tile) and splits K across its waves, so there is
+// no cross-workgroup reduction and no workspace: the int32 partials of the
+// waves are summed exactly through LDS and the fp32 epilogue runs in-register.
+//
+// MFMA operand mapping (v_mfma_i32_16x16x64_i8): lane l supplies 16 bytes of
+// A row (l % 16) and of B column (l % 16) for k-slice (l / 16); the same
+// k-slice is used for A and B, so the sum over k is exact whatever the
+// hardware's byte order inside the slice.  Result lane l holds rows
+// 4*(l/16) + v (v = 0..3) of column l % 16.  Rows >= M are fed zeros.
+#include "kernels.h"
+
+namespace w8a8 {
+
+template <int WAVES, int UNROLL, bool STORE_I32>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
+    const int8_t* __restrict__ qa, const float* __restrict__ sa, int M, int K, int64_t lda,
+    const int8_t* __restrict__ qw, const float* __restrict__ sw, int64_t ldw,
+    void* __restrict__ out, int64_t ldo) {
+  __shared__ v4i red[WAVES][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;  // A row (token) / B column (output channel)
+  const int g = lane >> 4;  // 16-byte k-slice inside a 64-wide k step
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+
+  const int nchunk = K >> 6;  // 64-wide k steps
+  const int per = (nchunk + WAVES - 1) / WAVES;
+  const int c_begin = wv * per;
+  const int c_end = min(nchunk, c_begin + per);
+
+  const int8_t* wp = qw + (n0 + j) * ldw + g * 16;
+  const bool a_ok = j < M;
+  const int8_t* ap = qa + (int64_t)(a_ok ? j : 0) * lda + g * 16;
+
+  v4i acc = {0, 0, 0, 0};
+  for (int c = c_begin; c < c_end; c += UNROLL) {
+    v4i b[UNROLL], a[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; u++) {
+      const int cc = c + u;
+      if (cc < c_end) {
+        b[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + (int64_t)cc * 64));
+        a[u] = a_ok ? *reinterpret_cast<const v4i*>(ap + (int64_t)cc * 64) : v4i{0, 0, 0, 0};
+      } else {
+        b[u] = v4i{0, 0, 0, 0};
+        a[u] = v4i{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; u++) acc = mfma_16x16x64_i8(a[u], b[u], acc);
+  }
+
+  if (WAVES > 1) {
+    red[wv][lane] = acc;
+    __syncthreads();
+    if (wv != 0) return;
+#pragma unroll
+    for (int w = 1; w < WAVES; w++) acc += red[w][lane];
+  }
+
+  const int64_t n = n0 + j;
+#pragma unroll
+  for (int v = 0; v < 4; v++) {
+    const int m = 4 * g + v;
+    if (m >= M) break;
+    if (STORE_I32) {
+      static_cast<int32_t*>(out)[(int64_t)m * ldo + n] = acc[v];
+    } else {
+      float r = (float)acc[v];
+      r = r * sa[m];
+      r = r * sw[n];
+      static_cast<uint16_t*>(out)[(int64_t)m * ldo + n] = (uint16_t)f32_to_bf16_bits(r);
+    }
+  }
+}
+
+template <bool STORE_I32>
+static hipError_t launch_skinny_impl(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                                     int64_t lda, const int8_t* qw, const float* sw, int64_t N,
+                                     int64_t ldw, void* out, int64_t ldo, hipStream_t stream) {
+  dim3 grid((unsigned)(N / 16));
+  // Many workgroups already (N/16 >= 512): four waves; few: eight waves to keep
+  // more loads in flight per workgroup.
+  if (N / 16 >= 512) {
+    hipLaunchKernelGGL((k_gemm_skinny<4, 4, STORE_I32>), grid, dim3(256), 0, stream, qa, sa,
+                       (int)M, (int)K, lda, qw, sw, ldw, out, ldo);
+  } else {
+    hipLaunchKernelGGL((k_gemm_skinny<8, 4, STORE_I32>), grid, dim3(512), 0, stream, qa, sa,
+                       (int)M, (int)K, lda, qw, sw, ldw, out, ldo);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_skinny(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                              int64_t lda, const int8_t* qw, const float* sw, int64_t N,
+                              int64_t ldw, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  return launch_skinny_impl<false>(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy, stream);
+}
+
+hipError_t launch_gemm_skinny_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
+                                  const int8_t* qw, int64_t N, int64_t ldw, int32_t* acc,
+                                  int64_t ldacc, hipStream_t stream) {
+  return launch_skinny_impl<true>(qa, nullptr, M, K, lda, qw, nullptr, N, ldw, acc, ldacc,
+                                  stream);
+}
+
+}  // namespace w8a8

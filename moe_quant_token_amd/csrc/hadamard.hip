@@ -1,0 +1,301 @@
+// Hadamard-domain (fwht128) W8A8: activation rotation + quant, rotated weight
+// preparation with a u8 scale per 256 of K under a bf16 row scale, and the
+// decode-shaped g256 GEMM.
+//
+// Source: "Qwen3.6-35B-A3B IQ8R - radiance container": Trunk row (int8 codes
+// -127..127, a u8 scale per row and 256 of K under a bf16 scale per row, each
+// 128 of K rotated by the unnormalised Hadamard, round to nearest);
+// Activations row (int8 activations under the same rotation); the recipe
+// under "How this file was made" (group=256 scale=u8 scale2=bf16 block2=1x*
+// transform=fwht128 clamp=sym).
+//
+// The transform is the fp32 fast Walsh-Hadamard butterfly in natural
+// (Sylvester) order with stages h = 1, 2, ..., 64; pair (i, i+h) becomes
+// (a + b, a - b).  Every stage performs exactly those additions, in that
+// order, so the rotated values are reproducible bit for bit.  Register
+// layout: 16 lanes hold one 128-block, 8 consecutive elements per lane;
+// stages 1, 2, 4 stay inside a lane, stages 8..64 exchange with lane ^ (h/8).
+#include "kernels.h"
+
+namespace w8a8 {
+
+namespace {
+
+struct Block8 {
+  float v[8];
+};
+
+// In-place butterfly of a 128-block spread over 16 lanes (l16 = lane % 16).
+__device__ __forceinline__ void fwht128_lanes(Block8& b, int l16) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int c = 0; c < 8; c++)
+      if ((c & h) == 0) {
+        const float lo = b.v[c], hi = b.v[c + h];
+        b.v[c] = lo + hi;
+        b.v[c + h] = lo - hi;
+      }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    const bool upper = (l16 & m) != 0;
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      const float mine = b.v[c];
+      const float other = __shfl_xor(mine, m, 64);
+      b.v[c] = upper ? (other - mine) : (mine + other);
+    }
+  }
+}
+
+__device__ __forceinline__ float block_max_256(float v, float* part) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+}
+
+}  // namespace
+
+constexpr int kMaxK = 16384;
+
+// One 256-thread workgroup per row: rotate into LDS, reduce amax, quantise.
+__global__ __launch_bounds__(256) void k_fwht128_quant(const uint16_t* __restrict__ x,
+                                                       int64_t ldx, int K,
+                                                       int8_t* __restrict__ q, int64_t ldq,
+                                                       float* __restrict__ s) {
+  __shared__ __attribute__((aligned(16))) float rot[kMaxK];
+  __shared__ float part[4];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * ldx;
+  const int l16 = threadIdx.x & 15;
+  const int nblk = K >> 7;
+  float amax = 0.0f;
+  for (int b0 = 0; b0 < nblk; b0 += 16) {
+    const int blk = b0 + (threadIdx.x >> 4);
+    const bool ok = blk < nblk;
+    Block8 b;
+    if (ok) {
+      const v4u raw = *reinterpret_cast<const v4u*>(xr + blk * 128 + l16 * 8);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        b.v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+        b.v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; c++) b.v[c] = 0.0f;
+    }
+    fwht128_lanes(b, l16);
+    if (ok) {
+      float* dst = rot + blk * 128 + l16 * 8;
+#pragma unroll
+      for (int c = 0; c < 8; c++) {
+        dst[c] = b.v[c];
+        amax = fmaxf(amax, fabsf(b.v[c]));
+      }
+    }
+  }
+  amax = block_max_256(amax, part);
+  const float sc = amax / 127.0f;
+  // codes: 16 per thread-iteration, one 16-byte store
+  for (int c16 = threadIdx.x; c16 < (K >> 4); c16 += 256) {
+    const float* src = rot + c16 * 16;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+      if (amax != 0.0f) {
+        a0 = quant_code(src[4 * i], sc);
+        a1 = quant_code(src[4 * i + 1], sc);
+        a2 = quant_code(src[4 * i + 2], sc);
+        a3 = quant_code(src[4 * i + 3], sc);
+      }
+      w[i] = pack4_i8(a0, a1, a2, a3);
+    }
+    *reinterpret_cast<v4u*>(q + row * ldq + c16 * 16) = v4u{w[0], w[1], w[2], w[3]};
+  }
+  if (threadIdx.x == 0) s[row] = amax != 0.0f ? sc : 0.0f;
+}
+
+// Rotated weight preparation, one 256-thread workgroup per weight row.
+__global__ __launch_bounds__(256) void k_fwht128_wprep(const float* __restrict__ W, int K,
+                                                       int8_t* __restrict__ qw,
+                                                       uint8_t* __restrict__ su8,
+                                                       uint16_t* __restrict__ s2) {
+  __shared__ __attribute__((aligned(16))) float rot[kMaxK];
+  __shared__ float gmax[kMaxK / 256];
+  __shared__ float eff_s[kMaxK / 256];
+  __shared__ float part[4];
+  const int64_t row = blockIdx.x;
+  const float* wr = W + row * K;
+  const int l16 = threadIdx.x & 15;
+  const int lane = threadIdx.x & 63;
+  const int nblk = K >> 7;
+  const int G = K >> 8;
+  for (int b0 = 0; b0 < nblk; b0 += 16) {
+    const int blk = b0 + (threadIdx.x >> 4);
+    const bool ok = blk < nblk;
+    Block8 b;
+    if (ok) {
+      const v4f lo = *reinterpret_cast<const v4f*>(wr + blk * 128 + l16 * 8);
+      const v4f hi = *reinterpret_cast<const v4f*>(wr + blk * 128 + l16 * 8 + 4);
+      b.v[0] = lo.x; b.v[1] = lo.y; b.v[2] = lo.z; b.v[3] = lo.w;
+      b.v[4] = hi.x; b.v[5] = hi.y; b.v[6] = hi.z; b.v[7] = hi.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; c++) b.v[c] = 0.0f;
+    }
+    fwht128_lanes(b, l16);
+    float m = 0.0f;
+    if (ok) {
+      float* dst = rot + blk * 128 + l16 * 8;
+#pragma unroll
+      for (int c = 0; c < 8; c++) {
+        dst[c] = b.v[c];
+        m = fmaxf(m, fabsf(b.v[c]));
+      }
+    }
+    // a 256-group is two consecutive blocks = 32 consecutive lanes
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (ok && (lane & 31) == 0) gmax[blk >> 1] = m;
+  }
+  __syncthreads();
+  // per-group scale a_g / 127 and the row maximum of those scales
+  float smax = 0.0f;
+  for (int gi = threadIdx.x; gi < G; gi += 256) smax = fmaxf(smax, gmax[gi] / 127.0f);
+  smax = block_max_256(smax, part);
+  const uint32_t s2b = f32_to_bf16_bits(smax / 255.0f);
+  const float s2f = bf16_bits_to_f32(s2b);
+  for (int gi = threadIdx.x; gi < G; gi += 256) {
+    const float sg = gmax[gi] / 127.0f;
+    int u = 0;
+    if (s2f != 0.0f && sg != 0.0f) {
+      float r = __builtin_rintf(sg / s2f);
+      r = fminf(fmaxf(r, 1.0f), 255.0f);
+      u = (int)r;
+    }
+    su8[row * G + gi] = (uint8_t)u;
+    eff_s[gi] = s2f * (float)u;
+  }
+  if (threadIdx.x == 0) s2[row] = (uint16_t)s2b;
+  __syncthreads();
+  for (int c16 = threadIdx.x; c16 < (K >> 4); c16 += 256) {
+    const float eff = eff_s[c16 >> 4];
+    const float* src = rot + c16 * 16;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      int a[4] = {0, 0, 0, 0};
+      if (eff != 0.0f) {
+#pragma unroll
+        for (int t = 0; t < 4; t++) a[t] = quant_code(src[4 * i + t], eff);
+      }
+      w[i] = pack4_i8(a[0], a[1], a[2], a[3]);
+    }
+    *reinterpret_cast<v4u*>(qw + row * K + c16 * 16) = v4u{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// g256 epilogue: exact int64 group sum -> fp64 scaling -> fp32 -> bf16.
+__device__ __forceinline__ uint16_t g256_out(long long tsum, float sa, float s2f) {
+  double v = (double)tsum * (double)sa;
+  v = v * (double)s2f;
+  v = v * 0.0078125;
+  return (uint16_t)f32_to_bf16_bits((float)v);
+}
+
+// Weight-streaming g256 GEMM for M <= 16 (same operand mapping as the dense
+// decode kernel).  Waves split K on 256-group boundaries; after each group the
+// exact int32 MFMA sum is scaled by that group's u8 and added to an int64
+// running sum.
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_gemm_g256_skinny(
+    const int8_t* __restrict__ qa, const float* __restrict__ sa, int M, int K,
+    const int8_t* __restrict__ qw, const uint8_t* __restrict__ su8,
+    const uint16_t* __restrict__ s2, uint16_t* __restrict__ y, int64_t ldy) {
+  __shared__ long long red[WAVES][64][4];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int G = K >> 8;
+  const int per = (G + WAVES - 1) / WAVES;
+  const int g_begin = wv * per;
+  const int g_end = min(G, g_begin + per);
+  const int8_t* wp = qw + (n0 + j) * K + g * 16;
+  const bool a_ok = j < M;
+  const int8_t* ap = qa + (int64_t)(a_ok ? j : 0) * K + g * 16;
+  const uint8_t* sp = su8 + (n0 + j) * G;
+
+  long long ts[4] = {0, 0, 0, 0};
+  for (int gr = g_begin; gr < g_end; gr++) {
+    v4i b[4], a[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int64_t off = (int64_t)gr * 256 + u * 64;
+      b[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + off));
+      a[u] = a_ok ? *reinterpret_cast<const v4i*>(ap + off) : v4i{0, 0, 0, 0};
+    }
+    v4i acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 4; u++) acc = mfma_16x16x64_i8(a[u], b[u], acc);
+    const long long u8 = sp[gr];
+#pragma unroll
+    for (int v = 0; v < 4; v++) ts[v] += (long long)acc[v] * u8;
+  }
+  if (WAVES > 1) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) red[wv][lane][v] = ts[v];
+    __syncthreads();
+    if (wv != 0) return;
+    for (int w = 1; w < WAVES; w++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) ts[v] += red[w][lane][v];
+  }
+  const int64_t n = n0 + j;
+  const float s2f = bf16_bits_to_f32(s2[n]);
+#pragma unroll
+  for (int v = 0; v < 4; v++) {
+    const int m = 4 * g + v;
+    if (m >= M) break;
+    y[(int64_t)m * ldy + n] = g256_out(ts[v], sa[m], s2f);
+  }
+}
+
+hipError_t launch_gemm_g256_tile(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                                 const int8_t* qw, const uint8_t* su8, const uint16_t* s2,
+                                 int64_t N, uint16_t* y, int64_t ldy, hipStream_t stream);
+
+hipError_t launch_fwht128_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                int64_t ldq, float* s, hipStream_t stream) {
+  hipLaunchKernelGGL(k_fwht128_quant, dim3((unsigned)M), dim3(256), 0, stream, x, ldx, (int)K,
+                     q, ldq, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwht128_weight_prep(const float* W, int64_t N, int64_t K, int8_t* qw,
+                                      uint8_t* su8, uint16_t* s2, hipStream_t stream) {
+  hipLaunchKernelGGL(k_fwht128_wprep, dim3((unsigned)N), dim3(256), 0, stream, W, (int)K, qw,
+                     su8, s2);
+  return hipGetLastError();
+}
+
+size_t g256_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+hipError_t launch_gemm_g256(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                            const int8_t* qw, const uint8_t* su8, const uint16_t* s2, int64_t N,
+                            uint16_t* y, int64_t ldy, void*, hipStream_t stream) {
+  if (M <= 16) {
+    hipLaunchKernelGGL(k_gemm_g256_skinny<4>, dim3((unsigned)(N / 16)), dim3(256), 0, stream, qa,
+                       sa, (int)M, (int)K, qw, su8, s2, y, ldy);
+    return hipGetLastError();
+  }
+  return launch_gemm_g256_tile(qa, sa, M, K, qw, su8, s2, N, y, ldy, stream);
+}
+
+}  // namespace w8a8

@@ -1,0 +1,61 @@
+// Launch helpers of the gfx950 kernels (internal to libw8a8).  Each enqueues
+// on `stream` and returns hipGetLastError(); shapes are validated by the
+// caller (abi.hip) before any of these runs.
+#pragma once
+
+#include "common.h"
+
+namespace w8a8 {
+
+hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             int8_t* q, int64_t ldq, float* s, hipStream_t stream);
+
+hipError_t launch_gemm_skinny(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                              int64_t lda, const int8_t* qw, const float* sw, int64_t N,
+                              int64_t ldw, uint16_t* y, int64_t ldy, hipStream_t stream);
+hipError_t launch_gemm_skinny_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
+                                  const int8_t* qw, int64_t N, int64_t ldw, int32_t* acc,
+                                  int64_t ldacc, hipStream_t stream);
+
+hipError_t launch_gemm_tile(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                            int64_t lda, const int8_t* qw, const float* sw, int64_t N,
+                            int64_t ldw, uint16_t* y, int64_t ldy, hipStream_t stream);
+hipError_t launch_gemm_tile_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
+                                const int8_t* qw, int64_t N, int64_t ldw, int32_t* acc,
+                                int64_t ldacc, hipStream_t stream);
+
+// Routed MoE.  Workspace layout is owned by moe.hip.
+struct MoeArgs {
+  const uint16_t* x;
+  const float* logits;
+  int T, H, E, I, k;
+  const int8_t* w13;
+  const float* s13;
+  const int8_t* w2;
+  const float* s2;
+  int32_t* topk_ids;
+  float* topk_w;
+  uint16_t* out;
+  void* ws;
+  int8_t* dbg_qx;
+  float* dbg_sx;
+  int32_t* dbg_acc1;
+  float* dbg_act;
+  int8_t* dbg_qa;
+  float* dbg_sa2;
+  int32_t* dbg_acc2;
+};
+size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int k);
+hipError_t launch_moe_forward(const MoeArgs& a, hipStream_t stream);
+
+// Hadamard-domain variant.
+hipError_t launch_fwht128_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                int64_t ldq, float* s, hipStream_t stream);
+hipError_t launch_fwht128_weight_prep(const float* W, int64_t N, int64_t K, int8_t* qw,
+                                      uint8_t* su8, uint16_t* s2, hipStream_t stream);
+size_t g256_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_g256(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                            const int8_t* qw, const uint8_t* su8, const uint16_t* s2, int64_t N,
+                            uint16_t* y, int64_t ldy, void* ws, hipStream_t stream);
+
+}  // namespace w8a8

@@ -1,0 +1,180 @@
+"""GPU parity of the dense path through the C ABI: per-token quant, the int8
+GEMM (decode weight-streaming kernel and LDS-tiled kernel) and the whole
+online W8A8 linear, against the CPU oracle on identical seeded inputs.
+
+Bar: int8 codes, fp32 scales and int32 sums bit-exact; bf16 outputs within
+1e-3 abs + 1e-2 rel (and, since the GPU evaluates the same fp32 epilogue
+operations, expected bit-exact: mismatches are counted and must be zero).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_quant_token_amd as mq
+import synth
+from tests._util import (DEV, assert_bf16_close, bf16_dev, bf16_host, dev, host, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mq.lib()
+
+
+def _inputs(xkey, wkey, M, K, N, n_out, scale):
+    x = synth.activations(xkey, M, K, n_out, scale)
+    W = synth.weights(wkey, N, K)
+    return x, W
+
+
+# ---------------------------------------------------------------- quant
+@pytest.mark.parametrize("M,K", [(16, 512), (1, 5120), (8, 8704), (4096, 5120), (37, 16),
+                                 (5, 48), (3, 65536)])
+def test_quant_bf16_bit_exact(orc, M, K):
+    say(f"quant bf16 M={M} K={K}")
+    x = synth.activations((7, M, K), M, K, max(1, K // 100), 10.0)
+    if M > 2:
+        x[1] = 0  # an all-zero row
+    q_ref, s_ref = orc.quant_rows(x)
+    q, s = mq.quant_per_token_i8(bf16_dev(x))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(q), q_ref)
+    np.testing.assert_array_equal(host(s), s_ref)
+
+
+@pytest.mark.parametrize("N,K", [(256, 512), (17408, 5120), (5120, 8704)])
+def test_quant_fp32_weights_bit_exact(orc, N, K):
+    say(f"quant fp32 weights N={N} K={K}")
+    W = synth.weights((8, N), N, K)
+    q_ref, s_ref = orc.quant_rows(W)
+    q, s = mq.quant_per_token_i8(dev(W))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(q), q_ref)
+    np.testing.assert_array_equal(host(s), s_ref)
+
+
+def test_quant_strided_rows(orc):
+    x = synth.activations((7, 1), 6, 256, 3, 10.0)
+    big = np.zeros((6, 384), np.uint16)
+    big[:, :256] = x
+    xd = bf16_dev(big)[:, :256]
+    qbuf = torch.zeros((6, 320), dtype=torch.int8, device=DEV)
+    q, s = mq.quant_per_token_i8(xd, q=qbuf[:, :256])
+    q_ref, s_ref = orc.quant_rows(x)
+    np.testing.assert_array_equal(host(qbuf)[:, :256], q_ref)
+    assert not host(qbuf)[:, 256:].any()
+    np.testing.assert_array_equal(host(s), s_ref)
+
+
+# ---------------------------------------------------------------- GEMM
+GEMM_SHAPES = [
+    (16, 512, 256),     # the small single-linear workload (decode kernel)
+    (1, 64, 16),        # smallest legal shape
+    (3, 640, 48),
+    (17, 512, 64),      # first M served by the tiled kernel
+    (300, 640, 272),    # several 64x64 tiles with ragged M
+    (64, 1024, 1024),
+    (2048, 512, 2048),  # 256x256 tiles
+    (2100, 256, 2064),  # 256x256 tiles, ragged M and N
+]
+
+
+@pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
+def test_gemm_i32_and_bf16(orc, M, K, N):
+    say(f"gemm M={M} K={K} N={N}")
+    x, W = _inputs((9, M), (9, N), M, K, N, 4, 20.0)
+    qa, sa = orc.quant_rows(x)
+    qw, sw = orc.quant_rows(W)
+    acc_ref = orc.gemm_i32(qa, qw)
+    y_ref = orc.gemm_w8a8(qa, sa, qw, sw)
+    qa_d, sa_d, qw_d, sw_d = dev(qa), dev(sa), dev(qw), dev(sw)
+    acc = mq.gemm_w8a8_i32acc(qa_d, qw_d)
+    y = mq.gemm_w8a8(qa_d, sa_d, qw_d, sw_d)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    mism = assert_bf16_close(bf16_host(y), y_ref, "gemm_w8a8")
+    assert mism == 0
+
+
+def test_gemm_extreme_codes_no_overflow():
+    # every code +-127 at the largest decode K: |acc| = 127*127*8704
+    K, N = 8704, 32
+    qa = torch.full((4, K), 127, dtype=torch.int8, device=DEV)
+    qa[1] = -127
+    qw = torch.full((N, K), 127, dtype=torch.int8, device=DEV)
+    qw[1::2, ::2] = -127
+    acc = host(mq.gemm_w8a8_i32acc(qa, qw))
+    big = 127 * 127 * K
+    assert (acc[0, 0::2] == big).all() and (acc[1, 0::2] == -big).all()
+    assert (acc[:, 1::2] == 0).all()
+    acc2 = host(mq.gemm_w8a8_i32acc(torch.cat([qa] * 8), qw))  # tiled kernel (M = 32)
+    np.testing.assert_array_equal(acc2[:4], acc)
+
+
+def test_gemm_strided_output_and_inputs(orc):
+    M, K, N = 5, 256, 64
+    x, W = _inputs((10, 1), (10, 2), M, K, N, 2, 20.0)
+    qa, sa = orc.quant_rows(x)
+    qw, sw = orc.quant_rows(W)
+    y_ref = orc.gemm_w8a8(qa, sa, qw, sw)
+    qa_big = torch.zeros((M, K + 64), dtype=torch.int8, device=DEV)
+    qa_big[:, :K] = dev(qa)
+    ybuf = torch.zeros((M, N + 16), dtype=torch.bfloat16, device=DEV)
+    mq.gemm_w8a8(qa_big[:, :K], dev(sa), dev(qw), dev(sw), y=ybuf[:, :N])
+    got = bf16_host(ybuf)
+    np.testing.assert_array_equal(got[:, :N], y_ref)
+    assert not got[:, N:].any()
+
+
+# ------------------------------------------------------ decode, full size
+@pytest.mark.parametrize("shape_idx", [0, 1])
+def test_decode_linear_full(orc, shape_idx):
+    for M in synth.DECODE_M:
+        cfg = synth.decode_linear(M, shape_idx)
+        say(f"decode linear {cfg['name']} M={M} K={cfg['K']} N={cfg['N']}")
+        if M == 1:
+            W = synth.weights(cfg["wkey"], cfg["N"], cfg["K"])
+            qw, sw = orc.quant_rows(W)
+            del W
+            qw_d, sw_d = dev(qw), dev(sw)
+        x = synth.activations(cfg["xkey"], M, cfg["K"], cfg["n_outliers"], cfg["outlier_scale"])
+        y_ref = orc.linear_w8a8(x, qw, sw)
+        y = mq.linear_w8a8(bf16_dev(x), qw_d, sw_d)
+        torch.cuda.synchronize()
+        assert assert_bf16_close(bf16_host(y), y_ref, "linear_w8a8") == 0
+
+
+# ----------------------------------------------------- prefill, full size
+@pytest.mark.parametrize("N", [5120, 17408])
+def test_prefill_full_sampled(orc, N):
+    cfg = synth.prefill_linear(N)
+    M, K = cfg["M"], cfg["K"]
+    say(f"prefill M={M} K={K} N={N}")
+    x, W = _inputs(cfg["xkey"], cfg["wkey"], M, K, N, cfg["n_outliers"], cfg["outlier_scale"])
+    qa, sa = orc.quant_rows(x)
+    qw, sw = orc.quant_rows(W)
+    del W
+    x_d, qw_d, sw_d = bf16_dev(x), dev(qw), dev(sw)
+    # quant on the GPU (bit-exact), then both the gemm-only and the fused call
+    q_d, s_d = mq.quant_per_token_i8(x_d)
+    np.testing.assert_array_equal(host(s_d), sa)
+    assert np.array_equal(host(q_d), qa)
+    y = mq.gemm_w8a8(q_d, s_d, qw_d, sw_d)
+    y2 = mq.linear_w8a8(x_d, qw_d, sw_d)
+    acc = mq.gemm_w8a8_i32acc(q_d, qw_d)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(N)
+    ms = np.concatenate([r.integers(0, M, 4000), np.full(N // 64, M - 1), np.arange(0, M, 64)])
+    ns = np.concatenate([r.integers(0, N, 4000), np.arange(0, N, 64), np.full(M // 64, N - 1)])
+    acc_ref, y_ref = orc.gemm_w8a8_points(qa, sa, qw, sw, ms, ns)
+    np.testing.assert_array_equal(host(acc)[ms, ns], acc_ref)
+    yh = bf16_host(y)
+    assert assert_bf16_close(yh[ms, ns], y_ref, "gemm_w8a8 sampled") == 0
+    np.testing.assert_array_equal(bf16_host(y2), yh)
+    # property at full size: every output is its int32 sum through the fp32
+    # epilogue (torch: int32 -> fp32, two fp32 products, bf16 rounding)
+    full = ((acc.to(torch.float32) * s_d[:, None]) * sw_d[None, :]).to(torch.bfloat16)
+    assert torch.equal(full.view(torch.int16), y.view(torch.int16))

@@ -1,0 +1,102 @@
+"""GPU parity of the Hadamard-domain (fwht128, g256) path through the C ABI.
+
+fwht128_quant codes/scales, the rotated weight preparation (codes, u8 group
+scales, bf16 row scales) and the g256 GEMM are compared bit-exactly with the
+oracle: the transform performs the same fp32 additions in the same stage
+order, and the g256 epilogue is an exact int64 sum followed by the same fp64
+products.  bf16 outputs are also checked against the 1e-3 abs + 1e-2 rel bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_quant_token_amd as mq
+import synth
+from tests._util import assert_bf16_close, bf16_dev, bf16_host, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mq.lib()
+
+
+@pytest.mark.parametrize("M,K", [(1, 2048), (256, 2048), (7, 128), (3, 16384), (33, 640)])
+def test_fwht128_quant_bit_exact(orc, M, K):
+    say(f"fwht128_quant M={M} K={K}")
+    x = synth.activations((50, M, K), M, K, max(1, K // 100), 10.0, heavy_tail=True)
+    if M > 2:
+        x[2] = 0
+    q_ref, s_ref = orc.fwht128_quant(x)
+    q, s = mq.fwht128_quant(bf16_dev(x))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(s), s_ref)
+    np.testing.assert_array_equal(host(q), q_ref)
+
+
+@pytest.mark.parametrize("N,K", [(64, 512), (8192, 2048), (16, 16384)])
+def test_weight_prep_bit_exact(orc, N, K):
+    say(f"weight prep N={N} K={K}")
+    W = synth.weights((51, N), N, K)
+    W[3 % N] = 0
+    W[min(5, N - 1), :256] = 0
+    qw_ref, su_ref, s2_ref = orc.weight_prep_g256(W)
+    qw, su8, s2 = mq.fwht128_weight_prep_g256(dev(W))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_host(s2), s2_ref)
+    np.testing.assert_array_equal(host(su8), su_ref)
+    np.testing.assert_array_equal(host(qw), qw_ref)
+
+
+@pytest.fixture(scope="module")
+def rotated_weights(orc):
+    cfg = synth.hadamard_linear(1)
+    W = synth.weights(cfg["wkey"], cfg["N"], cfg["K"])
+    return orc.weight_prep_g256(W)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 17, 256])
+def test_g256_full_size(orc, rotated_weights, M):
+    cfg = synth.hadamard_linear(M)
+    K, N = cfg["K"], cfg["N"]
+    say(f"g256 M={M} K={K} N={N}")
+    qw, su8, s2 = rotated_weights
+    x = synth.activations(cfg["xkey"], M, K, cfg["n_outliers"], cfg["outlier_scale"],
+                          heavy_tail=True)
+    qa, sa = orc.fwht128_quant(x)
+    qa_d, sa_d = mq.fwht128_quant(bf16_dev(x))
+    y = mq.gemm_w8a8_g256(qa_d, sa_d, dev(qw), dev(su8), dev(s2))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(qa_d), qa)
+    yh = bf16_host(y)
+    if M <= 17:
+        y_ref = orc.gemm_g256(qa, sa, qw, su8, s2)
+        np.testing.assert_array_equal(yh, y_ref)
+        assert_bf16_close(yh, y_ref, "g256")
+    else:
+        r = np.random.default_rng(M)
+        ms = np.concatenate([r.integers(0, M, 6000), np.arange(M), np.full(256, M - 1)])
+        ns = np.concatenate([r.integers(0, N, 6000), np.full(M, N - 1), np.arange(0, N, 32)])
+        y_ref, _ = orc.gemm_g256_points(qa, sa, qw, su8, s2, ms, ns)
+        np.testing.assert_array_equal(yh[ms, ns], y_ref)
+        assert_bf16_close(yh[ms, ns], y_ref, "g256 sampled")
+
+
+def test_g256_small_all_edges(orc):
+    r = np.random.default_rng(3)
+    for (M, K, N) in [(1, 256, 16), (5, 512, 48), (40, 768, 80)]:
+        qa = r.integers(-127, 128, (M, K)).astype(np.int8)
+        qw = r.integers(-127, 128, (N, K)).astype(np.int8)
+        qa[0] = 127
+        qw[0] = 127  # large sums: 255 * 127^2 * K exceeds int32
+        su8 = r.integers(1, 256, (N, K // 256)).astype(np.uint8)
+        su8[0] = 255
+        s2 = synth.to_bf16_bits(r.random(N).astype(np.float32) * 1e-4)
+        sa = (r.random(M) * 0.1).astype(np.float32)
+        y_ref = orc.gemm_g256(qa, sa, qw, su8, s2)
+        y = mq.gemm_w8a8_g256(dev(qa), dev(sa), dev(qw), dev(su8),
+                              dev(s2.view(np.int16)).view(torch.bfloat16))
+        np.testing.assert_array_equal(bf16_host(y), y_ref)

@@ -1,0 +1,182 @@
+"""GPU parity of the routed int8 MoE layer through the C ABI.
+
+Routing ids are compared exactly (inputs are tie-free at the top-k boundary,
+checked), routing weights to within 1 fp32 ulp, the debug int32 sums of both
+grouped GEMMs bit-exactly (gemm2 wherever the requantised codes agree), the
+SiLU activation to within 1 fp32 ulp, and the bf16 output within
+1e-3 abs + 1e-2 rel.  Requantised codes may differ by one only where the
+oracle's act/scale lies next to a rounding boundary.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_quant_token_amd as mq
+import synth
+from tests._util import (DEV, assert_bf16_close, bf16_dev, bf16_host, dev, host, say,
+                         ulp_diff_f32)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mq.lib()
+
+
+def _weights(orc, wkey, E, H, I):
+    q13 = np.empty((E, 2 * I, H), np.int8)
+    s13 = np.empty((E, 2 * I), np.float32)
+    q2 = np.empty((E, H, I), np.int8)
+    s2 = np.empty((E, H), np.float32)
+    for e in range(E):
+        q13[e], s13[e] = orc.quant_rows(synth.expert_weights(wkey, e, 2 * I, H, synth.T_W))
+        q2[e], s2[e] = orc.quant_rows(synth.expert_weights(wkey, e, H, I, synth.T_W2))
+    return q13, s13, q2, s2
+
+
+def _tie_free(logits, k):
+    srt = -np.sort(-logits, axis=1)
+    return bool((srt[:, k - 1] != srt[:, k]).all()) if logits.shape[1] > k else True
+
+
+def _check_full(orc, x, logits, k, W, T, label):
+    q13, s13, q2, s2 = W
+    E = q13.shape[0]
+    ids_ref, w_ref = orc.route_topk(logits, k)
+    out_ref, dref = orc.moe_forward(x, ids_ref, w_ref, q13, s13, q2, s2, debug=True)
+    Wd = [dev(a) for a in W]
+    out, ids, w, dbg = mq.moe_w8a8_forward(bf16_dev(x), dev(logits), *Wd, topk=k, debug=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(ids), ids_ref)
+    assert ulp_diff_f32(host(w), w_ref).max() <= 1
+    np.testing.assert_array_equal(host(dbg["qx"]), dref["qx"])
+    np.testing.assert_array_equal(host(dbg["sx"]), dref["sx"])
+    np.testing.assert_array_equal(host(dbg["acc1"]), dref["acc1"])
+    act = host(dbg["act"])
+    assert ulp_diff_f32(act, dref["act"]).max() <= 1, "SiLU activation"
+    qa = host(dbg["qa"])
+    same_row = (act == dref["act"]).all(axis=1)
+    assert same_row.mean() > 0.99
+    np.testing.assert_array_equal(qa[same_row], dref["qa"][same_row])
+    np.testing.assert_array_equal(host(dbg["sa2"])[same_row], dref["sa2"][same_row])
+    flips = int((qa != dref["qa"]).sum())
+    assert np.abs(qa.astype(np.int32) - dref["qa"]).max() <= 1
+    assert flips <= max(2, qa.size // 1000)
+    qa_same = (qa == dref["qa"]).all(axis=1)
+    np.testing.assert_array_equal(host(dbg["acc2"])[qa_same], dref["acc2"][qa_same])
+    mism = assert_bf16_close(bf16_host(out), out_ref, label)
+    say(f"{label}: requant flips {flips}, bf16 mismatches {mism} of {out_ref.size}")
+    return out
+
+
+def test_small_full_pipeline(orc):
+    T, E, H, I, k = 37, 16, 256, 128, 4
+    key = (40, 1)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    logits = synth.router_logits(key, T, E)
+    assert _tie_free(logits, k)
+    out = _check_full(orc, x, logits, k, W, T, "moe small")
+    # determinism: a second run is bit-identical
+    out2 = mq.moe_w8a8_forward(bf16_dev(x), dev(logits), *[dev(a) for a in W], topk=k)[0]
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_given_routing_hot_expert_and_edges(orc):
+    # logits=None: the caller supplies ids/weights.  Most tokens go to expert 3
+    # (a segment far longer than one 64-pair pass); expert 0 gets none.
+    T, E, H, I, k = 150, 8, 128, 64, 2
+    key = (41, 1)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    x[5] = 0  # an all-zero token
+    r = np.random.default_rng(5)
+    ids = np.stack([np.full(T, 3), r.integers(1, E, T)], 1).astype(np.int32)
+    ids[ids[:, 1] == 3, 1] = 4
+    w = r.random((T, k)).astype(np.float32)
+    w /= w.sum(1, keepdims=True)
+    out_ref = orc.moe_forward(x, ids, w, *W)
+    out, ids_o, w_o = mq.moe_w8a8_forward(bf16_dev(x), None, *[dev(a) for a in W], topk=k,
+                                          topk_ids=dev(ids), topk_w=dev(w))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(ids_o), ids)
+    got = bf16_host(out)
+    assert_bf16_close(got, out_ref, "moe given routing")
+    assert not got[5].any()
+
+
+def test_single_expert_top1(orc):
+    T, E, H, I, k = 9, 1, 192, 64, 1
+    key = (42, 1)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    logits = synth.router_logits(key, T, E)
+    _check_full(orc, x, logits, k, W, T, "moe E=1 k=1")
+
+
+def test_routing_ties_lower_index():
+    T, E, k = 4, 32, 8
+    logits = np.zeros((T, E), np.float32)
+    logits[0, [5, 9, 2]] = 1.0          # three-way tie at the top
+    logits[1, :] = 0.5                  # all equal: ids 0..7
+    logits[2, ::-1] = np.arange(E, dtype=np.float32)
+    logits[3, [31, 30]] = 2.0
+    H, I = 64, 64
+    x = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
+    w13 = torch.zeros((E, 2 * I, H), dtype=torch.int8, device=DEV)
+    s13 = torch.zeros((E, 2 * I), dtype=torch.float32, device=DEV)
+    w2 = torch.zeros((E, H, I), dtype=torch.int8, device=DEV)
+    s2 = torch.zeros((E, H), dtype=torch.float32, device=DEV)
+    out, ids, w = mq.moe_w8a8_forward(x, dev(logits), w13, s13, w2, s2, topk=k)
+    ids = host(ids)
+    np.testing.assert_array_equal(ids[0, :3], [2, 5, 9])
+    np.testing.assert_array_equal(ids[0, 3:], [0, 1, 3, 4, 6])
+    np.testing.assert_array_equal(ids[1], np.arange(8))
+    np.testing.assert_array_equal(ids[2], np.arange(8))
+    np.testing.assert_array_equal(ids[3, :2], [30, 31])
+    np.testing.assert_allclose(host(w).sum(1), 1.0, atol=1e-6)
+    assert not bf16_host(out).any()
+
+
+@pytest.fixture(scope="module")
+def full_moe(orc):
+    cfg = synth.moe(1)
+    E, H, I = cfg["E"], cfg["H"], cfg["I"]
+    say("generating full-size MoE weights (256 experts)")
+    W = _weights(orc, cfg["wkey"], E, H, I)
+    return W, [dev(a) for a in W]
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_full_size_all_tokens(orc, full_moe, T):
+    cfg = synth.moe(T)
+    say(f"moe full size T={T}")
+    W, Wd = full_moe
+    x = synth.activations(cfg["xkey"], T, cfg["H"], 0, 1.0)
+    logits = synth.router_logits(cfg["xkey"], T, cfg["E"])
+    assert _tie_free(logits, cfg["k"])
+    _check_full(orc, x, logits, cfg["k"], W, T, f"moe T={T}")
+
+
+def test_full_size_t2048_sampled_tokens(orc, full_moe):
+    cfg = synth.moe(2048)
+    T, k = 2048, cfg["k"]
+    say("moe full size T=2048 (sampled tokens)")
+    W, Wd = full_moe
+    x = synth.activations(cfg["xkey"], T, cfg["H"], 0, 1.0)
+    logits = synth.router_logits(cfg["xkey"], T, cfg["E"])
+    assert _tie_free(logits, k)
+    out, ids, w = mq.moe_w8a8_forward(bf16_dev(x), dev(logits), *Wd, topk=k)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = orc.route_topk(logits, k)
+    np.testing.assert_array_equal(host(ids), ids_ref)
+    # tokens are independent given the routing: the oracle runs a sample of them
+    sample = np.sort(np.random.default_rng(7).choice(T, 48, replace=False))
+    out_ref = orc.moe_forward(np.ascontiguousarray(x[sample]), ids_ref[sample], w_ref[sample], *W)
+    assert_bf16_close(bf16_host(out)[sample], out_ref, "moe T=2048 sampled")
+    # property at any size: every expert's count equals its routed pairs
+    counts = np.bincount(host(ids).ravel(), minlength=cfg["E"])
+    assert counts.sum() == T * k
