@@ -4,8 +4,8 @@
 One step = the decode-shaped dense W8A8 workload: for every M in {1, 2, 4, 8}
 the gate_up (K=5120, N=17408) and down (K=8704, N=5120) linears, each as
 per-token int8 quant of the bf16 activations followed by the int8 GEMM with
-the fp32 epilogue to bf16 (quant_per_token_i8 + gemm_w8a8, the two kernels
-linear_w8a8 runs).  Weights rotate over enough copies that every launch reads
+the fp32 epilogue to bf16 (quant_per_token_i8 + gemm_w8a8_packed, the two
+kernels linear_w8a8_packed runs; weights pre-packed at load).  Weights rotate over enough copies that every launch reads
 them from HBM, not from the 256 MB Infinity Cache.  `value` is the step's
 algorithmic bytes over its time (GB/s).
 
@@ -127,6 +127,7 @@ def main():
         W = torch.from_numpy(synth.weights(synth.decode_linear(1, si)["wkey"], N, K)).to(dev)
         qw, sw = mq.quant_per_token_i8(W)          # weight preparation, untimed
         del W
+        qw = mq.pack_weights(qw)                   # MFMA tile layout, untimed
         wbytes = N * K + 4 * N
         ncopy = max(2, math.ceil(2 * MALL_BYTES / wbytes) + 1)
         copies = [(qw, sw)] + [(qw.clone(), sw.clone()) for _ in range(ncopy - 1)]
@@ -161,9 +162,9 @@ def main():
             sh = c["sh"]
             qw, sw = sh["copies"][c["use"] % len(sh["copies"])]
             c["use"] += 1
-            st = L.gemm_w8a8(c["q"].data_ptr(), c["s"].data_ptr(), c["M"], sh["K"], sh["K"],
-                             qw.data_ptr(), sw.data_ptr(), sh["N"], sh["K"], c["y"].data_ptr(),
-                             sh["N"], None, 0, stream)
+            st = L.gemm_w8a8_packed(c["q"].data_ptr(), c["s"].data_ptr(), c["M"], sh["K"],
+                                    sh["K"], qw.data_ptr(), sw.data_ptr(), sh["N"],
+                                    c["y"].data_ptr(), sh["N"], None, 0, stream)
             if st != 0:
                 raise RuntimeError(f"gemm_w8a8 failed: {st}")
         if record:
@@ -255,16 +256,17 @@ def prefill_cases(torch, np, mq, synth, dev, timer, bf16_dev):
         W = torch.from_numpy(synth.weights(cfg["wkey"], N, K)).to(dev)
         qw, sw = mq.quant_per_token_i8(W)
         del W
+        qw = mq.pack_weights(qw)
         x = bf16_dev(synth.activations(cfg["xkey"], M, K, cfg["n_outliers"],
                                        cfg["outlier_scale"]))
         q, s = mq.quant_per_token_i8(x)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(mq.linear_w8a8_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
         for _ in range(2):
-            mq.gemm_w8a8(q, s, qw, sw, y=y)
+            mq.gemm_w8a8_packed(q, s, qw, sw, N, y=y)
         it = 10
-        t_g = timer.run(lambda i: mq.gemm_w8a8(q, s, qw, sw, y=y), it) / it
-        t_l = timer.run(lambda i: mq.linear_w8a8(x, qw, sw, y=y, ws=ws), it) / it
+        t_g = timer.run(lambda i: mq.gemm_w8a8_packed(q, s, qw, sw, N, y=y), it) / it
+        t_l = timer.run(lambda i: mq.linear_w8a8_packed(x, qw, sw, N, y=y, ws=ws), it) / it
         ops = 2.0 * M * N * K
         res[f"prefill_M{M}_K{K}_N{N}"] = {
             "gemm_us": round(t_g * 1e3, 2),

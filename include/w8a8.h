@@ -114,6 +114,31 @@ int linear_w8a8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const int8
                 size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Packed weight layout (done once, at load, like the weight quantisation).  */
+/* A pure byte permutation of an int8 [N, K] weight into MFMA operand tiles: */
+/* tile t = rows 16t..16t+15; its 64-byte k step c is the contiguous 1 KiB   */
+/* block at offset (t * K/64 + c) * 1024; inside it the 16 bytes at offset   */
+/* 16*l are row 16t + (l % 16), columns 64c + 16*(l / 16) .. +15.  Every     */
+/* wave-wide weight load then reads 1 KiB of consecutive bytes.              */
+/* qw: int8 [N, K] row-major (ldw); qw_packed: int8, N*K bytes, must not     */
+/* overlap qw.  Requires N % 16 == 0, K % 64 == 0, K <= 131072.              */
+/* ------------------------------------------------------------------------ */
+int w8a8_pack_weights(const int8_t *qw, int64_t N, int64_t K, int64_t ldw, int8_t *qw_packed,
+                      void *stream);
+
+/* gemm_w8a8 / gemm_w8a8_i32acc / linear_w8a8 with packed weights: same      */
+/* arithmetic, same results, same shape rules (weight row stride is implied). */
+int gemm_w8a8_packed(const int8_t *qa, const float *sa, int64_t M, int64_t K, int64_t lda,
+                     const int8_t *qw_packed, const float *sw, int64_t N, uint16_t *y,
+                     int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+int gemm_w8a8_packed_i32acc(const int8_t *qa, int64_t M, int64_t K, int64_t lda,
+                            const int8_t *qw_packed, int64_t N, int32_t *acc, int64_t ldacc,
+                            void *ws, size_t ws_bytes, void *stream);
+int linear_w8a8_packed(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                       const int8_t *qw_packed, const float *sw, int64_t N, uint16_t *y,
+                       int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Routed int8 MoE layer.                                                    */
 /* [ATOM] Changes, fused_moe_triton.py bullet: routing -> per-token int8     */
 /* quant -> gemm1 with fused gated SiLU over interleaved w13 -> per-token    */

@@ -56,6 +56,13 @@ _SIGS = {
     "linear_w8a8_workspace_bytes": ([_i64, _i64, _i64], _sz),
     "linear_w8a8": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp],
                     _i32),
+    "w8a8_pack_weights": ([_vp, _i64, _i64, _i64, _vp, _vp], _i32),
+    "gemm_w8a8_packed": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp],
+                         _i32),
+    "gemm_w8a8_packed_i32acc": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp],
+                                _i32),
+    "linear_w8a8_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp],
+                           _i32),
     "moe_w8a8_workspace_bytes": ([_i64, _i64, _i64, _i64, _i32], _sz),
     "moe_w8a8_forward": ([_vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _vp, _sz, ctypes.POINTER(MoeDebug), _vp], _i32),
@@ -182,6 +189,55 @@ def linear_w8a8(x, qw, sw, y: torch.Tensor | None = None, ws: torch.Tensor | Non
     _check("linear_w8a8",
            lib().linear_w8a8(_ptr(x), M, K, x.stride(0), _ptr(qw), _ptr(sw), N, qw.stride(0),
                              _ptr(y), y.stride(0), _ptr(ws), wsb, _stream(x.device)))
+    return y
+
+
+def pack_weights(qw: torch.Tensor) -> torch.Tensor:
+    """Row-major int8 [N, K] weights -> the packed MFMA tile layout (same bytes, permuted)."""
+    _req(qw, torch.int8, "qw")
+    N, K = qw.shape
+    out = torch.empty((N * K,), dtype=torch.int8, device=qw.device)
+    _check("w8a8_pack_weights",
+           lib().w8a8_pack_weights(_ptr(qw), N, K, qw.stride(0), _ptr(out), _stream(qw.device)))
+    return out
+
+
+def gemm_w8a8_packed(qa, sa, qw_packed, sw, N: int, y: torch.Tensor | None = None,
+                     ws: torch.Tensor | None = None):
+    """gemm_w8a8 with packed weights (``pack_weights``); N = output channels."""
+    _req(qa, torch.int8, "qa")
+    M, K = qa.shape
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device) if y is None else y
+    ws, wsb = _workspace(lib().gemm_w8a8_workspace_bytes(M, N, K), qa.device, ws)
+    _check("gemm_w8a8_packed",
+           lib().gemm_w8a8_packed(_ptr(qa), _ptr(sa), M, K, qa.stride(0), _ptr(qw_packed),
+                                  _ptr(sw), N, _ptr(y), y.stride(0), _ptr(ws), wsb,
+                                  _stream(qa.device)))
+    return y
+
+
+def gemm_w8a8_packed_i32acc(qa, qw_packed, N: int, acc: torch.Tensor | None = None,
+                            ws: torch.Tensor | None = None):
+    _req(qa, torch.int8, "qa")
+    M, K = qa.shape
+    acc = torch.empty((M, N), dtype=torch.int32, device=qa.device) if acc is None else acc
+    ws, wsb = _workspace(lib().gemm_w8a8_workspace_bytes(M, N, K), qa.device, ws)
+    _check("gemm_w8a8_packed_i32acc",
+           lib().gemm_w8a8_packed_i32acc(_ptr(qa), M, K, qa.stride(0), _ptr(qw_packed), N,
+                                         _ptr(acc), acc.stride(0), _ptr(ws), wsb,
+                                         _stream(qa.device)))
+    return acc
+
+
+def linear_w8a8_packed(x, qw_packed, sw, N: int, y: torch.Tensor | None = None,
+                       ws: torch.Tensor | None = None):
+    _req(x, torch.bfloat16, "x")
+    M, K = x.shape
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    ws, wsb = _workspace(linear_w8a8_workspace_bytes(M, N, K), x.device, ws)
+    _check("linear_w8a8_packed",
+           lib().linear_w8a8_packed(_ptr(x), M, K, x.stride(0), _ptr(qw_packed), _ptr(sw), N,
+                                    _ptr(y), y.stride(0), _ptr(ws), wsb, _stream(x.device)))
     return y
 
 

@@ -58,11 +58,68 @@ int check_gemm_shape(int64_t M, int64_t K, int64_t lda, int64_t N, int64_t ldw, 
 }
 
 int dispatch_gemm(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t lda,
-                  const int8_t* qw, const float* sw, int64_t N, int64_t ldw, uint16_t* y,
-                  int64_t ldy, hipStream_t st) {
-  hipError_t e = (M <= 16) ? launch_gemm_skinny(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy, st)
-                           : launch_gemm_tile(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy, st);
+                  const int8_t* qw, const float* sw, int64_t N, int64_t ldw, bool packed,
+                  uint16_t* y, int64_t ldy, hipStream_t st) {
+  hipError_t e =
+      (M <= 16) ? launch_gemm_skinny(qa, sa, M, K, lda, qw, sw, N, ldw, packed, y, ldy, st)
+                : launch_gemm_tile(qa, sa, M, K, lda, qw, sw, N, ldw, packed, y, ldy, st);
   return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+int dispatch_gemm_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda, const int8_t* qw,
+                      int64_t N, int64_t ldw, bool packed, int32_t* acc, int64_t ldacc,
+                      hipStream_t st) {
+  hipError_t e =
+      (M <= 16) ? launch_gemm_skinny_i32(qa, M, K, lda, qw, N, ldw, packed, acc, ldacc, st)
+                : launch_gemm_tile_i32(qa, M, K, lda, qw, N, ldw, packed, acc, ldacc, st);
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+int gemm_common(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t lda,
+                const int8_t* qw, const float* sw, int64_t N, int64_t ldw, bool packed,
+                uint16_t* y, int64_t ldy, size_t ws_bytes, void* stream) {
+  int r = check_gemm_shape(M, K, lda, N, ldw, ldy);
+  if (r != W8A8_OK) return r;
+  if (M == 0) return W8A8_OK;
+  if (!qa || !sa || !qw || !sw || !y) return W8A8_INVALID_ARG;
+  if (!al16(qa) || !al16(qw) || !al4(sa) || !al4(sw) || !al4(y) || ldy % 2 != 0)
+    return W8A8_MISALIGNED;
+  if (ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  if ((r = check_device()) != W8A8_OK) return r;
+  return dispatch_gemm(qa, sa, M, K, lda, qw, sw, N, ldw, packed, y, ldy, as_stream(stream));
+}
+
+int gemm_i32_common(const int8_t* qa, int64_t M, int64_t K, int64_t lda, const int8_t* qw,
+                    int64_t N, int64_t ldw, bool packed, int32_t* acc, int64_t ldacc,
+                    size_t ws_bytes, void* stream) {
+  int r = check_gemm_shape(M, K, lda, N, ldw, ldacc);
+  if (r != W8A8_OK) return r;
+  if (M == 0) return W8A8_OK;
+  if (!qa || !qw || !acc) return W8A8_INVALID_ARG;
+  if (!al16(qa) || !al16(qw) || !al4(acc)) return W8A8_MISALIGNED;
+  if (ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  if ((r = check_device()) != W8A8_OK) return r;
+  return dispatch_gemm_i32(qa, M, K, lda, qw, N, ldw, packed, acc, ldacc, as_stream(stream));
+}
+
+int linear_common(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* qw,
+                  const float* sw, int64_t N, int64_t ldw, bool packed, uint16_t* y,
+                  int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  int r = check_gemm_shape(M, K, ldx, N, ldw, ldy);
+  if (r != W8A8_OK) return r;
+  if (M == 0) return W8A8_OK;
+  if (!x || !qw || !sw || !y) return W8A8_INVALID_ARG;
+  if (!al16(x) || !al16(qw) || !al4(sw) || !al4(y) || ldy % 2 != 0 || ldx % 16 != 0)
+    return W8A8_MISALIGNED;
+  if (ws_bytes < linear_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  if (!ws || !al16(ws)) return ws ? W8A8_MISALIGNED : W8A8_INVALID_ARG;
+  if ((r = check_device()) != W8A8_OK) return r;
+  hipStream_t st = as_stream(stream);
+  int8_t* q = static_cast<int8_t*>(ws);
+  float* s = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * (size_t)K));
+  hipError_t e = launch_quant_rows(x, 0, M, K, ldx, q, K, s, st);
+  if (e != hipSuccess) return hip_fail(e);
+  return dispatch_gemm(q, s, M, K, K, qw, sw, N, ldw, packed, y, ldy, st);
 }
 
 }  // namespace
@@ -106,32 +163,14 @@ int gemm_w8a8(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t l
               const int8_t* qw, const float* sw, int64_t N, int64_t ldw, uint16_t* y,
               int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
-  int r = check_gemm_shape(M, K, lda, N, ldw, ldy);
-  if (r != W8A8_OK) return r;
-  if (M == 0) return W8A8_OK;
-  if (!qa || !sa || !qw || !sw || !y) return W8A8_INVALID_ARG;
-  if (!al16(qa) || !al16(qw) || !al4(sa) || !al4(sw) || !al4(y) || ldy % 2 != 0)
-    return W8A8_MISALIGNED;
-  if (ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
-  if ((r = check_device()) != W8A8_OK) return r;
-  return dispatch_gemm(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy, as_stream(stream));
+  return gemm_common(qa, sa, M, K, lda, qw, sw, N, ldw, false, y, ldy, ws_bytes, stream);
 }
 
 int gemm_w8a8_i32acc(const int8_t* qa, int64_t M, int64_t K, int64_t lda, const int8_t* qw,
                      int64_t N, int64_t ldw, int32_t* acc, int64_t ldacc, void* ws,
                      size_t ws_bytes, void* stream) {
   (void)ws;
-  int r = check_gemm_shape(M, K, lda, N, ldw, ldacc);
-  if (r != W8A8_OK) return r;
-  if (M == 0) return W8A8_OK;
-  if (!qa || !qw || !acc) return W8A8_INVALID_ARG;
-  if (!al16(qa) || !al16(qw) || !al4(acc)) return W8A8_MISALIGNED;
-  if (ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
-  if ((r = check_device()) != W8A8_OK) return r;
-  hipStream_t st = as_stream(stream);
-  hipError_t e = (M <= 16) ? launch_gemm_skinny_i32(qa, M, K, lda, qw, N, ldw, acc, ldacc, st)
-                           : launch_gemm_tile_i32(qa, M, K, lda, qw, N, ldw, acc, ldacc, st);
-  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+  return gemm_i32_common(qa, M, K, lda, qw, N, ldw, false, acc, ldacc, ws_bytes, stream);
 }
 
 size_t linear_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -143,20 +182,41 @@ size_t linear_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 int linear_w8a8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* qw,
                 const float* sw, int64_t N, int64_t ldw, uint16_t* y, int64_t ldy, void* ws,
                 size_t ws_bytes, void* stream) {
-  int r = check_gemm_shape(M, K, ldx, N, ldw, ldy);
+  return linear_common(x, M, K, ldx, qw, sw, N, ldw, false, y, ldy, ws, ws_bytes, stream);
+}
+
+int w8a8_pack_weights(const int8_t* qw, int64_t N, int64_t K, int64_t ldw, int8_t* qw_packed,
+                      void* stream) {
+  if (N < 0 || K <= 0 || ldw < K) return W8A8_INVALID_ARG;
+  if (N % 16 != 0 || K % 64 != 0 || K > 131072 || N > (int64_t)1 << 30)
+    return W8A8_UNSUPPORTED_SHAPE;
+  if (N == 0) return W8A8_OK;
+  if (!qw || !qw_packed) return W8A8_INVALID_ARG;
+  if (!al16(qw) || !al16(qw_packed) || ldw % 16 != 0) return W8A8_MISALIGNED;
+  int r = check_device();
   if (r != W8A8_OK) return r;
-  if (M == 0) return W8A8_OK;
-  if (!x || !qw || !sw || !y) return W8A8_INVALID_ARG;
-  if (!al16(x) || !al16(qw) || !al4(sw) || !al4(y) || ldy % 2 != 0) return W8A8_MISALIGNED;
-  if (ws_bytes < linear_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
-  if (!ws || !al16(ws)) return ws ? W8A8_MISALIGNED : W8A8_INVALID_ARG;
-  if ((r = check_device()) != W8A8_OK) return r;
-  hipStream_t st = as_stream(stream);
-  int8_t* q = static_cast<int8_t*>(ws);
-  float* s = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * (size_t)K));
-  hipError_t e = launch_quant_rows(x, 0, M, K, ldx, q, K, s, st);
-  if (e != hipSuccess) return hip_fail(e);
-  return dispatch_gemm(q, s, M, K, K, qw, sw, N, ldw, y, ldy, st);
+  hipError_t e = launch_pack_weights(qw, N, K, ldw, qw_packed, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+int gemm_w8a8_packed(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t lda,
+                     const int8_t* qw_packed, const float* sw, int64_t N, uint16_t* y,
+                     int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  return gemm_common(qa, sa, M, K, lda, qw_packed, sw, N, K, true, y, ldy, ws_bytes, stream);
+}
+
+int gemm_w8a8_packed_i32acc(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
+                            const int8_t* qw_packed, int64_t N, int32_t* acc, int64_t ldacc,
+                            void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  return gemm_i32_common(qa, M, K, lda, qw_packed, N, K, true, acc, ldacc, ws_bytes, stream);
+}
+
+int linear_w8a8_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                       const int8_t* qw_packed, const float* sw, int64_t N, uint16_t* y,
+                       int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  return linear_common(x, M, K, ldx, qw_packed, sw, N, K, true, y, ldy, ws, ws_bytes, stream);
 }
 
 size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int topk) {

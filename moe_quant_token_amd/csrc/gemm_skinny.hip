@@ -7,9 +7,16 @@
 //
 // At M <= 16 every weight byte is used once, so the kernel is bound by HBM
 // reads of the [N, K] int8 weights.  Each workgroup owns 16 output channels
-// (one 16x16x64 MFMA column tile) and splits K across its waves, so there is
-// no cross-workgroup reduction and no workspace: the int32 partials of the
-// waves are summed exactly through LDS and the fp32 epilogue runs in-register.
+// (one 16x16x64 MFMA column tile).  Its 16 waves take the tile's 64-byte k
+// steps round-robin (wave w: steps w, w+16, ...), so at any moment the
+// workgroup streams one contiguous stretch of the tile; every wave keeps four
+// 1 KiB weight loads in flight.  The waves' int32 partial sums are added
+// exactly through LDS and the fp32 epilogue runs in registers: no workspace
+// and no cross-workgroup traffic.
+//
+// Weight layouts: row-major [N, K], or the packed tile layout (see pack.hip)
+// in which each 16-row x 64-byte MFMA operand tile is one contiguous 1 KiB
+// block, so every wave-wide load reads 1 KiB of consecutive bytes.
 //
 // MFMA operand mapping (v_mfma_i32_16x16x64_i8): lane l supplies 16 bytes of
 // A row (l % 16) and of B column (l % 16) for k-slice (l / 16); the same
@@ -20,7 +27,7 @@
 
 namespace w8a8 {
 
-template <int WAVES, int UNROLL, bool STORE_I32>
+template <int WAVES, int U, bool PACKED, bool STORE_I32>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, int M, int K, int64_t lda,
     const int8_t* __restrict__ qw, const float* __restrict__ sw, int64_t ldw,
@@ -30,44 +37,37 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
   const int wv = threadIdx.x >> 6;
   const int j = lane & 15;  // A row (token) / B column (output channel)
   const int g = lane >> 4;  // 16-byte k-slice inside a 64-wide k step
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-
+  const int64_t tile = blockIdx.x;
   const int nchunk = K >> 6;  // 64-wide k steps
-  const int per = (nchunk + WAVES - 1) / WAVES;
-  const int c_begin = wv * per;
-  const int c_end = min(nchunk, c_begin + per);
 
-  const int8_t* wp = qw + (n0 + j) * ldw + g * 16;
+  const int8_t* wp = PACKED ? qw + tile * nchunk * 1024 + lane * 16
+                            : qw + (tile * 16 + j) * ldw + g * 16;
+  constexpr int64_t wstep = PACKED ? 1024 : 64;
   const bool a_ok = j < M;
   const int8_t* ap = qa + (int64_t)(a_ok ? j : 0) * lda + g * 16;
 
   v4i acc = {0, 0, 0, 0};
-  for (int c = c_begin; c < c_end; c += UNROLL) {
-    v4i b[UNROLL], a[UNROLL];
+  for (int c0 = wv; c0 < nchunk; c0 += WAVES * U) {
+    v4i b[U], a[U];
 #pragma unroll
-    for (int u = 0; u < UNROLL; u++) {
-      const int cc = c + u;
-      if (cc < c_end) {
-        b[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + (int64_t)cc * 64));
-        a[u] = a_ok ? *reinterpret_cast<const v4i*>(ap + (int64_t)cc * 64) : v4i{0, 0, 0, 0};
-      } else {
-        b[u] = v4i{0, 0, 0, 0};
-        a[u] = v4i{0, 0, 0, 0};
-      }
+    for (int u = 0; u < U; u++) {
+      const int c = c0 + u * WAVES;
+      const bool in = c < nchunk;
+      b[u] = in ? *reinterpret_cast<const v4i*>(wp + c * wstep) : v4i{0, 0, 0, 0};
+      a[u] = (in && a_ok) ? *reinterpret_cast<const v4i*>(ap + (int64_t)c * 64)
+                          : v4i{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < UNROLL; u++) acc = mfma_16x16x64_i8(a[u], b[u], acc);
+    for (int u = 0; u < U; u++) acc = mfma_16x16x64_i8(a[u], b[u], acc);
   }
 
-  if (WAVES > 1) {
-    red[wv][lane] = acc;
-    __syncthreads();
-    if (wv != 0) return;
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv != 0) return;
 #pragma unroll
-    for (int w = 1; w < WAVES; w++) acc += red[w][lane];
-  }
+  for (int w = 1; w < WAVES; w++) acc += red[w][lane];
 
-  const int64_t n = n0 + j;
+  const int64_t n = tile * 16 + j;
 #pragma unroll
   for (int v = 0; v < 4; v++) {
     const int m = 4 * g + v;
@@ -83,34 +83,32 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
   }
 }
 
-template <bool STORE_I32>
+template <bool PACKED, bool STORE_I32>
 static hipError_t launch_skinny_impl(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                                      int64_t lda, const int8_t* qw, const float* sw, int64_t N,
                                      int64_t ldw, void* out, int64_t ldo, hipStream_t stream) {
-  dim3 grid((unsigned)(N / 16));
-  // Many workgroups already (N/16 >= 512): four waves; few: eight waves to keep
-  // more loads in flight per workgroup.
-  if (N / 16 >= 512) {
-    hipLaunchKernelGGL((k_gemm_skinny<4, 4, STORE_I32>), grid, dim3(256), 0, stream, qa, sa,
-                       (int)M, (int)K, lda, qw, sw, ldw, out, ldo);
-  } else {
-    hipLaunchKernelGGL((k_gemm_skinny<8, 4, STORE_I32>), grid, dim3(512), 0, stream, qa, sa,
-                       (int)M, (int)K, lda, qw, sw, ldw, out, ldo);
-  }
+  hipLaunchKernelGGL((k_gemm_skinny<16, 4, PACKED, STORE_I32>), dim3((unsigned)(N / 16)),
+                     dim3(1024), 0, stream, qa, sa, (int)M, (int)K, lda, qw, sw, ldw, out, ldo);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_skinny(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                               int64_t lda, const int8_t* qw, const float* sw, int64_t N,
-                              int64_t ldw, uint16_t* y, int64_t ldy, hipStream_t stream) {
-  return launch_skinny_impl<false>(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy, stream);
+                              int64_t ldw, bool packed, uint16_t* y, int64_t ldy,
+                              hipStream_t stream) {
+  return packed ? launch_skinny_impl<true, false>(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy,
+                                                  stream)
+                : launch_skinny_impl<false, false>(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy,
+                                                   stream);
 }
 
 hipError_t launch_gemm_skinny_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
-                                  const int8_t* qw, int64_t N, int64_t ldw, int32_t* acc,
-                                  int64_t ldacc, hipStream_t stream) {
-  return launch_skinny_impl<true>(qa, nullptr, M, K, lda, qw, nullptr, N, ldw, acc, ldacc,
-                                  stream);
+                                  const int8_t* qw, int64_t N, int64_t ldw, bool packed,
+                                  int32_t* acc, int64_t ldacc, hipStream_t stream) {
+  return packed ? launch_skinny_impl<true, true>(qa, nullptr, M, K, lda, qw, nullptr, N, ldw,
+                                                 acc, ldacc, stream)
+                : launch_skinny_impl<false, true>(qa, nullptr, M, K, lda, qw, nullptr, N, ldw,
+                                                  acc, ldacc, stream);
 }
 
 }  // namespace w8a8

@@ -10,19 +10,25 @@ namespace w8a8 {
 hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                              int8_t* q, int64_t ldq, float* s, hipStream_t stream);
 
+// `packed`: weights in the MFMA tile layout of pack.hip instead of row-major.
+hipError_t launch_pack_weights(const int8_t* qw, int64_t N, int64_t K, int64_t ldw,
+                               int8_t* out, hipStream_t stream);
+
 hipError_t launch_gemm_skinny(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                               int64_t lda, const int8_t* qw, const float* sw, int64_t N,
-                              int64_t ldw, uint16_t* y, int64_t ldy, hipStream_t stream);
+                              int64_t ldw, bool packed, uint16_t* y, int64_t ldy,
+                              hipStream_t stream);
 hipError_t launch_gemm_skinny_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
-                                  const int8_t* qw, int64_t N, int64_t ldw, int32_t* acc,
-                                  int64_t ldacc, hipStream_t stream);
+                                  const int8_t* qw, int64_t N, int64_t ldw, bool packed,
+                                  int32_t* acc, int64_t ldacc, hipStream_t stream);
 
 hipError_t launch_gemm_tile(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                             int64_t lda, const int8_t* qw, const float* sw, int64_t N,
-                            int64_t ldw, uint16_t* y, int64_t ldy, hipStream_t stream);
+                            int64_t ldw, bool packed, uint16_t* y, int64_t ldy,
+                            hipStream_t stream);
 hipError_t launch_gemm_tile_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
-                                const int8_t* qw, int64_t N, int64_t ldw, int32_t* acc,
-                                int64_t ldacc, hipStream_t stream);
+                                const int8_t* qw, int64_t N, int64_t ldw, bool packed,
+                                int32_t* acc, int64_t ldacc, hipStream_t stream);
 
 // Routed MoE.  Workspace layout is owned by moe.hip.
 struct MoeArgs {

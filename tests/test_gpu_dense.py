@@ -82,21 +82,47 @@ GEMM_SHAPES = [
 ]
 
 
+def _packed_ref(qw):
+    """The packed tile layout by array reshaping (marshalling only)."""
+    N, K = qw.shape
+    return np.ascontiguousarray(qw.reshape(N // 16, 16, K // 64, 4, 16)
+                                .transpose(0, 2, 3, 1, 4)).reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(16, 64), (48, 640), (17408, 5120)])
+def test_pack_weights_layout(N, K):
+    r = np.random.default_rng(N)
+    qw = r.integers(-127, 128, (N, K)).astype(np.int8)
+    big = torch.zeros((N, K + 64), dtype=torch.int8, device=DEV)
+    big[:, :K] = dev(qw)
+    packed = mq.pack_weights(big[:, :K])
+    np.testing.assert_array_equal(host(packed), _packed_ref(qw))
+
+
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("M,K,N", GEMM_SHAPES)
-def test_gemm_i32_and_bf16(orc, M, K, N):
-    say(f"gemm M={M} K={K} N={N}")
+def test_gemm_i32_and_bf16(orc, M, K, N, packed):
+    say(f"gemm M={M} K={K} N={N} packed={packed}")
     x, W = _inputs((9, M), (9, N), M, K, N, 4, 20.0)
     qa, sa = orc.quant_rows(x)
     qw, sw = orc.quant_rows(W)
     acc_ref = orc.gemm_i32(qa, qw)
     y_ref = orc.gemm_w8a8(qa, sa, qw, sw)
     qa_d, sa_d, qw_d, sw_d = dev(qa), dev(sa), dev(qw), dev(sw)
-    acc = mq.gemm_w8a8_i32acc(qa_d, qw_d)
-    y = mq.gemm_w8a8(qa_d, sa_d, qw_d, sw_d)
+    if packed:
+        qp = mq.pack_weights(qw_d)
+        acc = mq.gemm_w8a8_packed_i32acc(qa_d, qp, N)
+        y = mq.gemm_w8a8_packed(qa_d, sa_d, qp, sw_d, N)
+        y2 = mq.linear_w8a8_packed(bf16_dev(x), qp, sw_d, N)
+    else:
+        acc = mq.gemm_w8a8_i32acc(qa_d, qw_d)
+        y = mq.gemm_w8a8(qa_d, sa_d, qw_d, sw_d)
+        y2 = mq.linear_w8a8(bf16_dev(x), qw_d, sw_d)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(acc), acc_ref)
     mism = assert_bf16_close(bf16_host(y), y_ref, "gemm_w8a8")
     assert mism == 0
+    np.testing.assert_array_equal(bf16_host(y2), y_ref)
 
 
 def test_gemm_extreme_codes_no_overflow():
@@ -132,7 +158,7 @@ def test_gemm_strided_output_and_inputs(orc):
 # ------------------------------------------------------ decode, full size
 @pytest.mark.parametrize("shape_idx", [0, 1])
 def test_decode_linear_full(orc, shape_idx):
-    for M in synth.DECODE_M:
+    for M in synth.DECODE_M + [16]:
         cfg = synth.decode_linear(M, shape_idx)
         say(f"decode linear {cfg['name']} M={M} K={cfg['K']} N={cfg['N']}")
         if M == 1:
@@ -140,11 +166,14 @@ def test_decode_linear_full(orc, shape_idx):
             qw, sw = orc.quant_rows(W)
             del W
             qw_d, sw_d = dev(qw), dev(sw)
+            qp_d = mq.pack_weights(qw_d)
         x = synth.activations(cfg["xkey"], M, cfg["K"], cfg["n_outliers"], cfg["outlier_scale"])
         y_ref = orc.linear_w8a8(x, qw, sw)
         y = mq.linear_w8a8(bf16_dev(x), qw_d, sw_d)
+        yp = mq.linear_w8a8_packed(bf16_dev(x), qp_d, sw_d, cfg["N"])
         torch.cuda.synchronize()
         assert assert_bf16_close(bf16_host(y), y_ref, "linear_w8a8") == 0
+        assert assert_bf16_close(bf16_host(yp), y_ref, "linear_w8a8_packed") == 0
 
 
 # ----------------------------------------------------- prefill, full size
@@ -162,9 +191,10 @@ def test_prefill_full_sampled(orc, N):
     q_d, s_d = mq.quant_per_token_i8(x_d)
     np.testing.assert_array_equal(host(s_d), sa)
     assert np.array_equal(host(q_d), qa)
-    y = mq.gemm_w8a8(q_d, s_d, qw_d, sw_d)
+    qp_d = mq.pack_weights(qw_d)
+    y = mq.gemm_w8a8_packed(q_d, s_d, qp_d, sw_d, N)
     y2 = mq.linear_w8a8(x_d, qw_d, sw_d)
-    acc = mq.gemm_w8a8_i32acc(q_d, qw_d)
+    acc = mq.gemm_w8a8_packed_i32acc(q_d, qp_d, N)
     torch.cuda.synchronize()
     r = np.random.default_rng(N)
     ms = np.concatenate([r.integers(0, M, 4000), np.full(N // 64, M - 1), np.arange(0, M, 64)])
