@@ -46,6 +46,11 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// activation codes in the workspace: rows rounded up to whole 16-row tiles
+size_t act_codes_bytes(int64_t M, int64_t K) {
+  return align_up((size_t)((M + 15) / 16 * 16) * (size_t)K);
+}
+
 // Shape rules shared by gemm_w8a8, gemm_w8a8_i32acc and linear_w8a8.
 int check_gemm_shape(int64_t M, int64_t K, int64_t lda, int64_t N, int64_t ldw, int64_t ldo) {
   if (M < 0 || K <= 0 || N <= 0) return W8A8_INVALID_ARG;
@@ -116,7 +121,15 @@ int linear_common(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const in
   if ((r = check_device()) != W8A8_OK) return r;
   hipStream_t st = as_stream(stream);
   int8_t* q = static_cast<int8_t*>(ws);
-  float* s = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)M * (size_t)K));
+  float* s = reinterpret_cast<float*>(static_cast<char*>(ws) + act_codes_bytes(M, K));
+  if (packed && M > 16) {
+    // prefill: activation codes in the packed tile layout too, so both
+    // operands stream as contiguous 1 KiB blocks
+    hipError_t e = launch_quant_rows_packed(x, M, K, ldx, q, s, st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_gemm_tile_apacked(q, s, M, K, qw, sw, N, y, ldy, st);
+    return e == hipSuccess ? W8A8_OK : hip_fail(e);
+  }
   hipError_t e = launch_quant_rows(x, 0, M, K, ldx, q, K, s, st);
   if (e != hipSuccess) return hip_fail(e);
   return dispatch_gemm(q, s, M, K, K, qw, sw, N, ldw, packed, y, ldy, st);
@@ -175,8 +188,7 @@ int gemm_w8a8_i32acc(const int8_t* qa, int64_t M, int64_t K, int64_t lda, const 
 
 size_t linear_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || K <= 0) return 0;
-  return align_up((size_t)M * (size_t)K) + align_up((size_t)M * 4) +
-         gemm_w8a8_workspace_bytes(M, N, K);
+  return act_codes_bytes(M, K) + align_up((size_t)M * 4) + gemm_w8a8_workspace_bytes(M, N, K);
 }
 
 int linear_w8a8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* qw,

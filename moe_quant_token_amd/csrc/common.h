@@ -9,6 +9,7 @@ namespace w8a8 {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
@@ -46,6 +47,14 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 
 __device__ __forceinline__ v4i mfma_16x16x64_i8(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// 32x32x32 int8 MFMA.  On gfx950 it issues at twice the rate of the 16x16x64
+// form for the same work.  Operands: lane l supplies 16 bytes of A row (l % 32)
+// and of B column (l % 32) for k-slice (l / 32) of the 32-wide k step.
+// Result lane l holds column l % 32, rows 8*(r/4) + 4*(l/32) + r%4, r < 16.
+__device__ __forceinline__ v16i mfma_32x32x32_i8(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
 // Pack four int8 codes (values in [-127, 127]) into one 32-bit word.

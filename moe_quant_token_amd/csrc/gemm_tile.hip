@@ -6,12 +6,15 @@
 // activations per token x int8 weights per channel, fp32 scales, bf16 out);
 // its Performance section notes that prefill is compute-bound.
 //
-// Both operands are K-contiguous, the native operand order of
-// v_mfma_i32_16x16x64_i8 (each lane feeds 16 consecutive k bytes of one row).
+// Both operands are K-contiguous, the native operand order of the int8 MFMAs
+// (each lane feeds 16 consecutive k bytes of one row).  The compute uses
+// v_mfma_i32_32x32x32_i8, which on gfx950 does the same work as the 16x16x64
+// form at twice the issue rate.
 // Every 64-byte k step the workgroup stages a BM x 64 activation tile and a
-// BN x 64 weight tile in LDS as 1 KiB blocks in MFMA lane order (16 rows x 4
-// k-slices, lane l's 16 bytes at offset 16*l), so the operand reads are
-// consecutive 16-byte LDS reads with no bank conflicts and no swizzle.  A wave
+// BN x 64 weight tile in LDS as 1 KiB blocks of 16 rows x 4 k-slices (slot
+// j + 16*s holds row j, k bytes 16s..16s+15).  A 32x32x32 operand fragment
+// (32 rows, one 32-byte k half) is then four runs of 256 consecutive bytes,
+// read without bank conflicts and without a swizzle.  A wave
 // fetches one block per global load: 16 rows x 64 bytes for row-major
 // operands, or 1 KiB of consecutive bytes for packed weights (pack.hip).
 //
@@ -39,8 +42,11 @@ constexpr int kXcds = 8;
 // 15:14, expcnt at 6:4, lgkmcnt at 11:8).
 constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MODE, bool BPACKED>
-__global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void k_gemm_tile(
+// MINB: workgroups that must fit on one CU at once (the register budget the
+// compiler gets follows from it).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MODE, bool BPACKED,
+          bool APACKED = false, int KSUB = 1, int MINB = 1>
+__global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, int M, int K, int64_t lda,
     const int8_t* __restrict__ qw, const float* __restrict__ sw, int N, int64_t ldw,
     void* __restrict__ out, int64_t ldo, int tiles_m, int tiles_n, int group_m,
@@ -48,13 +54,15 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void k_gemm_tile(
   constexpr int W = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M;  // rows of the wave tile
   constexpr int WN = BN / WAVES_N;  // columns of the wave tile
-  constexpr int TM = WM / 16;
-  constexpr int TN = WN / 16;
+  constexpr int TM = WM / 32;       // 32x32 MFMA blocks per wave
+  constexpr int TN = WN / 32;
   constexpr int NA = BM / 16;  // 1 KiB blocks per k step
   constexpr int NB = BN / 16;
-  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
 
-  constexpr int STAGE_BYTES = (NA + NB) * 1024;
+  // a pipeline step covers KSUB 64-byte k chunks
+  constexpr int CHUNK_BYTES = (NA + NB) * 1024;
+  constexpr int STAGE_BYTES = KSUB * CHUNK_BYTES;
   __shared__ __attribute__((aligned(1024))) int8_t smem[NSTAGE * STAGE_BYTES];
 
   // ---- tile selection: XCD-contiguous ranges, then row groups
@@ -79,7 +87,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void k_gemm_tile(
   const int wn = wv % WAVES_N;
   const int j = lane & 15;
   const int g = lane >> 4;
-  const int nk = K >> 6;
+  const int nk = K >> 6;          // 64-byte k chunks
+  const int nsteps = nk / KSUB;   // pipeline steps (K % (64 * KSUB) == 0)
   const int ntile_n = N >> 4;
 
   // per-wave block assignment: wave wv loads A blocks wv, wv+W, ... (< NA) and
@@ -90,10 +99,15 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void k_gemm_tile(
   constexpr int BSTEP = BPACKED ? 1024 : 64;
   const int8_t* srcA[LA];
   const int8_t* srcB[LB];
+  constexpr int ASTEP = APACKED ? 1024 : 64;
+  const int ntile_m = (M + 15) >> 4;
 #pragma unroll
   for (int i = 0; i < LA; i++) {
     const int b = min(wv + i * W, NA - 1);
-    srcA[i] = qa + (int64_t)min(m0 + b * 16 + j, M - 1) * lda + g * 16;
+    if (APACKED)
+      srcA[i] = qa + (int64_t)min(m0 / 16 + b, ntile_m - 1) * nk * 1024 + lane * 16;
+    else
+      srcA[i] = qa + (int64_t)min(m0 + b * 16 + j, M - 1) * lda + g * 16;
   }
 #pragma unroll
   for (int i = 0; i < LB; i++) {
@@ -104,109 +118,142 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void k_gemm_tile(
       srcB[i] = qw + (int64_t)min(n0 + b * 16 + j, N - 1) * ldw + g * 16;
   }
 
-  // global -> LDS for k step kt into ring stage st (each wave its own blocks)
-  auto issue = [&](int kt, int st) {
-    int8_t* stage = smem + st * STAGE_BYTES;
+  // global -> LDS for pipeline step ks (KSUB chunks) into ring stage st
+  auto issue = [&](int ks, int st) {
 #pragma unroll
-    for (int i = 0; i < LA; i++)
-      if (NA % W == 0 || wv + i * W < NA)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(srcA[i] + kt * 64),
-            (__attribute__((address_space(3))) void*)(stage + (wv + i * W) * 1024), 16, 0, 0);
+    for (int c = 0; c < KSUB; c++) {
+      const int kt = ks * KSUB + c;
+      int8_t* stage = smem + st * STAGE_BYTES + c * CHUNK_BYTES;
 #pragma unroll
-    for (int i = 0; i < LB; i++)
-      if (NB % W == 0 || wv + i * W < NB)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(srcB[i] + kt * BSTEP),
-            (__attribute__((address_space(3))) void*)(stage + (NA + wv + i * W) * 1024), 16, 0,
-            0);
+      for (int i = 0; i < LA; i++)
+        if (NA % W == 0 || wv + i * W < NA)
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(srcA[i] + kt * ASTEP),
+              (__attribute__((address_space(3))) void*)(stage + (wv + i * W) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < LB; i++)
+        if (NB % W == 0 || wv + i * W < NB)
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(srcB[i] + kt * BSTEP),
+              (__attribute__((address_space(3))) void*)(stage + (NA + wv + i * W) * 1024), 16,
+              0, 0);
+    }
   };
   // loads every wave issues per k step, at least (waves 0.. may issue one
   // more of each operand when W does not divide the block counts); waiting
   // on this lower bound is conservative for the waves that issue more
-  constexpr int PER_STEP_MIN = NA / W + NB / W;
+  constexpr int PER_STEP_MIN = KSUB * (NA / W + NB / W);
   static_assert(PER_STEP_MIN >= 1, "every wave must load at least one block per step");
+  static_assert(NSTAGE >= 2, "the pipeline needs at least two stages");
 
-  v4i acc[TM][TN];
+  v16i acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; i++)
 #pragma unroll
-    for (int n = 0; n < TN; n++) acc[i][n] = v4i{0, 0, 0, 0};
-  long long ts[MODE == kEpiG256 ? TM : 1][MODE == kEpiG256 ? TN : 1][4];
+    for (int n = 0; n < TN; n++) acc[i][n] = v16i{0};
+  long long ts[MODE == kEpiG256 ? TM : 1][MODE == kEpiG256 ? TN : 1][16];
   if (MODE == kEpiG256) {
 #pragma unroll
     for (int i = 0; i < TM; i++)
 #pragma unroll
       for (int n = 0; n < TN; n++)
 #pragma unroll
-        for (int v = 0; v < 4; v++) ts[i][n][v] = 0;
+        for (int v = 0; v < 16; v++) ts[i][n][v] = 0;
   }
   const int G = K >> 8;
 
-  auto compute = [&](int st, int kt) {
-    const int8_t* stage = smem + st * STAGE_BYTES;
-    v4i fa[TM], fb[TN];
+  // Operand fragments of one 32-byte k half: LDS -> registers.  Lane l reads
+  // row (l % 32) of a 32-row block, k-slice 2h + l/32: 16-row block
+  // (l % 32) / 16, slot (l % 16) + 16 * (2h + l/32).
+  const int frag_off = ((lane >> 4) & 1) * 1024 + ((lane & 15) + 16 * (lane >> 5)) * 16;
+  // One k step: every fragment of both 32-byte halves is read first, then
+  // the MFMAs run; the scheduling groups keep the compiler from interleaving
+  // a wait for each read into the MFMA stream (one wave per SIMD has nothing
+  // else to hide LDS latency with).
+  auto k_step = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < TM; i++)
-      fa[i] = *reinterpret_cast<const v4i*>(stage + (wm * TM + i) * 1024 + lane * 16);
+    for (int c = 0; c < KSUB; c++) {
+      const int8_t* stage = smem + st * STAGE_BYTES + c * CHUNK_BYTES + frag_off;
+      v4i fa[2][TM], fb[2][TN];
 #pragma unroll
-    for (int n = 0; n < TN; n++)
-      fb[n] = *reinterpret_cast<const v4i*>(stage + (NA + wn * TN + n) * 1024 + lane * 16);
+      for (int h = 0; h < 2; h++) {
 #pragma unroll
-    for (int i = 0; i < TM; i++)
+        for (int i = 0; i < TM; i++)
+          fa[h][i] = *reinterpret_cast<const v4i*>(stage + h * 512 + (wm * TM + i) * 2048);
 #pragma unroll
-      for (int n = 0; n < TN; n++) acc[i][n] = mfma_16x16x64_i8(fa[i], fb[n], acc[i][n]);
+        for (int n = 0; n < TN; n++)
+          fb[h][n] = *reinterpret_cast<const v4i*>(stage + h * 512 +
+                                                   (NA + (wn * TN + n) * 2) * 1024);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+          for (int n = 0; n < TN; n++)
+            acc[i][n] = mfma_32x32x32_i8(fa[h][i], fb[h][n], acc[i][n]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN, 0);    // MFMAs
+    }
+  };
+  auto fold_g256 = [&](int kt) {
     if (MODE == kEpiG256 && (kt & 3) == 3) {
 #pragma unroll
       for (int n = 0; n < TN; n++) {
-        const int col = min(n0 + wn * WN + n * 16 + j, N - 1);
+        const int col = min(n0 + wn * WN + n * 32 + (lane & 31), N - 1);
         const long long u8 = su8[(int64_t)col * G + (kt >> 2)];
 #pragma unroll
         for (int i = 0; i < TM; i++) {
 #pragma unroll
-          for (int v = 0; v < 4; v++) ts[i][n][v] += (long long)acc[i][n][v] * u8;
-          acc[i][n] = v4i{0, 0, 0, 0};
+          for (int v = 0; v < 16; v++) ts[i][n][v] += (long long)acc[i][n][v] * u8;
+          acc[i][n] = v16i{0};
         }
       }
     }
   };
-
-  // prologue: steps 0 .. NSTAGE-2 in flight
-#pragma unroll
-  for (int p = 0; p < NSTAGE - 1; p++)
-    if (p < nk) issue(p, p);
-
-  for (int kt = 0; kt < nk; kt++) {
-    // this wave's loads of step kt are done once at most (NSTAGE-2) steps'
-    // worth of newer loads are still outstanding
-    const int newer = min(NSTAGE - 2, nk - 1 - kt);
-    if (newer >= 2)
+  // Steps issued before arrive(kt): 0..NSTAGE-2 by the prologue, then one more
+  // after each earlier arrive: NSTAGE-2 newer steps than kt (fewer near the
+  // end of K).
+  auto arrive = [&](int kt) {
+    const int newer = min(NSTAGE - 2, nsteps - 1 - kt);
+    if (newer >= 3)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PER_STEP_MIN));
+    else if (newer == 2)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER_STEP_MIN));
     else if (newer == 1)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_STEP_MIN));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    // a bare barrier: __syncthreads() would also wait for every outstanding
-    // load (vmcnt(0)), draining the prefetch of the later stages
     __builtin_amdgcn_s_barrier();
-    // the stage that step kt+NSTAGE-1 overwrites was read in step kt-1, which
-    // every wave finished before the barrier above
-    if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1, (kt + NSTAGE - 1) % NSTAGE);
-    compute(kt % NSTAGE, kt);
+  };
+
+  // Pipeline.  Step ks: wait for its blocks (arrive), send the loads of step
+  // ks+NSTAGE-1 into the stage step ks-1 used (every wave finished reading it
+  // before the barrier in arrive), then run step ks.
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; p++)
+    if (p < nsteps) issue(p, p);
+  for (int ks = 0; ks < nsteps; ks++) {
+    arrive(ks);
+    if (ks + NSTAGE - 1 < nsteps) issue(ks + NSTAGE - 1, (ks + NSTAGE - 1) % NSTAGE);
+    k_step(ks % NSTAGE);
+#pragma unroll
+    for (int c = 0; c < KSUB; c++) fold_g256(ks * KSUB + c);
   }
 
-  // epilogue: lane holds rows 4g+v of column j of every 16x16 block
+  // epilogue: lane holds column (lane % 32) of every 32x32 block, rows
+  // 8*(r/4) + 4*(lane/32) + r%4 for r < 16
 #pragma unroll
   for (int n = 0; n < TN; n++) {
-    const int col = n0 + wn * WN + n * 16 + j;
+    const int col = n0 + wn * WN + n * 32 + (lane & 31);
     if (col >= N) continue;
     const float swn = MODE == kEpiBf16 ? sw[col] : 0.0f;
     const float s2f = MODE == kEpiG256 ? __uint_as_float((uint32_t)s2[col] << 16) : 0.0f;
 #pragma unroll
     for (int i = 0; i < TM; i++) {
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int row = m0 + wm * WM + i * 16 + 4 * g + v;
+      for (int v = 0; v < 16; v++) {
+        const int row = m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (row >= M) continue;
         if (MODE == kEpiI32) {
           static_cast<int32_t*>(out)[(int64_t)row * ldo + col] = acc[i][n][v];
@@ -224,11 +271,16 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void k_gemm_tile(
               (uint16_t)f32_to_bf16_bits(rr);
         }
       }
+      // one 32x32 block at a time: keeps the accumulators in AGPRs until
+      // their block is stored, so the epilogue does not raise the kernel's
+      // VGPR count (and with it the workgroups that fit on a CU)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MODE, bool BPACKED>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MODE, bool BPACKED,
+          bool APACKED = false, int KSUB = 1, int MINB = 1>
 hipError_t launch_tile_cfg(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t lda,
                            const int8_t* qw, const float* sw, int64_t N, int64_t ldw, void* out,
                            int64_t ldo, const uint8_t* su8, const uint16_t* s2,
@@ -237,30 +289,41 @@ hipError_t launch_tile_cfg(const int8_t* qa, const float* sa, int64_t M, int64_t
   const int tiles_n = (int)((N + BN - 1) / BN);
   const int group_m = 4;
   dim3 grid((unsigned)(tiles_m * tiles_n)), block(WAVES_M * WAVES_N * 64);
-  hipLaunchKernelGGL((k_gemm_tile<BM, BN, WAVES_M, WAVES_N, NSTAGE, MODE, BPACKED>), grid, block,
-                     0,
+  hipLaunchKernelGGL(
+      (k_gemm_tile<BM, BN, WAVES_M, WAVES_N, NSTAGE, MODE, BPACKED, APACKED, KSUB, MINB>), grid,
+      block,
+      0,
                      stream, qa, sa, (int)M, (int)K, lda, qw, sw, (int)N, ldw, out, ldo, tiles_m,
                      tiles_n, group_m, su8, s2);
   return hipGetLastError();
 }
 
-// Tile shape per problem: large problems use 256-row tiles (256 x 160 when N
-// is a multiple of 160 and 256 x 256 tiles would leave a partial last wave of
-// workgroups, else 256 x 256); small ones 64 x 64 so there are enough tiles.
-template <int MODE, bool BPACKED>
+// Tile shape per problem (measured on MI355X at M=4096, K=5120): 256 x 160
+// when N is a multiple of 160 and 256 x 256 tiles would leave a partial last
+// round of workgroups (N=5120: 512 tiles, two full rounds on 256 CUs), else
+// 256 x 256; small problems 64 x 64 so there are enough tiles.
+template <int MODE, bool BPACKED, bool APACKED = false>
 static hipError_t launch_tile_impl(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                                    int64_t lda, const int8_t* qw, const float* sw, int64_t N,
                                    int64_t ldw, void* out, int64_t ldo, hipStream_t stream) {
   if (M >= 1024 && N >= 1024) {
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     if (N % 160 == 0 && (t256 % 256) != 0 && (t256 % 256) < 192)
-      return launch_tile_cfg<256, 160, 4, 2, 3, MODE, BPACKED>(qa, sa, M, K, lda, qw, sw, N, ldw,
-                                                            out, ldo, nullptr, nullptr, stream);
-    return launch_tile_cfg<256, 256, 4, 2, 3, MODE, BPACKED>(qa, sa, M, K, lda, qw, sw, N, ldw, out,
-                                                          ldo, nullptr, nullptr, stream);
+      return launch_tile_cfg<256, 160, 4, 1, 3, MODE, BPACKED, APACKED, 1, 2>(
+          qa, sa, M, K, lda, qw, sw, N, ldw, out, ldo, nullptr, nullptr, stream);
+    return launch_tile_cfg<256, 256, 4, 2, 4, MODE, BPACKED, APACKED>(
+        qa, sa, M, K, lda, qw, sw, N, ldw, out, ldo, nullptr, nullptr, stream);
   }
-  return launch_tile_cfg<64, 64, 2, 2, 3, MODE, BPACKED>(qa, sa, M, K, lda, qw, sw, N, ldw, out,
-                                                      ldo, nullptr, nullptr, stream);
+  return launch_tile_cfg<64, 64, 2, 2, 4, MODE, BPACKED, APACKED>(qa, sa, M, K, lda, qw, sw, N,
+                                                                  ldw, out, ldo, nullptr,
+                                                                  nullptr, stream);
+}
+
+hipError_t launch_gemm_tile_apacked(const int8_t* qa_packed, const float* sa, int64_t M,
+                                    int64_t K, const int8_t* qw_packed, const float* sw,
+                                    int64_t N, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  return launch_tile_impl<kEpiBf16, true, true>(qa_packed, sa, M, K, K, qw_packed, sw, N, K, y,
+                                                ldy, stream);
 }
 
 hipError_t launch_gemm_tile(const int8_t* qa, const float* sa, int64_t M, int64_t K,
@@ -285,7 +348,7 @@ hipError_t launch_gemm_tile_i32(const int8_t* qa, int64_t M, int64_t K, int64_t 
 hipError_t launch_gemm_g256_tile(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                                  const int8_t* qw, const uint8_t* su8, const uint16_t* s2,
                                  int64_t N, uint16_t* y, int64_t ldy, hipStream_t stream) {
-  return launch_tile_cfg<64, 64, 2, 2, 3, kEpiG256, false>(qa, sa, M, K, K, qw, nullptr, N, K, y,
+  return launch_tile_cfg<64, 64, 2, 2, 4, kEpiG256, false>(qa, sa, M, K, K, qw, nullptr, N, K, y,
                                                         ldy, su8, s2, stream);
 }
 

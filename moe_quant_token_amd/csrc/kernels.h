@@ -10,6 +10,11 @@ namespace w8a8 {
 hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                              int8_t* q, int64_t ldq, float* s, hipStream_t stream);
 
+// Codes written in the packed tile layout of pack.hip (K % 64 == 0; rows up
+// to the next multiple of 16 are left unwritten).
+hipError_t launch_quant_rows_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                    int8_t* q, float* s, hipStream_t stream);
+
 // `packed`: weights in the MFMA tile layout of pack.hip instead of row-major.
 hipError_t launch_pack_weights(const int8_t* qw, int64_t N, int64_t K, int64_t ldw,
                                int8_t* out, hipStream_t stream);
@@ -29,6 +34,10 @@ hipError_t launch_gemm_tile(const int8_t* qa, const float* sa, int64_t M, int64_
 hipError_t launch_gemm_tile_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
                                 const int8_t* qw, int64_t N, int64_t ldw, bool packed,
                                 int32_t* acc, int64_t ldacc, hipStream_t stream);
+// Both operands packed (activations from launch_quant_rows_packed).
+hipError_t launch_gemm_tile_apacked(const int8_t* qa_packed, const float* sa, int64_t M,
+                                    int64_t K, const int8_t* qw_packed, const float* sw,
+                                    int64_t N, uint16_t* y, int64_t ldy, hipStream_t stream);
 
 // Routed MoE.  Workspace layout is owned by moe.hip.
 struct MoeArgs {

@@ -46,14 +46,17 @@ struct Chunk16<float> {
   }
 };
 
-template <typename T>
+// PACKED_OUT: write the codes in the 16-row x 64-byte MFMA tile layout of
+// pack.hip (row m, bytes 16c..16c+15 of k chunk kc go to tile m/16, block kc,
+// slot (m % 16) + 16 * (c % 4)) instead of row-major; ldq is then unused.
+template <typename T, bool PACKED_OUT = false>
 __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int64_t ldx, int K,
                                                     int8_t* __restrict__ q, int64_t ldq,
                                                     float* __restrict__ s) {
   __shared__ float part[4];
   const int64_t row = blockIdx.x;
   const T* xr = x + row * ldx;
-  int8_t* qr = q + row * ldq;
+  int8_t* qr = PACKED_OUT ? nullptr : q + row * ldq;
   const int nchunk = K >> 4;
 
   float amax = 0.0f;
@@ -85,9 +88,22 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int
       w[i] = pack4_i8(c0, c1, c2, c3);
     }
     v4u out = {w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<v4u*>(qr + c * 16) = out;
+    if (PACKED_OUT) {
+      const int64_t off = ((row >> 4) * (int64_t)(K >> 6) + (c >> 2)) * 1024 +
+                          ((row & 15) + 16 * (c & 3)) * 16;
+      *reinterpret_cast<v4u*>(q + off) = out;
+    } else {
+      *reinterpret_cast<v4u*>(qr + c * 16) = out;
+    }
   }
   if (threadIdx.x == 0) s[row] = (amax != 0.0f) ? sc : 0.0f;
+}
+
+hipError_t launch_quant_rows_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                    int8_t* q, float* s, hipStream_t stream) {
+  hipLaunchKernelGGL((k_quant_rows<uint16_t, true>), dim3((unsigned)M), dim3(256), 0, stream, x,
+                     ldx, (int)K, q, (int64_t)0, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
