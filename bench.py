@@ -293,6 +293,7 @@ def moe_cases(torch, np, mq, synth, dev, timer, bf16_dev):
         mq.quant_per_token_i8(a, q=w13[e], s=s13[e])
         b = torch.from_numpy(synth.expert_weights(cfg["wkey"], e, H, I, synth.T_W2)).to(dev)
         mq.quant_per_token_i8(b, q=w2[e], s=s2[e])
+    w13, w2 = mq.pack_moe_weights(w13, w2)  # MFMA tile layout, untimed
     res = {}
     for T in (1, 64, 2048):
         c = synth.moe(T)
@@ -304,7 +305,7 @@ def moe_cases(torch, np, mq, synth, dev, timer, bf16_dev):
         wt = torch.empty((T, k), dtype=torch.float32, device=dev)
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         fn = lambda i: mq.moe_w8a8_forward(x, logits, w13, s13, w2, s2, k, topk_ids=ids,
-                                           topk_w=wt, out=out, ws=ws)
+                                           topk_w=wt, out=out, ws=ws, packed=True)
         for _ in range(3):
             fn(0)
         it = 20 if T < 2048 else 10

@@ -174,6 +174,14 @@ typedef struct moe_w8a8_debug {
 } moe_w8a8_debug;
 
 size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int topk);
+/* Same call with the expert weights in the packed tile layout: w13 packed  */
+/* as one [E*2I, H] matrix and w2 as one [E*H, I] matrix (w8a8_pack_weights). */
+/* Results are identical to moe_w8a8_forward on the unpacked weights.       */
+int moe_w8a8_forward_packed(const uint16_t *x, const float *logits, int64_t T, int64_t H,
+                            int64_t E, int64_t I, int topk, const int8_t *w13_packed,
+                            const float *s13, const int8_t *w2_packed, const float *s2,
+                            int32_t *topk_ids, float *topk_w, uint16_t *out, void *ws,
+                            size_t ws_bytes, const moe_w8a8_debug *dbg, void *stream);
 int moe_w8a8_forward(const uint16_t *x, const float *logits, int64_t T, int64_t H, int64_t E,
                      int64_t I, int topk, const int8_t *w13, const float *s13,
                      const int8_t *w2, const float *s2, int32_t *topk_ids, float *topk_w,

@@ -66,6 +66,8 @@ _SIGS = {
     "moe_w8a8_workspace_bytes": ([_i64, _i64, _i64, _i64, _i32], _sz),
     "moe_w8a8_forward": ([_vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _vp, _sz, ctypes.POINTER(MoeDebug), _vp], _i32),
+    "moe_w8a8_forward_packed": ([_vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _vp, _sz, ctypes.POINTER(MoeDebug), _vp], _i32),
     "fwht128_quant": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp], _i32),
     "fwht128_weight_prep_g256": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp], _i32),
     "gemm_w8a8_g256_workspace_bytes": ([_i64, _i64, _i64], _sz),
@@ -245,10 +247,18 @@ def moe_w8a8_workspace_bytes(T: int, H: int, E: int, I: int, topk: int) -> int:
     return int(lib().moe_w8a8_workspace_bytes(T, H, E, I, topk))
 
 
+def pack_moe_weights(w13: torch.Tensor, w2: torch.Tensor):
+    """Pack [E, 2I, H] and [E, H, I] int8 expert weights into the tile layout."""
+    E, I2, H = w13.shape
+    return (pack_weights(w13.reshape(E * I2, H)).reshape(E, I2, H),
+            pack_weights(w2.reshape(E * H, w2.shape[2])).reshape(w2.shape))
+
+
 def moe_w8a8_forward(x, logits, w13, s13, w2, s2, topk: int, topk_ids=None, topk_w=None,
-                     out=None, ws=None, debug: bool = False):
+                     out=None, ws=None, debug: bool = False, packed: bool = False):
     """Routed int8 MoE layer.  ``logits`` None -> ``topk_ids``/``topk_w`` are inputs.
 
+    ``packed``: w13/w2 come from ``pack_moe_weights`` (shapes unchanged).
     Returns ``out`` (bf16 [T, H]) and, with ``debug``, a dict of intermediates.
     """
     _req(x, torch.bfloat16, "x")
@@ -274,8 +284,8 @@ def moe_w8a8_forward(x, logits, w13, s13, w2, s2, topk: int, topk_ids=None, topk
                      sa2=torch.empty((R,), dtype=torch.float32, device=dev),
                      acc2=torch.empty((R, H), dtype=torch.int32, device=dev))
         dbg_p = ctypes.pointer(MoeDebug(**{k: v.data_ptr() for k, v in dbg_t.items()}))
-    _check("moe_w8a8_forward",
-           lib().moe_w8a8_forward(_ptr(x), _ptr(logits), T, H, E, I, topk, _ptr(w13), _ptr(s13),
+    fn = lib().moe_w8a8_forward_packed if packed else lib().moe_w8a8_forward
+    _check("moe_w8a8_forward", fn(_ptr(x), _ptr(logits), T, H, E, I, topk, _ptr(w13), _ptr(s13),
                                   _ptr(w2), _ptr(s2), _ptr(topk_ids), _ptr(topk_w), _ptr(out),
                                   _ptr(ws), wsb, dbg_p, _stream(dev)))
     if debug:

@@ -236,10 +236,11 @@ size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int 
   return moe_workspace_bytes(T, H, E, I, topk);
 }
 
-int moe_w8a8_forward(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t E,
-                     int64_t I, int topk, const int8_t* w13, const float* s13, const int8_t* w2,
-                     const float* s2, int32_t* topk_ids, float* topk_w, uint16_t* out, void* ws,
-                     size_t ws_bytes, const moe_w8a8_debug* dbg, void* stream) {
+static int moe_common(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t E,
+                      int64_t I, int topk, const int8_t* w13, const float* s13, const int8_t* w2,
+                      const float* s2, int32_t* topk_ids, float* topk_w, uint16_t* out,
+                      void* ws, size_t ws_bytes, const moe_w8a8_debug* dbg, bool packed,
+                      void* stream) {
   if (T < 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0) return W8A8_INVALID_ARG;
   if (H % 64 != 0 || I % 64 != 0 || H > 16384 || I > 4096 || topk > 16 || topk > E ||
       E > 1024 || T * topk > ((int64_t)1 << 24))
@@ -271,6 +272,7 @@ int moe_w8a8_forward(const uint16_t* x, const float* logits, int64_t T, int64_t 
   a.topk_w = topk_w;
   a.out = out;
   a.ws = ws;
+  a.packed = packed;
   if (dbg) {
     a.dbg_qx = dbg->qx;
     a.dbg_sx = dbg->sx;
@@ -282,6 +284,23 @@ int moe_w8a8_forward(const uint16_t* x, const float* logits, int64_t T, int64_t 
   }
   hipError_t e = launch_moe_forward(a, as_stream(stream));
   return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+int moe_w8a8_forward(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t E,
+                     int64_t I, int topk, const int8_t* w13, const float* s13, const int8_t* w2,
+                     const float* s2, int32_t* topk_ids, float* topk_w, uint16_t* out, void* ws,
+                     size_t ws_bytes, const moe_w8a8_debug* dbg, void* stream) {
+  return moe_common(x, logits, T, H, E, I, topk, w13, s13, w2, s2, topk_ids, topk_w, out, ws,
+                    ws_bytes, dbg, false, stream);
+}
+
+int moe_w8a8_forward_packed(const uint16_t* x, const float* logits, int64_t T, int64_t H,
+                            int64_t E, int64_t I, int topk, const int8_t* w13_packed,
+                            const float* s13, const int8_t* w2_packed, const float* s2,
+                            int32_t* topk_ids, float* topk_w, uint16_t* out, void* ws,
+                            size_t ws_bytes, const moe_w8a8_debug* dbg, void* stream) {
+  return moe_common(x, logits, T, H, E, I, topk, w13_packed, s13, w2_packed, s2, topk_ids,
+                    topk_w, out, ws, ws_bytes, dbg, true, stream);
 }
 
 int fwht128_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,

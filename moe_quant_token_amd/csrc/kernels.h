@@ -59,6 +59,7 @@ struct MoeArgs {
   int8_t* dbg_qa;
   float* dbg_sa2;
   int32_t* dbg_acc2;
+  bool packed;  // w13 / w2 in the packed tile layout (per expert, as [E*rows, cols])
 };
 size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int k);
 hipError_t launch_moe_forward(const MoeArgs& a, hipStream_t stream);

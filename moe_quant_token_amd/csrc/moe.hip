@@ -76,86 +76,142 @@ MoeWs carve(void* base, int64_t T, int64_t H, int64_t E, int64_t I, int k) {
 
 }  // namespace
 
+// Wave-wide maximum of a 32-bit unsigned key through DPP row shifts and row
+// broadcasts (no LDS traffic); every lane gets the result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#define W8A8_DPP_MAX(ctrl, rmask)                                                          \
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, rmask, 0xf, false))
+  W8A8_DPP_MAX(0x111, 0xf);  // row_shr:1
+  W8A8_DPP_MAX(0x112, 0xf);  // row_shr:2
+  W8A8_DPP_MAX(0x114, 0xf);  // row_shr:4
+  W8A8_DPP_MAX(0x118, 0xf);  // row_shr:8
+  W8A8_DPP_MAX(0x142, 0xa);  // row_bcast:15
+  W8A8_DPP_MAX(0x143, 0xc);  // row_bcast:31
+#undef W8A8_DPP_MAX
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Order-preserving map of a finite fp32 value to an unsigned key.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // ---------------------------------------------------------------------------
-// Routing: softmax over E, top-k, renormalise.  Selection compares the fp32
-// logits (softmax is monotonic): slot s gets the s-th largest, equal logits
-// go to the lower expert index.  Probabilities are formed in fp64 and the
-// renormalised weight is rounded once to fp32.
+// Routing of one token by one wave: softmax over E, top-k, renormalise.
+// Selection compares the fp32 logits (softmax is monotonic): slot s gets the
+// s-th largest, equal logits go to the lower expert index.  Each round takes
+// the wave maximum of the key (logit, then 2^32-1-index) over the experts not
+// yet taken.  Each probability exp(l - max) / sum is formed in fp64 (every
+// lane evaluates the winner's, so nothing is broadcast), the kept ones are
+// summed in slot order and each renormalised weight is rounded once to fp32.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_moe_route(const float* __restrict__ logits, int T,
-                                                   int E, int k, int32_t* __restrict__ ids,
-                                                   float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* lt = logits + (int64_t)t * E;
+__device__ __forceinline__ void route_token(const float* __restrict__ lt, int E, int k,
+                                            int32_t* __restrict__ ids, float* __restrict__ w,
+                                            int lane) {
   float v[16];
+  float lmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const int e = lane + 64 * i;
     v[i] = e < E ? lt[e] : -INFINITY;
+    lmax = fmaxf(lmax, v[i]);
   }
+  const double mx = (double)wave_max(lmax);
+  double z = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; i++)
+    if (lane + 64 * i < E) z += exp((double)v[i] - mx);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+
   uint32_t taken = 0;
-  float selv[16];
+  double kept = 0.0, myp = 0.0;
   for (int s = 0; s < k; s++) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    uint32_t hi = 0, lo = 0;  // best local key; 0 = none
 #pragma unroll
     for (int i = 0; i < 16; i++) {
       const int e = lane + 64 * i;
-      // ascending e within a lane, strict '>' keeps the lower index on ties
-      if (e < E && !(taken & (1u << i)) && (be == 0x7fffffff || v[i] > bv)) {
-        bv = v[i];
-        be = e;
+      if (e < E && !(taken & (1u << i))) {
+        const uint32_t kh = float_key(v[i]);
+        if (kh > hi) {  // ascending e: ties keep the lower index
+          hi = kh;
+          lo = 0xffffffffu - (uint32_t)e;
+        }
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    const uint32_t mh = wave_max_u32(hi);
+    const uint32_t ml = wave_max_u32(hi == mh ? lo : 0u);
+    const int be = (int)(0xffffffffu - ml);
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    selv[s & 15] = bv;
-    if (lane == 0) ids[(int64_t)t * k + s] = be;
+    const double ps = exp((double)key_float(mh) - mx) / z;
+    kept += ps;
+    if (lane == s) myp = ps;
+    if (lane == 0) ids[s] = be;
   }
-  // softmax denominator over all experts (fp64); the maximum is slot 0
-  const double mx = (double)selv[0];
-  double z = 0.0;
+  if (lane < k) w[lane] = (float)(myp / kept);
+}
+
+__global__ __launch_bounds__(256) void k_moe_route(const float* __restrict__ logits, int T,
+                                                   int E, int k, int32_t* __restrict__ ids,
+                                                   float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  route_token(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k,
+              threadIdx.x & 63);
+}
+
+// One wave quantises one bf16 row of length K (K % 16 == 0), exactly as
+// k_quant_rows does: amax / 127 in fp32, round-half-even of the quotient.
+__device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ x, int K,
+                                               int8_t* __restrict__ q, float* __restrict__ s,
+                                               int lane) {
+  float amax = 0.0f;
+  for (int c = lane; c < (K >> 3); c += 64) {
+    const v4u raw = *reinterpret_cast<const v4u*>(x + c * 8);
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int e = lane + 64 * i;
-    if (e < E) z += exp((double)v[i] - mx);
+    for (int i = 0; i < 4; i++)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(wd[i] & 0xffffu)),
+                               fabsf(bf16_bits_to_f32(wd[i] >> 16))));
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
-  double p[16];
-  double kept = 0.0;
-  for (int s = 0; s < k; s++) {
-    p[s] = exp((double)selv[s] - mx) / z;
-    kept += p[s];
+  amax = wave_max(amax);
+  const float sc = amax / 127.0f;
+  for (int c = lane; c < (K >> 3); c += 64) {
+    const v4u raw = *reinterpret_cast<const v4u*>(x + c * 8);
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t lo = 0, hi = 0;
+    if (amax != 0.0f) {
+      lo = pack4_i8(quant_code(bf16_bits_to_f32(wd[0] & 0xffffu), sc),
+                    quant_code(bf16_bits_to_f32(wd[0] >> 16), sc),
+                    quant_code(bf16_bits_to_f32(wd[1] & 0xffffu), sc),
+                    quant_code(bf16_bits_to_f32(wd[1] >> 16), sc));
+      hi = pack4_i8(quant_code(bf16_bits_to_f32(wd[2] & 0xffffu), sc),
+                    quant_code(bf16_bits_to_f32(wd[2] >> 16), sc),
+                    quant_code(bf16_bits_to_f32(wd[3] & 0xffffu), sc),
+                    quant_code(bf16_bits_to_f32(wd[3] >> 16), sc));
+    }
+    uint32_t* o = reinterpret_cast<uint32_t*>(q + c * 8);
+    o[0] = lo;
+    o[1] = hi;
   }
-  if (lane < k) {
-    double ps = 0.0;
-    for (int s = 0; s < k; s++)
-      if (s == lane) ps = p[s];
-    w[(int64_t)t * k + lane] = (float)(ps / kept);
-  }
+  if (lane == 0) s[0] = amax != 0.0f ? sc : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
 // Sort / align by expert (one workgroup of 1024 threads).  Pairs with an id
 // outside [0, E) are dropped.  Also clears the per-pair |act| maxima.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_moe_sort(const int32_t* __restrict__ ids, int P,
-                                                   int E, int32_t* __restrict__ expert_list,
-                                                   int32_t* __restrict__ seg_off,
-                                                   int32_t* __restrict__ n_active,
-                                                   int32_t* __restrict__ sorted_pairs,
-                                                   uint32_t* __restrict__ amax) {
+// Runs on a whole 1024-thread workgroup.
+__device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int P, int E,
+                                           int32_t* __restrict__ expert_list,
+                                           int32_t* __restrict__ seg_off,
+                                           int32_t* __restrict__ n_active,
+                                           int32_t* __restrict__ sorted_pairs,
+                                           uint32_t* __restrict__ amax) {
   __shared__ int cnt[1024];
   __shared__ int cursor[1024];
   __shared__ int wsum_c[16], wsum_f[16];
@@ -217,6 +273,211 @@ __global__ __launch_bounds__(1024) void k_moe_sort(const int32_t* __restrict__ i
   }
 }
 
+__global__ __launch_bounds__(1024) void k_moe_sort(const int32_t* __restrict__ ids, int P,
+                                                   int E, int32_t* __restrict__ expert_list,
+                                                   int32_t* __restrict__ seg_off,
+                                                   int32_t* __restrict__ n_active,
+                                                   int32_t* __restrict__ sorted_pairs,
+                                                   uint32_t* __restrict__ amax) {
+  sort_pairs(ids, P, E, expert_list, seg_off, n_active, sorted_pairs, amax);
+}
+
+// Small batches: routing, per-token quant of x and the sort in one
+// 1024-thread workgroup (one launch instead of three).
+__global__ __launch_bounds__(1024) void k_moe_prep(
+    const uint16_t* __restrict__ x, const float* __restrict__ logits, int T, int H, int E, int k,
+    int32_t* __restrict__ ids, float* __restrict__ w, int8_t* __restrict__ qx,
+    float* __restrict__ sx, int32_t* __restrict__ expert_list, int32_t* __restrict__ seg_off,
+    int32_t* __restrict__ n_active, int32_t* __restrict__ sorted_pairs,
+    uint32_t* __restrict__ amax) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int t = wv; t < T; t += 16) {
+    if (logits)
+      route_token(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k,
+                  lane);
+    quant_row_wave(x + (int64_t)t * H, H, qx + (int64_t)t * H, sx + t, lane);
+  }
+  __syncthreads();  // the routing ids written above are read by the sort
+  sort_pairs(ids, T * k, E, expert_list, seg_off, n_active, sorted_pairs, amax);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM for small batches (few pairs per expert): the weight-streaming
+// structure of the dense decode kernel.  Workgroup = (16 weight rows of one
+// expert, that expert's pairs in blocks of 16); its WAVES waves take the k
+// steps round-robin and their int32 partials are added through LDS.
+// MODE 1 = gemm1 (A = the pairs' token rows of qx; epilogue dequantises,
+// applies SiLU(gate) * up on the interleaved rows, stores the fp32 activation
+// and records the pair's |act| maximum with an integer atomic max).
+// MODE 2 = gemm2 (prologue requantises the block's activation rows into LDS
+// from that maximum; epilogue stores dequantised fp32 rows).
+// Operand mapping as in gemm_skinny.hip (16x16x64 MFMA).
+// ---------------------------------------------------------------------------
+constexpr int kMoeSkinnyMaxK2 = 2048;  // gemm2 reduction length (I) staged in LDS
+
+// NT: consecutive 16-row weight tiles per workgroup (amortises the chain of
+// dependent reads -- active count, expert id, segment, pair ids -- over more
+// weight bytes).  The first batch of weight loads is issued as soon as the
+// expert id is known, before the pair data is read, and every batch's MFMAs
+// run while the next batch's weight loads are in flight.
+template <int WAVES, int NT, int MODE, bool PACKED>
+__global__ __launch_bounds__(WAVES * 64) void k_moe_skinny(
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, const float* __restrict__ act,
+    const uint32_t* __restrict__ amax_in, int k, const int8_t* __restrict__ W,
+    const float* __restrict__ sW, int Nw, int K, const int32_t* __restrict__ expert_list,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ n_active,
+    const int32_t* __restrict__ sorted_pairs, float* __restrict__ out, int ldo,
+    uint32_t* __restrict__ amax_out, int8_t* __restrict__ qa_rec, float* __restrict__ sa2_rec,
+    int32_t* __restrict__ dbg_acc) {
+  constexpr int U = NT >= 4 ? 2 : 4;  // 64-byte k steps per batch
+  __shared__ v4i red[NT][WAVES][64];
+  __shared__ __attribute__((aligned(16))) int8_t a_lds[MODE == 2 ? 16 * kMoeSkinnyMaxK2 : 16];
+  __shared__ float sa2_lds[16];
+  __shared__ int pair_lds[16];
+  const int slot = blockIdx.y;
+  const int nact = n_active[0];
+  const int e = expert_list[slot];
+  if (slot >= nact) return;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int nk = K >> 6;
+  const int ntile0 = blockIdx.x * NT;
+  const int8_t* wbase = PACKED
+                            ? W + ((int64_t)e * (Nw >> 4) + ntile0) * nk * 1024 + lane * 16
+                            : W + ((int64_t)e * Nw + ntile0 * 16 + j) * K + g * 16;
+  constexpr int64_t wstep = PACKED ? 1024 : 64;
+  const int64_t tstep = PACKED ? (int64_t)nk * 1024 : (int64_t)16 * K;
+
+  auto load_w = [&](v4i (*b)[NT], int c0) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int c = c0 + u * WAVES;
+#pragma unroll
+      for (int t = 0; t < NT; t++)
+        b[u][t] = c < nk ? *reinterpret_cast<const v4i*>(wbase + t * tstep + c * wstep)
+                         : v4i{0, 0, 0, 0};
+    }
+  };
+  v4i bq[U][NT];
+  load_w(bq, wv);  // first batch, in flight while the pair data is read
+
+  const int seg_begin = seg_off[slot];
+  const int seg_end = seg_off[slot + 1];
+  for (int pb = seg_begin; pb < seg_end; pb += 16) {
+    const int nrows = min(16, seg_end - pb);
+    __syncthreads();  // LDS of the previous block fully consumed
+    if (threadIdx.x < 16)
+      pair_lds[threadIdx.x] = threadIdx.x < nrows ? sorted_pairs[pb + threadIdx.x] : 0;
+    if (MODE == 2) {
+      __syncthreads();
+      if (threadIdx.x < nrows) {
+        const float am = __uint_as_float(amax_in[pair_lds[threadIdx.x]]);
+        sa2_lds[threadIdx.x] = am != 0.0f ? am / 127.0f : 0.0f;
+      }
+      __syncthreads();
+      // requantise the block's activation rows straight into the packed
+      // operand layout: row r, bytes 16s..16s+15 of k step c at c*1024 + (r + 16s)*16
+      const int per_row = K >> 2;
+      for (int idx = threadIdx.x; idx < nrows * per_row; idx += WAVES * 64) {
+        const int r = idx / per_row;
+        const int kk = (idx - r * per_row) * 4;
+        const int p = pair_lds[r];
+        const float sc = sa2_lds[r];
+        const v4f a = *reinterpret_cast<const v4f*>(act + (int64_t)p * K + kk);
+        uint32_t wd = 0;
+        if (sc != 0.0f)
+          wd = pack4_i8(quant_code(a.x, sc), quant_code(a.y, sc), quant_code(a.z, sc),
+                        quant_code(a.w, sc));
+        const int c = kk >> 6, sl = (kk & 63) >> 4;
+        *reinterpret_cast<uint32_t*>(&a_lds[c * 1024 + (r + 16 * sl) * 16 + (kk & 15)]) = wd;
+        if (blockIdx.x == 0 && qa_rec)
+          *reinterpret_cast<uint32_t*>(qa_rec + (int64_t)p * K + kk) = wd;
+      }
+      if (blockIdx.x == 0 && sa2_rec && threadIdx.x < nrows)
+        sa2_rec[pair_lds[threadIdx.x]] = sa2_lds[threadIdx.x];
+    }
+    __syncthreads();
+
+    const bool a_ok = j < nrows;
+    const int8_t* ap = qx + (int64_t)(pair_lds[a_ok ? j : 0] / k) * K + g * 16;
+    v4i acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = v4i{0, 0, 0, 0};
+    for (int c0 = wv; c0 < nk; c0 += WAVES * U) {
+      v4i bn[U][NT];
+      if (c0 + WAVES * U < nk) load_w(bn, c0 + WAVES * U);
+      v4i a[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int c = c0 + u * WAVES;
+        const bool in = c < nk;
+        if (MODE == 1)
+          a[u] = (in && a_ok) ? *reinterpret_cast<const v4i*>(ap + (int64_t)c * 64)
+                              : v4i{0, 0, 0, 0};
+        else
+          a[u] = in ? *reinterpret_cast<const v4i*>(&a_lds[c * 1024 + lane * 16])
+                    : v4i{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++)
+#pragma unroll
+        for (int t = 0; t < NT; t++) acc[t] = mfma_16x16x64_i8(a[u], bq[u][t], acc[t]);
+      if (c0 + WAVES * U < nk) {
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+          for (int t = 0; t < NT; t++) bq[u][t] = bn[u][t];
+      }
+    }
+    if (pb + 16 < seg_end) load_w(bq, wv);  // the next pair block streams the tiles again
+#pragma unroll
+    for (int t = 0; t < NT; t++) red[t][wv][lane] = acc[t];
+    __syncthreads();
+    // wave w finishes tiles w, w + WAVES, ...
+    for (int t = wv; t < NT; t += WAVES) {
+      v4i sum = red[t][0][lane];
+#pragma unroll
+      for (int w2 = 1; w2 < WAVES; w2++) sum += red[t][w2][lane];
+      const int col = (ntile0 + t) * 16 + j;
+      const float swc = sW[(int64_t)e * Nw + col];
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int r = 4 * g + v;
+        const bool valid = r < nrows;
+        const int p = pair_lds[valid ? r : 0];
+        if (dbg_acc && valid) dbg_acc[(int64_t)p * Nw + col] = sum[v];
+        if (MODE == 1) {
+          float h = 0.0f;
+          if (valid) {
+            h = (float)sum[v];
+            h = h * sx[p / k];
+            h = h * swc;
+          }
+          const float partner = __shfl_xor(h, 1, 64);
+          float mag = 0.0f;
+          if ((j & 1) == 0 && valid) {
+            // SiLU(gate) * up; the gate is the even interleaved row
+            const float sg = (float)((double)h / (1.0 + exp(-(double)h)));
+            const float av = sg * partner;
+            out[(int64_t)p * ldo + (col >> 1)] = av;
+            mag = fabsf(av);
+          }
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) mag = fmaxf(mag, __shfl_xor(mag, off, 64));
+          if (j == 0 && valid) atomicMax(&amax_out[p], __float_as_uint(mag));
+        } else if (valid) {
+          float yv = (float)sum[v];
+          yv = yv * sa2_lds[r];
+          yv = yv * swc;
+          out[(int64_t)p * ldo + col] = yv;
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Grouped GEMM over the pairs of one expert.  MODE 1 = gemm1 (A = qx rows of
 // the pairs' tokens, epilogue SiLU(gate)*up), MODE 2 = gemm2 (A = qa rows of
@@ -224,7 +485,7 @@ __global__ __launch_bounds__(1024) void k_moe_sort(const int32_t* __restrict__ i
 // weight rows; up to 4 pair blocks share each weight load.  Operand mapping as
 // in gemm_skinny.hip.
 // ---------------------------------------------------------------------------
-template <int WAVES, int MODE>
+template <int WAVES, int MODE, bool PACKED>
 __global__ __launch_bounds__(WAVES * 64) void k_moe_gemm(
     const int8_t* __restrict__ A, const float* __restrict__ sA, int a_div,
     const int8_t* __restrict__ W, const float* __restrict__ sW, int Nw, int K,
@@ -244,8 +505,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_gemm(
   const int seg_end = seg_off[slot + 1];
   const int n0 = (blockIdx.y * WAVES + wv) * 16;
   if (n0 >= Nw) return;
-  const int8_t* wp = W + ((int64_t)e * Nw + n0 + j) * K + g * 16;
   const int nk = K >> 6;
+  const int8_t* wp = PACKED ? W + ((int64_t)e * (Nw >> 4) + (n0 >> 4)) * nk * 1024 + lane * 16
+                            : W + ((int64_t)e * Nw + n0 + j) * K + g * 16;
+  constexpr int64_t wstep = PACKED ? 1024 : 64;
 
   for (int pb = seg_begin; pb < seg_end; pb += 64) {
     const int nb = min(4, (seg_end - pb + 15) >> 4);  // wave-uniform
@@ -268,7 +531,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_gemm(
 #pragma unroll
       for (int u = 0; u < U; u++) {
         const bool in = c + u < nk;
-        wb[u] = in ? *reinterpret_cast<const v4i*>(wp + (int64_t)(c + u) * 64) : v4i{0, 0, 0, 0};
+        wb[u] = in ? *reinterpret_cast<const v4i*>(wp + (int64_t)(c + u) * wstep)
+                   : v4i{0, 0, 0, 0};
 #pragma unroll
         for (int b = 0; b < 4; b++)
           a[b][u] = (in && b < nb && aok[b])
@@ -377,53 +641,87 @@ size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int k) {
   return carve(nullptr, T, H, E, I, k).bytes;
 }
 
-hipError_t launch_moe_forward(const MoeArgs& a, hipStream_t stream) {
+// Small batches (at most kMoeSmallPairs routed pairs) take the fused prep
+// kernel and the skinny grouped GEMMs (gemm2 requantises in its prologue):
+// four launches.  Larger batches: routing, sort and quant kernels, the
+// 64-pair-block grouped GEMMs, a requant kernel and the combine.
+constexpr int64_t kMoeSmallPairs = 2048;
+
+template <bool PACKED>
+static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
   const int64_t P = (int64_t)a.T * a.k;
   MoeWs ws = carve(a.ws, a.T, a.H, a.E, a.I, a.k);
-  hipError_t err;
-  if (a.logits) {
-    hipLaunchKernelGGL(k_moe_route, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.logits, a.T,
-                       a.E, a.k, a.topk_ids, a.topk_w);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
-                     ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if ((err = launch_quant_rows(a.x, 0, a.T, a.H, a.H, ws.qx, a.H, ws.sx, stream)) != hipSuccess)
-    return err;
-
   const int slots = (int)std::min<int64_t>(a.E, P);
   const int I2 = 2 * a.I;
-  // Few pairs: one wave per workgroup spreads the weight stream over more CUs.
-  if (P <= 256) {
-    hipLaunchKernelGGL((k_moe_gemm<1, 1>), dim3(slots, I2 / 16), dim3(64), 0, stream, ws.qx,
-                       ws.sx, a.k, a.w13, a.s13, I2, a.H, ws.expert_list, ws.seg_off,
-                       ws.n_active, ws.sorted_pairs, ws.act, a.I, ws.amax, a.dbg_acc1);
+  hipError_t err;
+  const bool small = P <= kMoeSmallPairs && a.I <= kMoeSkinnyMaxK2;
+  if (small) {
+    hipLaunchKernelGGL(k_moe_prep, dim3(1), dim3(1024), 0, stream, a.x, a.logits, a.T, a.H, a.E,
+                       a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx, ws.expert_list, ws.seg_off,
+                       ws.n_active, ws.sorted_pairs, ws.amax);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // tiny batches: one weight tile per workgroup (most parallelism); else
+    // eight tiles per workgroup
+    const int tiles1 = I2 / 16, tiles2 = a.H / 16;
+    if (P <= 64 || tiles1 % 8 != 0 || tiles2 % 8 != 0) {
+      hipLaunchKernelGGL((k_moe_skinny<8, 1, 1, PACKED>), dim3(tiles1, slots), dim3(512), 0,
+                         stream, ws.qx, ws.sx, nullptr, nullptr, a.k, a.w13, a.s13, I2, a.H,
+                         ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.act, a.I,
+                         ws.amax, nullptr, nullptr, a.dbg_acc1);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      hipLaunchKernelGGL((k_moe_skinny<8, 1, 2, PACKED>), dim3(tiles2, slots), dim3(512), 0,
+                         stream, nullptr, nullptr, ws.act, ws.amax, a.k, a.w2, a.s2, a.H, a.I,
+                         ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.y2, a.H,
+                         nullptr, a.dbg_qa, a.dbg_sa2, a.dbg_acc2);
+    } else {
+      hipLaunchKernelGGL((k_moe_skinny<4, 8, 1, PACKED>), dim3(tiles1 / 8, slots), dim3(256), 0,
+                         stream, ws.qx, ws.sx, nullptr, nullptr, a.k, a.w13, a.s13, I2, a.H,
+                         ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.act, a.I,
+                         ws.amax, nullptr, nullptr, a.dbg_acc1);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      hipLaunchKernelGGL((k_moe_skinny<4, 8, 2, PACKED>), dim3(tiles2 / 8, slots), dim3(256), 0,
+                         stream, nullptr, nullptr, ws.act, ws.amax, a.k, a.w2, a.s2, a.H, a.I,
+                         ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.y2, a.H,
+                         nullptr, a.dbg_qa, a.dbg_sa2, a.dbg_acc2);
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   } else {
-    hipLaunchKernelGGL((k_moe_gemm<4, 1>), dim3(slots, (I2 / 16 + 3) / 4), dim3(256), 0, stream,
-                       ws.qx, ws.sx, a.k, a.w13, a.s13, I2, a.H, ws.expert_list, ws.seg_off,
-                       ws.n_active, ws.sorted_pairs, ws.act, a.I, ws.amax, a.dbg_acc1);
-  }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_moe_requant, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, stream, ws.act,
-                     ws.amax, (int)P, a.I, ws.qa, ws.sa2);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (P <= 256) {
-    hipLaunchKernelGGL((k_moe_gemm<1, 2>), dim3(slots, a.H / 16), dim3(64), 0, stream, ws.qa,
-                       ws.sa2, 1, a.w2, a.s2, a.H, a.I, ws.expert_list, ws.seg_off, ws.n_active,
-                       ws.sorted_pairs, ws.y2, a.H, nullptr, a.dbg_acc2);
-  } else {
-    hipLaunchKernelGGL((k_moe_gemm<4, 2>), dim3(slots, (a.H / 16 + 3) / 4), dim3(256), 0,
+    if (a.logits) {
+      hipLaunchKernelGGL(k_moe_route, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.logits, a.T,
+                         a.E, a.k, a.topk_ids, a.topk_w);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
+                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch_quant_rows(a.x, 0, a.T, a.H, a.H, ws.qx, a.H, ws.sx, stream)) !=
+        hipSuccess)
+      return err;
+    hipLaunchKernelGGL((k_moe_gemm<4, 1, PACKED>), dim3(slots, (I2 / 16 + 3) / 4), dim3(256), 0,
+                       stream, ws.qx, ws.sx, a.k, a.w13, a.s13, I2, a.H, ws.expert_list,
+                       ws.seg_off, ws.n_active, ws.sorted_pairs, ws.act, a.I, ws.amax,
+                       a.dbg_acc1);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_moe_requant, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, stream,
+                       ws.act, ws.amax, (int)P, a.I, ws.qa, ws.sa2);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((k_moe_gemm<4, 2, PACKED>), dim3(slots, (a.H / 16 + 3) / 4), dim3(256), 0,
                        stream, ws.qa, ws.sa2, 1, a.w2, a.s2, a.H, a.I, ws.expert_list,
                        ws.seg_off, ws.n_active, ws.sorted_pairs, ws.y2, a.H, nullptr,
                        a.dbg_acc2);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)P * a.I,
+                                          hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+      return err;
+    if (a.dbg_sa2 && (err = hipMemcpyAsync(a.dbg_sa2, ws.sa2, (size_t)P * 4,
+                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+      return err;
   }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(k_moe_combine, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, stream,
                      ws.y2, a.topk_ids, a.topk_w, a.T, a.H, a.E, a.k, a.out);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
-  // optional copies of the intermediates, in pair order
+  // optional copies of the remaining intermediates, in pair order
   if (a.dbg_qx && (err = hipMemcpyAsync(a.dbg_qx, ws.qx, (size_t)a.T * a.H,
                                         hipMemcpyDeviceToDevice, stream)) != hipSuccess)
     return err;
@@ -433,13 +731,11 @@ hipError_t launch_moe_forward(const MoeArgs& a, hipStream_t stream) {
   if (a.dbg_act && (err = hipMemcpyAsync(a.dbg_act, ws.act, (size_t)P * a.I * 4,
                                          hipMemcpyDeviceToDevice, stream)) != hipSuccess)
     return err;
-  if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)P * a.I,
-                                        hipMemcpyDeviceToDevice, stream)) != hipSuccess)
-    return err;
-  if (a.dbg_sa2 && (err = hipMemcpyAsync(a.dbg_sa2, ws.sa2, (size_t)P * 4,
-                                         hipMemcpyDeviceToDevice, stream)) != hipSuccess)
-    return err;
   return hipSuccess;
+}
+
+hipError_t launch_moe_forward(const MoeArgs& a, hipStream_t stream) {
+  return a.packed ? moe_forward_impl<true>(a, stream) : moe_forward_impl<false>(a, stream);
 }
 
 }  // namespace w8a8

@@ -42,13 +42,21 @@ def _tie_free(logits, k):
     return bool((srt[:, k - 1] != srt[:, k]).all()) if logits.shape[1] > k else True
 
 
-def _check_full(orc, x, logits, k, W, T, label):
+def _dev_weights(W, packed):
+    q13, s13, q2, s2 = [dev(a) for a in W]
+    if packed:
+        q13, q2 = mq.pack_moe_weights(q13, q2)
+    return q13, s13, q2, s2
+
+
+def _check_full(orc, x, logits, k, W, T, label, packed=False, Wd=None):
     q13, s13, q2, s2 = W
     E = q13.shape[0]
     ids_ref, w_ref = orc.route_topk(logits, k)
     out_ref, dref = orc.moe_forward(x, ids_ref, w_ref, q13, s13, q2, s2, debug=True)
-    Wd = [dev(a) for a in W]
-    out, ids, w, dbg = mq.moe_w8a8_forward(bf16_dev(x), dev(logits), *Wd, topk=k, debug=True)
+    Wd = _dev_weights(W, packed) if Wd is None else Wd
+    out, ids, w, dbg = mq.moe_w8a8_forward(bf16_dev(x), dev(logits), *Wd, topk=k, debug=True,
+                                           packed=packed)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(ids), ids_ref)
     assert ulp_diff_f32(host(w), w_ref).max() <= 1
@@ -72,17 +80,33 @@ def _check_full(orc, x, logits, k, W, T, label):
     return out
 
 
-def test_small_full_pipeline(orc):
+@pytest.mark.parametrize("packed", [False, True])
+def test_small_full_pipeline(orc, packed):
     T, E, H, I, k = 37, 16, 256, 128, 4
     key = (40, 1)
     W = _weights(orc, key, E, H, I)
     x = synth.activations(key, T, H, 0, 1.0)
     logits = synth.router_logits(key, T, E)
     assert _tie_free(logits, k)
-    out = _check_full(orc, x, logits, k, W, T, "moe small")
+    Wd = _dev_weights(W, packed)
+    out = _check_full(orc, x, logits, k, W, T, "moe small", packed=packed, Wd=Wd)
     # determinism: a second run is bit-identical
-    out2 = mq.moe_w8a8_forward(bf16_dev(x), dev(logits), *[dev(a) for a in W], topk=k)[0]
+    out2 = mq.moe_w8a8_forward(bf16_dev(x), dev(logits), *Wd, topk=k, packed=packed)[0]
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_large_batch_path(orc, packed):
+    # more than 2048 routed pairs: the routing/sort/quant kernels, the
+    # 64-pair-block grouped GEMMs and the separate requant kernel
+    T, E, H, I, k = 700, 8, 128, 64, 4
+    key = (43, 1)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    logits = synth.router_logits(key, T, E)
+    logits[:, 2] += 1.5  # a hot expert: most tokens route to expert 2
+    assert _tie_free(logits, k)
+    _check_full(orc, x, logits, k, W, T, "moe large-batch path", packed=packed)
 
 
 def test_given_routing_hot_expert_and_edges(orc):
@@ -99,13 +123,14 @@ def test_given_routing_hot_expert_and_edges(orc):
     w = r.random((T, k)).astype(np.float32)
     w /= w.sum(1, keepdims=True)
     out_ref = orc.moe_forward(x, ids, w, *W)
-    out, ids_o, w_o = mq.moe_w8a8_forward(bf16_dev(x), None, *[dev(a) for a in W], topk=k,
-                                          topk_ids=dev(ids), topk_w=dev(w))
-    torch.cuda.synchronize()
-    np.testing.assert_array_equal(host(ids_o), ids)
-    got = bf16_host(out)
-    assert_bf16_close(got, out_ref, "moe given routing")
-    assert not got[5].any()
+    for packed in (False, True):
+        out, ids_o, w_o = mq.moe_w8a8_forward(bf16_dev(x), None, *_dev_weights(W, packed), topk=k,
+                                              topk_ids=dev(ids), topk_w=dev(w), packed=packed)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(ids_o), ids)
+        got = bf16_host(out)
+        assert_bf16_close(got, out_ref, "moe given routing")
+        assert not got[5].any()
 
 
 def test_single_expert_top1(orc):
@@ -147,7 +172,7 @@ def full_moe(orc):
     E, H, I = cfg["E"], cfg["H"], cfg["I"]
     say("generating full-size MoE weights (256 experts)")
     W = _weights(orc, cfg["wkey"], E, H, I)
-    return W, [dev(a) for a in W]
+    return W, _dev_weights(W, True)
 
 
 @pytest.mark.parametrize("T", [1, 64])
@@ -158,7 +183,7 @@ def test_full_size_all_tokens(orc, full_moe, T):
     x = synth.activations(cfg["xkey"], T, cfg["H"], 0, 1.0)
     logits = synth.router_logits(cfg["xkey"], T, cfg["E"])
     assert _tie_free(logits, cfg["k"])
-    _check_full(orc, x, logits, cfg["k"], W, T, f"moe T={T}")
+    _check_full(orc, x, logits, cfg["k"], W, T, f"moe T={T}", packed=True, Wd=Wd)
 
 
 def test_full_size_t2048_sampled_tokens(orc, full_moe):
@@ -169,7 +194,7 @@ def test_full_size_t2048_sampled_tokens(orc, full_moe):
     x = synth.activations(cfg["xkey"], T, cfg["H"], 0, 1.0)
     logits = synth.router_logits(cfg["xkey"], T, cfg["E"])
     assert _tie_free(logits, k)
-    out, ids, w = mq.moe_w8a8_forward(bf16_dev(x), dev(logits), *Wd, topk=k)
+    out, ids, w = mq.moe_w8a8_forward(bf16_dev(x), dev(logits), *Wd, topk=k, packed=True)
     torch.cuda.synchronize()
     ids_ref, w_ref = orc.route_topk(logits, k)
     np.testing.assert_array_equal(host(ids), ids_ref)
