@@ -34,6 +34,8 @@ METRIC = "W8A8 GEMM TOPS + HBM GB/s (M=1 & M=4096, % roofline); MoE tokens/s"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 I8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA (5.0 POPS)
 MALL_BYTES = 256 << 20     # Infinity Cache
+PROBE_ELEMS = 1 << 28      # --probe-copy: 1 GiB of fp32 read and 1 GiB written
+DECODE_KERNEL = "k_gemm_skinny"
 
 
 def parse():
@@ -46,7 +48,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--probe-copy", action="store_true",
-                   help="also run a 1 GiB device copy (counter scale reference)")
+                   help="also run a 1 GiB fp32 negation (reads 1 GiB, writes 1 GiB): the "
+                        "reference kernel that scales the HBM byte counters")
+    p.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no benchmark: turn two rocprofv3 --pmc runs of this script "
+                        "(FETCH_SIZE, then WRITE_SIZE, with --probe-copy) into "
+                        "profiles/traffic_decode_gemm.json")
     return p.parse_args()
 
 
@@ -99,8 +106,54 @@ def linear_bytes(M, N, K, bf16_in: bool) -> int:
     return N * K + 4 * N + a + 2 * M * N
 
 
+def _counter_rows(d: str, counter: str):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_from_counters(fetch_dir: str, write_dir: str) -> None:
+    """HBM bytes per decode GEMM launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch).
+
+    Each counter is scaled by what it reads for the probe kernel, a plain fp32
+    negation over 1 GiB (1 GiB fetched, 1 GiB written), so the figure is in
+    bytes of the same kind as the algorithmic ones."""
+    out = {"kernel": DECODE_KERNEL, "src_hash": src_hash("gemm_skinny.hip")}
+    total = 0.0
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(d, counter)
+        probe = [v for n, v in rows if "neg" in n]
+        gemm = [v for n, v in rows if DECODE_KERNEL in n]
+        if not probe or not gemm:
+            raise SystemExit(f"{counter}: probe dispatches {len(probe)}, gemm dispatches {len(gemm)}")
+        scale = float(PROBE_ELEMS * 4) / (max(probe) * 1024.0)
+        per = sum(gemm) / len(gemm) * 1024.0 * scale
+        out[key] = {"counter": counter, "dispatches": len(gemm), "raw_kib_avg": sum(gemm) / len(gemm),
+                    "probe_kib": max(probe), "scale": scale, "bytes_per_launch": per}
+        total += per
+    out["bytes_per_launch"] = total
+    path = os.path.join(ROOT, "profiles", "traffic_decode_gemm.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.traffic:
+        traffic_from_counters(*args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this "
               "single-GPU build (the path is sharded by design, not run across GPUs here)",
@@ -236,10 +289,11 @@ def main():
         out["enqueue_bound_warning"] = True
 
     if args.probe_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        a = torch.zeros(PROBE_ELEMS, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
+        torch.neg(a, out=b)
         torch.cuda.synchronize()
+        del a, b
 
     # ------------------------------------------------------------ CPU baseline
     if not args.no_cpu_baseline:
