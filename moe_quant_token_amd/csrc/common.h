@@ -57,6 +57,38 @@ __device__ __forceinline__ v16i mfma_32x32x32_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
+// s_waitcnt immediate that waits for vmcnt <= v and leaves the other counters
+// unconstrained (gfx9 encoding: vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at bits
+// 15:14, expcnt at 6:4, lgkmcnt at 11:8).
+constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait until at most n (wave-uniform, 0..15) vector memory operations of this
+// wave are outstanding.
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  switch (n) {
+#define W8A8_VMCNT_CASE(v) \
+  case v:                  \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(v)); \
+    break;
+    W8A8_VMCNT_CASE(1) W8A8_VMCNT_CASE(2) W8A8_VMCNT_CASE(3) W8A8_VMCNT_CASE(4)
+    W8A8_VMCNT_CASE(5) W8A8_VMCNT_CASE(6) W8A8_VMCNT_CASE(7) W8A8_VMCNT_CASE(8)
+    W8A8_VMCNT_CASE(9) W8A8_VMCNT_CASE(10) W8A8_VMCNT_CASE(11) W8A8_VMCNT_CASE(12)
+    W8A8_VMCNT_CASE(13) W8A8_VMCNT_CASE(14) W8A8_VMCNT_CASE(15)
+#undef W8A8_VMCNT_CASE
+    default:
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+}
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
+// does not wait for outstanding global loads, so register prefetches stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Pack four int8 codes (values in [-127, 127]) into one 32-bit word.
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |

@@ -37,11 +37,6 @@ enum { kEpiBf16 = 0, kEpiI32 = 1, kEpiG256 = 2 };
 
 constexpr int kXcds = 8;
 
-// s_waitcnt immediate that waits for vmcnt <= v and leaves the other counters
-// unconstrained (gfx9 encoding: vmcnt[3:0] at bits 3:0 and vmcnt[5:4] at bits
-// 15:14, expcnt at 6:4, lgkmcnt at 11:8).
-constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 // MINB: workgroups that must fit on one CU at once (the register budget the
 // compiler gets follows from it).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MODE, bool BPACKED,

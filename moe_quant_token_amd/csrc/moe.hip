@@ -8,22 +8,28 @@
 // scales.
 //
 // Kernels, in launch order (all on the caller's stream, no host sync; every
-// count that depends on the routing stays on the device):
-//   k_moe_route    softmax top-k over the logits, one wave per token
-//   k_moe_sort     one workgroup: per-expert counts, the list of experts that
-//                  received pairs, segment offsets, pairs grouped by expert
-//   k_quant_rows   per-token int8 codes of x (quant.hip)
-//   k_moe_gemm<1>  grouped gemm1: one grid row per active expert, each wave
-//                  owns 16 interleaved w13 rows (8 gate/up column pairs) and
-//                  walks every pair routed to that expert, 64 at a time, so a
-//                  weight byte is fetched from HBM once per 64 pairs; epilogue
-//                  dequantises, applies SiLU(gate)*up and records the per-pair
-//                  |act| maximum with an integer atomic max (exact, order-free)
-//   k_moe_requant  per-pair int8 codes of the activation, one wave per pair
-//   k_moe_gemm<2>  grouped gemm2, epilogue writes dequantised fp32 rows
+// count that depends on the routing stays on the device).
+// Small batches (at most 2048 routed pairs):
+//   k_moe_prep     one workgroup: routing (one wave per token), per-token int8
+//                  codes of x, and the sort of the pairs by expert
+//   k_moe_skinny<1> grouped gemm1 streaming each touched expert's w13 once,
+//                  SiLU(gate)*up epilogue, per-pair |act| maximum (atomic max)
+//   k_moe_skinny<2> grouped gemm2; its prologue requantises the pairs' rows
 //   k_moe_combine  out[t] = sum over the k slots, in slot order, one bf16
 //                  rounding; deterministic (no floating-point atomics)
+// Large batches:
+//   k_moe_route    softmax top-k over the logits, one wave per token
+//   k_moe_sort     one workgroup: per-expert counts, the list of experts that
+//                  received pairs, segment offsets, pairs grouped by expert,
+//                  and the table of 128-pair m-blocks
+//   k_quant_rows   per-token int8 codes of x (quant.hip)
+//   k_moe_tile<1>  grouped gemm1 on LDS-staged gathered rows (32x32x32 MFMA),
+//                  SiLU(gate)*up epilogue
+//   k_moe_requant  per-pair int8 codes of the activation, one wave per pair
+//   k_moe_tile<2>  grouped gemm2, epilogue writes dequantised fp32 rows
+//   k_moe_combine  as above
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -32,6 +38,8 @@ namespace w8a8 {
 namespace {
 
 constexpr size_t kAlign = 256;
+// pair rows per workgroup of the large-batch grouped GEMMs
+constexpr int kMoeBM = 128;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct MoeWs {
@@ -46,6 +54,9 @@ struct MoeWs {
   int8_t* qa;             // [P, I]
   float* sa2;             // [P]
   float* y2;              // [P, H]
+  int32_t* blk_slot;      // [P / kMoeBM + E + 1]  m-block -> expert slot
+  int32_t* blk_row0;      // [P / kMoeBM + E + 1]  m-block -> first sorted pair
+  int32_t* n_blocks;      // [1]
   size_t bytes;
 };
 
@@ -70,6 +81,9 @@ MoeWs carve(void* base, int64_t T, int64_t H, int64_t E, int64_t I, int k) {
   w.qa = reinterpret_cast<int8_t*>(take(P * I));
   w.sa2 = reinterpret_cast<float*>(take(P * 4));
   w.y2 = reinterpret_cast<float*>(take(P * H * 4));
+  w.blk_slot = reinterpret_cast<int32_t*>(take((P / kMoeBM + E + 1) * 4));
+  w.blk_row0 = reinterpret_cast<int32_t*>(take((P / kMoeBM + E + 1) * 4));
+  w.n_blocks = reinterpret_cast<int32_t*>(take(4));
   w.bytes = off;
   return w;
 }
@@ -206,15 +220,20 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ x, i
 // outside [0, E) are dropped.  Also clears the per-pair |act| maxima.
 // ---------------------------------------------------------------------------
 // Runs on a whole 1024-thread workgroup.
+// With blk_slot set it also writes the m-block table of the large-batch
+// GEMMs: each expert segment split into blocks of kMoeBM sorted pairs.
 __device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int P, int E,
                                            int32_t* __restrict__ expert_list,
                                            int32_t* __restrict__ seg_off,
                                            int32_t* __restrict__ n_active,
                                            int32_t* __restrict__ sorted_pairs,
-                                           uint32_t* __restrict__ amax) {
+                                           uint32_t* __restrict__ amax,
+                                           int32_t* __restrict__ blk_slot = nullptr,
+                                           int32_t* __restrict__ blk_row0 = nullptr,
+                                           int32_t* __restrict__ n_blocks = nullptr) {
   __shared__ int cnt[1024];
   __shared__ int cursor[1024];
-  __shared__ int wsum_c[16], wsum_f[16];
+  __shared__ int wsum_c[16], wsum_f[16], wsum_b[16];
   const int tid = threadIdx.x;
   cnt[tid] = 0;
   __syncthreads();
@@ -227,36 +246,50 @@ __device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int 
   // exclusive scans of the counts and of the "expert is active" flags
   const int c = tid < E ? cnt[tid] : 0;
   const int f = c > 0 ? 1 : 0;
+  const int nb = (c + kMoeBM - 1) / kMoeBM;
   const int lane = tid & 63, wv = tid >> 6;
-  int ic = c, iflag = f;
+  int ic = c, iflag = f, ib = nb;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int oc = __shfl_up(ic, off, 64);
     const int of = __shfl_up(iflag, off, 64);
+    const int ob = __shfl_up(ib, off, 64);
     if (lane >= off) {
       ic += oc;
       iflag += of;
+      ib += ob;
     }
   }
   if (lane == 63) {
     wsum_c[wv] = ic;
     wsum_f[wv] = iflag;
+    wsum_b[wv] = ib;
   }
   __syncthreads();
-  int base_c = 0, base_f = 0, tot_c = 0, tot_f = 0;
+  int base_c = 0, base_f = 0, base_b = 0, tot_c = 0, tot_f = 0, tot_b = 0;
   for (int i = 0; i < 16; i++) {
     if (i < wv) {
       base_c += wsum_c[i];
       base_f += wsum_f[i];
+      base_b += wsum_b[i];
     }
     tot_c += wsum_c[i];
     tot_f += wsum_f[i];
+    tot_b += wsum_b[i];
   }
   const int off_c = base_c + ic - c;
   const int slot = base_f + iflag - f;
   if (f) {
     expert_list[slot] = tid;
     seg_off[slot] = off_c;
+  }
+  if (blk_slot) {
+    const int off_b = base_b + ib - nb;
+    for (int i = 0; i < nb; i++) {
+      blk_slot[off_b + i] = slot;
+      blk_row0[off_b + i] = off_c + i * kMoeBM;
+    }
+    if (tid == 0) n_blocks[0] = tot_b;
   }
   if (tid < E) cursor[tid] = off_c;
   if (tid == 0) {
@@ -273,13 +306,14 @@ __device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int 
   }
 }
 
-__global__ __launch_bounds__(1024) void k_moe_sort(const int32_t* __restrict__ ids, int P,
-                                                   int E, int32_t* __restrict__ expert_list,
-                                                   int32_t* __restrict__ seg_off,
-                                                   int32_t* __restrict__ n_active,
-                                                   int32_t* __restrict__ sorted_pairs,
-                                                   uint32_t* __restrict__ amax) {
-  sort_pairs(ids, P, E, expert_list, seg_off, n_active, sorted_pairs, amax);
+__global__ __launch_bounds__(1024) void k_moe_sort(
+    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ expert_list,
+    int32_t* __restrict__ seg_off, int32_t* __restrict__ n_active,
+    int32_t* __restrict__ sorted_pairs, uint32_t* __restrict__ amax,
+    int32_t* __restrict__ blk_slot, int32_t* __restrict__ blk_row0,
+    int32_t* __restrict__ n_blocks) {
+  sort_pairs(ids, P, E, expert_list, seg_off, n_active, sorted_pairs, amax, blk_slot, blk_row0,
+             n_blocks);
 }
 
 // Small batches: routing, per-token quant of x and the sort in one
@@ -479,131 +513,246 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_skinny(
 }
 
 // ---------------------------------------------------------------------------
-// Grouped GEMM over the pairs of one expert.  MODE 1 = gemm1 (A = qx rows of
-// the pairs' tokens, epilogue SiLU(gate)*up), MODE 2 = gemm2 (A = qa rows of
-// the pairs, epilogue dequantised fp32 rows).  Wave tile: 16 pairs x 16
-// weight rows; up to 4 pair blocks share each weight load.  Operand mapping as
-// in gemm_skinny.hip.
+// Grouped GEMM for large batches.  Workgroup = (one m-block of up to kMoeBM
+// sorted pairs of one expert, BN = 32 * WAVES weight rows of that expert);
+// wave w owns weight rows n0 + 32w .. +31 and all the block's pair rows
+// (v_mfma_i32_32x32x32_i8).  The kernel streams weights from HBM, so the
+// weight operand goes straight from global memory into a ring of PF k steps
+// of registers per wave (with 2 waves per SIMD that keeps ~128 KiB of weight
+// loads in flight per CU; LDS could stage far less).  The gathered activation
+// rows are shared by the waves and come from L2: each k step every wave
+// loads two 16-row x 64-byte blocks into registers DA = 2 steps ahead and
+// writes them to one of two LDS buffers (1 KiB blocks of 16 rows x 4
+// k-slices, conflict-free), one barrier per step.  Loads never branch: rows
+// past the segment end re-read its last row, and steps past K read step 0
+// with the weight fragment zeroed.  32-row blocks past the segment end are
+// not multiplied.
+// MODE 1 = gemm1: A = qx rows of the pairs' tokens; epilogue dequantises and
+//          writes SiLU(gate) * up (gate = even interleaved row) as fp32 rows.
+// MODE 2 = gemm2: A = qa rows of the pairs; epilogue writes dequantised fp32.
 // ---------------------------------------------------------------------------
-template <int WAVES, int MODE, bool PACKED>
-__global__ __launch_bounds__(WAVES * 64) void k_moe_gemm(
+template <int MODE, int WAVES, int PF, bool PACKED, int MINB = 2>
+__global__ __launch_bounds__(WAVES * 64, MINB) void k_moe_tile(
     const int8_t* __restrict__ A, const float* __restrict__ sA, int a_div,
-    const int8_t* __restrict__ W, const float* __restrict__ sW, int Nw, int K,
+    const int8_t* __restrict__ W, const float* __restrict__ sW, int Nw, int K, int npw,
     const int32_t* __restrict__ expert_list, const int32_t* __restrict__ seg_off,
-    const int32_t* __restrict__ n_active, const int32_t* __restrict__ sorted_pairs,
-    float* __restrict__ out, int ldo, uint32_t* __restrict__ amax,
-    int32_t* __restrict__ dbg_acc) {
-  constexpr int U = 4;
-  const int slot = blockIdx.x;
-  if (slot >= n_active[0]) return;
+    const int32_t* __restrict__ blk_slot, const int32_t* __restrict__ blk_row0,
+    const int32_t* __restrict__ n_blocks, const int32_t* __restrict__ sorted_pairs,
+    float* __restrict__ out, int ldo, int32_t* __restrict__ dbg_acc) {
+  constexpr int BM = kMoeBM;
+  constexpr int BN = 32 * WAVES;
+  constexpr int NA = BM / 16;  // activation blocks per k step
+  constexpr int LA = NA / WAVES;
+  constexpr int DA = 2;        // activation register ring depth (steps)
+  static_assert(NA % WAVES == 0, "activation blocks must split evenly over waves");
+  static_assert(PF % DA == 0, "ring depths must nest");
+  // gemm2 walks npw weight blocks per workgroup with an epilogue after each;
+  // gemm1 (heavier epilogue, longer k) takes one block (npw must be 1)
+  constexpr bool kMulti = MODE == 2;
+  __shared__ __attribute__((aligned(1024))) int8_t a_lds[2][NA * 1024];
+  __shared__ int pair_lds[BM];
+  __shared__ float sa_lds[BM];
+
+  // Workgroups go to the 8 XCDs round-robin.  All the workgroups of one
+  // m-block run on the same XCD back to back, so its gathered activation rows
+  // are fetched into that XCD's L2 once.  Workgroup = npw consecutive BN-row
+  // weight blocks of the m-block's expert, streamed as one sequence of k steps.
+  const int ngrp = Nw / (BN * npw);
+  const int xcd = blockIdx.x & 7;
+  const int t = blockIdx.x >> 3;
+  const int mb = (t / ngrp) * 8 + xcd;
+  if (mb >= n_blocks[0]) return;
+  const int slot = blk_slot[mb];
+  const int row0 = blk_row0[mb];
+  const int e = expert_list[slot];
+  const int rows = min(BM, seg_off[slot + 1] - row0);
+  const int nfirst = (t % ngrp) * npw * BN;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int j = lane & 15;
   const int g = lane >> 4;
-  const int e = expert_list[slot];
-  const int seg_begin = seg_off[slot];
-  const int seg_end = seg_off[slot + 1];
-  const int n0 = (blockIdx.y * WAVES + wv) * 16;
-  if (n0 >= Nw) return;
   const int nk = K >> 6;
-  const int8_t* wp = PACKED ? W + ((int64_t)e * (Nw >> 4) + (n0 >> 4)) * nk * 1024 + lane * 16
-                            : W + ((int64_t)e * Nw + n0 + j) * K + g * 16;
-  constexpr int64_t wstep = PACKED ? 1024 : 64;
+  const int nsteps = (nk + PF - 1) / PF * PF;  // k steps per weight block, padded
 
-  for (int pb = seg_begin; pb < seg_end; pb += 64) {
-    const int nb = min(4, (seg_end - pb + 15) >> 4);  // wave-uniform
-    const int8_t* ap[4];
-    bool aok[4];
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-      const int idx = pb + b * 16 + j;
-      aok[b] = idx < seg_end;
-      const int p = aok[b] ? sorted_pairs[idx] : 0;
-      ap[b] = A + (int64_t)(p / a_div) * K + g * 16;
-    }
-    v4i acc[4];
-#pragma unroll
-    for (int b = 0; b < 4; b++) acc[b] = v4i{0, 0, 0, 0};
+  // weight fragment addresses: lane l feeds column c = n0 + 32 wv + l % 32,
+  // k-slice 2h + l/32 of each 32-byte half h of a 64-byte k step.  Global
+  // step s = (weight block s / nsteps, k step s % nsteps); padded steps read
+  // k step 0 and are zeroed before use.
+  const int c0 = nfirst + 32 * wv + (lane & 31);
+  const int8_t* bsrc =
+      PACKED ? W + ((int64_t)e * (Nw >> 4) + (c0 >> 4)) * nk * 1024 +
+                   ((c0 & 15) + 16 * (lane >> 5)) * 16
+             : W + ((int64_t)e * Nw + c0) * K + (lane >> 5) * 16;
+  constexpr int BSTEP = PACKED ? 1024 : 64;
+  constexpr int BHALF = PACKED ? 512 : 32;
+  const int64_t bblock = PACKED ? (int64_t)(BN >> 4) * nk * 1024 : (int64_t)BN * K;
+  const int send = npw * nsteps;
+  auto load_b = [&](int sg, v4i* b) __attribute__((always_inline)) {
+    const int sc = sg < send ? sg : 0;
+    const int nb = sc / nsteps, kt = sc - nb * nsteps;
+    const int8_t* q = bsrc + nb * bblock + (int64_t)(kt < nk ? kt : 0) * BSTEP;
+    b[0] = *reinterpret_cast<const v4i*>(q);
+    b[1] = *reinterpret_cast<const v4i*>(q + BHALF);
+  };
 
-    for (int c = 0; c < nk; c += U) {
-      v4i wb[U];
-      v4i a[4][U];
+  // the block's pair ids and activation scales, read once into LDS (the
+  // gather addresses and the epilogue use them)
+  for (int r = threadIdx.x; r < rows; r += WAVES * 64) {
+    const int p = sorted_pairs[row0 + r];
+    pair_lds[r] = p;
+    sa_lds[r] = sA[p / a_div];
+  }
+  // first weight loads go out before the wait for the pair table
+  v4i bq[PF][2];
 #pragma unroll
-      for (int u = 0; u < U; u++) {
-        const bool in = c + u < nk;
-        wb[u] = in ? *reinterpret_cast<const v4i*>(wp + (int64_t)(c + u) * wstep)
-                   : v4i{0, 0, 0, 0};
+  for (int s = 0; s < PF; s++) load_b(s, bq[s]);
+  lds_barrier();
+  const int8_t* asrc[LA];
 #pragma unroll
-        for (int b = 0; b < 4; b++)
-          a[b][u] = (in && b < nb && aok[b])
-                        ? *reinterpret_cast<const v4i*>(ap[b] + (int64_t)(c + u) * 64)
-                        : v4i{0, 0, 0, 0};
-      }
+  for (int i = 0; i < LA; i++) {
+    const int r = min((wv + i * WAVES) * 16 + j, rows - 1);
+    asrc[i] = A + (int64_t)(pair_lds[r] / a_div) * K + g * 16;
+  }
+  auto load_a = [&](int sg, v4i* a) __attribute__((always_inline)) {
+    const int kt = sg % nsteps;
+    const int kc = kt < nk ? kt : 0;
 #pragma unroll
-      for (int u = 0; u < U; u++)
+    for (int i = 0; i < LA; i++) a[i] = *reinterpret_cast<const v4i*>(asrc[i] + kc * 64);
+  };
+  v4i aq[DA][LA];
 #pragma unroll
-        for (int b = 0; b < 4; b++)
-          if (b < nb) acc[b] = mfma_16x16x64_i8(a[b][u], wb[u], acc[b]);
-    }
+  for (int s = 0; s < DA; s++) load_a(s, aq[s]);
 
-    // epilogue: lane holds pair rows 4g+v of weight row n0 + j, per block b
-    const int col = n0 + j;
+  // 32x32x32 fragment of one 32-byte k half: lane l reads row (l % 32) of a
+  // 32-row pair of blocks, k-slice 2h + l/32.
+  const int frag_off = ((lane >> 4) & 1) * 1024 + ((lane & 15) + 16 * (lane >> 5)) * 16;
+  v16i acc[BM / 32];
+  const int odd = lane & 1;
+
+  // epilogue of one weight block: lane holds weight row (product column)
+  // n0 + 32 wv + lane % 32 and pair rows 8*(v/4) + 4*(lane/32) + v%4 of each
+  // 32-row block
+  auto epilogue = [&](int n0) __attribute__((always_inline)) {
+    const int col = n0 + 32 * wv + (lane & 31);
     const float swc = sW[(int64_t)e * Nw + col];
 #pragma unroll
-    for (int b = 0; b < 4; b++) {
-      if (b >= nb) break;
+    for (int i = 0; i < BM / 32; i++) {
+      if (32 * i >= rows) break;
+      float h[16];
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int idx = pb + b * 16 + 4 * g + v;
-        const bool valid = idx < seg_end;
-        const int p = valid ? sorted_pairs[idx] : 0;
-        const int32_t av = acc[b][v];
-        if (dbg_acc && valid) dbg_acc[(int64_t)p * Nw + col] = av;
-        float h = 0.0f;
+      for (int v = 0; v < 16; v++) {
+        const int r = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const bool valid = r < rows;
+        const int32_t av = acc[i][v];
+        if (dbg_acc && valid) dbg_acc[(int64_t)pair_lds[r] * Nw + col] = av;
+        h[v] = 0.0f;
         if (valid) {
-          h = (float)av;
-          h = h * sA[p / a_div];
-          h = h * swc;
+          h[v] = (float)av;
+          h[v] = h[v] * sa_lds[r];
+          h[v] = h[v] * swc;
         }
-        if (MODE == 1) {
-          const float partner = __shfl_xor(h, 1, 64);
-          float mag = 0.0f;
-          if ((j & 1) == 0 && valid) {
-            // SiLU(gate) * up; the gate is the even interleaved row
-            const float sg = (float)((double)h / (1.0 + exp(-(double)h)));
-            const float act = sg * partner;
-            out[(int64_t)p * ldo + (col >> 1)] = act;
-            mag = fabsf(act);
-          }
+        if (MODE == 2 && valid) out[(int64_t)pair_lds[r] * ldo + col] = h[v];
+      }
+      if (MODE == 1) {
+        // gate = even interleaved row, up = the odd one in the neighbouring
+        // lane.  The pair of lanes splits the 16 rows: the even lane finishes
+        // rows v < 8, the odd lane rows v >= 8.
+        float x[16];
 #pragma unroll
-          for (int off = 1; off < 16; off <<= 1) mag = fmaxf(mag, __shfl_xor(mag, off, 64));
-          if (j == 0 && valid) atomicMax(&amax[p], __float_as_uint(mag));
-        } else {
-          if (valid) out[(int64_t)p * ldo + col] = h;
+        for (int v = 0; v < 16; v++) x[v] = __shfl_xor(h[v], 1, 64);
+#pragma unroll
+        for (int v = 0; v < 8; v++) {
+          const int vv = v + 8 * odd;
+          const int r = 32 * i + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
+          const float gate = odd ? x[v + 8] : h[v];
+          const float up = odd ? h[v + 8] : x[v];
+          if (r < rows) {
+            const float sg = (float)((double)gate / (1.0 + exp(-(double)gate)));
+            out[(int64_t)pair_lds[r] * ldo + (col >> 1)] = sg * up;
+          }
         }
       }
     }
-  }
+  };
+
+  auto mainloop = [&](auto tma_c) __attribute__((always_inline)) {
+    constexpr int TMA = decltype(tma_c)::value;  // 32-row blocks holding pairs
+#pragma unroll
+    for (int i = 0; i < BM / 32; i++) acc[i] = v16i{0};
+    for (int s0 = 0; s0 < send; s0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; u++) {
+        const int sg = s0 + u;
+        int8_t* buf = a_lds[u & 1];
+#pragma unroll
+        for (int i = 0; i < LA; i++)
+          *reinterpret_cast<v4i*>(buf + (wv + i * WAVES) * 1024 + lane * 16) = aq[u % DA][i];
+        load_a(sg + DA, aq[u % DA]);
+        lds_barrier();
+        const int8_t* st = buf + frag_off;
+        v4i fa[2][TMA];
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+          for (int i = 0; i < TMA; i++)
+            fa[h][i] = *reinterpret_cast<const v4i*>(st + h * 512 + i * 2048);
+        const bool kin = (sg % nsteps) < nk;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const v4i bf = kin ? bq[u][h] : v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int i = 0; i < TMA; i++) acc[i] = mfma_32x32x32_i8(fa[h][i], bf, acc[i]);
+        }
+        load_b(sg + PF, bq[u]);
+      }
+      if (kMulti && (s0 + PF) % nsteps == 0) {  // a weight block is complete
+        epilogue(nfirst + ((s0 + PF) / nsteps - 1) * BN);
+#pragma unroll
+        for (int i = 0; i < BM / 32; i++) acc[i] = v16i{0};
+      }
+    }
+  };
+  const int tma = (rows + 31) >> 5;
+  if (tma >= 4)
+    mainloop(std::integral_constant<int, 4>{});
+  else if (tma == 3)
+    mainloop(std::integral_constant<int, 3>{});
+  else if (tma == 2)
+    mainloop(std::integral_constant<int, 2>{});
+  else
+    mainloop(std::integral_constant<int, 1>{});
+  if (!kMulti) epilogue(nfirst);
 }
 
-// Per-pair requant of the fp32 activation rows (one wave per pair).
-__global__ __launch_bounds__(256) void k_moe_requant(const float* __restrict__ act,
-                                                     const uint32_t* __restrict__ amax, int P,
+// Per-pair requant of the fp32 activation rows (one wave per pair row; the
+// row maximum is found here).  I <= 4096: at most 64 values per lane.
+template <int VPL>  // values per lane, I <= 64 * VPL
+__global__ __launch_bounds__(256) void k_moe_requant(const float* __restrict__ act, int P,
                                                      int I, int8_t* __restrict__ qa,
                                                      float* __restrict__ sa2) {
   const int lane = threadIdx.x & 63;
   const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (p >= P) return;
-  const float am = __uint_as_float(amax[p]);
-  const float sc = am / 127.0f;
   const float* ar = act + (int64_t)p * I;
+  v4f a[VPL / 4];
+  float am = 0.0f;
+#pragma unroll
+  for (int u = 0; u < VPL / 4; u++) {
+    const int c = (u * 64 + lane) * 4;
+    a[u] = c < I ? *reinterpret_cast<const v4f*>(ar + c) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    am = fmaxf(am, fmaxf(fmaxf(fabsf(a[u].x), fabsf(a[u].y)), fmaxf(fabsf(a[u].z), fabsf(a[u].w))));
+  }
+  am = wave_max(am);
+  const float sc = am / 127.0f;
   int8_t* qr = qa + (int64_t)p * I;
-  for (int c = lane * 4; c < I; c += 256) {
-    const v4f a = *reinterpret_cast<const v4f*>(ar + c);
+#pragma unroll
+  for (int u = 0; u < VPL / 4; u++) {
+    const int c = (u * 64 + lane) * 4;
+    if (c >= I) break;
     uint32_t wd = 0;
     if (am != 0.0f)
-      wd = pack4_i8(quant_code(a.x, sc), quant_code(a.y, sc), quant_code(a.z, sc),
-                    quant_code(a.w, sc));
+      wd = pack4_i8(quant_code(a[u].x, sc), quant_code(a[u].y, sc), quant_code(a[u].z, sc),
+                    quant_code(a[u].w, sc));
     *reinterpret_cast<uint32_t*>(qr + c) = wd;
   }
   if (lane == 0) sa2[p] = am != 0.0f ? sc : 0.0f;
@@ -692,23 +841,39 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
-                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax);
+                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax,
+                       ws.blk_slot, ws.blk_row0, ws.n_blocks);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_quant_rows(a.x, 0, a.T, a.H, a.H, ws.qx, a.H, ws.sx, stream)) !=
         hipSuccess)
       return err;
-    hipLaunchKernelGGL((k_moe_gemm<4, 1, PACKED>), dim3(slots, (I2 / 16 + 3) / 4), dim3(256), 0,
-                       stream, ws.qx, ws.sx, a.k, a.w13, a.s13, I2, a.H, ws.expert_list,
-                       ws.seg_off, ws.n_active, ws.sorted_pairs, ws.act, a.I, ws.amax,
-                       a.dbg_acc1);
+    // m-blocks: at most one partial block per expert that received pairs;
+    // the grid covers that bound rounded up to the 8 XCDs
+    const unsigned max_blocks = (unsigned)((P / kMoeBM + slots + 7) / 8 * 8);
+    hipLaunchKernelGGL((k_moe_tile<1, 4, 4, PACKED>), dim3(max_blocks * (I2 / 128)),
+                       dim3(256), 0, stream, ws.qx, ws.sx, a.k, a.w13, a.s13, I2, a.H, 1,
+                       ws.expert_list,
+                       ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks, ws.sorted_pairs,
+                       ws.act, a.I, a.dbg_acc1);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_moe_requant, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, stream,
-                       ws.act, ws.amax, (int)P, a.I, ws.qa, ws.sa2);
+    if (a.I <= 1024)
+      hipLaunchKernelGGL(k_moe_requant<16>, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, stream,
+                         ws.act, (int)P, a.I, ws.qa, ws.sa2);
+    else
+      hipLaunchKernelGGL(k_moe_requant<64>, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, stream,
+                         ws.act, (int)P, a.I, ws.qa, ws.sa2);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_moe_gemm<4, 2, PACKED>), dim3(slots, (a.H / 16 + 3) / 4), dim3(256), 0,
-                       stream, ws.qa, ws.sa2, 1, a.w2, a.s2, a.H, a.I, ws.expert_list,
-                       ws.seg_off, ws.n_active, ws.sorted_pairs, ws.y2, a.H, nullptr,
-                       a.dbg_acc2);
+    const int npw2 = (a.H / 128) % 8 == 0 ? 8 : (a.H / 128) % 4 == 0 ? 4 : 1;
+    if (a.H % 128 == 0)
+      hipLaunchKernelGGL((k_moe_tile<2, 4, 4, PACKED>), dim3(max_blocks * (a.H / 128 / npw2)),
+                         dim3(256), 0, stream, ws.qa, ws.sa2, 1, a.w2, a.s2, a.H, a.I, npw2,
+                         ws.expert_list, ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks,
+                         ws.sorted_pairs, ws.y2, a.H, a.dbg_acc2);
+    else
+      hipLaunchKernelGGL((k_moe_tile<2, 2, 4, PACKED>), dim3(max_blocks * (a.H / 64)),
+                         dim3(128), 0, stream, ws.qa, ws.sa2, 1, a.w2, a.s2, a.H, a.I, 1,
+                         ws.expert_list, ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks,
+                         ws.sorted_pairs, ws.y2, a.H, a.dbg_acc2);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)P * a.I,
                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)

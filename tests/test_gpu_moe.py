@@ -98,7 +98,8 @@ def test_small_full_pipeline(orc, packed):
 @pytest.mark.parametrize("packed", [False, True])
 def test_large_batch_path(orc, packed):
     # more than 2048 routed pairs: the routing/sort/quant kernels, the
-    # 64-pair-block grouped GEMMs and the separate requant kernel
+    # 128-pair m-block grouped GEMMs (several blocks per expert here) and the
+    # separate requant kernel
     T, E, H, I, k = 700, 8, 128, 64, 4
     key = (43, 1)
     W = _weights(orc, key, E, H, I)
@@ -107,6 +108,41 @@ def test_large_batch_path(orc, packed):
     logits[:, 2] += 1.5  # a hot expert: most tokens route to expert 2
     assert _tie_free(logits, k)
     _check_full(orc, x, logits, k, W, T, "moe large-batch path", packed=packed)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_large_batch_narrow_hidden(orc, packed):
+    # large path with H % 128 != 0: gemm2 uses 64-row weight blocks
+    T, E, H, I, k = 600, 4, 192, 128, 4
+    key = (44, 1)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    logits = synth.router_logits(key, T, E)
+    assert _tie_free(logits, k)
+    _check_full(orc, x, logits, k, W, T, "moe large-batch H=192", packed=packed)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_large_batch_wide_hidden(orc, packed):
+    # large path with H = 1024: each gemm2 workgroup walks 8 weight blocks
+    T, E, H, I, k = 520, 4, 1024, 64, 4
+    key = (46, 1)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    logits = synth.router_logits(key, T, E)
+    assert _tie_free(logits, k)
+    _check_full(orc, x, logits, k, W, T, "moe large-batch H=1024", packed=packed)
+
+
+def test_large_batch_wide_intermediate(orc):
+    # large path with I > 1024 (the requant keeps 64 values per lane)
+    T, E, H, I, k = 520, 4, 64, 1088, 4
+    key = (45, 1)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    logits = synth.router_logits(key, T, E)
+    assert _tie_free(logits, k)
+    _check_full(orc, x, logits, k, W, T, "moe large-batch I=1088", packed=True)
 
 
 def test_given_routing_hot_expert_and_edges(orc):
