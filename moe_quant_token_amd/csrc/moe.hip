@@ -91,10 +91,11 @@ MoeWs carve(void* base, int64_t T, int64_t H, int64_t E, int64_t I, int k) {
 }  // namespace
 
 // Wave-wide maximum of a 32-bit unsigned key through DPP row shifts and row
-// broadcasts (no LDS traffic); every lane gets the result.
+// broadcasts (no LDS traffic); every lane gets the result.  Lanes a shift
+// reads past the row edge get 0, the identity of the maximum.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#define W8A8_DPP_MAX(ctrl, rmask)                                                          \
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, rmask, 0xf, false))
+#define W8A8_DPP_MAX(ctrl, rmask) \
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, rmask, 0xf, true))
   W8A8_DPP_MAX(0x111, 0xf);  // row_shr:1
   W8A8_DPP_MAX(0x112, 0xf);  // row_shr:2
   W8A8_DPP_MAX(0x114, 0xf);  // row_shr:4
@@ -119,9 +120,10 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // Selection compares the fp32 logits (softmax is monotonic): slot s gets the
 // s-th largest, equal logits go to the lower expert index.  Each round takes
 // the wave maximum of the key (logit, then 2^32-1-index) over the experts not
-// yet taken.  Each probability exp(l - max) / sum is formed in fp64 (every
-// lane evaluates the winner's, so nothing is broadcast), the kept ones are
-// summed in slot order and each renormalised weight is rounded once to fp32.
+// yet taken; lane s keeps slot s.  The rounds hold no floating-point work:
+// afterwards lane s forms its probability exp(l - max) / sum in fp64 (all
+// slots at once), the kept probabilities are summed in slot order and each
+// renormalised weight is rounded once to fp32.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E, int k,
                                             int32_t* __restrict__ ids, float* __restrict__ w,
@@ -131,42 +133,59 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E,
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? lt[e] : -INFINITY;
+    v[i] = (64 * i < E && e < E) ? lt[e] : -INFINITY;
     lmax = fmaxf(lmax, v[i]);
   }
   const double mx = (double)wave_max(lmax);
-  double z = 0.0;
-#pragma unroll
-  for (int i = 0; i < 16; i++)
-    if (lane + 64 * i < E) z += exp((double)v[i] - mx);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
 
   uint32_t taken = 0;
-  double kept = 0.0, myp = 0.0;
+  int my_e = 0;
+  float my_l = 0.0f;
   for (int s = 0; s < k; s++) {
     uint32_t hi = 0, lo = 0;  // best local key; 0 = none
 #pragma unroll
     for (int i = 0; i < 16; i++) {
+      if (64 * i >= E) break;  // uniform
       const int e = lane + 64 * i;
-      if (e < E && !(taken & (1u << i))) {
-        const uint32_t kh = float_key(v[i]);
-        if (kh > hi) {  // ascending e: ties keep the lower index
-          hi = kh;
-          lo = 0xffffffffu - (uint32_t)e;
-        }
+      const uint32_t kh = float_key(v[i]);
+      // ascending e: ties keep the lower index
+      if (e < E && !(taken & (1u << i)) && kh > hi) {
+        hi = kh;
+        lo = 0xffffffffu - (uint32_t)e;
       }
     }
     const uint32_t mh = wave_max_u32(hi);
-    const uint32_t ml = wave_max_u32(hi == mh ? lo : 0u);
+    // the lane holding the maximum; equal keys on several lanes (tied
+    // logits) take a second reduction for the lowest index
+    const uint64_t holders = __ballot(hi == mh);
+    uint32_t ml;
+    if (__popcll(holders) == 1)
+      ml = (uint32_t)__builtin_amdgcn_readlane((int)lo, __ffsll((long long)holders) - 1);
+    else
+      ml = wave_max_u32(hi == mh ? lo : 0u);
     const int be = (int)(0xffffffffu - ml);
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    const double ps = exp((double)key_float(mh) - mx) / z;
-    kept += ps;
-    if (lane == s) myp = ps;
-    if (lane == 0) ids[s] = be;
+    if (lane == s) {
+      my_e = be;
+      my_l = key_float(mh);
+    }
   }
-  if (lane < k) w[lane] = (float)(myp / kept);
+  // softmax denominator: each lane's terms, then the wave sum
+  double z = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    if (64 * i >= E) break;
+    if (lane + 64 * i < E) z += exp((double)v[i] - mx);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+  const double myp = exp((double)my_l - mx) / z;
+  double kept = 0.0;
+  for (int s = 0; s < k; s++) kept += __shfl(myp, s, 64);
+  if (lane < k) {
+    ids[lane] = my_e;
+    w[lane] = (float)(myp / kept);
+  }
 }
 
 __global__ __launch_bounds__(256) void k_moe_route(const float* __restrict__ logits, int T,
@@ -180,33 +199,65 @@ __global__ __launch_bounds__(256) void k_moe_route(const float* __restrict__ log
 
 // One wave quantises one bf16 row of length K (K % 16 == 0), exactly as
 // k_quant_rows does: amax / 127 in fp32, round-half-even of the quotient.
+// Rows up to 4096 are held in registers (one read); longer rows are read
+// twice (the second time from L2).
+__device__ __forceinline__ uint32_t quant_pack4_bf16(uint32_t w0, uint32_t w1, float sc) {
+  return pack4_i8(quant_code(bf16_bits_to_f32(w0 & 0xffffu), sc),
+                  quant_code(bf16_bits_to_f32(w0 >> 16), sc),
+                  quant_code(bf16_bits_to_f32(w1 & 0xffffu), sc),
+                  quant_code(bf16_bits_to_f32(w1 >> 16), sc));
+}
+__device__ __forceinline__ float amax8_bf16(v4u raw) {
+  const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    a = fmaxf(a, fmaxf(fabsf(bf16_bits_to_f32(wd[i] & 0xffffu)),
+                       fabsf(bf16_bits_to_f32(wd[i] >> 16))));
+  return a;
+}
 __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ x, int K,
                                                int8_t* __restrict__ q, float* __restrict__ s,
                                                int lane) {
-  float amax = 0.0f;
-  for (int c = lane; c < (K >> 3); c += 64) {
-    const v4u raw = *reinterpret_cast<const v4u*>(x + c * 8);
-    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+  const int nc = K >> 3;  // 8-element (16-byte) chunks
+  if (nc <= 512) {
+    v4u raw[8];
+    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(wd[i] & 0xffffu)),
-                               fabsf(bf16_bits_to_f32(wd[i] >> 16))));
+    for (int u = 0; u < 8; u++) {
+      const int c = lane + 64 * u;
+      raw[u] = c < nc ? *reinterpret_cast<const v4u*>(x + c * 8) : v4u{0u, 0u, 0u, 0u};
+      amax = fmaxf(amax, amax8_bf16(raw[u]));
+    }
+    amax = wave_max(amax);
+    const float sc = amax / 127.0f;
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int c = lane + 64 * u;
+      if (c >= nc) break;
+      uint32_t lo = 0, hi = 0;
+      if (amax != 0.0f) {
+        lo = quant_pack4_bf16(raw[u].x, raw[u].y, sc);
+        hi = quant_pack4_bf16(raw[u].z, raw[u].w, sc);
+      }
+      uint32_t* o = reinterpret_cast<uint32_t*>(q + c * 8);
+      o[0] = lo;
+      o[1] = hi;
+    }
+    if (lane == 0) s[0] = amax != 0.0f ? sc : 0.0f;
+    return;
   }
+  float amax = 0.0f;
+  for (int c = lane; c < nc; c += 64)
+    amax = fmaxf(amax, amax8_bf16(*reinterpret_cast<const v4u*>(x + c * 8)));
   amax = wave_max(amax);
   const float sc = amax / 127.0f;
-  for (int c = lane; c < (K >> 3); c += 64) {
+  for (int c = lane; c < nc; c += 64) {
     const v4u raw = *reinterpret_cast<const v4u*>(x + c * 8);
-    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
     uint32_t lo = 0, hi = 0;
     if (amax != 0.0f) {
-      lo = pack4_i8(quant_code(bf16_bits_to_f32(wd[0] & 0xffffu), sc),
-                    quant_code(bf16_bits_to_f32(wd[0] >> 16), sc),
-                    quant_code(bf16_bits_to_f32(wd[1] & 0xffffu), sc),
-                    quant_code(bf16_bits_to_f32(wd[1] >> 16), sc));
-      hi = pack4_i8(quant_code(bf16_bits_to_f32(wd[2] & 0xffffu), sc),
-                    quant_code(bf16_bits_to_f32(wd[2] >> 16), sc),
-                    quant_code(bf16_bits_to_f32(wd[3] & 0xffffu), sc),
-                    quant_code(bf16_bits_to_f32(wd[3] >> 16), sc));
+      lo = quant_pack4_bf16(raw.x, raw.y, sc);
+      hi = quant_pack4_bf16(raw.z, raw.w, sc);
     }
     uint32_t* o = reinterpret_cast<uint32_t*>(q + c * 8);
     o[0] = lo;
@@ -314,6 +365,20 @@ __global__ __launch_bounds__(1024) void k_moe_sort(
     int32_t* __restrict__ n_blocks) {
   sort_pairs(ids, P, E, expert_list, seg_off, n_active, sorted_pairs, amax, blk_slot, blk_row0,
              n_blocks);
+}
+
+// Routing and per-token quant, one wave per token (small batches with more
+// tokens than the single-workgroup prep has waves).
+__global__ __launch_bounds__(256) void k_moe_route_quant(
+    const uint16_t* __restrict__ x, const float* __restrict__ logits, int T, int H, int E, int k,
+    int32_t* __restrict__ ids, float* __restrict__ w, int8_t* __restrict__ qx,
+    float* __restrict__ sx) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  if (logits)
+    route_token(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k, lane);
+  quant_row_wave(x + (int64_t)t * H, H, qx + (int64_t)t * H, sx + t, lane);
 }
 
 // Small batches: routing, per-token quant of x and the sort in one
@@ -795,6 +860,9 @@ size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int k) {
 // four launches.  Larger batches: routing, sort and quant kernels, the
 // 64-pair-block grouped GEMMs, a requant kernel and the combine.
 constexpr int64_t kMoeSmallPairs = 2048;
+// up to this many tokens the small path routes, quantises and sorts in one
+// workgroup (16 waves); beyond, one wave per token and a separate sort
+constexpr int kMoePrepTokens = 16;
 
 template <bool PACKED>
 static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
@@ -805,9 +873,18 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
   hipError_t err;
   const bool small = P <= kMoeSmallPairs && a.I <= kMoeSkinnyMaxK2;
   if (small) {
-    hipLaunchKernelGGL(k_moe_prep, dim3(1), dim3(1024), 0, stream, a.x, a.logits, a.T, a.H, a.E,
-                       a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx, ws.expert_list, ws.seg_off,
-                       ws.n_active, ws.sorted_pairs, ws.amax);
+    if (a.T <= kMoePrepTokens) {
+      hipLaunchKernelGGL(k_moe_prep, dim3(1), dim3(1024), 0, stream, a.x, a.logits, a.T, a.H,
+                         a.E, a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx, ws.expert_list,
+                         ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax);
+    } else {
+      hipLaunchKernelGGL(k_moe_route_quant, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.x,
+                         a.logits, a.T, a.H, a.E, a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
+                         ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax,
+                         nullptr, nullptr, nullptr);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // tiny batches: one weight tile per workgroup (most parallelism); else
     // eight tiles per workgroup
