@@ -7,9 +7,9 @@
 //
 // At M <= 16 every weight byte is used once, so the kernel is bound by HBM
 // reads of the [N, K] int8 weights.  Each workgroup owns 16 output channels
-// (one 16x16x64 MFMA column tile).  Its 16 waves take the tile's 64-byte k
-// steps round-robin (wave w: steps w, w+16, ...), so at any moment the
-// workgroup streams one contiguous stretch of the tile; every wave keeps four
+// (one 16x16x64 MFMA column tile).  Its waves take the tile's 64-byte k
+// steps round-robin (wave w of W: steps w, w+W, ...), so at any moment the
+// workgroup streams one contiguous stretch of the tile; every wave keeps U
 // 1 KiB weight loads in flight.  The waves' int32 partial sums are added
 // exactly through LDS and the fp32 epilogue runs in registers: no workspace
 // and no cross-workgroup traffic.
@@ -83,12 +83,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
   }
 }
 
+// 8 waves x 8 loads of 1 KiB in flight per wave (measured on MI355X over
+// waves in {4, 8, 16} and depths 4..24 at the decode shapes)
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyU = 8;
+
 template <bool PACKED, bool STORE_I32>
 static hipError_t launch_skinny_impl(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                                      int64_t lda, const int8_t* qw, const float* sw, int64_t N,
                                      int64_t ldw, void* out, int64_t ldo, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_skinny<16, 4, PACKED, STORE_I32>), dim3((unsigned)(N / 16)),
-                     dim3(1024), 0, stream, qa, sa, (int)M, (int)K, lda, qw, sw, ldw, out, ldo);
+  hipLaunchKernelGGL((k_gemm_skinny<kSkinnyWaves, kSkinnyU, PACKED, STORE_I32>),
+                     dim3((unsigned)(N / 16)), dim3(kSkinnyWaves * 64), 0, stream, qa, sa, (int)M,
+                     (int)K, lda, qw, sw, ldw, out, ldo);
   return hipGetLastError();
 }
 

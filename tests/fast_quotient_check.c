@@ -1,0 +1,44 @@
+/* Exhaustive check of the reciprocal quotient the quantisation kernels use
+ * for bf16 rows.  For every positive finite bf16 value a (a row maximum) with
+ * s = fl(a / 127) >= 2^-100, and every bf16 x with 0 <= x <= a:
+ *   r = fl(1 / s), q0 = fl(x * r), e = fma(-q0, s, x), q = fma(e, r, q0)
+ * must satisfy rint(q) == rint(fl(x / s)).  Negative x need no check: every
+ * step is symmetric in the sign of x.  Prints the number of pairs checked and
+ * the number of mismatches (also for the bare product q0, which is not exact:
+ * the check can tell the two apart). */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+static float bf16(uint32_t h)
+{
+    uint32_t u = h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+int main(void)
+{
+    long long pairs = 0, bad = 0, bad_product = 0;
+#pragma omp parallel for reduction(+ : pairs, bad, bad_product) schedule(dynamic, 64)
+    for (uint32_t ha = 1; ha < 0x7f80; ha++) {
+        const float a = bf16(ha);
+        const float s = a / 127.0f;
+        if (!(s >= 0x1p-100f)) continue;
+        const float r = 1.0f / s;
+        for (uint32_t hx = 0; hx <= ha; hx++) {
+            const float x = bf16(hx);
+            const float ref = rintf(x / s);
+            const float q0 = x * r;
+            const float e = fmaf(-q0, s, x);
+            const float q = fmaf(e, r, q0);
+            bad += rintf(q) != ref;
+            bad_product += rintf(q0) != ref;
+            pairs++;
+        }
+    }
+    printf("%lld %lld %lld\n", pairs, bad, bad_product);
+    return 0;
+}

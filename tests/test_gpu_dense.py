@@ -125,6 +125,28 @@ def test_gemm_i32_and_bf16(orc, M, K, N, packed):
     np.testing.assert_array_equal(bf16_host(y2), y_ref)
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_linear_decode_zero_row_and_stride(orc, packed):
+    # the fused decode linear: an all-zero token, a strided activation matrix
+    M, K, N = 5, 640, 48
+    x, W = _inputs((10, M), (10, N), M, K, N, 4, 20.0)
+    x[2] = 0
+    qw, sw = orc.quant_rows(W)
+    y_ref = orc.linear_w8a8(x, qw, sw)
+    big = np.zeros((M, K + 64), np.uint16)
+    big[:, :K] = x
+    xd = bf16_dev(big)[:, :K]
+    qw_d, sw_d = dev(qw), dev(sw)
+    if packed:
+        y = mq.linear_w8a8_packed(xd, mq.pack_weights(qw_d), sw_d, N)
+    else:
+        y = mq.linear_w8a8(xd, qw_d, sw_d)
+    torch.cuda.synchronize()
+    got = bf16_host(y)
+    np.testing.assert_array_equal(got, y_ref)
+    assert not got[2].any()
+
+
 def test_gemm_extreme_codes_no_overflow():
     # every code +-127 at the largest decode K: |acc| = 127*127*8704
     K, N = 8704, 32
