@@ -385,6 +385,7 @@ def hadamard_cases(torch, np, mq, synth, dev, timer, bf16_dev):
     K, N = cfg["K"], cfg["N"]
     W = torch.from_numpy(synth.weights(cfg["wkey"], N, K)).to(dev)
     qw, su8, s2 = mq.fwht128_weight_prep_g256(W)
+    qw = mq.pack_weights(qw)  # MFMA tile layout, untimed
     del W
     wbytes = N * K + N * K // 256 + 2 * N
     ncopy = max(2, math.ceil(2 * MALL_BYTES / wbytes) + 1)
@@ -398,10 +399,12 @@ def hadamard_cases(torch, np, mq, synth, dev, timer, bf16_dev):
         s = torch.empty((M,), dtype=torch.float32, device=dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
+        ws = torch.empty(max(mq.linear_w8a8_g256_workspace_bytes(M, N, K), 256),
+                         dtype=torch.uint8, device=dev)
+
         def fn(i):
             w = copies[i % len(copies)]
-            mq.fwht128_quant(x, q=q, s=s)
-            mq.gemm_w8a8_g256(q, s, w[0], w[1], w[2], y=y)
+            mq.linear_w8a8_g256_packed(x, w[0], w[1], w[2], y=y, ws=ws)
 
         for i in range(3):
             fn(i)

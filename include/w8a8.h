@@ -232,6 +232,28 @@ int gemm_w8a8_g256(const int8_t *qa, const float *sa, int64_t M, int64_t K, cons
                    const uint8_t *su8, const uint16_t *s2, int64_t N, uint16_t *y, int64_t ldy,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* gemm_w8a8_g256 with the codes in the packed tile layout of                */
+/* w8a8_pack_weights (applied to the prepared qw once, at load): same        */
+/* arithmetic, same results, same shape rules and workspace.                 */
+int gemm_w8a8_g256_packed(const int8_t *qa, const float *sa, int64_t M, int64_t K,
+                          const int8_t *qw_packed, const uint8_t *su8, const uint16_t *s2,
+                          int64_t N, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* The whole Hadamard-domain linear: bf16 x -> fwht128 + per-token quant    */
+/* (as fwht128_quant) -> g256 GEMM (as gemm_w8a8_g256) on packed codes ->    */
+/* bf16 y.  [IQ8R] Trunk and Activations rows.  The activation codes and     */
+/* scales live in the workspace (linear_w8a8_g256_workspace_bytes).          */
+/* x: bf16 [M, K] (ldx, multiple of 16, 16-byte aligned); other operands as  */
+/* gemm_w8a8_g256_packed.  Requires K % 256 == 0, K <= 16384, N % 16 == 0.   */
+/* ------------------------------------------------------------------------ */
+size_t linear_w8a8_g256_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int linear_w8a8_g256_packed(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                            const int8_t *qw_packed, const uint8_t *su8, const uint16_t *s2,
+                            int64_t N, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,6 +71,11 @@ _SIGS = {
     "fwht128_quant": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp], _i32),
     "fwht128_weight_prep_g256": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp], _i32),
     "gemm_w8a8_g256_workspace_bytes": ([_i64, _i64, _i64], _sz),
+    "linear_w8a8_g256_workspace_bytes": ([_i64, _i64, _i64], _sz),
+    "linear_w8a8_g256_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
+                                 _sz, _vp], _i32),
+    "gemm_w8a8_g256_packed": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz,
+                               _vp], _i32),
     "gemm_w8a8_g256": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp],
                        _i32),
 }
@@ -320,15 +325,38 @@ def fwht128_weight_prep_g256(W):
 
 
 def gemm_w8a8_g256(qa, sa, qw, su8, s2, y: torch.Tensor | None = None,
-                   ws: torch.Tensor | None = None):
-    """Hadamard-domain GEMM with per-256 u8 group scales and a bf16 row scale."""
+                   ws: torch.Tensor | None = None, packed: bool = False):
+    """Hadamard-domain GEMM with per-256 u8 group scales and a bf16 row scale.
+
+    With ``packed`` the codes ``qw`` are in the packed tile layout
+    (``pack_weights`` of the prepared codes); ``N`` is then ``su8.shape[0]``."""
     _req(qa, torch.int8, "qa")
     _req(qw, torch.int8, "qw")
     M, K = qa.shape
-    N = qw.shape[0]
+    N = su8.shape[0]
     y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device) if y is None else y
     ws, wsb = _workspace(lib().gemm_w8a8_g256_workspace_bytes(M, N, K), qa.device, ws)
-    _check("gemm_w8a8_g256",
-           lib().gemm_w8a8_g256(_ptr(qa), _ptr(sa), M, K, _ptr(qw), _ptr(su8), _ptr(s2), N,
-                                _ptr(y), y.stride(0), _ptr(ws), wsb, _stream(qa.device)))
+    fn = "gemm_w8a8_g256_packed" if packed else "gemm_w8a8_g256"
+    _check(fn, getattr(lib(), fn)(_ptr(qa), _ptr(sa), M, K, _ptr(qw), _ptr(su8), _ptr(s2), N,
+                                  _ptr(y), y.stride(0), _ptr(ws), wsb, _stream(qa.device)))
+    return y
+
+
+def linear_w8a8_g256_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().linear_w8a8_g256_workspace_bytes(M, N, K))
+
+
+def linear_w8a8_g256_packed(x, qw_packed, su8, s2, y: torch.Tensor | None = None,
+                            ws: torch.Tensor | None = None):
+    """bf16 x -> fwht128 + per-token int8 -> g256 GEMM on packed codes -> bf16 y."""
+    _req(x, torch.bfloat16, "x")
+    _req(qw_packed, torch.int8, "qw_packed")
+    M, K = x.shape
+    N = su8.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    ws, wsb = _workspace(lib().linear_w8a8_g256_workspace_bytes(M, N, K), x.device, ws)
+    _check("linear_w8a8_g256_packed",
+           lib().linear_w8a8_g256_packed(_ptr(x), M, K, x.stride(0), _ptr(qw_packed), _ptr(su8),
+                                         _ptr(s2), N, _ptr(y), y.stride(0), _ptr(ws), wsb,
+                                         _stream(x.device)))
     return y

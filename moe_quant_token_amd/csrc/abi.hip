@@ -333,9 +333,10 @@ size_t gemm_w8a8_g256_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return g256_workspace_bytes(M, N, K);
 }
 
-int gemm_w8a8_g256(const int8_t* qa, const float* sa, int64_t M, int64_t K, const int8_t* qw,
-                   const uint8_t* su8, const uint16_t* s2, int64_t N, uint16_t* y, int64_t ldy,
-                   void* ws, size_t ws_bytes, void* stream) {
+static int g256_common(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                       const int8_t* qw, const uint8_t* su8, const uint16_t* s2, int64_t N,
+                       bool packed, uint16_t* y, int64_t ldy, void* ws, size_t ws_bytes,
+                       void* stream) {
   if (M < 0 || K <= 0 || N <= 0 || ldy < N) return W8A8_INVALID_ARG;
   if (K % 256 != 0 || K > 16384 || N % 16 != 0 || N > (int64_t)1 << 30 || M > (int64_t)1 << 30)
     return W8A8_UNSUPPORTED_SHAPE;
@@ -345,8 +346,49 @@ int gemm_w8a8_g256(const int8_t* qa, const float* sa, int64_t M, int64_t K, cons
   if (ws_bytes < gemm_w8a8_g256_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
   int r = check_device();
   if (r != W8A8_OK) return r;
-  hipError_t e = launch_gemm_g256(qa, sa, M, K, qw, su8, s2, N, y, ldy, ws, as_stream(stream));
+  hipError_t e =
+      launch_gemm_g256(qa, sa, M, K, qw, su8, s2, N, packed, y, ldy, ws, as_stream(stream));
   return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+size_t linear_w8a8_g256_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
+  return act_codes_bytes(M, K) + align_up((size_t)M * 4);
+}
+
+int linear_w8a8_g256_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            const int8_t* qw_packed, const uint8_t* su8, const uint16_t* s2,
+                            int64_t N, uint16_t* y, int64_t ldy, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (M < 0 || K <= 0 || N <= 0 || ldx < K || ldy < N) return W8A8_INVALID_ARG;
+  if (K % 256 != 0 || K > 16384 || N % 16 != 0 || N > (int64_t)1 << 30 || M > (int64_t)1 << 30)
+    return W8A8_UNSUPPORTED_SHAPE;
+  if (M == 0) return W8A8_OK;
+  if (!x || !qw_packed || !su8 || !s2 || !y) return W8A8_INVALID_ARG;
+  if (!al16(x) || !al16(qw_packed) || !al4(y) || ldy % 2 != 0 || ldx % 16 != 0)
+    return W8A8_MISALIGNED;
+  if (ws_bytes < linear_w8a8_g256_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  if (!ws || !al16(ws)) return ws ? W8A8_MISALIGNED : W8A8_INVALID_ARG;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  int8_t* q = static_cast<int8_t*>(ws);
+  float* s = reinterpret_cast<float*>(static_cast<char*>(ws) + act_codes_bytes(M, K));
+  hipError_t e =
+      launch_linear_g256(x, M, K, ldx, qw_packed, su8, s2, N, y, ldy, q, s, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+int gemm_w8a8_g256(const int8_t* qa, const float* sa, int64_t M, int64_t K, const int8_t* qw,
+                   const uint8_t* su8, const uint16_t* s2, int64_t N, uint16_t* y, int64_t ldy,
+                   void* ws, size_t ws_bytes, void* stream) {
+  return g256_common(qa, sa, M, K, qw, su8, s2, N, false, y, ldy, ws, ws_bytes, stream);
+}
+
+int gemm_w8a8_g256_packed(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                          const int8_t* qw_packed, const uint8_t* su8, const uint16_t* s2,
+                          int64_t N, uint16_t* y, int64_t ldy, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return g256_common(qa, sa, M, K, qw_packed, su8, s2, N, true, y, ldy, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -78,6 +78,17 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
+  // g256: the tile's u8 group scales (K <= 16384: at most 64 groups a row),
+  // read once into LDS so the main loop issues no other global loads
+  __shared__ uint8_t su8_lds[MODE == kEpiG256 ? BN * 64 : 1];
+  if (MODE == kEpiG256) {
+    const int G = K >> 8;
+    for (int i = threadIdx.x; i < BN * G; i += W * 64) {
+      const int c = i / G, gg = i - c * G;
+      su8_lds[c * 64 + gg] = su8[(int64_t)min(n0 + c, N - 1) * G + gg];
+    }
+    __syncthreads();
+  }
   const int wm = wv / WAVES_N;
   const int wn = wv % WAVES_N;
   const int j = lane & 15;
@@ -155,7 +166,6 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
 #pragma unroll
         for (int v = 0; v < 16; v++) ts[i][n][v] = 0;
   }
-  const int G = K >> 8;
 
   // Operand fragments of one 32-byte k half: LDS -> registers.  Lane l reads
   // row (l % 32) of a 32-row block, k-slice 2h + l/32: 16-row block
@@ -195,12 +205,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
     if (MODE == kEpiG256 && (kt & 3) == 3) {
 #pragma unroll
       for (int n = 0; n < TN; n++) {
-        const int col = min(n0 + wn * WN + n * 32 + (lane & 31), N - 1);
-        const long long u8 = su8[(int64_t)col * G + (kt >> 2)];
+        // |acc| <= 256 * 127^2 per group, so acc * u8 < 2^31 is exact in int32
+        const int u8 = su8_lds[(wn * WN + n * 32 + (lane & 31)) * 64 + (kt >> 2)];
 #pragma unroll
         for (int i = 0; i < TM; i++) {
 #pragma unroll
-          for (int v = 0; v < 16; v++) ts[i][n][v] += (long long)acc[i][n][v] * u8;
+          for (int v = 0; v < 16; v++) ts[i][n][v] += (long long)(acc[i][n][v] * u8);
           acc[i][n] = v16i{0};
         }
       }
@@ -342,9 +352,18 @@ hipError_t launch_gemm_tile_i32(const int8_t* qa, int64_t M, int64_t K, int64_t 
 
 hipError_t launch_gemm_g256_tile(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                                  const int8_t* qw, const uint8_t* su8, const uint16_t* s2,
-                                 int64_t N, uint16_t* y, int64_t ldy, hipStream_t stream) {
-  return launch_tile_cfg<64, 64, 2, 2, 4, kEpiG256, false>(qa, sa, M, K, K, qw, nullptr, N, K, y,
-                                                        ldy, su8, s2, stream);
+                                 int64_t N, bool packed, bool apacked, uint16_t* y, int64_t ldy,
+                                 hipStream_t stream) {
+  // 64 x 64 tiles, two 64-byte k chunks per pipeline step (K % 256 == 0),
+  // two workgroups per CU
+  if (packed && apacked)
+    return launch_tile_cfg<64, 64, 2, 2, 4, kEpiG256, true, true, 2, 2>(
+        qa, sa, M, K, K, qw, nullptr, N, K, y, ldy, su8, s2, stream);
+  if (packed)
+    return launch_tile_cfg<64, 64, 2, 2, 4, kEpiG256, true, false, 2, 2>(
+        qa, sa, M, K, K, qw, nullptr, N, K, y, ldy, su8, s2, stream);
+  return launch_tile_cfg<64, 64, 2, 2, 4, kEpiG256, false, false, 2, 2>(
+      qa, sa, M, K, K, qw, nullptr, N, K, y, ldy, su8, s2, stream);
 }
 
 }  // namespace w8a8

@@ -61,6 +61,10 @@ __device__ __forceinline__ float block_max_256(float v, float* part) {
 constexpr int kMaxK = 16384;
 
 // One 256-thread workgroup per row: rotate into LDS, reduce amax, quantise.
+// PACKED_OUT: codes in the 16-row x 64-byte MFMA tile layout of pack.hip
+// (row m, k bytes 16c..16c+15 -> tile m/16, block c/4, slot m%16 + 16*(c%4)),
+// the operand layout of the tiled GEMM; ldq is then unused.
+template <bool PACKED_OUT>
 __global__ __launch_bounds__(256) void k_fwht128_quant(const uint16_t* __restrict__ x,
                                                        int64_t ldx, int K,
                                                        int8_t* __restrict__ q, int64_t ldq,
@@ -115,7 +119,10 @@ __global__ __launch_bounds__(256) void k_fwht128_quant(const uint16_t* __restric
       }
       w[i] = pack4_i8(a0, a1, a2, a3);
     }
-    *reinterpret_cast<v4u*>(q + row * ldq + c16 * 16) = v4u{w[0], w[1], w[2], w[3]};
+    const int64_t off = PACKED_OUT ? ((row >> 4) * (int64_t)(K >> 6) + (c16 >> 2)) * 1024 +
+                                         ((row & 15) + 16 * (c16 & 3)) * 16
+                                   : row * ldq + c16 * 16;
+    *reinterpret_cast<v4u*>(q + off) = v4u{w[0], w[1], w[2], w[3]};
   }
   if (threadIdx.x == 0) s[row] = amax != 0.0f ? sc : 0.0f;
 }
@@ -209,10 +216,12 @@ __device__ __forceinline__ uint16_t g256_out(long long tsum, float sa, float s2f
 }
 
 // Weight-streaming g256 GEMM for M <= 16 (same operand mapping as the dense
-// decode kernel).  Waves split K on 256-group boundaries; after each group the
-// exact int32 MFMA sum is scaled by that group's u8 and added to an int64
-// running sum.
-template <int WAVES>
+// decode kernel).  Wave w takes the 256-groups w, w + WAVES, ...; each group
+// is four 64-byte k steps (four 1 KiB loads with packed weights), and the
+// loads of two groups are in flight at once.  After each group the exact
+// int32 MFMA sum times that group's u8 (< 2^31: |sum| <= 256 * 127^2) is added
+// to an int64 running sum; the waves' sums are added through LDS.
+template <int WAVES, bool PACKED>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_g256_skinny(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, int M, int K,
     const int8_t* __restrict__ qw, const uint8_t* __restrict__ su8,
@@ -222,31 +231,43 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_g256_skinny(
   const int wv = threadIdx.x >> 6;
   const int j = lane & 15;
   const int g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t tile = blockIdx.x;
+  const int64_t n0 = tile * 16;
   const int G = K >> 8;
-  const int per = (G + WAVES - 1) / WAVES;
-  const int g_begin = wv * per;
-  const int g_end = min(G, g_begin + per);
-  const int8_t* wp = qw + (n0 + j) * K + g * 16;
+  const int nk = K >> 6;
+  // k step c of this lane's weight fragment
+  const int8_t* wp = PACKED ? qw + tile * nk * 1024 + lane * 16 : qw + (n0 + j) * K + g * 16;
+  constexpr int64_t wstep = PACKED ? 1024 : 64;
   const bool a_ok = j < M;
   const int8_t* ap = qa + (int64_t)(a_ok ? j : 0) * K + g * 16;
   const uint8_t* sp = su8 + (n0 + j) * G;
 
   long long ts[4] = {0, 0, 0, 0};
-  for (int gr = g_begin; gr < g_end; gr++) {
-    v4i b[4], a[4];
+  for (int g0 = wv; g0 < G; g0 += 2 * WAVES) {
+    v4i b[2][4], a[2][4];
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int64_t off = (int64_t)gr * 256 + u * 64;
-      b[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + off));
-      a[u] = a_ok ? *reinterpret_cast<const v4i*>(ap + off) : v4i{0, 0, 0, 0};
+    for (int h = 0; h < 2; h++) {
+      const int gr = g0 + h * WAVES;
+      const bool in = gr < G;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int c = gr * 4 + u;
+        b[h][u] = in ? *reinterpret_cast<const v4i*>(wp + c * wstep) : v4i{0, 0, 0, 0};
+        a[h][u] = (in && a_ok) ? *reinterpret_cast<const v4i*>(ap + (int64_t)c * 64)
+                               : v4i{0, 0, 0, 0};
+      }
     }
-    v4i acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int u = 0; u < 4; u++) acc = mfma_16x16x64_i8(a[u], b[u], acc);
-    const long long u8 = sp[gr];
+    for (int h = 0; h < 2; h++) {
+      const int gr = g0 + h * WAVES;
+      if (gr >= G) break;
+      v4i acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int v = 0; v < 4; v++) ts[v] += (long long)acc[v] * u8;
+      for (int u = 0; u < 4; u++) acc = mfma_16x16x64_i8(a[h][u], b[h][u], acc);
+      const int u8 = sp[gr];
+#pragma unroll
+      for (int v = 0; v < 4; v++) ts[v] += (long long)(acc[v] * u8);
+    }
   }
   if (WAVES > 1) {
 #pragma unroll
@@ -269,12 +290,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_g256_skinny(
 
 hipError_t launch_gemm_g256_tile(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                                  const int8_t* qw, const uint8_t* su8, const uint16_t* s2,
-                                 int64_t N, uint16_t* y, int64_t ldy, hipStream_t stream);
+                                 int64_t N, bool packed, bool apacked, uint16_t* y, int64_t ldy,
+                                 hipStream_t stream);
 
 hipError_t launch_fwht128_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                 int64_t ldq, float* s, hipStream_t stream) {
-  hipLaunchKernelGGL(k_fwht128_quant, dim3((unsigned)M), dim3(256), 0, stream, x, ldx, (int)K,
-                     q, ldq, s);
+  hipLaunchKernelGGL(k_fwht128_quant<false>, dim3((unsigned)M), dim3(256), 0, stream, x, ldx,
+                     (int)K, q, ldq, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwht128_quant_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                       int8_t* q, float* s, hipStream_t stream) {
+  hipLaunchKernelGGL(k_fwht128_quant<true>, dim3((unsigned)M), dim3(256), 0, stream, x, ldx,
+                     (int)K, q, (int64_t)0, s);
   return hipGetLastError();
 }
 
@@ -289,13 +318,33 @@ size_t g256_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
 hipError_t launch_gemm_g256(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                             const int8_t* qw, const uint8_t* su8, const uint16_t* s2, int64_t N,
-                            uint16_t* y, int64_t ldy, void*, hipStream_t stream) {
+                            bool packed, uint16_t* y, int64_t ldy, void*, hipStream_t stream) {
   if (M <= 16) {
-    hipLaunchKernelGGL(k_gemm_g256_skinny<4>, dim3((unsigned)(N / 16)), dim3(256), 0, stream, qa,
-                       sa, (int)M, (int)K, qw, su8, s2, y, ldy);
+    if (packed)
+      hipLaunchKernelGGL((k_gemm_g256_skinny<8, true>), dim3((unsigned)(N / 16)), dim3(512), 0,
+                         stream, qa, sa, (int)M, (int)K, qw, su8, s2, y, ldy);
+    else
+      hipLaunchKernelGGL((k_gemm_g256_skinny<8, false>), dim3((unsigned)(N / 16)), dim3(512), 0,
+                         stream, qa, sa, (int)M, (int)K, qw, su8, s2, y, ldy);
     return hipGetLastError();
   }
-  return launch_gemm_g256_tile(qa, sa, M, K, qw, su8, s2, N, y, ldy, stream);
+  return launch_gemm_g256_tile(qa, sa, M, K, qw, su8, s2, N, packed, false, y, ldy, stream);
+}
+
+// The whole Hadamard-domain linear: fwht128 + per-token quant into the
+// workspace (codes in the tile layout when the tiled GEMM runs), then the
+// g256 GEMM on packed weights.
+hipError_t launch_linear_g256(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              const int8_t* qw_packed, const uint8_t* su8, const uint16_t* s2,
+                              int64_t N, uint16_t* y, int64_t ldy, int8_t* q, float* s,
+                              hipStream_t stream) {
+  hipError_t e;
+  if (M <= 16) {
+    if ((e = launch_fwht128_quant(x, M, K, ldx, q, K, s, stream)) != hipSuccess) return e;
+    return launch_gemm_g256(q, s, M, K, qw_packed, su8, s2, N, true, y, ldy, nullptr, stream);
+  }
+  if ((e = launch_fwht128_quant_packed(x, M, K, ldx, q, s, stream)) != hipSuccess) return e;
+  return launch_gemm_g256_tile(q, s, M, K, qw_packed, su8, s2, N, true, true, y, ldy, stream);
 }
 
 }  // namespace w8a8

@@ -70,8 +70,14 @@ hipError_t launch_fwht128_quant(const uint16_t* x, int64_t M, int64_t K, int64_t
 hipError_t launch_fwht128_weight_prep(const float* W, int64_t N, int64_t K, int8_t* qw,
                                       uint8_t* su8, uint16_t* s2, hipStream_t stream);
 size_t g256_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_fwht128_quant_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                       int8_t* q, float* s, hipStream_t stream);
+hipError_t launch_linear_g256(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              const int8_t* qw_packed, const uint8_t* su8, const uint16_t* s2,
+                              int64_t N, uint16_t* y, int64_t ldy, int8_t* q, float* s,
+                              hipStream_t stream);
 hipError_t launch_gemm_g256(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                             const int8_t* qw, const uint8_t* su8, const uint16_t* s2, int64_t N,
-                            uint16_t* y, int64_t ldy, void* ws, hipStream_t stream);
+                            bool packed, uint16_t* y, int64_t ldy, void* ws, hipStream_t stream);
 
 }  // namespace w8a8

@@ -58,17 +58,19 @@ def rotated_weights(orc):
     return orc.weight_prep_g256(W)
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("M", [1, 4, 16, 17, 256])
-def test_g256_full_size(orc, rotated_weights, M):
+def test_g256_full_size(orc, rotated_weights, M, packed):
     cfg = synth.hadamard_linear(M)
     K, N = cfg["K"], cfg["N"]
-    say(f"g256 M={M} K={K} N={N}")
+    say(f"g256 M={M} K={K} N={N} packed={packed}")
     qw, su8, s2 = rotated_weights
     x = synth.activations(cfg["xkey"], M, K, cfg["n_outliers"], cfg["outlier_scale"],
                           heavy_tail=True)
     qa, sa = orc.fwht128_quant(x)
     qa_d, sa_d = mq.fwht128_quant(bf16_dev(x))
-    y = mq.gemm_w8a8_g256(qa_d, sa_d, dev(qw), dev(su8), dev(s2))
+    qw_d = mq.pack_weights(dev(qw)) if packed else dev(qw)
+    y = mq.gemm_w8a8_g256(qa_d, sa_d, qw_d, dev(su8), dev(s2), packed=packed)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(qa_d), qa)
     yh = bf16_host(y)
@@ -85,9 +87,51 @@ def test_g256_full_size(orc, rotated_weights, M):
         assert_bf16_close(yh[ms, ns], y_ref, "g256 sampled")
 
 
-def test_g256_small_all_edges(orc):
+@pytest.mark.parametrize("M", [1, 16, 17, 256])
+def test_linear_g256_full_size(orc, rotated_weights, M):
+    # the fused entry: fwht128 + quant (tile-layout codes when M > 16) + g256
+    cfg = synth.hadamard_linear(M)
+    K, N = cfg["K"], cfg["N"]
+    say(f"linear g256 M={M}")
+    qw, su8, s2 = rotated_weights
+    x = synth.activations(cfg["xkey"], M, K, cfg["n_outliers"], cfg["outlier_scale"],
+                          heavy_tail=True)
+    if M > 2:
+        x[1] = 0
+    qa, sa = orc.fwht128_quant(x)
+    y = bf16_host(mq.linear_w8a8_g256_packed(bf16_dev(x), mq.pack_weights(dev(qw)), dev(su8),
+                                             dev(s2)))
+    if M <= 17:
+        np.testing.assert_array_equal(y, orc.gemm_g256(qa, sa, qw, su8, s2))
+    else:
+        r = np.random.default_rng(M + 1)
+        ms = np.concatenate([r.integers(0, M, 6000), np.arange(M)])
+        ns = np.concatenate([r.integers(0, N, 6000), np.full(M, N - 1)])
+        y_ref, _ = orc.gemm_g256_points(qa, sa, qw, su8, s2, ms, ns)
+        np.testing.assert_array_equal(y[ms, ns], y_ref)
+    if M > 2:
+        assert not y[1].any()
+
+
+def test_linear_g256_ragged_stride(orc):
+    r = np.random.default_rng(9)
+    M, K, N = 37, 768, 80
+    W = synth.weights((52, N), N, K)
+    qw, su8, s2 = orc.weight_prep_g256(W)
+    x = synth.activations((53, M), M, K, 8, 10.0, heavy_tail=True)
+    big = np.zeros((M, K + 128), np.uint16)
+    big[:, :K] = x
+    qa, sa = orc.fwht128_quant(x)
+    y = mq.linear_w8a8_g256_packed(bf16_dev(big)[:, :K], mq.pack_weights(dev(qw)), dev(su8),
+                                   dev(s2.view(np.int16)).view(torch.bfloat16))
+    np.testing.assert_array_equal(bf16_host(y), orc.gemm_g256(qa, sa, qw, su8, s2))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_g256_small_all_edges(orc, packed):
     r = np.random.default_rng(3)
-    for (M, K, N) in [(1, 256, 16), (5, 512, 48), (40, 768, 80)]:
+    for (M, K, N) in [(1, 256, 16), (5, 512, 48), (40, 768, 80), (16, 16384, 32),
+                      (70, 2304, 144)]:
         qa = r.integers(-127, 128, (M, K)).astype(np.int8)
         qw = r.integers(-127, 128, (N, K)).astype(np.int8)
         qa[0] = 127
@@ -97,6 +141,7 @@ def test_g256_small_all_edges(orc):
         s2 = synth.to_bf16_bits(r.random(N).astype(np.float32) * 1e-4)
         sa = (r.random(M) * 0.1).astype(np.float32)
         y_ref = orc.gemm_g256(qa, sa, qw, su8, s2)
-        y = mq.gemm_w8a8_g256(dev(qa), dev(sa), dev(qw), dev(su8),
-                              dev(s2.view(np.int16)).view(torch.bfloat16))
+        qw_d = mq.pack_weights(dev(qw)) if packed else dev(qw)
+        y = mq.gemm_w8a8_g256(dev(qa), dev(sa), qw_d, dev(su8),
+                              dev(s2.view(np.int16)).view(torch.bfloat16), packed=packed)
         np.testing.assert_array_equal(bf16_host(y), y_ref)
