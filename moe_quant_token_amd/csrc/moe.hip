@@ -11,19 +11,22 @@
 // count that depends on the routing stays on the device).
 // Small batches (at most 2048 routed pairs):
 //   k_moe_prep     one workgroup: routing (one wave per token), per-token int8
-//                  codes of x, and the sort of the pairs by expert
+//                  codes of x, and the sort of the pairs by expert (up to 16
+//                  tokens; beyond, k_moe_route_quant and k_moe_sort)
 //   k_moe_skinny<1> grouped gemm1 streaming each touched expert's w13 once,
 //                  SiLU(gate)*up epilogue, per-pair |act| maximum (atomic max)
 //   k_moe_skinny<2> grouped gemm2; its prologue requantises the pairs' rows
 //   k_moe_combine  out[t] = sum over the k slots, in slot order, one bf16
 //                  rounding; deterministic (no floating-point atomics)
 // Large batches:
-//   k_moe_route    softmax top-k over the logits, one wave per token
-//   k_moe_sort     one workgroup: per-expert counts, the list of experts that
-//                  received pairs, segment offsets, pairs grouped by expert,
+//   k_moe_route_quant  routing and per-token int8 codes of x, one wave per
+//                  token
+//   k_moe_sort     one workgroup: per-expert counts (each pair keeps its place
+//                  in its expert's segment), segment offsets, the list of
+//                  experts that received pairs, the pairs grouped by expert,
 //                  and the table of 128-pair m-blocks
-//   k_quant_rows   per-token int8 codes of x (quant.hip)
-//   k_moe_tile<1>  grouped gemm1 on LDS-staged gathered rows (32x32x32 MFMA),
+//   k_moe_tile<1>  grouped gemm1 (32x32x32 MFMA): gathered activation rows
+//                  through LDS, weights prefetched into registers,
 //                  SiLU(gate)*up epilogue
 //   k_moe_requant  per-pair int8 codes of the activation, one wave per pair
 //   k_moe_tile<2>  grouped gemm2, epilogue writes dequantised fp32 rows
@@ -57,6 +60,7 @@ struct MoeWs {
   int32_t* blk_slot;      // [P / kMoeBM + E + 1]  m-block -> expert slot
   int32_t* blk_row0;      // [P / kMoeBM + E + 1]  m-block -> first sorted pair
   int32_t* n_blocks;      // [1]
+  int32_t* rank;          // [P]  a pair's position inside its expert's segment
   size_t bytes;
 };
 
@@ -84,6 +88,7 @@ MoeWs carve(void* base, int64_t T, int64_t H, int64_t E, int64_t I, int k) {
   w.blk_slot = reinterpret_cast<int32_t*>(take((P / kMoeBM + E + 1) * 4));
   w.blk_row0 = reinterpret_cast<int32_t*>(take((P / kMoeBM + E + 1) * 4));
   w.n_blocks = reinterpret_cast<int32_t*>(take(4));
+  w.rank = reinterpret_cast<int32_t*>(take(P * 4));
   w.bytes = off;
   return w;
 }
@@ -120,10 +125,12 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // Selection compares the fp32 logits (softmax is monotonic): slot s gets the
 // s-th largest, equal logits go to the lower expert index.  Each round takes
 // the wave maximum of the key (logit, then 2^32-1-index) over the experts not
-// yet taken; lane s keeps slot s.  The rounds hold no floating-point work:
-// afterwards lane s forms its probability exp(l - max) / sum in fp64 (all
-// slots at once), the kept probabilities are summed in slot order and each
-// renormalised weight is rounded once to fp32.
+// yet taken; lane s keeps slot s.  The rounds hold no floating-point work.
+// Weights: w_s = p_s / (sum of the kept p) with p = softmax; the softmax
+// denominator cancels, so lane s forms e_s = exp(l_s - max) in fp64, the
+// kept e are summed in slot order and w_s = e_s / sum is rounded once to
+// fp32 (within one fp32 ulp of the quotient of the rounded fp64 softmax
+// probabilities).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E, int k,
                                             int32_t* __restrict__ ids, float* __restrict__ w,
@@ -170,16 +177,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E,
       my_l = key_float(mh);
     }
   }
-  // softmax denominator: each lane's terms, then the wave sum
-  double z = 0.0;
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    if (64 * i >= E) break;
-    if (lane + 64 * i < E) z += exp((double)v[i] - mx);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
-  const double myp = exp((double)my_l - mx) / z;
+  const double myp = exp((double)my_l - mx);
   double kept = 0.0;
   for (int s = 0; s < k; s++) kept += __shfl(myp, s, 64);
   if (lane < k) {
@@ -188,24 +186,27 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E,
   }
 }
 
-__global__ __launch_bounds__(256) void k_moe_route(const float* __restrict__ logits, int T,
-                                                   int E, int k, int32_t* __restrict__ ids,
-                                                   float* __restrict__ w) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  route_token(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k,
-              threadIdx.x & 63);
-}
 
 // One wave quantises one bf16 row of length K (K % 16 == 0), exactly as
 // k_quant_rows does: amax / 127 in fp32, round-half-even of the quotient.
 // Rows up to 4096 are held in registers (one read); longer rows are read
 // twice (the second time from L2).
-__device__ __forceinline__ uint32_t quant_pack4_bf16(uint32_t w0, uint32_t w1, float sc) {
-  return pack4_i8(quant_code(bf16_bits_to_f32(w0 & 0xffffu), sc),
-                  quant_code(bf16_bits_to_f32(w0 >> 16), sc),
-                  quant_code(bf16_bits_to_f32(w1 & 0xffffu), sc),
-                  quant_code(bf16_bits_to_f32(w1 >> 16), sc));
+// Codes of four bf16 values.  Quotient: with r = 1/s (IEEE), q0 = x*r,
+// e = fma(-q0, s, x), q = fma(e, r, q0); for bf16 x with |x| <= amax and
+// s = amax/127 >= 2^-100, rint(q) equals rint of the IEEE quotient x/s
+// (checked exhaustively over every such pair); smaller scales divide.
+__device__ __forceinline__ int code_bf16(uint32_t h, float sc, float rc) {
+  const float x = bf16_bits_to_f32(h);
+  if (sc < 0x1p-100f) return quant_code(x, sc);
+  const float q0 = x * rc;
+  const float e = __builtin_fmaf(-q0, sc, x);
+  const float q = __builtin_fmaf(e, rc, q0);
+  return (int)fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f);
+}
+__device__ __forceinline__ uint32_t quant_pack4_bf16(uint32_t w0, uint32_t w1, float sc,
+                                                     float rc) {
+  return pack4_i8(code_bf16(w0 & 0xffffu, sc, rc), code_bf16(w0 >> 16, sc, rc),
+                  code_bf16(w1 & 0xffffu, sc, rc), code_bf16(w1 >> 16, sc, rc));
 }
 __device__ __forceinline__ float amax8_bf16(v4u raw) {
   const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -231,14 +232,15 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ x, i
     }
     amax = wave_max(amax);
     const float sc = amax / 127.0f;
+    const float rc = 1.0f / sc;
 #pragma unroll
     for (int u = 0; u < 8; u++) {
       const int c = lane + 64 * u;
       if (c >= nc) break;
       uint32_t lo = 0, hi = 0;
       if (amax != 0.0f) {
-        lo = quant_pack4_bf16(raw[u].x, raw[u].y, sc);
-        hi = quant_pack4_bf16(raw[u].z, raw[u].w, sc);
+        lo = quant_pack4_bf16(raw[u].x, raw[u].y, sc, rc);
+        hi = quant_pack4_bf16(raw[u].z, raw[u].w, sc, rc);
       }
       uint32_t* o = reinterpret_cast<uint32_t*>(q + c * 8);
       o[0] = lo;
@@ -252,12 +254,13 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ x, i
     amax = fmaxf(amax, amax8_bf16(*reinterpret_cast<const v4u*>(x + c * 8)));
   amax = wave_max(amax);
   const float sc = amax / 127.0f;
+  const float rc = 1.0f / sc;
   for (int c = lane; c < nc; c += 64) {
     const v4u raw = *reinterpret_cast<const v4u*>(x + c * 8);
     uint32_t lo = 0, hi = 0;
     if (amax != 0.0f) {
-      lo = quant_pack4_bf16(raw.x, raw.y, sc);
-      hi = quant_pack4_bf16(raw.z, raw.w, sc);
+      lo = quant_pack4_bf16(raw.x, raw.y, sc, rc);
+      hi = quant_pack4_bf16(raw.z, raw.w, sc, rc);
     }
     uint32_t* o = reinterpret_cast<uint32_t*>(q + c * 8);
     o[0] = lo;
@@ -281,17 +284,35 @@ __device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int 
                                            uint32_t* __restrict__ amax,
                                            int32_t* __restrict__ blk_slot = nullptr,
                                            int32_t* __restrict__ blk_row0 = nullptr,
-                                           int32_t* __restrict__ n_blocks = nullptr) {
+                                           int32_t* __restrict__ n_blocks = nullptr,
+                                           int32_t* __restrict__ rank = nullptr) {
   __shared__ int cnt[1024];
   __shared__ int cursor[1024];
   __shared__ int wsum_c[16], wsum_f[16], wsum_b[16];
   const int tid = threadIdx.x;
   cnt[tid] = 0;
   __syncthreads();
-  for (int r = tid; r < P; r += 1024) {
-    const int e = ids[r];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    amax[r] = 0u;
+  // counts; with rank set each pair also keeps the count it saw (its place
+  // in its expert's segment; the order inside a segment does not matter)
+  // (batches of 16 pairs per thread: the id loads of a batch are all in
+  // flight before its first atomic)
+  constexpr int B = 16;
+  for (int r0 = tid; r0 < P; r0 += 1024 * B) {
+    int e[B];
+#pragma unroll
+    for (int b = 0; b < B; b++) {
+      const int r = r0 + 1024 * b;
+      e[b] = r < P ? ids[r] : -1;
+    }
+#pragma unroll
+    for (int b = 0; b < B; b++) {
+      const int r = r0 + 1024 * b;
+      if (e[b] >= 0 && e[b] < E) {
+        const int k = atomicAdd(&cnt[e[b]], 1);
+        if (rank) rank[r] = k;
+      }
+      if (amax && r < P) amax[r] = 0u;
+    }
   }
   __syncthreads();
   // exclusive scans of the counts and of the "expert is active" flags
@@ -348,11 +369,20 @@ __device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int 
     seg_off[tot_f] = tot_c;
   }
   __syncthreads();
-  for (int r = tid; r < P; r += 1024) {
-    const int e = ids[r];
-    if (e >= 0 && e < E) {
-      const int pos = atomicAdd(&cursor[e], 1);
-      sorted_pairs[pos] = r;
+  for (int r0 = tid; r0 < P; r0 += 1024 * B) {
+    int e[B], k[B];
+#pragma unroll
+    for (int b = 0; b < B; b++) {
+      const int r = r0 + 1024 * b;
+      e[b] = r < P ? ids[r] : -1;
+      k[b] = (rank && r < P) ? rank[r] : 0;
+    }
+#pragma unroll
+    for (int b = 0; b < B; b++) {
+      if (e[b] >= 0 && e[b] < E) {
+        const int pos = rank ? cursor[e[b]] + k[b] : atomicAdd(&cursor[e[b]], 1);
+        sorted_pairs[pos] = r0 + 1024 * b;
+      }
     }
   }
 }
@@ -362,9 +392,9 @@ __global__ __launch_bounds__(1024) void k_moe_sort(
     int32_t* __restrict__ seg_off, int32_t* __restrict__ n_active,
     int32_t* __restrict__ sorted_pairs, uint32_t* __restrict__ amax,
     int32_t* __restrict__ blk_slot, int32_t* __restrict__ blk_row0,
-    int32_t* __restrict__ n_blocks) {
+    int32_t* __restrict__ n_blocks, int32_t* __restrict__ rank) {
   sort_pairs(ids, P, E, expert_list, seg_off, n_active, sorted_pairs, amax, blk_slot, blk_row0,
-             n_blocks);
+             n_blocks, rank);
 }
 
 // Routing and per-token quant, one wave per token (small batches with more
@@ -883,7 +913,7 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
       if ((err = hipGetLastError()) != hipSuccess) return err;
       hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
                          ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax,
-                         nullptr, nullptr, nullptr);
+                         nullptr, nullptr, nullptr, nullptr);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // tiny batches: one weight tile per workgroup (most parallelism); else
@@ -912,18 +942,15 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   } else {
-    if (a.logits) {
-      hipLaunchKernelGGL(k_moe_route, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.logits, a.T,
-                         a.E, a.k, a.topk_ids, a.topk_w);
-      if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
-    hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
-                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax,
-                       ws.blk_slot, ws.blk_row0, ws.n_blocks);
+    // routing + per-token quant (one wave per token), then the sort by
+    // expert with the m-block table
+    hipLaunchKernelGGL(k_moe_route_quant, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.x,
+                       a.logits, a.T, a.H, a.E, a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if ((err = launch_quant_rows(a.x, 0, a.T, a.H, a.H, ws.qx, a.H, ws.sx, stream)) !=
-        hipSuccess)
-      return err;
+    hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
+                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, nullptr,
+                       ws.blk_slot, ws.blk_row0, ws.n_blocks, ws.rank);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     // m-blocks: at most one partial block per expert that received pairs;
     // the grid covers that bound rounded up to the 8 XCDs
     const unsigned max_blocks = (unsigned)((P / kMoeBM + slots + 7) / 8 * 8);
