@@ -916,26 +916,29 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
                          nullptr, nullptr, nullptr, nullptr);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    // tiny batches: one weight tile per workgroup (most parallelism); else
-    // eight tiles per workgroup
+    // Workgroup shapes measured on MI355X at 256 experts, H=2048, I=512: up to
+    // 64 pairs gemm1 takes one 16-row weight tile per 8-wave workgroup (most
+    // parallelism) and gemm2 two tiles per 4-wave workgroup; larger batches
+    // take two (gemm1) and four (gemm2) tiles per 4-wave workgroup.  H and I
+    // are multiples of 64, so 2I/16 is even and H/16 a multiple of 4.
     const int tiles1 = I2 / 16, tiles2 = a.H / 16;
-    if (P <= 64 || tiles1 % 8 != 0 || tiles2 % 8 != 0) {
+    if (P <= 64) {
       hipLaunchKernelGGL((k_moe_skinny<8, 1, 1, PACKED>), dim3(tiles1, slots), dim3(512), 0,
                          stream, ws.qx, ws.sx, nullptr, nullptr, a.k, a.w13, a.s13, I2, a.H,
                          ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.act, a.I,
                          ws.amax, nullptr, nullptr, a.dbg_acc1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      hipLaunchKernelGGL((k_moe_skinny<8, 1, 2, PACKED>), dim3(tiles2, slots), dim3(512), 0,
+      hipLaunchKernelGGL((k_moe_skinny<4, 2, 2, PACKED>), dim3(tiles2 / 2, slots), dim3(256), 0,
                          stream, nullptr, nullptr, ws.act, ws.amax, a.k, a.w2, a.s2, a.H, a.I,
                          ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.y2, a.H,
                          nullptr, a.dbg_qa, a.dbg_sa2, a.dbg_acc2);
     } else {
-      hipLaunchKernelGGL((k_moe_skinny<4, 8, 1, PACKED>), dim3(tiles1 / 8, slots), dim3(256), 0,
+      hipLaunchKernelGGL((k_moe_skinny<4, 2, 1, PACKED>), dim3(tiles1 / 2, slots), dim3(256), 0,
                          stream, ws.qx, ws.sx, nullptr, nullptr, a.k, a.w13, a.s13, I2, a.H,
                          ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.act, a.I,
                          ws.amax, nullptr, nullptr, a.dbg_acc1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      hipLaunchKernelGGL((k_moe_skinny<4, 8, 2, PACKED>), dim3(tiles2 / 8, slots), dim3(256), 0,
+      hipLaunchKernelGGL((k_moe_skinny<4, 4, 2, PACKED>), dim3(tiles2 / 4, slots), dim3(256), 0,
                          stream, nullptr, nullptr, ws.act, ws.amax, a.k, a.w2, a.s2, a.H, a.I,
                          ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.y2, a.H,
                          nullptr, a.dbg_qa, a.dbg_sa2, a.dbg_acc2);
