@@ -420,11 +420,16 @@ __global__ __launch_bounds__(1024) void k_moe_prep(
     int32_t* __restrict__ n_active, int32_t* __restrict__ sorted_pairs,
     uint32_t* __restrict__ amax) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int t = wv; t < T; t += 16) {
-    if (logits)
-      route_token(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k,
-                  lane);
-    quant_row_wave(x + (int64_t)t * H, H, qx + (int64_t)t * H, sx + t, lane);
+  // waves 0-7 route tokens, waves 8-15 quantise them, side by side
+  const int t0 = wv & 7;
+  for (int t = t0; t < T; t += 8) {
+    if (wv < 8) {
+      if (logits)
+        route_token(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k,
+                    lane);
+    } else {
+      quant_row_wave(x + (int64_t)t * H, H, qx + (int64_t)t * H, sx + t, lane);
+    }
   }
   __syncthreads();  // the routing ids written above are read by the sort
   sort_pairs(ids, T * k, E, expert_list, seg_off, n_active, sorted_pairs, amax);
