@@ -162,6 +162,28 @@ def test_gemm_extreme_codes_no_overflow():
     np.testing.assert_array_equal(acc2[:4], acc)
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_largest_k_extreme_codes(packed):
+    # K = 131072 is the largest K accepted: 127^2 * K = 2,114,060,288 < 2^31
+    K, N = 131072, 16
+    qa = torch.full((2, K), 127, dtype=torch.int8, device=DEV)
+    qa[1] = -127
+    qw = torch.full((N, K), 127, dtype=torch.int8, device=DEV)
+    qw[1::2] = -127
+    big = 127 * 127 * K
+    expect = np.array([[big, -big] * (N // 2), [-big, big] * (N // 2)], np.int64)
+    if packed:
+        qp = mq.pack_weights(qw)
+        acc = host(mq.gemm_w8a8_packed_i32acc(qa, qp, N))
+        acc17 = host(mq.gemm_w8a8_packed_i32acc(torch.cat([qa] * 9)[:17], qp, N))
+    else:
+        acc = host(mq.gemm_w8a8_i32acc(qa, qw))
+        acc17 = host(mq.gemm_w8a8_i32acc(torch.cat([qa] * 9)[:17], qw))  # tiled kernel
+    np.testing.assert_array_equal(acc, expect)
+    np.testing.assert_array_equal(acc17[:2], expect)
+    np.testing.assert_array_equal(acc17[16], expect[0])
+
+
 def test_gemm_strided_output_and_inputs(orc):
     M, K, N = 5, 256, 64
     x, W = _inputs((10, 1), (10, 2), M, K, N, 2, 20.0)
