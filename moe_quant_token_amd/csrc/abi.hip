@@ -18,9 +18,11 @@ int hip_fail(hipError_t e) {
   return W8A8_HIP_ERROR;
 }
 
-// Device check, cached per device id (gfx950 only).
+// Device check, cached per device id (gfx950 only), with the CU count the
+// launch plans use.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_dev_cus[kMaxDevices];
 
 int check_device() {
   int dev = 0;
@@ -33,10 +35,22 @@ int check_device() {
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return hip_fail(e);
     st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     g_dev_ok[dev].store(st, std::memory_order_relaxed);
   }
   return st == 1 ? W8A8_OK : W8A8_UNSUPPORTED_DEVICE;
 }
+
+}  // namespace
+
+int w8a8::device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  const int n = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return n > 0 ? n : 256;
+}
+
+namespace {
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }

@@ -303,25 +303,76 @@ hipError_t launch_tile_cfg(const int8_t* qa, const float* sa, int64_t M, int64_t
   return hipGetLastError();
 }
 
-// Tile shape per problem (measured on MI355X at M=4096, K=5120): 256 x 160
-// when N is a multiple of 160 and 256 x 256 tiles would leave a partial last
-// round of workgroups (N=5120: 512 tiles, two full rounds on 256 CUs), else
-// 256 x 256; small problems 64 x 64 so there are enough tiles.
+// Output columns [n0, n0 + nn) as a launch of their own: the weight rows,
+// channel scales and output columns move by n0 (n0 % 16 == 0, so packed
+// weights keep whole 16-row tiles); the activations are shared.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MODE, bool BPACKED,
+          bool APACKED, int KSUB, int MINB>
+static hipError_t launch_cols(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                              int64_t lda, const int8_t* qw, const float* sw, int64_t ldw,
+                              void* out, int64_t ldo, int64_t n0, int64_t nn,
+                              hipStream_t stream) {
+  const size_t esz = MODE == kEpiI32 ? 4 : 2;
+  return launch_tile_cfg<BM, BN, WAVES_M, WAVES_N, NSTAGE, MODE, BPACKED, APACKED, KSUB, MINB>(
+      qa, sa, M, K, lda, qw + n0 * (BPACKED ? K : ldw), sw ? sw + n0 : nullptr, nn, ldw,
+      static_cast<char*>(out) + n0 * esz, ldo, nullptr, nullptr, stream);
+}
+
+static int64_t gcd64(int64_t a, int64_t b) {
+  while (b) {
+    const int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Launch plan per problem.  A 256 x 256 tile needs a whole CU (one workgroup
+// per CU), so the tile count should be a multiple of the CU count: a partial
+// last round leaves most CUs idle for a whole tile time.  In order:
+//  - 256 x 256 when the tiles fill whole rounds;
+//  - 256 x 160, two workgroups per CU, when N is a multiple of 160 and the
+//    256 x 256 tiling would leave under 3/4 of a round (N=5120: 512 tiles,
+//    one round of 2 x 256);
+//  - otherwise the widest column range whose 256 x 256 tiles fill whole
+//    rounds, then the remaining columns as 128 x 64 tiles (two per CU), when
+//    that is cheaper than the partial round.  Measured on MI355X at
+//    M=4096, K=5120: one round of 128 x 64 tiles takes ~0.4 of a 256 x 256
+//    round (N=17408: 492 -> ~395 us);
+//  - small problems: 64 x 64 tiles so there are enough of them.
 template <int MODE, bool BPACKED, bool APACKED = false>
 static hipError_t launch_tile_impl(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                                    int64_t lda, const int8_t* qw, const float* sw, int64_t N,
                                    int64_t ldw, void* out, int64_t ldo, hipStream_t stream) {
   if (M >= 1024 && N >= 1024) {
-    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    if (N % 160 == 0 && (t256 % 256) != 0 && (t256 % 256) < 192)
-      return launch_tile_cfg<256, 160, 4, 1, 3, MODE, BPACKED, APACKED, 1, 2>(
-          qa, sa, M, K, lda, qw, sw, N, ldw, out, ldo, nullptr, nullptr, stream);
-    return launch_tile_cfg<256, 256, 4, 2, 4, MODE, BPACKED, APACKED>(
-        qa, sa, M, K, lda, qw, sw, N, ldw, out, ldo, nullptr, nullptr, stream);
+    const int64_t cus = device_cus();
+    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256, t256 = tm * tn;
+    const int64_t rounds = (t256 + cus - 1) / cus;
+    if (t256 % cus != 0) {
+      if (N % 160 == 0 && (t256 % cus) * 4 < cus * 3)
+        return launch_cols<256, 160, 4, 1, 3, MODE, BPACKED, APACKED, 1, 2>(
+            qa, sa, M, K, lda, qw, sw, ldw, out, ldo, 0, N, stream);
+      const int64_t q = cus / gcd64(tm, cus);  // column tiles per whole number of rounds
+      const int64_t tn_main = tn / q * q;      // < tn, so the main range ends before N
+      if (tn_main > 0) {
+        const int64_t n_main = tn_main * 256;
+        const int64_t rem_tiles = ((M + 127) / 128) * ((N - n_main + 63) / 64);
+        const int64_t rem_rounds = (rem_tiles + 2 * cus - 1) / (2 * cus);
+        // in tenths of a 256 x 256 round
+        if (10 * (tm * tn_main / cus) + 4 * rem_rounds < 10 * rounds) {
+          hipError_t e = launch_cols<256, 256, 4, 2, 4, MODE, BPACKED, APACKED, 1, 1>(
+              qa, sa, M, K, lda, qw, sw, ldw, out, ldo, 0, n_main, stream);
+          if (e != hipSuccess) return e;
+          return launch_cols<128, 64, 2, 2, 4, MODE, BPACKED, APACKED, 1, 2>(
+              qa, sa, M, K, lda, qw, sw, ldw, out, ldo, n_main, N - n_main, stream);
+        }
+      }
+    }
+    return launch_cols<256, 256, 4, 2, 4, MODE, BPACKED, APACKED, 1, 1>(
+        qa, sa, M, K, lda, qw, sw, ldw, out, ldo, 0, N, stream);
   }
-  return launch_tile_cfg<64, 64, 2, 2, 4, MODE, BPACKED, APACKED>(qa, sa, M, K, lda, qw, sw, N,
-                                                                  ldw, out, ldo, nullptr,
-                                                                  nullptr, stream);
+  return launch_cols<64, 64, 2, 2, 4, MODE, BPACKED, APACKED, 1, 1>(
+      qa, sa, M, K, lda, qw, sw, ldw, out, ldo, 0, N, stream);
 }
 
 hipError_t launch_gemm_tile_apacked(const int8_t* qa_packed, const float* sa, int64_t M,

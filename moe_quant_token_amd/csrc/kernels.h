@@ -7,6 +7,10 @@
 
 namespace w8a8 {
 
+// Compute units of the current device, cached when the entry point checked
+// the device (256 on MI355X).
+int device_cus();
+
 hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                              int8_t* q, int64_t ldq, float* s, hipStream_t stream);
 

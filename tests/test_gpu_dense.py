@@ -79,6 +79,8 @@ GEMM_SHAPES = [
     (64, 1024, 1024),
     (2048, 512, 2048),  # 256x256 tiles
     (2100, 256, 2064),  # 256x256 tiles, ragged M and N
+    (4096, 64, 4352),   # 256x256 tiles over whole rounds, remaining columns 128x64
+    (4000, 128, 4368),  # the same split with ragged M and a ragged last column tile
 ]
 
 
