@@ -89,6 +89,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Marks v as needed here: the compiler can neither sink the load that
+// produces it below this point nor defer the wait for that load past it.
+__device__ __forceinline__ void keep_live(float v) { asm volatile("" ::"v"(v)); }
+
 // Pack four int8 codes (values in [-127, 127]) into one 32-bit word.
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |

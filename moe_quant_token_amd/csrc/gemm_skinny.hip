@@ -61,13 +61,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
     for (int u = 0; u < U; u++) acc = mfma_16x16x64_i8(a[u], b[u], acc);
   }
 
+  // wave 0 writes the tile: its scales are loaded before the reduction
+  // (row index clamped into range) and waited for once, so no store waits
+  // on a scale load (a load between two stores would also wait for the
+  // earlier store)
+  const int64_t n = tile * 16 + j;
+  float sam[4] = {0.0f, 0.0f, 0.0f, 0.0f}, swn = 0.0f;
+  if (!STORE_I32 && wv == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) sam[v] = sa[min(4 * g + v, M - 1)];
+    swn = sw[n];
+  }
   red[wv][lane] = acc;
   __syncthreads();
   if (wv != 0) return;
 #pragma unroll
   for (int w = 1; w < WAVES; w++) acc += red[w][lane];
-
-  const int64_t n = tile * 16 + j;
+  if (!STORE_I32) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) keep_live(sam[v]);
+    keep_live(swn);
+  }
 #pragma unroll
   for (int v = 0; v < 4; v++) {
     const int m = 4 * g + v;
@@ -76,8 +90,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
       static_cast<int32_t*>(out)[(int64_t)m * ldo + n] = acc[v];
     } else {
       float r = (float)acc[v];
-      r = r * sa[m];
-      r = r * sw[n];
+      r = r * sam[v];
+      r = r * swn;
       static_cast<uint16_t*>(out)[(int64_t)m * ldo + n] = (uint16_t)f32_to_bf16_bits(r);
     }
   }

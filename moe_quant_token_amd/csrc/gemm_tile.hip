@@ -247,31 +247,55 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
   }
 
   // epilogue: lane holds column (lane % 32) of every 32x32 block, rows
-  // 8*(r/4) + 4*(lane/32) + r%4 for r < 16
+  // 8*(r/4) + 4*(lane/32) + r%4 for r < 16.  The scales of the lane's rows
+  // and columns are loaded up front (indices clamped into range), so the
+  // stores never wait on a scale load.
+  const int row0 = m0 + wm * WM + 4 * (lane >> 5);
+  const int col0 = n0 + wn * WN + (lane & 31);
+  float sar[MODE == kEpiI32 ? 1 : TM][MODE == kEpiI32 ? 1 : 16];
+  float scol[MODE == kEpiI32 ? 1 : TN];
+  if (MODE != kEpiI32) {
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int v = 0; v < 16; v++)
+        sar[i][v] = sa[min(row0 + i * 32 + 8 * (v >> 2) + (v & 3), M - 1)];
+#pragma unroll
+    for (int n = 0; n < TN; n++) {
+      const int c = min(col0 + n * 32, N - 1);
+      scol[n] = MODE == kEpiBf16 ? sw[c] : __uint_as_float((uint32_t)s2[c] << 16);
+    }
+    // one wait for all of them: the stores below sit in per-element
+    // branches, across which the compiler would otherwise wait again
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) keep_live(sar[i][v]);
+#pragma unroll
+    for (int n = 0; n < TN; n++) keep_live(scol[n]);
+  }
 #pragma unroll
   for (int n = 0; n < TN; n++) {
-    const int col = n0 + wn * WN + n * 32 + (lane & 31);
-    if (col >= N) continue;
-    const float swn = MODE == kEpiBf16 ? sw[col] : 0.0f;
-    const float s2f = MODE == kEpiG256 ? __uint_as_float((uint32_t)s2[col] << 16) : 0.0f;
+    const int col = col0 + n * 32;
+    const bool col_ok = col < N;
 #pragma unroll
     for (int i = 0; i < TM; i++) {
 #pragma unroll
       for (int v = 0; v < 16; v++) {
-        const int row = m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row >= M) continue;
+        const int row = row0 + i * 32 + 8 * (v >> 2) + (v & 3);
+        if (!col_ok || row >= M) continue;
         if (MODE == kEpiI32) {
           static_cast<int32_t*>(out)[(int64_t)row * ldo + col] = acc[i][n][v];
         } else if (MODE == kEpiG256) {
-          double rr = (double)ts[i][n][v] * (double)sa[row];
-          rr = rr * (double)s2f;
+          double rr = (double)ts[i][n][v] * (double)sar[i][v];
+          rr = rr * (double)scol[n];
           rr = rr * 0.0078125;
           static_cast<uint16_t*>(out)[(int64_t)row * ldo + col] =
               (uint16_t)f32_to_bf16_bits((float)rr);
         } else {
           float rr = (float)acc[i][n][v];
-          rr = rr * sa[row];
-          rr = rr * swn;
+          rr = rr * sar[i][v];
+          rr = rr * scol[n];
           static_cast<uint16_t*>(out)[(int64_t)row * ldo + col] =
               (uint16_t)f32_to_bf16_bits(rr);
         }

@@ -269,6 +269,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_g256_skinny(
       for (int v = 0; v < 4; v++) ts[v] += (long long)(acc[v] * u8);
     }
   }
+  // wave 0 writes the tile: its scales are loaded before the reduction (row
+  // index clamped into range) and waited for once, so no store waits on a
+  // scale load
+  const int64_t n = n0 + j;
+  float sam[4] = {0.0f, 0.0f, 0.0f, 0.0f}, s2f = 0.0f;
+  if (wv == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) sam[v] = sa[min(4 * g + v, M - 1)];
+    s2f = bf16_bits_to_f32(s2[n]);
+  }
   if (WAVES > 1) {
 #pragma unroll
     for (int v = 0; v < 4; v++) red[wv][lane][v] = ts[v];
@@ -278,13 +288,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_g256_skinny(
 #pragma unroll
       for (int v = 0; v < 4; v++) ts[v] += red[w][lane][v];
   }
-  const int64_t n = n0 + j;
-  const float s2f = bf16_bits_to_f32(s2[n]);
+#pragma unroll
+  for (int v = 0; v < 4; v++) keep_live(sam[v]);
+  keep_live(s2f);
 #pragma unroll
   for (int v = 0; v < 4; v++) {
     const int m = 4 * g + v;
     if (m >= M) break;
-    y[(int64_t)m * ldy + n] = g256_out(ts[v], sa[m], s2f);
+    y[(int64_t)m * ldy + n] = g256_out(ts[v], sam[v], s2f);
   }
 }
 

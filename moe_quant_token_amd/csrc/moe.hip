@@ -43,6 +43,8 @@ namespace {
 constexpr size_t kAlign = 256;
 // pair rows per workgroup of the large-batch grouped GEMMs
 constexpr int kMoeBM = 128;
+// largest number of weight blocks one gemm2 workgroup walks (npw)
+constexpr int kMoeMaxNpw = 8;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct MoeWs {
@@ -496,6 +498,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_skinny(
   };
   v4i bq[U][NT];
   load_w(bq, wv);  // first batch, in flight while the pair data is read
+  // wave w finishes tile w (NT <= WAVES): its column scale is loaded now, so
+  // the epilogue issues no global load behind the next weight prefetch
+  static_assert(NT <= WAVES, "each wave finishes at most one tile");
+  const float swc_w = wv < NT ? sW[(int64_t)e * Nw + (ntile0 + wv) * 16 + j] : 0.0f;
 
   const int seg_begin = seg_off[slot];
   const int seg_end = seg_off[slot + 1];
@@ -536,6 +542,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_skinny(
 
     const bool a_ok = j < nrows;
     const int8_t* ap = qx + (int64_t)(pair_lds[a_ok ? j : 0] / k) * K + g * 16;
+    // gemm1: the token scales of the lane's four pair rows (rows past the
+    // block read pair id 0), loaded before the k loop
+    float sxv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (MODE == 1) {
+#pragma unroll
+      for (int v = 0; v < 4; v++) sxv[v] = sx[pair_lds[4 * g + v] / k];
+    }
     v4i acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] = v4i{0, 0, 0, 0};
@@ -575,7 +588,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_skinny(
 #pragma unroll
       for (int w2 = 1; w2 < WAVES; w2++) sum += red[t][w2][lane];
       const int col = (ntile0 + t) * 16 + j;
-      const float swc = sW[(int64_t)e * Nw + col];
+      const float swc = swc_w;
 #pragma unroll
       for (int v = 0; v < 4; v++) {
         const int r = 4 * g + v;
@@ -586,7 +599,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_skinny(
           float h = 0.0f;
           if (valid) {
             h = (float)sum[v];
-            h = h * sx[p / k];
+            h = h * sxv[v];
             h = h * swc;
           }
           const float partner = __shfl_xor(h, 1, 64);
@@ -652,6 +665,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_moe_tile(
   __shared__ __attribute__((aligned(1024))) int8_t a_lds[2][NA * 1024];
   __shared__ int pair_lds[BM];
   __shared__ float sa_lds[BM];
+  __shared__ float sw_lds[kMulti ? BN * kMoeMaxNpw : BN];
 
   // Workgroups go to the 8 XCDs round-robin.  All the workgroups of one
   // m-block run on the same XCD back to back, so its gathered activation rows
@@ -695,13 +709,16 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_moe_tile(
     b[1] = *reinterpret_cast<const v4i*>(q + BHALF);
   };
 
-  // the block's pair ids and activation scales, read once into LDS (the
-  // gather addresses and the epilogue use them)
+  // the block's pair ids and activation scales, and the weight rows' scales,
+  // read once into LDS (the gather addresses and the epilogue use them; the
+  // epilogue then issues no global load)
   for (int r = threadIdx.x; r < rows; r += WAVES * 64) {
     const int p = sorted_pairs[row0 + r];
     pair_lds[r] = p;
     sa_lds[r] = sA[p / a_div];
   }
+  for (int c = threadIdx.x; c < npw * BN; c += WAVES * 64)
+    sw_lds[c] = sW[(int64_t)e * Nw + nfirst + c];
   // first weight loads go out before the wait for the pair table
   v4i bq[PF][2];
 #pragma unroll
@@ -731,27 +748,34 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_moe_tile(
 
   // epilogue of one weight block: lane holds weight row (product column)
   // n0 + 32 wv + lane % 32 and pair rows 8*(v/4) + 4*(lane/32) + v%4 of each
-  // 32-row block
+  // 32-row block.  Rows past the segment end hold the sums of its last row
+  // (their activation loads re-read that row), so they are finished and
+  // stored as that row: the duplicate stores write the same values to the
+  // same places, and no store sits in a branch (a branch would make the
+  // compiler wait for the stores before the next weight loads are used).
   auto epilogue = [&](int n0) __attribute__((always_inline)) {
     const int col = n0 + 32 * wv + (lane & 31);
-    const float swc = sW[(int64_t)e * Nw + col];
+    const float swc = sw_lds[col - nfirst];
+    // opaque to the optimiser: otherwise the 128 row indices and their LDS
+    // addresses are hoisted out of the main loop and spill
+    int rlane = 4 * (lane >> 5);
+    asm volatile("" : "+v"(rlane));
 #pragma unroll
     for (int i = 0; i < BM / 32; i++) {
       if (32 * i >= rows) break;
       float h[16];
+      int prow[MODE == 1 ? 16 : 1];  // gemm1 keeps the pair ids for the SiLU stores
 #pragma unroll
       for (int v = 0; v < 16; v++) {
-        const int r = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const bool valid = r < rows;
+        const int r = min(32 * i + 8 * (v >> 2) + rlane + (v & 3), rows - 1);
         const int32_t av = acc[i][v];
-        if (dbg_acc && valid) dbg_acc[(int64_t)pair_lds[r] * Nw + col] = av;
-        h[v] = 0.0f;
-        if (valid) {
-          h[v] = (float)av;
-          h[v] = h[v] * sa_lds[r];
-          h[v] = h[v] * swc;
-        }
-        if (MODE == 2 && valid) out[(int64_t)pair_lds[r] * ldo + col] = h[v];
+        const int p = pair_lds[r];
+        if (MODE == 1) prow[v] = p;
+        if (dbg_acc) dbg_acc[(int64_t)p * Nw + col] = av;
+        h[v] = (float)av;
+        h[v] = h[v] * sa_lds[r];
+        h[v] = h[v] * swc;
+        if (MODE == 2) out[(int64_t)p * ldo + col] = h[v];
       }
       if (MODE == 1) {
         // gate = even interleaved row, up = the odd one in the neighbouring
@@ -762,14 +786,10 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_moe_tile(
         for (int v = 0; v < 16; v++) x[v] = __shfl_xor(h[v], 1, 64);
 #pragma unroll
         for (int v = 0; v < 8; v++) {
-          const int vv = v + 8 * odd;
-          const int r = 32 * i + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
           const float gate = odd ? x[v + 8] : h[v];
           const float up = odd ? h[v + 8] : x[v];
-          if (r < rows) {
-            const float sg = (float)((double)gate / (1.0 + exp(-(double)gate)));
-            out[(int64_t)pair_lds[r] * ldo + (col >> 1)] = sg * up;
-          }
+          const float sg = (float)((double)gate / (1.0 + exp(-(double)gate)));
+          out[(int64_t)(odd ? prow[v + 8] : prow[v]) * ldo + (col >> 1)] = sg * up;
         }
       }
     }
