@@ -62,6 +62,9 @@ __device__ __forceinline__ v16i mfma_32x32x32_i8(v4i a, v4i b, v16i c) {
 // 15:14, expcnt at 6:4, lgkmcnt at 11:8).
 constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// s_waitcnt immediate that waits for lgkmcnt == 0 only (LDS, scalar memory).
+constexpr int lgkmcnt0_imm() { return 15 | (3 << 14) | (7 << 4); }
+
 // Wait until at most n (wave-uniform, 0..15) vector memory operations of this
 // wave are outstanding.
 __device__ __forceinline__ void wait_vmcnt_le(int n) {

@@ -37,10 +37,28 @@ enum { kEpiBf16 = 0, kEpiI32 = 1, kEpiG256 = 2 };
 
 constexpr int kXcds = 8;
 
+// One wave-wide 1 KiB copy global -> LDS (lane l: 16 bytes to dst + 16 l).
+// buf: as a buffer load at byte offset voff + soff of [base, base + span);
+// else as a global load from src.  The compiler counts global_load_lds as a
+// possible LDS access that completes out of order, so with those in flight
+// every LDS wait is a full lgkmcnt(0) (each step's MFMAs then wait for all of
+// the step's fragment reads); buffer loads to LDS are not counted that way.
+__device__ __forceinline__ void lds_dma(bool buf, const int8_t* base, int span, int voff,
+                                        int soff, const int8_t* src, int8_t* dst) {
+  auto* d = (__attribute__((address_space(3))) void*)dst;
+  if (buf) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, span, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff, soff, 0, 0);
+  } else {
+    __builtin_amdgcn_global_load_lds((const void*)src, d, 16, 0, 0);
+  }
+}
+
 // MINB: workgroups that must fit on one CU at once (the register budget the
 // compiler gets follows from it).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int MODE, bool BPACKED,
-          bool APACKED = false, int KSUB = 1, int MINB = 1>
+          bool APACKED = false, int KSUB = 1, int MINB = 1, bool BUF = false>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, int M, int K, int64_t lda,
     const int8_t* __restrict__ qw, const float* __restrict__ sw, int N, int64_t ldw,
@@ -107,6 +125,11 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
   const int8_t* srcB[LB];
   constexpr int ASTEP = APACKED ? 1024 : 64;
   const int ntile_m = (M + 15) >> 4;
+  // BUF: the same loads as buffer loads from the workgroup's own operand
+  // ranges (32-bit offsets; the host picks BUF only when they fit)
+  const int8_t* baseA = APACKED ? qa + (int64_t)(m0 / 16) * nk * 1024 : qa + (int64_t)m0 * lda;
+  const int8_t* baseB = BPACKED ? qw + (int64_t)(n0 / 16) * nk * 1024 : qw + (int64_t)n0 * ldw;
+  int voffA[LA], voffB[LB];
 #pragma unroll
   for (int i = 0; i < LA; i++) {
     const int b = min(wv + i * W, NA - 1);
@@ -114,6 +137,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
       srcA[i] = qa + (int64_t)min(m0 / 16 + b, ntile_m - 1) * nk * 1024 + lane * 16;
     else
       srcA[i] = qa + (int64_t)min(m0 + b * 16 + j, M - 1) * lda + g * 16;
+    voffA[i] = (int)(srcA[i] - baseA);
   }
 #pragma unroll
   for (int i = 0; i < LB; i++) {
@@ -122,7 +146,11 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
       srcB[i] = qw + (int64_t)min(n0 / 16 + b, ntile_n - 1) * nk * 1024 + lane * 16;
     else
       srcB[i] = qw + (int64_t)min(n0 + b * 16 + j, N - 1) * ldw + g * 16;
+    voffB[i] = (int)(srcB[i] - baseB);
   }
+  // byte ranges the offsets above stay in (clamped rows)
+  const int spanA = !BUF ? 0 : APACKED ? NA * nk * 1024 : (BM - 1) * (int)lda + K;
+  const int spanB = !BUF ? 0 : BPACKED ? NB * nk * 1024 : (BN - 1) * (int)ldw + K;
 
   // global -> LDS for pipeline step ks (KSUB chunks) into ring stage st
   auto issue = [&](int ks, int st) {
@@ -133,16 +161,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
 #pragma unroll
       for (int i = 0; i < LA; i++)
         if (NA % W == 0 || wv + i * W < NA)
-          __builtin_amdgcn_global_load_lds(
-              (const void*)(srcA[i] + kt * ASTEP),
-              (__attribute__((address_space(3))) void*)(stage + (wv + i * W) * 1024), 16, 0, 0);
+          lds_dma(BUF, baseA, spanA, voffA[i], kt * ASTEP, srcA[i] + kt * ASTEP,
+                  stage + (wv + i * W) * 1024);
 #pragma unroll
       for (int i = 0; i < LB; i++)
         if (NB % W == 0 || wv + i * W < NB)
-          __builtin_amdgcn_global_load_lds(
-              (const void*)(srcB[i] + kt * BSTEP),
-              (__attribute__((address_space(3))) void*)(stage + (NA + wv + i * W) * 1024), 16,
-              0, 0);
+          lds_dma(BUF, baseB, spanB, voffB[i], kt * BSTEP, srcB[i] + kt * BSTEP,
+                  stage + (NA + wv + i * W) * 1024);
     }
   };
   // loads every wave issues per k step, at least (waves 0.. may issue one
@@ -239,6 +264,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
   for (int p = 0; p < NSTAGE - 1; p++)
     if (p < nsteps) issue(p, p);
   for (int ks = 0; ks < nsteps; ks++) {
+    // Scalar loads still in flight (the compiler issues the epilogue's
+    // argument loads before this loop) return out of order, and while any
+    // is pending every LDS wait must be a full lgkmcnt(0): each step's MFMAs
+    // would then wait for all of its fragment reads.  Retiring them here
+    // (free after the first step) lets each MFMA wait only for its own.
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
     arrive(ks);
     if (ks + NSTAGE - 1 < nsteps) issue(ks + NSTAGE - 1, (ks + NSTAGE - 1) % NSTAGE);
     k_step(ks % NSTAGE);
@@ -318,12 +349,20 @@ hipError_t launch_tile_cfg(const int8_t* qa, const float* sa, int64_t M, int64_t
   const int tiles_n = (int)((N + BN - 1) / BN);
   const int group_m = 4;
   dim3 grid((unsigned)(tiles_m * tiles_n)), block(WAVES_M * WAVES_N * 64);
-  hipLaunchKernelGGL(
-      (k_gemm_tile<BM, BN, WAVES_M, WAVES_N, NSTAGE, MODE, BPACKED, APACKED, KSUB, MINB>), grid,
-      block,
-      0,
-                     stream, qa, sa, (int)M, (int)K, lda, qw, sw, (int)N, ldw, out, ldo, tiles_m,
-                     tiles_n, group_m, su8, s2);
+  // buffer-load operand feed when a workgroup's operand bytes span < 2 GiB
+  // (always for packed operands: BM x K or BN x K bytes)
+  constexpr int64_t kSpan = (int64_t)1 << 31;
+  const bool buf = (APACKED || (BM - 1) * lda + K < kSpan) && (BPACKED || (BN - 1) * ldw + K < kSpan);
+  if (buf)
+    hipLaunchKernelGGL(
+        (k_gemm_tile<BM, BN, WAVES_M, WAVES_N, NSTAGE, MODE, BPACKED, APACKED, KSUB, MINB, true>),
+        grid, block, 0, stream, qa, sa, (int)M, (int)K, lda, qw, sw, (int)N, ldw, out, ldo,
+        tiles_m, tiles_n, group_m, su8, s2);
+  else
+    hipLaunchKernelGGL(
+        (k_gemm_tile<BM, BN, WAVES_M, WAVES_N, NSTAGE, MODE, BPACKED, APACKED, KSUB, MINB, false>),
+        grid, block, 0, stream, qa, sa, (int)M, (int)K, lda, qw, sw, (int)N, ldw, out, ldo,
+        tiles_m, tiles_n, group_m, su8, s2);
   return hipGetLastError();
 }
 

@@ -45,6 +45,11 @@ constexpr size_t kAlign = 256;
 constexpr int kMoeBM = 128;
 // largest number of weight blocks one gemm2 workgroup walks (npw)
 constexpr int kMoeMaxNpw = 8;
+// batches up to this many tokens run routing, quantisation and the sort in
+// one workgroup (k_moe_prep); top-k is at most kMoeMaxTopk (checked at the
+// entry point)
+constexpr int kMoePrepTokens = 16;
+constexpr int kMoeMaxTopk = 16;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct MoeWs {
@@ -136,7 +141,7 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E, int k,
                                             int32_t* __restrict__ ids, float* __restrict__ w,
-                                            int lane) {
+                                            int lane, int32_t* ids_copy = nullptr) {
   float v[16];
   float lmax = -INFINITY;
 #pragma unroll
@@ -185,6 +190,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E,
   if (lane < k) {
     ids[lane] = my_e;
     w[lane] = (float)(myp / kept);
+    if (ids_copy) ids_copy[lane] = my_e;
   }
 }
 
@@ -422,19 +428,23 @@ __global__ __launch_bounds__(1024) void k_moe_prep(
     int32_t* __restrict__ n_active, int32_t* __restrict__ sorted_pairs,
     uint32_t* __restrict__ amax) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // routed ids also go to LDS, where the sort reads them (no round trip
+  // through global memory); caller-provided ids are read from global memory
+  __shared__ int32_t ids_lds[kMoePrepTokens * kMoeMaxTopk];
   // waves 0-7 route tokens, waves 8-15 quantise them, side by side
   const int t0 = wv & 7;
   for (int t = t0; t < T; t += 8) {
     if (wv < 8) {
       if (logits)
         route_token(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k,
-                    lane);
+                    lane, ids_lds + t * k);
     } else {
       quant_row_wave(x + (int64_t)t * H, H, qx + (int64_t)t * H, sx + t, lane);
     }
   }
   __syncthreads();  // the routing ids written above are read by the sort
-  sort_pairs(ids, T * k, E, expert_list, seg_off, n_active, sorted_pairs, amax);
+  sort_pairs(logits ? ids_lds : ids, T * k, E, expert_list, seg_off, n_active, sorted_pairs,
+             amax);
 }
 
 // ---------------------------------------------------------------------------
@@ -917,7 +927,6 @@ size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int k) {
 constexpr int64_t kMoeSmallPairs = 2048;
 // up to this many tokens the small path routes, quantises and sorts in one
 // workgroup (16 waves); beyond, one wave per token and a separate sort
-constexpr int kMoePrepTokens = 16;
 
 template <bool PACKED>
 static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
