@@ -434,13 +434,21 @@ static hipError_t launch_tile_impl(const int8_t* qa, const float* sa, int64_t M,
       const int64_t tn_main = tn / q * q;      // < tn, so the main range ends before N
       if (tn_main > 0) {
         const int64_t n_main = tn_main * 256;
-        const int64_t rem_tiles = ((M + 127) / 128) * ((N - n_main + 63) / 64);
+        const int64_t rem_tiles =
+            APACKED ? ((M + 127) / 128) * ((N - n_main + 63) / 64)
+                    : ((M + 63) / 64) * ((N - n_main + 127) / 128);
         const int64_t rem_rounds = (rem_tiles + 2 * cus - 1) / (2 * cus);
         // in tenths of a 256 x 256 round
         if (10 * (tm * tn_main / cus) + 4 * rem_rounds < 10 * rounds) {
           hipError_t e = launch_256<MODE, BPACKED, APACKED>(qa, sa, M, K, lda, qw, sw, ldw, out,
                                                             ldo, 0, n_main, stream);
           if (e != hipSuccess) return e;
+          // row-major activations cost more per row than packed ones (16
+          // separate 64-byte pieces per 1 KiB load), so their remainder tiles
+          // take fewer rows and more columns
+          if (!APACKED)
+            return launch_cols<64, 128, 2, 2, 4, MODE, BPACKED, APACKED, 1, 2>(
+                qa, sa, M, K, lda, qw, sw, ldw, out, ldo, n_main, N - n_main, stream);
           return launch_cols<128, 64, 2, 2, 4, MODE, BPACKED, APACKED, 1, 2>(
               qa, sa, M, K, lda, qw, sw, ldw, out, ldo, n_main, N - n_main, stream);
         }
