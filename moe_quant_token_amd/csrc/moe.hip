@@ -305,6 +305,12 @@ __device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int 
   // (batches of 16 pairs per thread: the id loads of a batch are all in
   // flight before its first atomic)
   constexpr int B = 16;
+  // one batch covers every pair (P <= 16384): the ids and counts stay in
+  // registers for the scatter below, which then reads nothing back
+  const bool one = P <= 1024 * B;
+  int e1[B], k1[B];
+#pragma unroll
+  for (int b = 0; b < B; b++) e1[b] = -1, k1[b] = 0;
   for (int r0 = tid; r0 < P; r0 += 1024 * B) {
     int e[B];
 #pragma unroll
@@ -317,7 +323,12 @@ __device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int 
       const int r = r0 + 1024 * b;
       if (e[b] >= 0 && e[b] < E) {
         const int k = atomicAdd(&cnt[e[b]], 1);
-        if (rank) rank[r] = k;
+        if (one) {
+          e1[b] = e[b];
+          k1[b] = k;
+        } else if (rank) {
+          rank[r] = k;
+        }
       }
       if (amax && r < P) amax[r] = 0u;
     }
@@ -377,6 +388,12 @@ __device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int 
     seg_off[tot_f] = tot_c;
   }
   __syncthreads();
+  if (one) {
+#pragma unroll
+    for (int b = 0; b < B; b++)
+      if (e1[b] >= 0) sorted_pairs[cursor[e1[b]] + k1[b]] = tid + 1024 * b;
+    return;
+  }
   for (int r0 = tid; r0 < P; r0 += 1024 * B) {
     int e[B], k[B];
 #pragma unroll

@@ -145,6 +145,18 @@ def test_large_batch_wide_intermediate(orc):
     _check_full(orc, x, logits, k, W, T, "moe large-batch I=1088", packed=True)
 
 
+def test_large_batch_more_pairs_than_one_sort_batch(orc):
+    # 16800 routed pairs: more than the 16 x 1024 the sort keeps in registers,
+    # so it takes the path that stores each pair's rank and reads it back
+    T, E, H, I, k = 2100, 16, 64, 64, 8
+    key = (47, 1)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    logits = synth.router_logits(key, T, E)
+    assert T * k > 16 * 1024 and _tie_free(logits, k)
+    _check_full(orc, x, logits, k, W, T, "moe 16800 pairs", packed=True)
+
+
 def test_given_routing_hot_expert_and_edges(orc):
     # logits=None: the caller supplies ids/weights.  Most tokens go to expert 3
     # (a segment far longer than one 64-pair pass); expert 0 gets none.
