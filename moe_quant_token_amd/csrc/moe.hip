@@ -68,6 +68,7 @@ struct MoeWs {
   int32_t* blk_row0;      // [P / kMoeBM + E + 1]  m-block -> first sorted pair
   int32_t* n_blocks;      // [1]
   int32_t* rank;          // [P]  a pair's position inside its expert's segment
+  uint32_t* amax_part;    // [P, 2I/16] (T == 1 only) per-tile partial |act| maxima
   size_t bytes;
 };
 
@@ -96,6 +97,7 @@ MoeWs carve(void* base, int64_t T, int64_t H, int64_t E, int64_t I, int k) {
   w.blk_row0 = reinterpret_cast<int32_t*>(take((P / kMoeBM + E + 1) * 4));
   w.n_blocks = reinterpret_cast<int32_t*>(take(4));
   w.rank = reinterpret_cast<int32_t*>(take(P * 4));
+  w.amax_part = reinterpret_cast<uint32_t*>(take(T == 1 ? P * (2 * I / 16) * 4 : 0));
   w.bytes = off;
   return w;
 }
@@ -139,9 +141,10 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // fp32 (within one fp32 ulp of the quotient of the rounded fp64 softmax
 // probabilities).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void route_token(const float* __restrict__ lt, int E, int k,
-                                            int32_t* __restrict__ ids, float* __restrict__ w,
-                                            int lane, int32_t* ids_copy = nullptr) {
+// Routing of one token by one wave: lane s < k ends with the expert of slot
+// s and its renormalised weight.
+__device__ __forceinline__ void route_select(const float* __restrict__ lt, int E, int k,
+                                             int lane, int& sel_e, float& sel_w) {
   float v[16];
   float lmax = -INFINITY;
 #pragma unroll
@@ -187,9 +190,19 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E,
   const double myp = exp((double)my_l - mx);
   double kept = 0.0;
   for (int s = 0; s < k; s++) kept += __shfl(myp, s, 64);
+  sel_e = my_e;
+  sel_w = (float)(myp / kept);
+}
+
+__device__ __forceinline__ void route_token(const float* __restrict__ lt, int E, int k,
+                                            int32_t* __restrict__ ids, float* __restrict__ w,
+                                            int lane, int32_t* ids_copy = nullptr) {
+  int my_e;
+  float my_w;
+  route_select(lt, E, k, lane, my_e, my_w);
   if (lane < k) {
     ids[lane] = my_e;
-    w[lane] = (float)(myp / kept);
+    w[lane] = my_w;
     if (ids_copy) ids_copy[lane] = my_e;
   }
 }
@@ -491,7 +504,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_skinny(
     const int32_t* __restrict__ seg_off, const int32_t* __restrict__ n_active,
     const int32_t* __restrict__ sorted_pairs, float* __restrict__ out, int ldo,
     uint32_t* __restrict__ amax_out, int8_t* __restrict__ qa_rec, float* __restrict__ sa2_rec,
-    int32_t* __restrict__ dbg_acc) {
+    int32_t* __restrict__ dbg_acc, int amax_parts = 1) {
   constexpr int U = NT >= 4 ? 2 : 4;  // 64-byte k steps per batch
   __shared__ v4i red[NT][WAVES][64];
   __shared__ __attribute__((aligned(16))) int8_t a_lds[MODE == 2 ? 16 * kMoeSkinnyMaxK2 : 16];
@@ -539,9 +552,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_skinny(
       pair_lds[threadIdx.x] = threadIdx.x < nrows ? sorted_pairs[pb + threadIdx.x] : 0;
     if (MODE == 2) {
       __syncthreads();
-      if (threadIdx.x < nrows) {
-        const float am = __uint_as_float(amax_in[pair_lds[threadIdx.x]]);
-        sa2_lds[threadIdx.x] = am != 0.0f ? am / 127.0f : 0.0f;
+      // each pair's |act| maximum, kept as amax_parts partial maxima
+      // (non-negative fp32 bit patterns, so the integer maximum is theirs):
+      // one wave per row, the parts spread over its lanes
+      for (int r = wv; r < nrows; r += WAVES) {
+        const uint32_t* ap = amax_in + (int64_t)pair_lds[r] * amax_parts;
+        uint32_t mb = 0u;
+        for (int i = lane; i < amax_parts; i += 64) mb = max(mb, ap[i]);
+        mb = wave_max_u32(mb);
+        if (lane == 0) {
+          const float am = __uint_as_float(mb);
+          sa2_lds[r] = am != 0.0f ? am / 127.0f : 0.0f;
+        }
       }
       __syncthreads();
       // requantise the block's activation rows straight into the packed
@@ -648,6 +670,177 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_skinny(
           out[(int64_t)p * ldo + col] = yv;
         }
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One routed token (T == 1, router logits given): routing, the token's
+// quantisation and gemm1 in one launch.  With one token the k selected
+// experts are distinct, so slot s is pair s of expert ids[s] and no sort is
+// needed.  Every workgroup routes the token (wave 0) and every wave finds the
+// row maximum itself (the logits and the row are small and come from L2), so
+// each workgroup requests its expert's weights without waiting on another
+// launch.  Workgroup (tile,
+// slot) = one 16-row tile of that expert's interleaved w13, 8 waves over K
+// as in k_moe_skinny, epilogue SiLU(gate) * up.  The pair's |act| maximum is
+// left as one partial maximum per tile (gemm2's prologue takes their
+// maximum), so nothing needs clearing before the launch.  Workgroup
+// (tile 0, slot s) also writes the slot's segment record for gemm2, and
+// (tile 0, slot 0) the routing outputs and the token's codes and scale.
+// ---------------------------------------------------------------------------
+template <bool PACKED>
+__global__ __launch_bounds__(512) void k_moe_t1_gemm1(
+    const uint16_t* __restrict__ x, const float* __restrict__ logits, int H, int E, int k,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, const int8_t* __restrict__ W,
+    const float* __restrict__ sW, int Nw, int8_t* __restrict__ qx, float* __restrict__ sx,
+    int32_t* __restrict__ expert_list, int32_t* __restrict__ seg_off,
+    int32_t* __restrict__ n_active, int32_t* __restrict__ sorted_pairs,
+    float* __restrict__ out, int ldo, uint32_t* __restrict__ amax_part,
+    int32_t* __restrict__ dbg_acc) {
+  constexpr int WAVES = 8, U = 4;
+  __shared__ v4i red[WAVES][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int tile = blockIdx.x, slot = blockIdx.y, ntiles = gridDim.x;
+  const int nk = H >> 6;
+
+  // the token row goes out first (held for the row maximum: 8 16-byte
+  // chunks a lane cover H <= 4096), then the logits with the routing
+  constexpr int XR = 8;
+  const int nc8 = H >> 3;
+  v4u xr[XR];
+#pragma unroll
+  for (int u = 0; u < XR; u++) {
+    const int c = lane + 64 * u;
+    xr[u] = c < nc8 ? *reinterpret_cast<const v4u*>(x + c * 8) : v4u{0u, 0u, 0u, 0u};
+  }
+  // wave 0 routes the token (the selection is a chain of k wave-wide
+  // maximum rounds; on every wave it would fill the SIMDs for microseconds);
+  // the others wait at the barrier
+  __shared__ int e_lds;
+  int sel_e = 0;
+  float sel_w = 0.0f;
+  if (wv == 0) {
+    route_select(logits, E, k, lane, sel_e, sel_w);
+    const int es = __shfl(sel_e, slot, 64);
+    if (lane == 0) e_lds = es;
+  }
+  __syncthreads();
+  const int e = __builtin_amdgcn_readfirstlane(e_lds);
+
+  const int8_t* wbase = PACKED ? W + ((int64_t)e * (Nw >> 4) + tile) * nk * 1024 + lane * 16
+                               : W + ((int64_t)e * Nw + tile * 16 + j) * H + g * 16;
+  constexpr int64_t wstep = PACKED ? 1024 : 64;
+  auto load_w = [&](v4i* b, int c0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int c = c0 + u * WAVES;
+      b[u] = c < nk ? *reinterpret_cast<const v4i*>(wbase + c * wstep) : v4i{0, 0, 0, 0};
+    }
+  };
+  v4i bq[U];
+  load_w(bq, wv);
+  const int col = tile * 16 + j;
+  const float swc = wv == 0 ? sW[(int64_t)e * Nw + col] : 0.0f;  // wave 0's epilogue
+
+  // the token's scale: maximum of |x| over the row (every wave), as k_quant_rows
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < XR; u++) amax = fmaxf(amax, amax8_bf16(xr[u]));
+  for (int c = lane + 64 * XR; c < nc8; c += 64)
+    amax = fmaxf(amax, amax8_bf16(*reinterpret_cast<const v4u*>(x + c * 8)));
+  amax = wave_max(amax);
+  const float sc = amax / 127.0f;
+  const float rc = 1.0f / sc;
+  const float sxv = amax != 0.0f ? sc : 0.0f;
+  // A operand of k chunk c: lanes of row 0 (j == 0) hold the codes of
+  // x[64c + 16g .. +15]; the other rows are zero
+  auto load_a = [&](int c) __attribute__((always_inline)) {
+    v4i a = {0, 0, 0, 0};
+    if (j == 0 && c < nk && amax != 0.0f) {
+      const uint16_t* px = x + c * 64 + g * 16;
+      const v4u r0 = *reinterpret_cast<const v4u*>(px);
+      const v4u r1 = *reinterpret_cast<const v4u*>(px + 8);
+      a = v4i{(int)quant_pack4_bf16(r0.x, r0.y, sc, rc), (int)quant_pack4_bf16(r0.z, r0.w, sc, rc),
+              (int)quant_pack4_bf16(r1.x, r1.y, sc, rc), (int)quant_pack4_bf16(r1.z, r1.w, sc, rc)};
+    }
+    return a;
+  };
+
+  v4i acc = {0, 0, 0, 0};
+  for (int c0 = wv; c0 < nk; c0 += WAVES * U) {
+    v4i bn[U];
+    if (c0 + WAVES * U < nk) load_w(bn, c0 + WAVES * U);
+    v4i a[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) a[u] = load_a(c0 + u * WAVES);
+#pragma unroll
+    for (int u = 0; u < U; u++) acc = mfma_16x16x64_i8(a[u], bq[u], acc);
+    if (c0 + WAVES * U < nk) {
+#pragma unroll
+      for (int u = 0; u < U; u++) bq[u] = bn[u];
+    }
+  }
+
+  // wave 0 writes the tile
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int w2 = 1; w2 < WAVES; w2++) acc += red[w2][lane];
+    keep_live(swc);
+    // result lane l holds rows 4*(l/16)+v of column l%16: the token is row 0
+    float h = (float)acc[0];
+    h = h * sxv;
+    h = h * swc;
+    if (dbg_acc && g == 0) dbg_acc[(int64_t)slot * Nw + col] = acc[0];
+    const float partner = __shfl_xor(h, 1, 64);
+    float mag = 0.0f;
+    if (g == 0 && (j & 1) == 0) {
+      // SiLU(gate) * up; the gate is the even interleaved row
+      const float sg = (float)((double)h / (1.0 + exp(-(double)h)));
+      const float av = sg * partner;
+      out[(int64_t)slot * ldo + (col >> 1)] = av;
+      mag = fabsf(av);
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) mag = fmaxf(mag, __shfl_xor(mag, off, 64));
+    if (lane == 0) amax_part[(int64_t)slot * ntiles + tile] = __float_as_uint(mag);
+    if (tile == 0) {
+      // the slot's segment for gemm2: expert e, pair `slot`
+      if (lane == 0) {
+        expert_list[slot] = e;
+        seg_off[slot] = slot;
+        sorted_pairs[slot] = slot;
+      }
+      if (slot == 0) {
+        if (lane == 0) {
+          n_active[0] = k;
+          seg_off[k] = k;
+          sx[0] = sxv;
+        }
+        if (lane < k) {
+          topk_ids[lane] = sel_e;
+          topk_w[lane] = sel_w;
+        }
+      }
+    }
+  }
+  // the token's codes (debug output), by wave 1 of workgroup (0, 0)
+  if (wv == 1 && tile == 0 && slot == 0) {
+    for (int c = lane; c < (H >> 3); c += 64) {
+      const v4u raw = *reinterpret_cast<const v4u*>(x + c * 8);
+      uint32_t lo = 0, hi = 0;
+      if (amax != 0.0f) {
+        lo = quant_pack4_bf16(raw.x, raw.y, sc, rc);
+        hi = quant_pack4_bf16(raw.z, raw.w, sc, rc);
+      }
+      uint32_t* o = reinterpret_cast<uint32_t*>(qx + c * 8);
+      o[0] = lo;
+      o[1] = hi;
     }
   }
 }
@@ -953,7 +1146,20 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
   const int I2 = 2 * a.I;
   hipError_t err;
   const bool small = P <= kMoeSmallPairs && a.I <= kMoeSkinnyMaxK2;
-  if (small) {
+  if (small && a.T == 1 && a.logits) {
+    // one routed token: routing and quant fused into gemm1
+    const int tiles1 = I2 / 16, tiles2 = a.H / 16;
+    hipLaunchKernelGGL((k_moe_t1_gemm1<PACKED>), dim3(tiles1, a.k), dim3(512), 0, stream, a.x,
+                       a.logits, a.H, a.E, a.k, a.topk_ids, a.topk_w, a.w13, a.s13, I2, ws.qx,
+                       ws.sx, ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.act,
+                       a.I, ws.amax_part, a.dbg_acc1);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((k_moe_skinny<4, 2, 2, PACKED>), dim3(tiles2 / 2, a.k), dim3(256), 0,
+                       stream, nullptr, nullptr, ws.act, ws.amax_part, a.k, a.w2, a.s2, a.H, a.I,
+                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.y2, a.H,
+                       nullptr, a.dbg_qa, a.dbg_sa2, a.dbg_acc2, tiles1);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  } else if (small) {
     if (a.T <= kMoePrepTokens) {
       hipLaunchKernelGGL(k_moe_prep, dim3(1), dim3(1024), 0, stream, a.x, a.logits, a.T, a.H,
                          a.E, a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx, ws.expert_list,

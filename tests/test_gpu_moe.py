@@ -96,6 +96,27 @@ def test_small_full_pipeline(orc, packed):
 
 
 @pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("H,k,zero", [(256, 8, False), (2112, 1, False), (2112, 16, False),
+                                      (256, 8, True)])
+def test_single_token_fused_path(orc, H, k, zero, packed):
+    # T=1 with router logits: routing and quant run inside gemm1 (every
+    # workgroup routes the token itself).  H=256 leaves waves without a k
+    # chunk; H=2112 takes a second, partial round of weight loads; an
+    # all-zero token has scale 0 and zero activations.
+    T, E, I = 1, 32, 128
+    key = (48, H * 100 + k)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    if zero:
+        x[:] = 0
+    logits = synth.router_logits(key, T, E)
+    assert _tie_free(logits, k)
+    out = _check_full(orc, x, logits, k, W, T, f"moe T=1 H={H} k={k}", packed=packed)
+    if zero:
+        assert not bf16_host(out).any()
+
+
+@pytest.mark.parametrize("packed", [False, True])
 def test_large_batch_path(orc, packed):
     # more than 2048 routed pairs: the routing/sort/quant kernels, the
     # 128-pair m-block grouped GEMMs (several blocks per expert here) and the
