@@ -50,6 +50,7 @@ constexpr int kMoeMaxNpw = 8;
 // entry point)
 constexpr int kMoePrepTokens = 16;
 constexpr int kMoeMaxTopk = 16;
+constexpr int kMoeMaxH = 16384;  // hidden size limit (checked at the entry point)
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct MoeWs {
@@ -700,6 +701,7 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm1(
     int32_t* __restrict__ dbg_acc) {
   constexpr int WAVES = 8, U = 4;
   __shared__ v4i red[WAVES][64];
+  __shared__ __attribute__((aligned(16))) int8_t q_lds[kMoeMaxH];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int j = lane & 15;
@@ -756,18 +758,30 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm1(
   const float sc = amax / 127.0f;
   const float rc = 1.0f / sc;
   const float sxv = amax != 0.0f ? sc : 0.0f;
-  // A operand of k chunk c: lanes of row 0 (j == 0) hold the codes of
-  // x[64c + 16g .. +15]; the other rows are zero
-  auto load_a = [&](int c) __attribute__((always_inline)) {
-    v4i a = {0, 0, 0, 0};
-    if (j == 0 && c < nk && amax != 0.0f) {
-      const uint16_t* px = x + c * 64 + g * 16;
-      const v4u r0 = *reinterpret_cast<const v4u*>(px);
-      const v4u r1 = *reinterpret_cast<const v4u*>(px + 8);
-      a = v4i{(int)quant_pack4_bf16(r0.x, r0.y, sc, rc), (int)quant_pack4_bf16(r0.z, r0.w, sc, rc),
-              (int)quant_pack4_bf16(r1.x, r1.y, sc, rc), (int)quant_pack4_bf16(r1.z, r1.w, sc, rc)};
+  // the token's codes, by the whole workgroup (8 per thread), into LDS;
+  // workgroup (0, 0) also writes them out with the scale
+  for (int c8 = threadIdx.x; c8 < nc8; c8 += WAVES * 64) {
+    const v4u raw = *reinterpret_cast<const v4u*>(x + c8 * 8);
+    uint32_t lo = 0, hi = 0;
+    if (amax != 0.0f) {
+      lo = quant_pack4_bf16(raw.x, raw.y, sc, rc);
+      hi = quant_pack4_bf16(raw.z, raw.w, sc, rc);
     }
-    return a;
+    uint32_t* ql = reinterpret_cast<uint32_t*>(q_lds + c8 * 8);
+    ql[0] = lo;
+    ql[1] = hi;
+    if (tile == 0 && slot == 0) {
+      uint32_t* o = reinterpret_cast<uint32_t*>(qx + c8 * 8);
+      o[0] = lo;
+      o[1] = hi;
+    }
+  }
+  __syncthreads();
+  // A operand of k chunk c: lanes of row 0 (j == 0) hold codes 64c + 16g ..
+  // +15; the other rows are zero
+  auto load_a = [&](int c) __attribute__((always_inline)) {
+    return (j == 0 && c < nk) ? *reinterpret_cast<const v4i*>(q_lds + c * 64 + g * 16)
+                              : v4i{0, 0, 0, 0};
   };
 
   v4i acc = {0, 0, 0, 0};
@@ -829,19 +843,92 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm1(
       }
     }
   }
-  // the token's codes (debug output), by wave 1 of workgroup (0, 0)
-  if (wv == 1 && tile == 0 && slot == 0) {
-    for (int c = lane; c < (H >> 3); c += 64) {
-      const v4u raw = *reinterpret_cast<const v4u*>(x + c * 8);
-      uint32_t lo = 0, hi = 0;
-      if (amax != 0.0f) {
-        lo = quant_pack4_bf16(raw.x, raw.y, sc, rc);
-        hi = quant_pack4_bf16(raw.z, raw.w, sc, rc);
-      }
-      uint32_t* o = reinterpret_cast<uint32_t*>(qx + c * 8);
-      o[0] = lo;
-      o[1] = hi;
+}
+
+// ---------------------------------------------------------------------------
+// One routed token: requant, gemm2 and the weighted combine in one launch.
+// Workgroup = 16 output columns; wave w takes slot w (and w + 8): it
+// requantises the pair's activation row from the partial maxima gemm1 left,
+// multiplies it with the 16 rows of its expert's w2 (all of K = I on the one
+// wave), and puts the dequantised y2 values in LDS.  Wave 0 then forms
+// out = bf16(sum over slots of w_s * y2_s) in fp32, slot order, no FMA --
+// the combine of k_moe_combine -- without y2 going through memory.
+// ---------------------------------------------------------------------------
+template <bool PACKED>
+__global__ __launch_bounds__(512) void k_moe_t1_gemm2(
+    const float* __restrict__ act, const uint32_t* __restrict__ amax_part, int parts,
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int k,
+    const int8_t* __restrict__ W2, const float* __restrict__ s2, int H, int I,
+    uint16_t* __restrict__ out, int8_t* __restrict__ dbg_qa, float* __restrict__ dbg_sa2,
+    int32_t* __restrict__ dbg_acc) {
+  constexpr int WAVES = 8, U = 8;
+  __shared__ float ybuf[kMoeMaxTopk][16];
+  __shared__ __attribute__((aligned(16))) int8_t qa_lds[WAVES][kMoeSkinnyMaxK2];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int tile = blockIdx.x;
+  const int nk = I >> 6;
+  for (int sl = wv; sl < k; sl += WAVES) {
+    const int e = __builtin_amdgcn_readfirstlane(ids[sl]);
+    const int8_t* wbase = PACKED ? W2 + ((int64_t)e * (H >> 4) + tile) * nk * 1024 + lane * 16
+                                 : W2 + ((int64_t)e * H + tile * 16 + j) * I + g * 16;
+    constexpr int64_t wstep = PACKED ? 1024 : 64;
+    const int col = tile * 16 + j;
+    const float swc = s2[(int64_t)e * H + col];
+    // the pair's |act| maximum from gemm1's partial maxima (non-negative
+    // fp32 bit patterns), then its scale
+    uint32_t mb = 0u;
+    for (int i = lane; i < parts; i += 64) mb = max(mb, amax_part[(int64_t)sl * parts + i]);
+    mb = wave_max_u32(mb);
+    const float am = __uint_as_float(mb);
+    const float sc = am != 0.0f ? am / 127.0f : 0.0f;
+    // the row's codes, four per lane at a time, into this wave's LDS row
+    int8_t* qrow = qa_lds[wv];
+    for (int i = lane * 4; i < I; i += 256) {
+      const v4f v = *reinterpret_cast<const v4f*>(act + (int64_t)sl * I + i);
+      uint32_t wd = 0u;
+      if (sc != 0.0f)
+        wd = pack4_i8(quant_code(v.x, sc), quant_code(v.y, sc), quant_code(v.z, sc),
+                      quant_code(v.w, sc));
+      *reinterpret_cast<uint32_t*>(qrow + i) = wd;
+      if (dbg_qa && tile == 0) *reinterpret_cast<uint32_t*>(dbg_qa + (int64_t)sl * I + i) = wd;
     }
+    v4i acc = {0, 0, 0, 0};
+    for (int c0 = 0; c0 < nk; c0 += U) {
+      v4i b[U], a[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int c = c0 + u;
+        b[u] = c < nk ? *reinterpret_cast<const v4i*>(wbase + c * wstep) : v4i{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        // row 0 of the A operand (lanes j == 0): codes 64c + 16g .. +15; the
+        // other rows are zero
+        const int c = c0 + u;
+        a[u] = (j == 0 && c < nk) ? *reinterpret_cast<const v4i*>(qrow + c * 64 + g * 16)
+                                  : v4i{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) acc = mfma_16x16x64_i8(a[u], b[u], acc);
+    }
+    // result row 0 (lanes g == 0) holds the token's sums for the 16 columns
+    if (g == 0) {
+      float y = (float)acc[0];
+      y = y * sc;
+      y = y * swc;
+      ybuf[sl][j] = y;
+      if (dbg_acc) dbg_acc[(int64_t)sl * H + col] = acc[0];
+    }
+    if (dbg_sa2 && tile == 0 && lane == 0) dbg_sa2[sl] = sc;
+  }
+  __syncthreads();
+  if (wv == 0 && lane < 16) {
+    float o = 0.0f;
+    for (int sl = 0; sl < k; sl++) o = o + wts[sl] * ybuf[sl][lane];
+    out[tile * 16 + lane] = (uint16_t)f32_to_bf16_bits(o);
   }
 }
 
@@ -1146,7 +1233,8 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
   const int I2 = 2 * a.I;
   hipError_t err;
   const bool small = P <= kMoeSmallPairs && a.I <= kMoeSkinnyMaxK2;
-  if (small && a.T == 1 && a.logits) {
+  const bool t1 = small && a.T == 1 && a.logits;
+  if (t1) {
     // one routed token: routing and quant fused into gemm1
     const int tiles1 = I2 / 16, tiles2 = a.H / 16;
     hipLaunchKernelGGL((k_moe_t1_gemm1<PACKED>), dim3(tiles1, a.k), dim3(512), 0, stream, a.x,
@@ -1154,10 +1242,9 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
                        ws.sx, ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.act,
                        a.I, ws.amax_part, a.dbg_acc1);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_moe_skinny<4, 2, 2, PACKED>), dim3(tiles2 / 2, a.k), dim3(256), 0,
-                       stream, nullptr, nullptr, ws.act, ws.amax_part, a.k, a.w2, a.s2, a.H, a.I,
-                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.y2, a.H,
-                       nullptr, a.dbg_qa, a.dbg_sa2, a.dbg_acc2, tiles1);
+    hipLaunchKernelGGL((k_moe_t1_gemm2<PACKED>), dim3(tiles2), dim3(512), 0, stream, ws.act,
+                       ws.amax_part, tiles1, a.topk_ids, a.topk_w, a.k, a.w2, a.s2, a.H, a.I,
+                       a.out, a.dbg_qa, a.dbg_sa2, a.dbg_acc2);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   } else if (small) {
     if (a.T <= kMoePrepTokens) {
@@ -1246,9 +1333,11 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
                                            hipMemcpyDeviceToDevice, stream)) != hipSuccess)
       return err;
   }
-  hipLaunchKernelGGL(k_moe_combine, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, stream,
-                     ws.y2, a.topk_ids, a.topk_w, a.T, a.H, a.E, a.k, a.out);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (!t1) {  // the single-token path combined inside its gemm2
+    hipLaunchKernelGGL(k_moe_combine, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, stream,
+                       ws.y2, a.topk_ids, a.topk_w, a.T, a.H, a.E, a.k, a.out);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
 
   // optional copies of the remaining intermediates, in pair order
   if (a.dbg_qx && (err = hipMemcpyAsync(a.dbg_qx, ws.qx, (size_t)a.T * a.H,
