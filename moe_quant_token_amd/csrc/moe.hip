@@ -143,18 +143,19 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // probabilities).
 // ---------------------------------------------------------------------------
 // Routing of one token by one wave: lane s < k ends with the expert of slot
-// s and its renormalised weight.
-__device__ __forceinline__ void route_select(const float* __restrict__ lt, int E, int k,
-                                             int lane, int& sel_e, float& sel_w) {
-  float v[16];
-  float lmax = -INFINITY;
+// s and its renormalised weight.  VPL logits per lane (E <= 64 * VPL).
+template <int VPL>
+__device__ __forceinline__ void route_select_v(const float* __restrict__ lt, int E, int k,
+                                               int lane, int& sel_e, float& sel_w) {
+  uint32_t kv[VPL];  // order-preserving keys of the lane's logits; 0 = none
+  uint32_t kmax = 0;
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
+  for (int i = 0; i < VPL; i++) {
     const int e = lane + 64 * i;
-    v[i] = (64 * i < E && e < E) ? lt[e] : -INFINITY;
-    lmax = fmaxf(lmax, v[i]);
+    kv[i] = e < E ? float_key(lt[e]) : 0u;
+    kmax = max(kmax, kv[i]);
   }
-  const double mx = (double)wave_max(lmax);
+  const double mx = (double)key_float(wave_max_u32(kmax));  // the largest logit
 
   uint32_t taken = 0;
   int my_e = 0;
@@ -162,14 +163,11 @@ __device__ __forceinline__ void route_select(const float* __restrict__ lt, int E
   for (int s = 0; s < k; s++) {
     uint32_t hi = 0, lo = 0;  // best local key; 0 = none
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      if (64 * i >= E) break;  // uniform
-      const int e = lane + 64 * i;
-      const uint32_t kh = float_key(v[i]);
+    for (int i = 0; i < VPL; i++) {
       // ascending e: ties keep the lower index
-      if (e < E && !(taken & (1u << i)) && kh > hi) {
-        hi = kh;
-        lo = 0xffffffffu - (uint32_t)e;
+      if (!(taken & (1u << i)) && kv[i] > hi) {
+        hi = kv[i];
+        lo = 0xffffffffu - (uint32_t)(lane + 64 * i);
       }
     }
     const uint32_t mh = wave_max_u32(hi);
@@ -189,10 +187,24 @@ __device__ __forceinline__ void route_select(const float* __restrict__ lt, int E
     }
   }
   const double myp = exp((double)my_l - mx);
+  // kept probabilities summed in slot order (lane reads, no LDS traffic)
+  const uint64_t pb = (uint64_t)__double_as_longlong(myp);
   double kept = 0.0;
-  for (int s = 0; s < k; s++) kept += __shfl(myp, s, 64);
+  for (int s = 0; s < k; s++) {
+    const uint32_t plo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, s);
+    const uint32_t phi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), s);
+    kept += __longlong_as_double((long long)(((uint64_t)phi << 32) | plo));
+  }
   sel_e = my_e;
   sel_w = (float)(myp / kept);
+}
+
+__device__ __forceinline__ void route_select(const float* __restrict__ lt, int E, int k,
+                                             int lane, int& sel_e, float& sel_w) {
+  if (E <= 256)
+    route_select_v<4>(lt, E, k, lane, sel_e, sel_w);
+  else
+    route_select_v<16>(lt, E, k, lane, sel_e, sel_w);
 }
 
 __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E, int k,
