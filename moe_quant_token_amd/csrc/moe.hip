@@ -509,8 +509,8 @@ constexpr int kMoeSkinnyMaxK2 = 2048;  // gemm2 reduction length (I) staged in L
 // weight bytes).  The first batch of weight loads is issued as soon as the
 // expert id is known, before the pair data is read, and every batch's MFMAs
 // run while the next batch's weight loads are in flight.
-template <int WAVES, int NT, int MODE, bool PACKED>
-__global__ __launch_bounds__(WAVES * 64) void k_moe_skinny(
+template <int WAVES, int NT, int MODE, bool PACKED, int MINB = 1>
+__global__ __launch_bounds__(WAVES * 64, MINB) void k_moe_skinny(
     const int8_t* __restrict__ qx, const float* __restrict__ sx, const float* __restrict__ act,
     const uint32_t* __restrict__ amax_in, int k, const int8_t* __restrict__ W,
     const float* __restrict__ sW, int Nw, int K, const int32_t* __restrict__ expert_list,
@@ -520,7 +520,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_moe_skinny(
     int32_t* __restrict__ dbg_acc, int amax_parts = 1) {
   constexpr int U = NT >= 4 ? 2 : 4;  // 64-byte k steps per batch
   __shared__ v4i red[NT][WAVES][64];
-  __shared__ __attribute__((aligned(16))) int8_t a_lds[MODE == 2 ? 16 * kMoeSkinnyMaxK2 : 16];
+  // gemm2: the block's requantised rows, 16 x K bytes of dynamic LDS (sized
+  // at launch, so short rows leave room for more workgroups per CU)
+  extern __shared__ __attribute__((aligned(16))) int8_t a_lds[];
   __shared__ float sa2_lds[16];
   __shared__ int pair_lds[16];
   const int slot = blockIdx.y;
@@ -1284,17 +1286,17 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
                          ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.act, a.I,
                          ws.amax, nullptr, nullptr, a.dbg_acc1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      hipLaunchKernelGGL((k_moe_skinny<4, 2, 2, PACKED>), dim3(tiles2 / 2, slots), dim3(256), 0,
+      hipLaunchKernelGGL((k_moe_skinny<4, 2, 2, PACKED>), dim3(tiles2 / 2, slots), dim3(256), 16 * a.I,
                          stream, nullptr, nullptr, ws.act, ws.amax, a.k, a.w2, a.s2, a.H, a.I,
                          ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.y2, a.H,
                          nullptr, a.dbg_qa, a.dbg_sa2, a.dbg_acc2);
     } else {
-      hipLaunchKernelGGL((k_moe_skinny<4, 2, 1, PACKED>), dim3(tiles1 / 2, slots), dim3(256), 0,
+      hipLaunchKernelGGL((k_moe_skinny<4, 2, 1, PACKED, 3>), dim3(tiles1 / 2, slots), dim3(256), 0,
                          stream, ws.qx, ws.sx, nullptr, nullptr, a.k, a.w13, a.s13, I2, a.H,
                          ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.act, a.I,
                          ws.amax, nullptr, nullptr, a.dbg_acc1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
-      hipLaunchKernelGGL((k_moe_skinny<4, 4, 2, PACKED>), dim3(tiles2 / 4, slots), dim3(256), 0,
+      hipLaunchKernelGGL((k_moe_skinny<4, 4, 2, PACKED>), dim3(tiles2 / 4, slots), dim3(256), 16 * a.I,
                          stream, nullptr, nullptr, ws.act, ws.amax, a.k, a.w2, a.s2, a.H, a.I,
                          ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.y2, a.H,
                          nullptr, a.dbg_qa, a.dbg_sa2, a.dbg_acc2);
