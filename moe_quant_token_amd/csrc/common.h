@@ -33,10 +33,21 @@ __device__ __forceinline__ int quant_code(float x, float s) {
   return (int)r;
 }
 
+// Wave-wide maximum through DPP row shifts and row broadcasts (no LDS
+// traffic); every lane gets the result.  A lane whose DPP source lies outside
+// the row keeps its own value (bound_ctrl off, old = v), so any sign works.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+#define W8A8_DPP_FMAX(ctrl, rmask)                                                          \
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), \
+                                                          ctrl, rmask, 0xf, false)))
+  W8A8_DPP_FMAX(0x111, 0xf);  // row_shr:1
+  W8A8_DPP_FMAX(0x112, 0xf);  // row_shr:2
+  W8A8_DPP_FMAX(0x114, 0xf);  // row_shr:4
+  W8A8_DPP_FMAX(0x118, 0xf);  // row_shr:8
+  W8A8_DPP_FMAX(0x142, 0xa);  // row_bcast:15
+  W8A8_DPP_FMAX(0x143, 0xc);  // row_bcast:31
+#undef W8A8_DPP_FMAX
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ int wave_sum_i(int v) {
