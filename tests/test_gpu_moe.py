@@ -178,6 +178,21 @@ def test_large_batch_more_pairs_than_one_sort_batch(orc):
     _check_full(orc, x, logits, k, W, T, "moe 16800 pairs", packed=True)
 
 
+@pytest.mark.parametrize("T", [1, 5, 40])
+def test_routing_more_than_256_experts(orc, T):
+    # E > 256: each routing lane holds 16 logits instead of 4; T=1 takes the
+    # fused single-token path, T=5 the one-workgroup prep, T=40 routing +
+    # quant one wave per token
+    E, H, I, k = 320, 128, 64, 8
+    key = (49, T)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    logits = synth.router_logits(key, T, E)
+    logits[:, 300:] += 0.5  # favour experts past 256 so some are selected
+    assert _tie_free(logits, k)
+    _check_full(orc, x, logits, k, W, T, f"moe E=320 T={T}", packed=True)
+
+
 def test_given_routing_hot_expert_and_edges(orc):
     # logits=None: the caller supplies ids/weights.  Most tokens go to expert 3
     # (a segment far longer than one 64-pair pass); expert 0 gets none.
