@@ -143,8 +143,96 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int
   if (threadIdx.x == 0) s[row] = (amax != 0.0f) ? sc : 0.0f;
 }
 
+// Many rows (prefill): one wave per row, the row held in registers as raw
+// bf16 (8 values a 16-byte chunk, up to NCH chunks a lane: K <= 512 * NCH),
+// the maximum through DPP, no barrier.  A workgroup of 4 waves has four rows
+// in flight, and a CU up to ~24 waves, so far more bytes are in flight than
+// with a 256-thread workgroup per row.  Same arithmetic as k_quant_rows.
+// PACKED_OUT: lane pairs (2i, 2i+1) hold the two halves of a 16-code k slice
+// and store them as 8-byte pieces of the tile layout.
+template <int NCH, bool PACKED_OUT>
+__global__ __launch_bounds__(256) void k_quant_rows_wave(const uint16_t* __restrict__ x,
+                                                         int64_t ldx, int M, int K,
+                                                         int8_t* __restrict__ q, int64_t ldq,
+                                                         float* __restrict__ s) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const uint16_t* xr = x + row * ldx;
+  const int nc = K >> 3;  // 8-value chunks
+  v4u raw[NCH];
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < NCH; u++) {
+    const int c = lane + 64 * u;
+    raw[u] = c < nc ? *reinterpret_cast<const v4u*>(xr + c * 8) : v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[u][i] & 0xffffu)));
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[u][i] >> 16)));
+    }
+  }
+  amax = wave_max(amax);
+  const float sc = amax / 127.0f;
+  const bool recip = sc >= 0x1p-100f;
+  const float rc = 1.0f / sc;
+  auto code = [&](uint32_t h) __attribute__((always_inline)) {
+    const float v = bf16_bits_to_f32(h);
+    return recip ? quant_code_recip(v, sc, rc) : quant_code(v, sc);
+  };
+#pragma unroll
+  for (int u = 0; u < NCH; u++) {
+    const int c = lane + 64 * u;
+    if (c >= nc) break;
+    uint32_t w[2] = {0u, 0u};
+    if (amax != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+        w[i] = pack4_i8(code(raw[u][2 * i] & 0xffffu), code(raw[u][2 * i] >> 16),
+                        code(raw[u][2 * i + 1] & 0xffffu), code(raw[u][2 * i + 1] >> 16));
+    }
+    int8_t* dst;
+    if (PACKED_OUT) {
+      const int c16 = c >> 1;  // 16-code slice: k bytes 16*c16 .. +15
+      dst = q + ((row >> 4) * (int64_t)(K >> 6) + (c16 >> 2)) * 1024 +
+            ((row & 15) + 16 * (c16 & 3)) * 16 + (c & 1) * 8;
+    } else {
+      dst = q + row * ldq + c * 8;
+    }
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  }
+  if (lane == 0) s[row] = amax != 0.0f ? sc : 0.0f;
+}
+
+// bf16 rows of up to 8192 values, more than 16 rows: the wave-per-row kernel,
+// holding as few chunks a lane as the row needs (registers bound how many
+// rows a CU keeps in flight)
+constexpr int kQuantWaveNch = 16;
+static bool use_wave_quant(int64_t M, int64_t K) { return M > 16 && K <= 512 * kQuantWaveNch; }
+
+template <bool PACKED_OUT>
+static void launch_quant_wave(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, int8_t* q,
+                              int64_t ldq, float* s, hipStream_t stream) {
+  const int need = (int)((K + 511) / 512);
+  const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+#define W8A8_QW(n)                                                                            \
+  hipLaunchKernelGGL((k_quant_rows_wave<n, PACKED_OUT>), grid, block, 0, stream, x, ldx, (int)M, \
+                     (int)K, q, ldq, s)
+  if (need <= 2) W8A8_QW(2);
+  else if (need <= 4) W8A8_QW(4);
+  else if (need <= 8) W8A8_QW(8);
+  else if (need <= 10) W8A8_QW(10);
+  else if (need <= 12) W8A8_QW(12);
+  else W8A8_QW(16);
+#undef W8A8_QW
+}
+
 hipError_t launch_quant_rows_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                     int8_t* q, float* s, hipStream_t stream) {
+  if (use_wave_quant(M, K)) {
+    launch_quant_wave<true>(x, ldx, M, K, q, 0, s, stream);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((k_quant_rows<uint16_t, true>), dim3((unsigned)M), dim3(256), 0, stream, x,
                      ldx, (int)K, q, (int64_t)0, s);
   return hipGetLastError();
@@ -153,6 +241,10 @@ hipError_t launch_quant_rows_packed(const uint16_t* x, int64_t M, int64_t K, int
 hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                              int8_t* q, int64_t ldq, float* s, hipStream_t stream) {
   dim3 grid((unsigned)M), block(256);
+  if (x_dtype == 0 && use_wave_quant(M, K)) {
+    launch_quant_wave<false>(static_cast<const uint16_t*>(x), ldx, M, K, q, ldq, s, stream);
+    return hipGetLastError();
+  }
   if (x_dtype == 0)
     hipLaunchKernelGGL(k_quant_rows<uint16_t>, grid, block, 0, stream,
                        static_cast<const uint16_t*>(x), ldx, (int)K, q, ldq, s);

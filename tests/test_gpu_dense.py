@@ -32,7 +32,11 @@ def _inputs(xkey, wkey, M, K, N, n_out, scale):
 
 # ---------------------------------------------------------------- quant
 @pytest.mark.parametrize("M,K", [(16, 512), (1, 5120), (8, 8704), (4096, 5120), (37, 16),
-                                 (5, 48), (3, 65536)])
+                                 (5, 48), (3, 65536),
+                                 # more than 16 rows: one wave per row, every
+                                 # register depth (2, 4, 8, 10, 12, 16 chunks)
+                                 (17, 1008), (101, 1040), (66, 4096), (35, 5104),
+                                 (33, 6000), (20, 8192), (19, 8208)])
 def test_quant_bf16_bit_exact(orc, M, K):
     say(f"quant bf16 M={M} K={K}")
     x = synth.activations((7, M, K), M, K, max(1, K // 100), 10.0)
@@ -54,6 +58,25 @@ def test_quant_fp32_weights_bit_exact(orc, N, K):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(q), q_ref)
     np.testing.assert_array_equal(host(s), s_ref)
+
+
+def test_quant_tiny_and_huge_rows(orc):
+    # rows whose scale falls below 2^-100 (the kernels divide instead of
+    # multiplying by the reciprocal), rows at the bf16 extremes, a zero row
+    M, K = 24, 320
+    x = synth.activations((7, 2), M, K, 3, 10.0).view(np.uint16).copy()
+    r = np.random.default_rng(3)
+    f = r.standard_normal((3, K)).astype(np.float32)
+    x[0] = synth.to_bf16_bits(f[0] * np.float32(1e-35))
+    x[1] = synth.to_bf16_bits(f[1] * np.float32(2e-38))
+    x[2] = synth.to_bf16_bits(f[2] * np.float32(1e37))
+    x[3] = 0
+    q_ref, s_ref = orc.quant_rows(x)
+    for rows in (M, 8):  # the wave-per-row and the block-per-row kernels
+        q, s = mq.quant_per_token_i8(bf16_dev(x[:rows]))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(q), q_ref[:rows])
+        np.testing.assert_array_equal(host(s), s_ref[:rows])
 
 
 def test_quant_strided_rows(orc):
