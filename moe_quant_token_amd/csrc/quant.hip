@@ -65,23 +65,24 @@ __device__ __forceinline__ int quant_code_recip(float x, float s, float r) {
 // registers; longer rows are read a second time (from L2) for the codes.
 constexpr int kQuantHeld = 4;
 
-template <typename T, bool PACKED_OUT = false>
-__global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int64_t ldx, int K,
-                                                    int8_t* __restrict__ q, int64_t ldq,
-                                                    float* __restrict__ s) {
-  __shared__ float part[4];
+template <typename T, bool PACKED_OUT = false, int NT = 256>
+__global__ __launch_bounds__(NT) void k_quant_rows(const T* __restrict__ x, int64_t ldx, int K,
+                                                   int8_t* __restrict__ q, int64_t ldq,
+                                                   float* __restrict__ s) {
+  constexpr int NW = NT / 64;
+  __shared__ float part[NW];
   const int64_t row = blockIdx.x;
   const T* xr = x + row * ldx;
   int8_t* qr = PACKED_OUT ? nullptr : q + row * ldq;
   const int nchunk = K >> 4;
-  const bool held = nchunk <= 256 * kQuantHeld;
+  const bool held = nchunk <= NT * kQuantHeld;
 
   Chunk16<T> ch[kQuantHeld];
   float amax = 0.0f;
   if (held) {
 #pragma unroll
     for (int i = 0; i < kQuantHeld; i++) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       if (c < nchunk) {
         ch[i].load(xr + c * 16);
 #pragma unroll
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int
       }
     }
   } else {
-    for (int c = threadIdx.x; c < nchunk; c += 256) {
+    for (int c = threadIdx.x; c < nchunk; c += NT) {
       Chunk16<T> t;
       t.load(xr + c * 16);
 #pragma unroll
@@ -99,7 +100,9 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int
   amax = wave_max(amax);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  amax = part[0];
+#pragma unroll
+  for (int w = 1; w < NW; w++) amax = fmaxf(amax, part[w]);
   const float sc = amax / 127.0f;
   const bool recip = sizeof(T) == 2 && sc >= 0x1p-100f;
   const float rc = 1.0f / sc;
@@ -130,11 +133,11 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int
   if (held) {
 #pragma unroll
     for (int i = 0; i < kQuantHeld; i++) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       if (c < nchunk) emit(ch[i], c);
     }
   } else {
-    for (int c = threadIdx.x; c < nchunk; c += 256) {
+    for (int c = threadIdx.x; c < nchunk; c += NT) {
       Chunk16<T> t;
       t.load(xr + c * 16);
       emit(t, c);
@@ -245,7 +248,10 @@ hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t M, int64_t K, i
     launch_quant_wave<false>(static_cast<const uint16_t*>(x), ldx, M, K, q, ldq, s, stream);
     return hipGetLastError();
   }
-  if (x_dtype == 0)
+  if (x_dtype == 0 && M <= 16)
+    hipLaunchKernelGGL((k_quant_rows<uint16_t, false, 1024>), grid, dim3(1024), 0, stream,
+                       static_cast<const uint16_t*>(x), ldx, (int)K, q, ldq, s);
+  else if (x_dtype == 0)
     hipLaunchKernelGGL(k_quant_rows<uint16_t>, grid, block, 0, stream,
                        static_cast<const uint16_t*>(x), ldx, (int)K, q, ldq, s);
   else
