@@ -25,6 +25,22 @@ struct Block8 {
   float v[8];
 };
 
+// The value of lane (lane ^ m), m in {1, 2, 4, 8}: DPP quad permutations for
+// 1 and 2, a swizzle (xor mode, no LDS access) for 4 and 8.
+__device__ __forceinline__ float lane_xor(float v, int m) {
+  const int i = __float_as_int(v);
+  int r;
+  if (m == 1)
+    r = __builtin_amdgcn_mov_dpp(i, 0xb1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+  else if (m == 2)
+    r = __builtin_amdgcn_mov_dpp(i, 0x4e, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+  else if (m == 4)
+    r = __builtin_amdgcn_ds_swizzle(i, 0x1f | (4 << 10));  // and 0x1f, xor 4
+  else
+    r = __builtin_amdgcn_ds_swizzle(i, 0x1f | (8 << 10));  // and 0x1f, xor 8
+  return __int_as_float(r);
+}
+
 // In-place butterfly of a 128-block spread over 16 lanes (l16 = lane % 16).
 __device__ __forceinline__ void fwht128_lanes(Block8& b, int l16) {
 #pragma unroll
@@ -42,7 +58,7 @@ __device__ __forceinline__ void fwht128_lanes(Block8& b, int l16) {
 #pragma unroll
     for (int c = 0; c < 8; c++) {
       const float mine = b.v[c];
-      const float other = __shfl_xor(mine, m, 64);
+      const float other = lane_xor(mine, m);
       b.v[c] = upper ? (other - mine) : (mine + other);
     }
   }
