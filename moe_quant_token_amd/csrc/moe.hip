@@ -12,19 +12,20 @@
 // Small batches (at most 2048 routed pairs):
 //   k_moe_prep     one workgroup: routing (one wave per token), per-token int8
 //                  codes of x, and the sort of the pairs by expert (up to 16
-//                  tokens; beyond, k_moe_route_quant and k_moe_sort)
+//                  tokens; beyond, k_moe_route_quant and the one-workgroup
+//                  k_moe_sort)
 //   k_moe_skinny<1> grouped gemm1 streaming each touched expert's w13 once,
 //                  SiLU(gate)*up epilogue, per-pair |act| maximum (atomic max)
 //   k_moe_skinny<2> grouped gemm2; its prologue requantises the pairs' rows
 //   k_moe_combine  out[t] = sum over the k slots, in slot order, one bf16
 //                  rounding; deterministic (no floating-point atomics)
 // Large batches:
-//   k_moe_route_quant  routing and per-token int8 codes of x, one wave per
-//                  token
-//   k_moe_sort     one workgroup: per-expert counts (each pair keeps its place
-//                  in its expert's segment), segment offsets, the list of
-//                  experts that received pairs, the pairs grouped by expert,
-//                  and the table of 128-pair m-blocks
+//   k_moe_route_quant  routing and per-token int8 codes of x, four tokens per
+//                  8-wave workgroup (routing waves beside quantising waves)
+//   k_moe_sort_hist / k_moe_sort_scatter  the sort over chunks of pairs, one
+//                  workgroup per chunk: per-chunk expert counts, then segment
+//                  offsets, the list of experts that received pairs, the
+//                  pairs grouped by expert and the table of 128-pair m-blocks
 //   k_moe_tile<1>  grouped gemm1 (32x32x32 MFMA): gathered activation rows
 //                  through LDS, weights prefetched into registers,
 //                  SiLU(gate)*up epilogue
@@ -51,6 +52,8 @@ constexpr int kMoeMaxNpw = 8;
 constexpr int kMoePrepTokens = 16;
 constexpr int kMoeMaxTopk = 16;
 constexpr int kMoeMaxH = 16384;  // hidden size limit (checked at the entry point)
+// the large-batch sort splits the pairs into at most this many chunks
+constexpr int kMoeSortChunks = 64;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct MoeWs {
@@ -68,7 +71,8 @@ struct MoeWs {
   int32_t* blk_slot;      // [P / kMoeBM + E + 1]  m-block -> expert slot
   int32_t* blk_row0;      // [P / kMoeBM + E + 1]  m-block -> first sorted pair
   int32_t* n_blocks;      // [1]
-  int32_t* rank;          // [P]  a pair's position inside its expert's segment
+  int32_t* rank;          // [P]  a pair's place among its sort chunk's pairs of its expert
+  int32_t* hist;          // [kMoeSortChunks, E]  per-chunk expert counts of the sort
   uint32_t* amax_part;    // [P, 2I/16] (T == 1 only) per-tile partial |act| maxima
   size_t bytes;
 };
@@ -98,6 +102,7 @@ MoeWs carve(void* base, int64_t T, int64_t H, int64_t E, int64_t I, int k) {
   w.blk_row0 = reinterpret_cast<int32_t*>(take((P / kMoeBM + E + 1) * 4));
   w.n_blocks = reinterpret_cast<int32_t*>(take(4));
   w.rank = reinterpret_cast<int32_t*>(take(P * 4));
+  w.hist = reinterpret_cast<int32_t*>(take(kMoeSortChunks * E * 4));
   w.amax_part = reinterpret_cast<uint32_t*>(take(T == 1 ? P * (2 * I / 16) * 4 : 0));
   w.bytes = off;
   return w;
@@ -304,67 +309,27 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ x, i
 }
 
 // ---------------------------------------------------------------------------
-// Sort / align by expert (one workgroup of 1024 threads).  Pairs with an id
-// outside [0, E) are dropped.  Also clears the per-pair |act| maxima.
+// Sort / align by expert.  Pairs with an id outside [0, E) are dropped; the
+// order of the pairs inside an expert's segment is not fixed (every pair's
+// row is computed on its own, so results do not depend on it).
 // ---------------------------------------------------------------------------
-// Runs on a whole 1024-thread workgroup.
-// With blk_slot set it also writes the m-block table of the large-batch
-// GEMMs: each expert segment split into blocks of kMoeBM sorted pairs.
-__device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int P, int E,
-                                           int32_t* __restrict__ expert_list,
+// Exclusive scans over the experts, one thread per expert (a whole 1024-thread
+// workgroup; E <= 1024): c = the expert's pair count.  Returns the expert's
+// segment offset.  With write set the workgroup also stores the list of
+// experts that received pairs (ascending), their segment offsets, the active
+// count and the end of the last segment, and, with blk_slot set, the table of
+// kMoeBM-pair m-blocks of the large-batch GEMMs (each segment split into
+// blocks of kMoeBM sorted pairs) and its length.
+__device__ __forceinline__ int expert_scan(int c, bool write, int32_t* __restrict__ expert_list,
                                            int32_t* __restrict__ seg_off,
                                            int32_t* __restrict__ n_active,
-                                           int32_t* __restrict__ sorted_pairs,
-                                           uint32_t* __restrict__ amax,
-                                           int32_t* __restrict__ blk_slot = nullptr,
-                                           int32_t* __restrict__ blk_row0 = nullptr,
-                                           int32_t* __restrict__ n_blocks = nullptr,
-                                           int32_t* __restrict__ rank = nullptr) {
-  __shared__ int cnt[1024];
-  __shared__ int cursor[1024];
+                                           int32_t* __restrict__ blk_slot,
+                                           int32_t* __restrict__ blk_row0,
+                                           int32_t* __restrict__ n_blocks) {
   __shared__ int wsum_c[16], wsum_f[16], wsum_b[16];
-  const int tid = threadIdx.x;
-  cnt[tid] = 0;
-  __syncthreads();
-  // counts; with rank set each pair also keeps the count it saw (its place
-  // in its expert's segment; the order inside a segment does not matter)
-  // (batches of 16 pairs per thread: the id loads of a batch are all in
-  // flight before its first atomic)
-  constexpr int B = 16;
-  // one batch covers every pair (P <= 16384): the ids and counts stay in
-  // registers for the scatter below, which then reads nothing back
-  const bool one = P <= 1024 * B;
-  int e1[B], k1[B];
-#pragma unroll
-  for (int b = 0; b < B; b++) e1[b] = -1, k1[b] = 0;
-  for (int r0 = tid; r0 < P; r0 += 1024 * B) {
-    int e[B];
-#pragma unroll
-    for (int b = 0; b < B; b++) {
-      const int r = r0 + 1024 * b;
-      e[b] = r < P ? ids[r] : -1;
-    }
-#pragma unroll
-    for (int b = 0; b < B; b++) {
-      const int r = r0 + 1024 * b;
-      if (e[b] >= 0 && e[b] < E) {
-        const int k = atomicAdd(&cnt[e[b]], 1);
-        if (one) {
-          e1[b] = e[b];
-          k1[b] = k;
-        } else if (rank) {
-          rank[r] = k;
-        }
-      }
-      if (amax && r < P) amax[r] = 0u;
-    }
-  }
-  __syncthreads();
-  // exclusive scans of the counts and of the "expert is active" flags
-  const int c = tid < E ? cnt[tid] : 0;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int f = c > 0 ? 1 : 0;
   const int nb = (c + kMoeBM - 1) / kMoeBM;
-  const int lane = tid & 63, wv = tid >> 6;
   int ic = c, iflag = f, ib = nb;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -395,71 +360,159 @@ __device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int 
     tot_b += wsum_b[i];
   }
   const int off_c = base_c + ic - c;
-  const int slot = base_f + iflag - f;
-  if (f) {
-    expert_list[slot] = tid;
-    seg_off[slot] = off_c;
-  }
-  if (blk_slot) {
-    const int off_b = base_b + ib - nb;
-    for (int i = 0; i < nb; i++) {
-      blk_slot[off_b + i] = slot;
-      blk_row0[off_b + i] = off_c + i * kMoeBM;
+  if (write) {
+    const int slot = base_f + iflag - f;
+    if (f) {
+      expert_list[slot] = tid;
+      seg_off[slot] = off_c;
     }
-    if (tid == 0) n_blocks[0] = tot_b;
+    if (blk_slot) {
+      const int off_b = base_b + ib - nb;
+      for (int i = 0; i < nb; i++) {
+        blk_slot[off_b + i] = slot;
+        blk_row0[off_b + i] = off_c + i * kMoeBM;
+      }
+      if (tid == 0) n_blocks[0] = tot_b;
+    }
+    if (tid == 0) {
+      n_active[0] = tot_f;
+      seg_off[tot_f] = tot_c;
+    }
   }
-  if (tid < E) cursor[tid] = off_c;
-  if (tid == 0) {
-    n_active[0] = tot_f;
-    seg_off[tot_f] = tot_c;
+  return off_c;
+}
+
+// Small batches: the whole sort in one 1024-thread workgroup, for at most
+// kMoeSortOneWg pairs (16 a thread, held in registers between the count and
+// the scatter).  Also clears the per-pair |act| maxima.
+constexpr int kMoeSortOneWg = 16 * 1024;
+__device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int P, int E,
+                                           int32_t* __restrict__ expert_list,
+                                           int32_t* __restrict__ seg_off,
+                                           int32_t* __restrict__ n_active,
+                                           int32_t* __restrict__ sorted_pairs,
+                                           uint32_t* __restrict__ amax) {
+  __shared__ int cnt[1024];
+  __shared__ int cursor[1024];
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  // counts; each pair keeps the count it saw (its place in its expert's
+  // segment); the id loads are all in flight before the first atomic
+  constexpr int B = kMoeSortOneWg / 1024;
+  int e1[B], k1[B];
+#pragma unroll
+  for (int b = 0; b < B; b++) {
+    const int r = tid + 1024 * b;
+    e1[b] = r < P ? ids[r] : -1;
+    k1[b] = 0;
+  }
+#pragma unroll
+  for (int b = 0; b < B; b++) {
+    const int r = tid + 1024 * b;
+    if (e1[b] >= 0 && e1[b] < E)
+      k1[b] = atomicAdd(&cnt[e1[b]], 1);
+    else
+      e1[b] = -1;
+    if (amax && r < P) amax[r] = 0u;
   }
   __syncthreads();
-  if (one) {
+  const int off_c = expert_scan(tid < E ? cnt[tid] : 0, true, expert_list, seg_off, n_active,
+                                nullptr, nullptr, nullptr);
+  if (tid < E) cursor[tid] = off_c;
+  __syncthreads();
 #pragma unroll
-    for (int b = 0; b < B; b++)
-      if (e1[b] >= 0) sorted_pairs[cursor[e1[b]] + k1[b]] = tid + 1024 * b;
-    return;
-  }
-  for (int r0 = tid; r0 < P; r0 += 1024 * B) {
-    int e[B], k[B];
-#pragma unroll
-    for (int b = 0; b < B; b++) {
-      const int r = r0 + 1024 * b;
-      e[b] = r < P ? ids[r] : -1;
-      k[b] = (rank && r < P) ? rank[r] : 0;
-    }
-#pragma unroll
-    for (int b = 0; b < B; b++) {
-      if (e[b] >= 0 && e[b] < E) {
-        const int pos = rank ? cursor[e[b]] + k[b] : atomicAdd(&cursor[e[b]], 1);
-        sorted_pairs[pos] = r0 + 1024 * b;
-      }
-    }
-  }
+  for (int b = 0; b < B; b++)
+    if (e1[b] >= 0) sorted_pairs[cursor[e1[b]] + k1[b]] = tid + 1024 * b;
 }
 
 __global__ __launch_bounds__(1024) void k_moe_sort(
     const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ expert_list,
     int32_t* __restrict__ seg_off, int32_t* __restrict__ n_active,
-    int32_t* __restrict__ sorted_pairs, uint32_t* __restrict__ amax,
-    int32_t* __restrict__ blk_slot, int32_t* __restrict__ blk_row0,
-    int32_t* __restrict__ n_blocks, int32_t* __restrict__ rank) {
-  sort_pairs(ids, P, E, expert_list, seg_off, n_active, sorted_pairs, amax, blk_slot, blk_row0,
-             n_blocks, rank);
+    int32_t* __restrict__ sorted_pairs, uint32_t* __restrict__ amax) {
+  sort_pairs(ids, P, E, expert_list, seg_off, n_active, sorted_pairs, amax);
 }
 
-// Routing and per-token quant, one wave per token (small batches with more
-// tokens than the single-workgroup prep has waves).
-__global__ __launch_bounds__(256) void k_moe_route_quant(
+// Large batches: the sort in two launches over chunks of pairs, one
+// workgroup per chunk (at most kMoeSortChunks chunks).
+// k_moe_sort_hist: the chunk's per-expert counts (LDS atomics); each pair
+// keeps the count it saw, its place among the chunk's pairs of its expert.
+__global__ __launch_bounds__(1024) void k_moe_sort_hist(const int32_t* __restrict__ ids, int P,
+                                                        int E, int chunk,
+                                                        int32_t* __restrict__ hist,
+                                                        int32_t* __restrict__ rank) {
+  __shared__ int cnt[1024];
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * chunk, p1 = min(P, p0 + chunk);
+  for (int p = p0 + tid; p < p1; p += 1024) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) rank[p] = atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid < E) hist[blockIdx.x * E + tid] = cnt[tid];
+}
+
+// k_moe_sort_scatter: every workgroup reads all nb chunk counts, forms the
+// segment offsets (workgroup 0 also writes the expert list and the m-block
+// table) and places its chunk's pairs: pair p of expert e goes to
+// seg_off(e) + (pairs of e in earlier chunks) + its place in its chunk.
+__global__ __launch_bounds__(1024) void k_moe_sort_scatter(
+    const int32_t* __restrict__ ids, int P, int E, int chunk, int nb,
+    const int32_t* __restrict__ hist, const int32_t* __restrict__ rank,
+    int32_t* __restrict__ expert_list, int32_t* __restrict__ seg_off,
+    int32_t* __restrict__ n_active, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ blk_slot, int32_t* __restrict__ blk_row0,
+    int32_t* __restrict__ n_blocks) {
+  __shared__ int cursor[1024];
+  const int tid = threadIdx.x;
+  const int p0 = blockIdx.x * chunk, p1 = min(P, p0 + chunk);
+  // the thread's first pair is read before the counts (independent loads)
+  const int pf = p0 + tid;
+  const int e_first = pf < p1 ? ids[pf] : -1;
+  const int r_first = pf < p1 ? rank[pf] : 0;
+  int c = 0, before = 0;
+  if (tid < E) {
+    for (int b0 = 0; b0 < nb; b0 += 16) {
+      int h[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) h[i] = b0 + i < nb ? hist[(b0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        if (b0 + i < (int)blockIdx.x) before += h[i];
+        c += h[i];
+      }
+    }
+  }
+  const int off_c = expert_scan(c, blockIdx.x == 0, expert_list, seg_off, n_active, blk_slot,
+                                blk_row0, n_blocks);
+  if (tid < E) cursor[tid] = off_c + before;
+  __syncthreads();
+  if (e_first >= 0 && e_first < E) sorted_pairs[cursor[e_first] + r_first] = pf;
+  for (int p = pf + 1024; p < p1; p += 1024) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) sorted_pairs[cursor[e] + rank[p]] = p;
+  }
+}
+
+// Routing and per-token quant for batches beyond the single-workgroup prep:
+// workgroup b takes tokens 4b..4b+3; waves 0-3 route them while waves 4-7
+// quantise them, so a token costs the longer of the two, not their sum.
+__global__ __launch_bounds__(512) void k_moe_route_quant(
     const uint16_t* __restrict__ x, const float* __restrict__ logits, int T, int H, int E, int k,
     int32_t* __restrict__ ids, float* __restrict__ w, int8_t* __restrict__ qx,
     float* __restrict__ sx) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + (wv & 3);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
-  if (logits)
-    route_token(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k, lane);
-  quant_row_wave(x + (int64_t)t * H, H, qx + (int64_t)t * H, sx + t, lane);
+  if (wv < 4) {
+    if (logits)
+      route_token(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k, lane);
+  } else {
+    quant_row_wave(x + (int64_t)t * H, H, qx + (int64_t)t * H, sx + t, lane);
+  }
 }
 
 // Small batches: routing, per-token quant of x and the sort in one
@@ -1266,12 +1319,11 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
                          a.E, a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx, ws.expert_list,
                          ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax);
     } else {
-      hipLaunchKernelGGL(k_moe_route_quant, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.x,
+      hipLaunchKernelGGL(k_moe_route_quant, dim3((a.T + 3) / 4), dim3(512), 0, stream, a.x,
                          a.logits, a.T, a.H, a.E, a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx);
       if ((err = hipGetLastError()) != hipSuccess) return err;
       hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
-                         ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax,
-                         nullptr, nullptr, nullptr, nullptr);
+                         ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // Workgroup shapes measured on MI355X at 256 experts, H=2048, I=512: up to
@@ -1303,23 +1355,37 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   } else {
-    // routing + per-token quant (one wave per token), then the sort by
-    // expert with the m-block table
-    hipLaunchKernelGGL(k_moe_route_quant, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.x,
+    // routing + per-token quant, then the sort by expert with the m-block
+    // table (per-chunk counts, then the scatter)
+    hipLaunchKernelGGL(k_moe_route_quant, dim3((a.T + 3) / 4), dim3(512), 0, stream, a.x,
                        a.logits, a.T, a.H, a.E, a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
-                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, nullptr,
-                       ws.blk_slot, ws.blk_row0, ws.n_blocks, ws.rank);
+    const int chunk = (int)std::max<int64_t>(1024, (P + kMoeSortChunks - 1) / kMoeSortChunks);
+    const int nchunks = (int)((P + chunk - 1) / chunk);
+    hipLaunchKernelGGL(k_moe_sort_hist, dim3(nchunks), dim3(1024), 0, stream, a.topk_ids,
+                       (int)P, a.E, chunk, ws.hist, ws.rank);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_moe_sort_scatter, dim3(nchunks), dim3(1024), 0, stream, a.topk_ids,
+                       (int)P, a.E, chunk, nchunks, ws.hist, ws.rank, ws.expert_list, ws.seg_off,
+                       ws.n_active, ws.sorted_pairs, ws.blk_slot, ws.blk_row0, ws.n_blocks);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // m-blocks: at most one partial block per expert that received pairs;
-    // the grid covers that bound rounded up to the 8 XCDs
+    // the grid covers that bound rounded up to the 8 XCDs.  Workgroups of 8
+    // waves (256 weight rows, the gathered activation rows shared by twice
+    // the weight rows of a 4-wave group) with a 2-step weight ring where the
+    // weight rows allow it (measured on MI355X at 2048 tokens, 256 experts,
+    // H=2048, I=512: gemm1 127-138 -> 113-121 us, gemm2 92-106 -> 82-90 us).
     const unsigned max_blocks = (unsigned)((P / kMoeBM + slots + 7) / 8 * 8);
-    hipLaunchKernelGGL((k_moe_tile<1, 4, 4, PACKED>), dim3(max_blocks * (I2 / 128)),
-                       dim3(256), 0, stream, ws.qx, ws.sx, a.k, a.w13, a.s13, I2, a.H, 1,
-                       ws.expert_list,
-                       ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks, ws.sorted_pairs,
-                       ws.act, a.I, a.dbg_acc1);
+    if (I2 % 256 == 0)
+      hipLaunchKernelGGL((k_moe_tile<1, 8, 2, PACKED>), dim3(max_blocks * (I2 / 256)),
+                         dim3(512), 0, stream, ws.qx, ws.sx, a.k, a.w13, a.s13, I2, a.H, 1,
+                         ws.expert_list, ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks,
+                         ws.sorted_pairs, ws.act, a.I, a.dbg_acc1);
+    else
+      hipLaunchKernelGGL((k_moe_tile<1, 4, 4, PACKED>), dim3(max_blocks * (I2 / 128)),
+                         dim3(256), 0, stream, ws.qx, ws.sx, a.k, a.w13, a.s13, I2, a.H, 1,
+                         ws.expert_list, ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks,
+                         ws.sorted_pairs, ws.act, a.I, a.dbg_acc1);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.I <= 1024)
       hipLaunchKernelGGL(k_moe_requant<16>, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, stream,
@@ -1328,17 +1394,24 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(k_moe_requant<64>, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, stream,
                          ws.act, (int)P, a.I, ws.qa, ws.sa2);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    const int npw2 = (a.H / 128) % 8 == 0 ? 8 : (a.H / 128) % 4 == 0 ? 4 : 1;
-    if (a.H % 128 == 0)
+    if (a.H % 256 == 0) {
+      const int npw2 = (a.H / 256) % 2 == 0 ? 2 : 1;
+      hipLaunchKernelGGL((k_moe_tile<2, 8, 2, PACKED>), dim3(max_blocks * (a.H / 256 / npw2)),
+                         dim3(512), 0, stream, ws.qa, ws.sa2, 1, a.w2, a.s2, a.H, a.I, npw2,
+                         ws.expert_list, ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks,
+                         ws.sorted_pairs, ws.y2, a.H, a.dbg_acc2);
+    } else if (a.H % 128 == 0) {
+      const int npw2 = (a.H / 128) % 8 == 0 ? 8 : (a.H / 128) % 4 == 0 ? 4 : 1;
       hipLaunchKernelGGL((k_moe_tile<2, 4, 4, PACKED>), dim3(max_blocks * (a.H / 128 / npw2)),
                          dim3(256), 0, stream, ws.qa, ws.sa2, 1, a.w2, a.s2, a.H, a.I, npw2,
                          ws.expert_list, ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks,
                          ws.sorted_pairs, ws.y2, a.H, a.dbg_acc2);
-    else
+    } else {
       hipLaunchKernelGGL((k_moe_tile<2, 2, 4, PACKED>), dim3(max_blocks * (a.H / 64)),
                          dim3(128), 0, stream, ws.qa, ws.sa2, 1, a.w2, a.s2, a.H, a.I, 1,
                          ws.expert_list, ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks,
                          ws.sorted_pairs, ws.y2, a.H, a.dbg_acc2);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)P * a.I,
                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)
