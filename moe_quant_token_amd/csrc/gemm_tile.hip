@@ -76,7 +76,11 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
   // a pipeline step covers KSUB 64-byte k chunks
   constexpr int CHUNK_BYTES = (NA + NB) * 1024;
   constexpr int STAGE_BYTES = KSUB * CHUNK_BYTES;
-  __shared__ __attribute__((aligned(1024))) int8_t smem[NSTAGE * STAGE_BYTES];
+  // g256: the tile's u8 group scales (K <= 16384: at most 64 groups a row)
+  // sit after the stages in the same LDS array (a second LDS array makes the
+  // compiler wait for every LDS DMA in flight before each fragment read)
+  constexpr int SU8_BYTES = MODE == kEpiG256 ? BN * 64 : 0;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[NSTAGE * STAGE_BYTES + SU8_BYTES];
 
   // ---- tile selection: XCD-contiguous ranges, then row groups
   const int nwg = tiles_m * tiles_n;
@@ -96,9 +100,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  // g256: the tile's u8 group scales (K <= 16384: at most 64 groups a row),
-  // read once into LDS so the main loop issues no other global loads
-  __shared__ uint8_t su8_lds[MODE == kEpiG256 ? BN * 64 : 1];
+  // g256: the group scales are read once into LDS, so the main loop issues
+  // no other global loads
+  uint8_t* su8_lds = reinterpret_cast<uint8_t*>(smem + NSTAGE * STAGE_BYTES);
   if (MODE == kEpiG256) {
     const int G = K >> 8;
     for (int i = threadIdx.x; i < BN * G; i += W * 64) {
