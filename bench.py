@@ -5,13 +5,17 @@ One step = the decode-shaped dense W8A8 workload: for every M in {1, 2, 4, 8}
 the gate_up (K=5120, N=17408) and down (K=8704, N=5120) linears, each as
 per-token int8 quant of the bf16 activations followed by the int8 GEMM with
 the fp32 epilogue to bf16 (quant_per_token_i8 + gemm_w8a8_packed, the two
-kernels linear_w8a8_packed runs; weights pre-packed at load).  Weights rotate over enough copies that every launch reads
-them from HBM, not from the 256 MB Infinity Cache.  `value` is the step's
-algorithmic bytes over its time (GB/s).
+kernels linear_w8a8_packed runs; weights pre-packed at load).  Weights
+rotate over enough copies that every launch reads them from HBM, not from the
+256 MB Infinity Cache.  `value` is the step's algorithmic bytes over its time
+(GB/s).
 
 Extra cases on the same JSON line (``cases``): prefill M=4096 TOPS, the
 routed MoE layer tokens/s at T in {1, 64, 2048}, and the Hadamard-domain
 linear at M in {1, 256}, each with its fraction of the relevant roofline.
+Prefill and Hadamard weights rotate over copies as above; the MoE cases
+rotate over seeded routing inputs, so consecutive calls read different
+experts' weights.
 
 Timing: the stream is first parked on a short spin kernel while the host
 enqueues the timed launches, so HIP events measure GPU time rather than
@@ -311,16 +315,29 @@ def prefill_cases(torch, np, mq, synth, dev, timer, bf16_dev):
         qw, sw = mq.quant_per_token_i8(W)
         del W
         qw = mq.pack_weights(qw)
+        # weight copies rotate so each launch reads its weights from HBM, not
+        # from the Infinity Cache
+        ncopy = max(2, math.ceil(2 * MALL_BYTES / (N * K)) + 1)
+        copies = [(qw, sw)] + [(qw.clone(), sw.clone()) for _ in range(ncopy - 1)]
         x = bf16_dev(synth.activations(cfg["xkey"], M, K, cfg["n_outliers"],
                                        cfg["outlier_scale"]))
         q, s = mq.quant_per_token_i8(x)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(mq.linear_w8a8_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
-        for _ in range(2):
-            mq.gemm_w8a8_packed(q, s, qw, sw, N, y=y)
+        for i in range(2):
+            mq.gemm_w8a8_packed(q, s, *copies[-1 - i], N, y=y)
         it = 10
-        t_g = timer.run(lambda i: mq.gemm_w8a8_packed(q, s, qw, sw, N, y=y), it) / it
-        t_l = timer.run(lambda i: mq.linear_w8a8_packed(x, qw, sw, N, y=y, ws=ws), it) / it
+
+        def gemm(i):
+            w, sc = copies[i % ncopy]
+            mq.gemm_w8a8_packed(q, s, w, sc, N, y=y)
+
+        def linear(i):
+            w, sc = copies[i % ncopy]
+            mq.linear_w8a8_packed(x, w, sc, N, y=y, ws=ws)
+
+        t_g = timer.run(gemm, it) / it
+        t_l = timer.run(linear, it) / it
         ops = 2.0 * M * N * K
         res[f"prefill_M{M}_K{K}_N{N}"] = {
             "gemm_us": round(t_g * 1e3, 2),
@@ -329,8 +346,9 @@ def prefill_cases(torch, np, mq, synth, dev, timer, bf16_dev):
             "linear_bf16_us": round(t_l * 1e3, 2),
             "linear_bf16_tops": round(ops / (t_l * 1e-3) / 1e12, 1),
             "linear_frac_mfma": round(ops / (t_l * 1e-3) / 1e12 / I8_PEAK_TOPS, 4),
+            "weight_copies": ncopy,
         }
-        del qw, sw, x, q, s, y, ws
+        del qw, sw, x, q, s, y, ws, copies
         torch.cuda.empty_cache()
     return res
 
@@ -349,33 +367,45 @@ def moe_cases(torch, np, mq, synth, dev, timer, bf16_dev):
         mq.quant_per_token_i8(b, q=w2[e], s=s2[e])
     w13, w2 = mq.pack_moe_weights(w13, w2)  # MFMA tile layout, untimed
     res = {}
-    for T in (1, 64, 2048):
+    # Routing inputs rotate over seeded sets so that consecutive calls route to
+    # different experts: a call reuses an expert's weights only after far more
+    # than the 256 MB Infinity Cache has streamed by (at T=1 a call touches
+    # 8 experts, 25 MB; the larger batches touch 700-800 MB per call).
+    for T, nsets, it in ((1, 64, 64), (64, 4, 20), (2048, 2, 10)):
         c = synth.moe(T)
-        x = bf16_dev(synth.activations(c["xkey"], T, H, 0, 1.0))
-        logits = torch.from_numpy(synth.router_logits(c["xkey"], T, E)).to(dev)
         ws = torch.empty(mq.moe_w8a8_workspace_bytes(T, H, E, I, k), dtype=torch.uint8,
                          device=dev)
-        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-        wt = torch.empty((T, k), dtype=torch.float32, device=dev)
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        fn = lambda i: mq.moe_w8a8_forward(x, logits, w13, s13, w2, s2, k, topk_ids=ids,
-                                           topk_w=wt, out=out, ws=ws, packed=True)
-        for _ in range(3):
-            fn(0)
-        it = 20 if T < 2048 else 10
+        sets = []
+        for r in range(nsets):
+            key = c["xkey"] if r == 0 else (*c["xkey"], r)
+            x = bf16_dev(synth.activations(key, T, H, 0, 1.0))
+            logits = torch.from_numpy(synth.router_logits(key, T, E)).to(dev)
+            ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+            wt = torch.empty((T, k), dtype=torch.float32, device=dev)
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            sets.append((x, logits, ids, wt, out))
+
+        def fn(i):
+            x, logits, ids, wt, out = sets[i % nsets]
+            mq.moe_w8a8_forward(x, logits, w13, s13, w2, s2, k, topk_ids=ids, topk_w=wt,
+                                out=out, ws=ws, packed=True)
+
+        for r in range(nsets):  # every set routed once (ids filled), untimed
+            fn(r)
         t = timer.run(fn, it) / it
-        touched = int(torch.unique(ids).numel())
+        touched = sum(int(torch.unique(st[2]).numel()) for st in sets) / nsets
         nbytes = touched * (2 * I * H + H * I + 4 * (2 * I + H)) + T * H * 2 + T * E * 4 + \
             T * H * 2
         ops = 2.0 * T * k * (2 * I * H + H * I)
         res[f"moe_T{T}"] = {
             "us": round(t * 1e3, 2),
             "tokens_per_s": round(T / (t * 1e-3), 1),
-            "experts_touched": touched,
-            "alg_bytes": nbytes,
+            "experts_touched": round(touched, 1),
+            "alg_bytes": int(nbytes),
             "gbs": round(nbytes / (t * 1e-3) / 1e9, 1),
             "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "tops": round(ops / (t * 1e-3) / 1e12, 2),
+            "routing_sets": nsets,
         }
     return res
 
