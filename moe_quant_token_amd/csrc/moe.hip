@@ -154,10 +154,14 @@ __device__ __forceinline__ void route_select_v(const float* __restrict__ lt, int
                                                int lane, int& sel_e, float& sel_w) {
   uint32_t kv[VPL];  // order-preserving keys of the lane's logits; 0 = none
   uint32_t kmax = 0;
+  // every load is issued before any is used (a load whose value is used
+  // inside its own bounds branch gets a wait of its own: VPL round trips)
+  float lv[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; i++) lv[i] = lt[min(lane + 64 * i, E - 1)];
 #pragma unroll
   for (int i = 0; i < VPL; i++) {
-    const int e = lane + 64 * i;
-    kv[i] = e < E ? float_key(lt[e]) : 0u;
+    kv[i] = lane + 64 * i < E ? float_key(lv[i]) : 0u;
     kmax = max(kmax, kv[i]);
   }
   const double mx = (double)key_float(wave_max_u32(kmax));  // the largest logit
@@ -204,10 +208,78 @@ __device__ __forceinline__ void route_select_v(const float* __restrict__ lt, int
   sel_w = (float)(myp / kept);
 }
 
+// Up to 256 experts: each lane first orders its four (logit, expert) pairs
+// (logit descending, expert ascending), so a round needs no scan of the
+// lane's entries: the wave maximum of the lanes' first keys, then among the
+// lanes holding it the lowest expert (a second maximum, of the inverted
+// index), and the winning lane drops its first entry.  Same selection and
+// weights as route_select_v.
+__device__ __forceinline__ void order_pair(uint32_t& ka, int& ea, uint32_t& kb, int& eb) {
+  const bool sw = kb > ka || (kb == ka && eb < ea);
+  const uint32_t k0 = sw ? kb : ka, k1 = sw ? ka : kb;
+  const int e0 = sw ? eb : ea, e1 = sw ? ea : eb;
+  ka = k0;
+  kb = k1;
+  ea = e0;
+  eb = e1;
+}
+__device__ __forceinline__ void route_select_sorted4(const float* __restrict__ lt, int E, int k,
+                                                     int lane, int& sel_e, float& sel_w) {
+  float lv[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) lv[i] = lt[min(lane + 64 * i, E - 1)];
+  uint32_t q[4];  // order-preserving keys; 0 = none
+  int ee[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    ee[i] = lane + 64 * i;
+    q[i] = ee[i] < E ? float_key(lv[i]) : 0u;
+  }
+  // a sorting network over the four pairs (the pairs are distinct)
+  order_pair(q[0], ee[0], q[1], ee[1]);
+  order_pair(q[2], ee[2], q[3], ee[3]);
+  order_pair(q[0], ee[0], q[2], ee[2]);
+  order_pair(q[1], ee[1], q[3], ee[3]);
+  order_pair(q[1], ee[1], q[2], ee[2]);
+  int my_e = 0;
+  float my_l = 0.0f;
+  double mx = 0.0;
+  for (int s = 0; s < k; s++) {
+    const uint32_t mh = wave_max_u32(q[0]);
+    const uint32_t ml = wave_max_u32(q[0] == mh ? 0xffffffffu - (uint32_t)ee[0] : 0u);
+    const int be = (int)(0xffffffffu - ml);
+    if (s == 0) mx = (double)key_float(mh);  // the largest logit
+    if ((be & 63) == lane) {
+      q[0] = q[1];
+      ee[0] = ee[1];
+      q[1] = q[2];
+      ee[1] = ee[2];
+      q[2] = q[3];
+      ee[2] = ee[3];
+      q[3] = 0u;
+      ee[3] = 0x7fffffff;
+    }
+    if (lane == s) {
+      my_e = be;
+      my_l = key_float(mh);
+    }
+  }
+  const double myp = exp((double)my_l - mx);
+  const uint64_t pb = (uint64_t)__double_as_longlong(myp);
+  double kept = 0.0;
+  for (int s = 0; s < k; s++) {
+    const uint32_t plo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, s);
+    const uint32_t phi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), s);
+    kept += __longlong_as_double((long long)(((uint64_t)phi << 32) | plo));
+  }
+  sel_e = my_e;
+  sel_w = (float)(myp / kept);
+}
+
 __device__ __forceinline__ void route_select(const float* __restrict__ lt, int E, int k,
                                              int lane, int& sel_e, float& sel_w) {
   if (E <= 256)
-    route_select_v<4>(lt, E, k, lane, sel_e, sel_w);
+    route_select_sorted4(lt, E, k, lane, sel_e, sel_w);
   else
     route_select_v<16>(lt, E, k, lane, sel_e, sel_w);
 }
