@@ -315,6 +315,120 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_g256_skinny(
   }
 }
 
+// The single-token Hadamard-domain linear in one launch (packed weights,
+// K <= kFusedG256MaxK): every workgroup rotates and quantises the token row
+// itself (a few hundred instructions a wave) while its weight loads are in
+// flight, then runs the g256 GEMM of k_gemm_g256_skinny on those codes.  The
+// rotation, the row maximum and the codes are those of k_fwht128_quant (same
+// butterfly, same quotient); workgroup 0 also stores the codes and the scale.
+// Lane layout of the rotation: wave w holds the 128-blocks 4w .. 4w+3, 16
+// lanes a block, 8 values a lane.  The row's loads are issued before the
+// weight loads: loads retire in order, so the rotation then waits for the row
+// only.
+constexpr int kFusedG256MaxK = 4096;
+__global__ __launch_bounds__(512) void k_linear_g256_one(
+    const uint16_t* __restrict__ x, int K, const int8_t* __restrict__ qw,
+    const uint8_t* __restrict__ su8, const uint16_t* __restrict__ s2,
+    uint16_t* __restrict__ y, int8_t* __restrict__ q, float* __restrict__ s) {
+  constexpr int WAVES = 8;
+  __shared__ long long red[WAVES][16];
+  __shared__ float part[WAVES];
+  __shared__ __attribute__((aligned(16))) int8_t q_lds[kFusedG256MaxK];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int64_t tile = blockIdx.x;
+  const int64_t n0 = tile * 16;
+  const int G = K >> 8;
+  const int nk = K >> 6;
+  const int nblk = K >> 7;
+
+  // the token row: this lane's 8 values of block 4w + lane/16
+  const int blk = wv * 4 + (lane >> 4);
+  const int l16 = lane & 15;
+  const bool xin = blk < nblk;
+  const v4u raw = xin ? *reinterpret_cast<const v4u*>(x + blk * 128 + l16 * 8)
+                      : v4u{0u, 0u, 0u, 0u};
+  // the tile's weights (wave w: groups w and w + 8, four 1 KiB steps each),
+  // their u8 group scales, and the row scale of the tile's channels
+  const int8_t* wp = qw + tile * nk * 1024 + lane * 16;
+  const uint8_t* sp = su8 + (n0 + j) * G;
+  v4i b[2][4];
+  int u8[2];
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const int gr = wv + h * WAVES;
+    const bool in = gr < G;
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+      b[h][u] = in ? *reinterpret_cast<const v4i*>(wp + (gr * 4 + u) * 1024)
+                   : v4i{0, 0, 0, 0};
+    u8[h] = in ? sp[gr] : 0;
+  }
+  const float s2f = wv == 0 ? bf16_bits_to_f32(s2[n0 + j]) : 0.0f;
+
+  // rotate, row maximum, codes into LDS
+  Block8 bv;
+  const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    bv.v[2 * i] = bf16_bits_to_f32(w4[i] & 0xffffu);
+    bv.v[2 * i + 1] = bf16_bits_to_f32(w4[i] >> 16);
+  }
+  fwht128_lanes(bv, l16);
+  float am = 0.0f;
+  if (xin) {
+#pragma unroll
+    for (int c = 0; c < 8; c++) am = fmaxf(am, fabsf(bv.v[c]));
+  }
+  am = wave_max(am);
+  if (lane == 0) part[wv] = am;
+  __syncthreads();
+  am = part[0];
+#pragma unroll
+  for (int w = 1; w < WAVES; w++) am = fmaxf(am, part[w]);
+  const float sc = am / 127.0f;
+  if (xin) {
+    int cd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (am != 0.0f) {
+#pragma unroll
+      for (int c = 0; c < 8; c++) cd[c] = quant_code(bv.v[c], sc);
+    }
+    const uint2 wd = make_uint2(pack4_i8(cd[0], cd[1], cd[2], cd[3]),
+                                pack4_i8(cd[4], cd[5], cd[6], cd[7]));
+    *reinterpret_cast<uint2*>(q_lds + blk * 128 + l16 * 8) = wd;
+    if (tile == 0) *reinterpret_cast<uint2*>(q + blk * 128 + l16 * 8) = wd;
+  }
+  const float sa = am != 0.0f ? sc : 0.0f;
+  if (tile == 0 && threadIdx.x == 0) s[0] = sa;
+  __syncthreads();
+
+  // g256 GEMM: row 0 of the A operand (lanes j == 0) holds the codes; the
+  // result's row 0 is element 0 of lanes 0..15
+  long long ts = 0;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const int gr = wv + h * WAVES;
+    if (gr >= G) break;
+    v4i acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const v4i a = j == 0 ? *reinterpret_cast<const v4i*>(q_lds + (gr * 4 + u) * 64 + g * 16)
+                           : v4i{0, 0, 0, 0};
+      acc = mfma_16x16x64_i8(a, b[h][u], acc);
+    }
+    ts += (long long)(acc[0] * u8[h]);
+  }
+  if (g == 0) red[wv][j] = ts;
+  __syncthreads();
+  if (wv == 0 && g == 0) {
+#pragma unroll
+    for (int w = 1; w < WAVES; w++) ts += red[w][j];
+    y[n0 + j] = g256_out(ts, sa, s2f);
+  }
+}
+
 hipError_t launch_gemm_g256_tile(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                                  const int8_t* qw, const uint8_t* su8, const uint16_t* s2,
                                  int64_t N, bool packed, bool apacked, uint16_t* y, int64_t ldy,
@@ -366,6 +480,11 @@ hipError_t launch_linear_g256(const uint16_t* x, int64_t M, int64_t K, int64_t l
                               int64_t N, uint16_t* y, int64_t ldy, int8_t* q, float* s,
                               hipStream_t stream) {
   hipError_t e;
+  if (M == 1 && K <= kFusedG256MaxK) {
+    hipLaunchKernelGGL(k_linear_g256_one, dim3((unsigned)(N / 16)), dim3(512), 0, stream, x,
+                       (int)K, qw_packed, su8, s2, y, q, s);
+    return hipGetLastError();
+  }
   if (M <= 16) {
     if ((e = launch_fwht128_quant(x, M, K, ldx, q, K, s, stream)) != hipSuccess) return e;
     return launch_gemm_g256(q, s, M, K, qw_packed, su8, s2, N, true, y, ldy, nullptr, stream);

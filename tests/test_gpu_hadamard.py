@@ -113,6 +113,25 @@ def test_linear_g256_full_size(orc, rotated_weights, M):
         assert not y[1].any()
 
 
+@pytest.mark.parametrize("K,N,zero", [(256, 16, False), (768, 48, False), (4096, 64, False),
+                                       (4096, 32, True), (4352, 32, False)])
+def test_linear_g256_single_token(orc, K, N, zero):
+    # one token: rotation, quant and GEMM in one launch up to K=4096, the
+    # two-launch path beyond; bit-exact either way, an all-zero row included
+    say(f"linear g256 single token K={K} N={N} zero={zero}")
+    W = synth.weights((54, K), N, K)
+    qw, su8, s2 = orc.weight_prep_g256(W)
+    x = synth.activations((55, K), 1, K, 4, 10.0, heavy_tail=True)
+    if zero:
+        x[:] = 0
+    qa, sa = orc.fwht128_quant(x)
+    y = mq.linear_w8a8_g256_packed(bf16_dev(x), mq.pack_weights(dev(qw)), dev(su8),
+                                   dev(s2.view(np.int16)).view(torch.bfloat16))
+    np.testing.assert_array_equal(bf16_host(y), orc.gemm_g256(qa, sa, qw, su8, s2))
+    if zero:
+        assert not bf16_host(y).any()
+
+
 def test_linear_g256_ragged_stride(orc):
     r = np.random.default_rng(9)
     M, K, N = 37, 768, 80
