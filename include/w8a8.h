@@ -105,8 +105,10 @@ int gemm_w8a8_i32acc(const int8_t *qa, int64_t M, int64_t K, int64_t lda, const 
 /* ------------------------------------------------------------------------ */
 /* The whole online W8A8 linear: bf16 x -> per-token int8 (as               */
 /* quant_per_token_i8) -> GEMM and epilogue (as gemm_w8a8) -> bf16 y.        */
-/* The codes and scales live in the workspace.  Same shape rules as          */
-/* gemm_w8a8; x 16-byte aligned with ldx a multiple of 16.                   */
+/* The codes and scales go to the workspace, except where the quantisation   */
+/* runs inside the GEMM launch (one or two tokens, packed weights, few       */
+/* output tiles a CU).  Same shape rules as gemm_w8a8; x 16-byte aligned     */
+/* with ldx a multiple of 16.                                                */
 /* ------------------------------------------------------------------------ */
 size_t linear_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int linear_w8a8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const int8_t *qw,

@@ -144,6 +144,11 @@ int linear_common(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const in
     e = launch_gemm_tile_apacked(q, s, M, K, qw, sw, N, y, ldy, st);
     return e == hipSuccess ? W8A8_OK : hip_fail(e);
   }
+  if (packed && linear_fused_fits(M, N, K)) {
+    // one or two tokens: the quantisation inside the GEMM launch
+    hipError_t e = launch_linear_skinny_fused(x, ldx, M, K, qw, sw, N, y, ldy, st);
+    return e == hipSuccess ? W8A8_OK : hip_fail(e);
+  }
   hipError_t e = launch_quant_rows(x, 0, M, K, ldx, q, K, s, st);
   if (e != hipSuccess) return hip_fail(e);
   return dispatch_gemm(q, s, M, K, K, qw, sw, N, ldw, packed, y, ldy, st);

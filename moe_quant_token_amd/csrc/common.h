@@ -33,6 +33,18 @@ __device__ __forceinline__ int quant_code(float x, float s) {
   return (int)r;
 }
 
+// Fast quotient for bf16 rows: with r = 1/s (IEEE), q0 = x*r,
+// e = fma(-q0, s, x) (exact), q = fma(e, r, q0).  For bf16 x with
+// |x| <= amax and s = amax/127 >= 2^-100, rint(q) equals rint of the IEEE
+// quotient x/s: checked exhaustively over every such (x, amax) pair.  fp32
+// rows, and rows with a smaller scale, use the IEEE division.
+__device__ __forceinline__ int quant_code_recip(float x, float s, float r) {
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, s, x);
+  const float q = __builtin_fmaf(e, r, q0);
+  return (int)fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f);
+}
+
 // Wave-wide maximum through DPP row shifts and row broadcasts (no LDS
 // traffic); every lane gets the result.  A lane whose DPP source lies outside
 // the row keeps its own value (bound_ctrl off, old = v), so any sign works.

@@ -102,6 +102,188 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyU = 8;
 
+// The decode linear for one or two tokens in one launch (packed weights): every
+// workgroup quantises the bf16 rows itself into LDS while its first weight
+// batch is in flight, then runs the k_gemm_skinny main loop with the codes
+// read from LDS.  The row loads are issued before the weight loads (loads
+// retire in order, so the quantisation waits for the rows only).  Codes and
+// scales are those of k_quant_rows (row maximum, amax / 127, the same
+// quotient).  Every workgroup repeats the quantisation, which pays only while
+// a CU holds few workgroups: the launcher takes this kernel for at most two
+// 16-channel tiles per CU (the down projection of the decode workload: one
+// token 14.1 -> 11.8 us, two 14.1 -> 13.4 us; with four workgroups a CU, as
+// for the gate_up projection, it is slower).
+template <int MMAX, int XH>
+__global__ __launch_bounds__(kSkinnyWaves * 64) void k_linear_skinny_fused(
+    const uint16_t* __restrict__ x, int64_t ldx, int M, int K, const int8_t* __restrict__ qw,
+    const float* __restrict__ sw, uint16_t* __restrict__ out, int64_t ldo) {
+  constexpr int WAVES = kSkinnyWaves, U = kSkinnyU, NT = WAVES * 64;
+  __shared__ v4i red[WAVES][64];
+  __shared__ float part[WAVES][MMAX];
+  extern __shared__ __attribute__((aligned(16))) int8_t q_lds[];  // M rows of K codes
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int64_t tile = blockIdx.x;
+  const int nchunk = K >> 6;
+  const int nc8 = K >> 3;  // 8-value chunks a row
+  const int tot = M * nc8;
+
+  // the rows: chunk c = tid + NT * i of the M x nc8 chunks
+  v4u xr[XH];
+#pragma unroll
+  for (int i = 0; i < XH; i++) {
+    const int c = tid + NT * i;
+    const int r = c / nc8, col = c - r * nc8;
+    xr[i] = c < tot ? *reinterpret_cast<const v4u*>(x + (int64_t)r * ldx + col * 8)
+                    : v4u{0u, 0u, 0u, 0u};
+  }
+  // the first weight batch
+  const int8_t* wp = qw + tile * nchunk * 1024 + lane * 16;
+  v4i b0[U];
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const int c = wv + u * WAVES;
+    b0[u] = c < nchunk ? *reinterpret_cast<const v4i*>(wp + (int64_t)c * 1024)
+                       : v4i{0, 0, 0, 0};
+  }
+  const int64_t n = tile * 16 + j;
+  const float swn = wv == 0 ? sw[n] : 0.0f;
+
+  // row maxima: per thread, per wave, then across the waves
+  float am[MMAX];
+#pragma unroll
+  for (int r = 0; r < MMAX; r++) am[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < XH; i++) {
+    const int r = (tid + NT * i) / nc8;
+    const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+    float m8 = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+      m8 = fmaxf(m8, fmaxf(fabsf(bf16_bits_to_f32(w4[t] & 0xffffu)),
+                           fabsf(bf16_bits_to_f32(w4[t] >> 16))));
+#pragma unroll
+    for (int rr = 0; rr < MMAX; rr++)
+      if (rr == r) am[rr] = fmaxf(am[rr], m8);
+  }
+#pragma unroll
+  for (int r = 0; r < MMAX; r++) {
+    const float v = wave_max(am[r]);
+    if (lane == 0) part[wv][r] = v;
+  }
+  __syncthreads();
+  float sc[MMAX], rc[MMAX];
+#pragma unroll
+  for (int r = 0; r < MMAX; r++) {
+    am[r] = part[0][r];
+#pragma unroll
+    for (int w = 1; w < WAVES; w++) am[r] = fmaxf(am[r], part[w][r]);
+    sc[r] = am[r] / 127.0f;
+    rc[r] = 1.0f / sc[r];
+  }
+  // codes into LDS, row r at r * K
+#pragma unroll
+  for (int i = 0; i < XH; i++) {
+    const int c = tid + NT * i;
+    if (c >= tot) break;
+    const int r = c / nc8, col = c - r * nc8;
+    float s_ = sc[0], r_ = rc[0], a_ = am[0];
+#pragma unroll
+    for (int rr = 1; rr < MMAX; rr++)
+      if (rr == r) {
+        s_ = sc[rr];
+        r_ = rc[rr];
+        a_ = am[rr];
+      }
+    const bool recip = s_ >= 0x1p-100f;
+    const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+    uint32_t pk[2] = {0u, 0u};
+    if (a_ != 0.0f) {
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        int cd[4];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          const float v0 = bf16_bits_to_f32(w4[2 * hh + t] & 0xffffu);
+          const float v1 = bf16_bits_to_f32(w4[2 * hh + t] >> 16);
+          cd[2 * t] = recip ? quant_code_recip(v0, s_, r_) : quant_code(v0, s_);
+          cd[2 * t + 1] = recip ? quant_code_recip(v1, s_, r_) : quant_code(v1, s_);
+        }
+        pk[hh] = pack4_i8(cd[0], cd[1], cd[2], cd[3]);
+      }
+    }
+    *reinterpret_cast<uint2*>(q_lds + r * K + col * 8) = make_uint2(pk[0], pk[1]);
+  }
+  __syncthreads();
+
+  // the k_gemm_skinny main loop, A from LDS
+  const bool a_ok = j < M;
+  const int8_t* ap = q_lds + (a_ok ? j : 0) * K + g * 16;
+  v4i acc = {0, 0, 0, 0};
+  for (int c0 = wv; c0 < nchunk; c0 += WAVES * U) {
+    v4i b[U], a[U];
+    const bool first = c0 == wv;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int c = c0 + u * WAVES;
+      const bool in = c < nchunk;
+      b[u] = first ? b0[u]
+                   : (in ? *reinterpret_cast<const v4i*>(wp + (int64_t)c * 1024)
+                         : v4i{0, 0, 0, 0});
+      a[u] = (in && a_ok) ? *reinterpret_cast<const v4i*>(ap + c * 64) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) acc = mfma_16x16x64_i8(a[u], b[u], acc);
+  }
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv != 0) return;
+#pragma unroll
+  for (int w = 1; w < WAVES; w++) acc += red[w][lane];
+  keep_live(swn);
+#pragma unroll
+  for (int v = 0; v < 4; v++) {
+    const int m = 4 * g + v;
+    if (m >= M) break;
+    float sv = 0.0f;
+#pragma unroll
+    for (int rr = 0; rr < MMAX; rr++)
+      if (rr == m) sv = am[rr] != 0.0f ? sc[rr] : 0.0f;
+    float r = (float)acc[v];
+    r = r * sv;
+    r = r * swn;
+    out[(int64_t)m * ldo + n] = (uint16_t)f32_to_bf16_bits(r);
+  }
+}
+
+bool linear_fused_fits(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= 2 && K <= 16384 && N / 16 <= 2 * (int64_t)device_cus();
+}
+
+hipError_t launch_linear_skinny_fused(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
+                                      const int8_t* qw_packed, const float* sw, int64_t N,
+                                      uint16_t* y, int64_t ldy, hipStream_t stream) {
+  // 16-byte row chunks held a thread: ceil(M * K / 8 / 512), at most 4 for
+  // one row and 8 for two.  Two rows hold 5 up to K = 10240 (110 VGPRs: two
+  // workgroups a CU); holding 8 takes 150 VGPRs and one workgroup a CU.
+  const size_t lds = (size_t)(M * K);
+  const int64_t need = (M * (K / 8) + kSkinnyWaves * 64 - 1) / (kSkinnyWaves * 64);
+  const dim3 grid((unsigned)(N / 16)), block(kSkinnyWaves * 64);
+  if (M == 1)
+    hipLaunchKernelGGL((k_linear_skinny_fused<1, 4>), grid, block, lds, stream, x, ldx, (int)M,
+                       (int)K, qw_packed, sw, y, ldy);
+  else if (need <= 5)
+    hipLaunchKernelGGL((k_linear_skinny_fused<2, 5>), grid, block, lds, stream, x, ldx, (int)M,
+                       (int)K, qw_packed, sw, y, ldy);
+  else
+    hipLaunchKernelGGL((k_linear_skinny_fused<2, 8>), grid, block, lds, stream, x, ldx, (int)M,
+                       (int)K, qw_packed, sw, y, ldy);
+  return hipGetLastError();
+}
+
 template <bool PACKED, bool STORE_I32>
 static hipError_t launch_skinny_impl(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                                      int64_t lda, const int8_t* qw, const float* sw, int64_t N,

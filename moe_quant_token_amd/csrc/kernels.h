@@ -30,6 +30,12 @@ hipError_t launch_gemm_skinny(const int8_t* qa, const float* sa, int64_t M, int6
 hipError_t launch_gemm_skinny_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
                                   const int8_t* qw, int64_t N, int64_t ldw, bool packed,
                                   int32_t* acc, int64_t ldacc, hipStream_t stream);
+// The whole linear (bf16 rows -> codes -> GEMM -> bf16) in one launch, for
+// the shapes linear_fused_fits accepts (one or two rows, packed weights).
+bool linear_fused_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear_skinny_fused(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
+                                      const int8_t* qw_packed, const float* sw, int64_t N,
+                                      uint16_t* y, int64_t ldy, hipStream_t stream);
 
 hipError_t launch_gemm_tile(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                             int64_t lda, const int8_t* qw, const float* sw, int64_t N,

@@ -46,18 +46,6 @@ struct Chunk16<float> {
   }
 };
 
-// Fast quotient for bf16 rows: with r = 1/s (IEEE), q0 = x*r,
-// e = fma(-q0, s, x) (exact), q = fma(e, r, q0).  For bf16 x with
-// |x| <= amax and s = amax/127 >= 2^-100, rint(q) equals rint of the IEEE
-// quotient x/s: checked exhaustively over every such (x, amax) pair.  fp32
-// rows, and rows with a smaller scale, use the IEEE division.
-__device__ __forceinline__ int quant_code_recip(float x, float s, float r) {
-  const float q0 = x * r;
-  const float e = __builtin_fmaf(-q0, s, x);
-  const float q = __builtin_fmaf(e, r, q0);
-  return (int)fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f);
-}
-
 // PACKED_OUT: write the codes in the 16-row x 64-byte MFMA tile layout of
 // pack.hip (row m, bytes 16c..16c+15 of k chunk kc go to tile m/16, block kc,
 // slot (m % 16) + 16 * (c % 4)) instead of row-major; ldq is then unused.

@@ -172,6 +172,29 @@ def test_linear_decode_zero_row_and_stride(orc, packed):
     assert not got[2].any()
 
 
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("K,N", [(64, 16), (16384, 32), (640, 8192), (640, 8208)])
+def test_linear_one_or_two_tokens(orc, M, K, N):
+    # one or two tokens with packed weights: the quantisation runs inside the
+    # GEMM launch while the output has at most two 16-channel tiles per CU
+    # (N = 8192 on 256 CUs), the two-launch path beyond (N = 8208); strided
+    # rows, and an all-zero second token
+    say(f"linear one/two tokens M={M} K={K} N={N}")
+    x, W = _inputs((11, M, K), (11, N, K), M, K, N, 2, 20.0)
+    if M == 2:
+        x[1] = 0
+    qw, sw = orc.quant_rows(W)
+    y_ref = orc.linear_w8a8(x, qw, sw)
+    big = np.zeros((M, K + 32), np.uint16)
+    big[:, :K] = x
+    y = mq.linear_w8a8_packed(bf16_dev(big)[:, :K], mq.pack_weights(dev(qw)), dev(sw), N)
+    torch.cuda.synchronize()
+    got = bf16_host(y)
+    np.testing.assert_array_equal(got, y_ref)
+    if M == 2:
+        assert not got[1].any()
+
+
 def test_gemm_extreme_codes_no_overflow():
     # every code +-127 at the largest decode K: |acc| = 127*127*8704
     K, N = 8704, 32
