@@ -348,13 +348,15 @@ def prefill_cases(torch, np, mq, synth, dev, timer, bf16_dev):
         q, s = mq.quant_per_token_i8(x)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(mq.linear_w8a8_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+        ws_g = torch.empty(max(1, mq.gemm_w8a8_workspace_bytes(M, N, K)), dtype=torch.uint8,
+                           device=dev)
         for i in range(2):
-            mq.gemm_w8a8_packed(q, s, *copies[-1 - i], N, y=y)
+            mq.gemm_w8a8_packed(q, s, *copies[-1 - i], N, y=y, ws=ws_g)
         it = 10
 
         def gemm(i):
             w, sc = copies[i % ncopy]
-            mq.gemm_w8a8_packed(q, s, w, sc, N, y=y)
+            mq.gemm_w8a8_packed(q, s, w, sc, N, y=y, ws=ws_g)
 
         def linear(i):
             w, sc = copies[i % ncopy]
@@ -372,7 +374,7 @@ def prefill_cases(torch, np, mq, synth, dev, timer, bf16_dev):
             "linear_frac_mfma": round(ops / (t_l * 1e-3) / 1e12 / I8_PEAK_TOPS, 4),
             "weight_copies": ncopy,
         }
-        del qw, sw, x, q, s, y, ws, copies
+        del qw, sw, x, q, s, y, ws, ws_g, copies
         torch.cuda.empty_cache()
     return res
 

@@ -181,6 +181,10 @@ def gemm_w8a8_i32acc(qa, qw, acc: torch.Tensor | None = None, ws: torch.Tensor |
     return acc
 
 
+def gemm_w8a8_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().gemm_w8a8_workspace_bytes(M, N, K))
+
+
 def linear_w8a8_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib().linear_w8a8_workspace_bytes(M, N, K))
 

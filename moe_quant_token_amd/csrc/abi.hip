@@ -96,7 +96,7 @@ int dispatch_gemm_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda, const
 
 int gemm_common(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t lda,
                 const int8_t* qw, const float* sw, int64_t N, int64_t ldw, bool packed,
-                uint16_t* y, int64_t ldy, size_t ws_bytes, void* stream) {
+                uint16_t* y, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   int r = check_gemm_shape(M, K, lda, N, ldw, ldy);
   if (r != W8A8_OK) return r;
   if (M == 0) return W8A8_OK;
@@ -105,12 +105,24 @@ int gemm_common(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t
     return W8A8_MISALIGNED;
   if (ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
   if ((r = check_device()) != W8A8_OK) return r;
-  return dispatch_gemm(qa, sa, M, K, lda, qw, sw, N, ldw, packed, y, ldy, as_stream(stream));
+  hipStream_t st = as_stream(stream);
+  if (packed && M > 16) {
+    // the tiled GEMM reads its activation operand as contiguous 1 KiB tiles:
+    // the row-major codes are repacked into the workspace first (row-major
+    // operand loads fetch 16 half-line pieces per 1 KiB)
+    if (!ws || !al16(ws)) return ws ? W8A8_MISALIGNED : W8A8_INVALID_ARG;
+    int8_t* qp = static_cast<int8_t*>(ws);
+    hipError_t e = launch_pack_rows(qa, M, K, lda, qp, st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_gemm_tile_apacked(qp, sa, M, K, qw, sw, N, y, ldy, st);
+    return e == hipSuccess ? W8A8_OK : hip_fail(e);
+  }
+  return dispatch_gemm(qa, sa, M, K, lda, qw, sw, N, ldw, packed, y, ldy, st);
 }
 
 int gemm_i32_common(const int8_t* qa, int64_t M, int64_t K, int64_t lda, const int8_t* qw,
                     int64_t N, int64_t ldw, bool packed, int32_t* acc, int64_t ldacc,
-                    size_t ws_bytes, void* stream) {
+                    void* ws, size_t ws_bytes, void* stream) {
   int r = check_gemm_shape(M, K, lda, N, ldw, ldacc);
   if (r != W8A8_OK) return r;
   if (M == 0) return W8A8_OK;
@@ -118,7 +130,17 @@ int gemm_i32_common(const int8_t* qa, int64_t M, int64_t K, int64_t lda, const i
   if (!al16(qa) || !al16(qw) || !al4(acc)) return W8A8_MISALIGNED;
   if (ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
   if ((r = check_device()) != W8A8_OK) return r;
-  return dispatch_gemm_i32(qa, M, K, lda, qw, N, ldw, packed, acc, ldacc, as_stream(stream));
+  hipStream_t st = as_stream(stream);
+  if (packed && M > 16) {
+    // as gemm_common: repacked activation codes, the same tiled kernel
+    if (!ws || !al16(ws)) return ws ? W8A8_MISALIGNED : W8A8_INVALID_ARG;
+    int8_t* qp = static_cast<int8_t*>(ws);
+    hipError_t e = launch_pack_rows(qa, M, K, lda, qp, st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_gemm_tile_apacked_i32(qp, M, K, qw, N, acc, ldacc, st);
+    return e == hipSuccess ? W8A8_OK : hip_fail(e);
+  }
+  return dispatch_gemm_i32(qa, M, K, lda, qw, N, ldw, packed, acc, ldacc, st);
 }
 
 int linear_common(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* qw,
@@ -189,25 +211,28 @@ int quant_per_token_i8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t
   return e == hipSuccess ? W8A8_OK : hip_fail(e);
 }
 
-size_t gemm_w8a8_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+size_t gemm_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  // the tile-layout copy of the activation codes for the tiled GEMM
+  if (M <= 16 || N <= 0 || K <= 0) return 0;
+  return act_codes_bytes(M, K);
+}
 
 int gemm_w8a8(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t lda,
               const int8_t* qw, const float* sw, int64_t N, int64_t ldw, uint16_t* y,
               int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  return gemm_common(qa, sa, M, K, lda, qw, sw, N, ldw, false, y, ldy, ws_bytes, stream);
+  return gemm_common(qa, sa, M, K, lda, qw, sw, N, ldw, false, y, ldy, ws, ws_bytes, stream);
 }
 
 int gemm_w8a8_i32acc(const int8_t* qa, int64_t M, int64_t K, int64_t lda, const int8_t* qw,
                      int64_t N, int64_t ldw, int32_t* acc, int64_t ldacc, void* ws,
                      size_t ws_bytes, void* stream) {
-  (void)ws;
-  return gemm_i32_common(qa, M, K, lda, qw, N, ldw, false, acc, ldacc, ws_bytes, stream);
+  return gemm_i32_common(qa, M, K, lda, qw, N, ldw, false, acc, ldacc, ws, ws_bytes, stream);
 }
 
 size_t linear_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || K <= 0) return 0;
-  return act_codes_bytes(M, K) + align_up((size_t)M * 4) + gemm_w8a8_workspace_bytes(M, N, K);
+  (void)N;
+  return act_codes_bytes(M, K) + align_up((size_t)M * 4);
 }
 
 int linear_w8a8(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* qw,
@@ -233,15 +258,15 @@ int w8a8_pack_weights(const int8_t* qw, int64_t N, int64_t K, int64_t ldw, int8_
 int gemm_w8a8_packed(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t lda,
                      const int8_t* qw_packed, const float* sw, int64_t N, uint16_t* y,
                      int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  return gemm_common(qa, sa, M, K, lda, qw_packed, sw, N, K, true, y, ldy, ws_bytes, stream);
+  return gemm_common(qa, sa, M, K, lda, qw_packed, sw, N, K, true, y, ldy, ws, ws_bytes,
+                     stream);
 }
 
 int gemm_w8a8_packed_i32acc(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
                             const int8_t* qw_packed, int64_t N, int32_t* acc, int64_t ldacc,
                             void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  return gemm_i32_common(qa, M, K, lda, qw_packed, N, K, true, acc, ldacc, ws_bytes, stream);
+  return gemm_i32_common(qa, M, K, lda, qw_packed, N, K, true, acc, ldacc, ws, ws_bytes,
+                         stream);
 }
 
 int linear_w8a8_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,

@@ -472,6 +472,13 @@ hipError_t launch_gemm_tile_apacked(const int8_t* qa_packed, const float* sa, in
                                                 ldy, stream);
 }
 
+hipError_t launch_gemm_tile_apacked_i32(const int8_t* qa_packed, int64_t M, int64_t K,
+                                        const int8_t* qw_packed, int64_t N, int32_t* acc,
+                                        int64_t ldacc, hipStream_t stream) {
+  return launch_tile_impl<kEpiI32, true, true>(qa_packed, nullptr, M, K, K, qw_packed, nullptr, N,
+                                               K, acc, ldacc, stream);
+}
+
 hipError_t launch_gemm_tile(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                             int64_t lda, const int8_t* qw, const float* sw, int64_t N,
                             int64_t ldw, bool packed, uint16_t* y, int64_t ldy,

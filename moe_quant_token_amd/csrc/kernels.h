@@ -22,6 +22,10 @@ hipError_t launch_quant_rows_packed(const uint16_t* x, int64_t M, int64_t K, int
 // `packed`: weights in the MFMA tile layout of pack.hip instead of row-major.
 hipError_t launch_pack_weights(const int8_t* qw, int64_t N, int64_t K, int64_t ldw,
                                int8_t* out, hipStream_t stream);
+// Activation codes [M, K] (row stride ld) into the same tile layout, rows past
+// M in the last tile as zeros; out holds ceil(M / 16) * 16 * K bytes.
+hipError_t launch_pack_rows(const int8_t* q, int64_t M, int64_t K, int64_t ld, int8_t* out,
+                            hipStream_t stream);
 
 hipError_t launch_gemm_skinny(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                               int64_t lda, const int8_t* qw, const float* sw, int64_t N,
@@ -48,6 +52,9 @@ hipError_t launch_gemm_tile_i32(const int8_t* qa, int64_t M, int64_t K, int64_t 
 hipError_t launch_gemm_tile_apacked(const int8_t* qa_packed, const float* sa, int64_t M,
                                     int64_t K, const int8_t* qw_packed, const float* sw,
                                     int64_t N, uint16_t* y, int64_t ldy, hipStream_t stream);
+hipError_t launch_gemm_tile_apacked_i32(const int8_t* qa_packed, int64_t M, int64_t K,
+                                        const int8_t* qw_packed, int64_t N, int32_t* acc,
+                                        int64_t ldacc, hipStream_t stream);
 
 // Routed MoE.  Workspace layout is owned by moe.hip.
 struct MoeArgs {

@@ -41,7 +41,15 @@ def test_sweep_dense_linear(orc):
         qw, sw = orc.quant_rows(synth.weights((61, i), N, K))
         y_ref = orc.linear_w8a8(x, qw, sw)
         if packed:
-            y = mq.linear_w8a8_packed(bf16_dev(x), mq.pack_weights(dev(qw)), dev(sw), N)
+            qp = mq.pack_weights(dev(qw))
+            y = mq.linear_w8a8_packed(bf16_dev(x), qp, dev(sw), N)
+            # the GEMM alone on codes with a row stride past K
+            qa, sa = orc.quant_rows(x)
+            wide = torch.zeros((M, K + 48), dtype=torch.int8, device="cuda")
+            wide[:, :K] = dev(qa)
+            y_g = mq.gemm_w8a8_packed(wide[:, :K], dev(sa), qp, dev(sw), N)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(bf16_host(y_g), y_ref, err_msg=f"case {i} gemm")
         else:
             y = mq.linear_w8a8(bf16_dev(x), dev(qw), dev(sw))
         torch.cuda.synchronize()
