@@ -68,6 +68,12 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 
+// Weight bytes are read once per call: a non-temporal load keeps them from
+// displacing what is read again soon (activations, the MoE intermediates).
+__device__ __forceinline__ v4i ld_stream(const int8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
+
 __device__ __forceinline__ v4i mfma_16x16x64_i8(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_g256_skinny(
 #pragma unroll
       for (int u = 0; u < 4; u++) {
         const int c = gr * 4 + u;
-        b[h][u] = in ? *reinterpret_cast<const v4i*>(wp + c * wstep) : v4i{0, 0, 0, 0};
+        b[h][u] = in ? ld_stream(wp + c * wstep) : v4i{0, 0, 0, 0};
         a[h][u] = (in && a_ok) ? *reinterpret_cast<const v4i*>(ap + (int64_t)c * 64)
                                : v4i{0, 0, 0, 0};
       }
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(512) void k_linear_g256_one(
     const bool in = gr < G;
 #pragma unroll
     for (int u = 0; u < 4; u++)
-      b[h][u] = in ? *reinterpret_cast<const v4i*>(wp + (gr * 4 + u) * 1024)
+      b[h][u] = in ? ld_stream(wp + (gr * 4 + u) * 1024)
                    : v4i{0, 0, 0, 0};
     u8[h] = in ? sp[gr] : 0;
   }

@@ -672,7 +672,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_moe_skinny(
       const int c = c0 + u * WAVES;
 #pragma unroll
       for (int t = 0; t < NT; t++)
-        b[u][t] = c < nk ? *reinterpret_cast<const v4i*>(wbase + t * tstep + c * wstep)
+        b[u][t] = c < nk ? ld_stream(wbase + t * tstep + c * wstep)
                          : v4i{0, 0, 0, 0};
     }
   };
@@ -879,7 +879,7 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm1(
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int c = c0 + u * WAVES;
-      b[u] = c < nk ? *reinterpret_cast<const v4i*>(wbase + c * wstep) : v4i{0, 0, 0, 0};
+      b[u] = c < nk ? ld_stream(wbase + c * wstep) : v4i{0, 0, 0, 0};
     }
   };
   v4i bq[U];
@@ -1040,7 +1040,7 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm2(
 #pragma unroll
       for (int u = 0; u < U; u++) {
         const int c = c0 + u;
-        b[u] = c < nk ? *reinterpret_cast<const v4i*>(wbase + c * wstep) : v4i{0, 0, 0, 0};
+        b[u] = c < nk ? ld_stream(wbase + c * wstep) : v4i{0, 0, 0, 0};
       }
 #pragma unroll
       for (int u = 0; u < U; u++) {
@@ -1151,8 +1151,8 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_moe_tile(
     const int sc = sg < send ? sg : 0;
     const int nb = sc / nsteps, kt = sc - nb * nsteps;
     const int8_t* q = bsrc + nb * bblock + (int64_t)(kt < nk ? kt : 0) * BSTEP;
-    b[0] = *reinterpret_cast<const v4i*>(q);
-    b[1] = *reinterpret_cast<const v4i*>(q + BHALF);
+    b[0] = ld_stream(q);
+    b[1] = ld_stream(q + BHALF);
   };
 
   // the block's pair ids and activation scales, and the weight rows' scales,
