@@ -98,8 +98,10 @@ GEMM_SHAPES = [
     (1, 64, 16),        # smallest legal shape
     (3, 640, 48),
     (17, 512, 64),      # first M served by the tiled kernel
-    (300, 640, 272),    # several 64x64 tiles with ragged M
-    (64, 1024, 1024),
+    (300, 640, 272),    # ragged M; packed: 128x64 tiles, two chunks a step
+    (64, 1024, 1024),   # packed: 64x64 tiles, two chunks a step
+    (160, 4096, 272),   # packed: 128x128 tiles, ragged M and last column tile
+    (40, 576, 96),      # K % 128 != 0: 64x64 tiles, one chunk a step
     (2048, 512, 2048),  # 256x256 tiles
     (2100, 256, 2064),  # 256x256 tiles, ragged M and N
     (4096, 64, 4352),   # 256x256 tiles over whole rounds, remaining columns 128x64
