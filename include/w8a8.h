@@ -87,9 +87,11 @@ int quant_per_token_i8(const void *x, int x_dtype, int64_t M, int64_t K, int64_t
 /*   y[m,n]   = bf16_rne( (float(acc[m,n]) * sa[m]) * sw[n] )  (fp32)        */
 /* qa: int8 [M, K] (lda), sa: fp32 [M]; qw: int8 [N, K] (ldw), sw: fp32 [N]; */
 /* y: bf16 [M, N] (ldy).  M <= 16 runs the weight-streaming decode kernel,   */
-/* larger M the LDS-tiled MFMA kernel.  Workspace: none for M <= 16, else    */
-/* ceil(M/16)*16*K bytes; the packed-weight variants repack the activation   */
-/* codes there into the tile layout described at w8a8_pack_weights.        */
+/* larger M the LDS-tiled MFMA kernel.  gemm_w8a8 and gemm_w8a8_i32acc use  */
+/* no workspace (ws may be NULL).  The packed-weight variants below need     */
+/* gemm_w8a8_workspace_bytes(M, N, K): none for M <= 16, else                */
+/* ceil(M/16)*16*K bytes, where they repack the activation codes into the    */
+/* tile layout described at w8a8_pack_weights.                               */
 /* Requires K % 64 == 0, K <= 131072, N % 16 == 0; qa, qw 16-byte aligned;   */
 /* lda, ldw multiples of 16; y 4-byte aligned and ldy even.                  */
 /* ------------------------------------------------------------------------ */

@@ -159,7 +159,7 @@ def gemm_w8a8(qa, sa, qw, sw, y: torch.Tensor | None = None, ws: torch.Tensor | 
     M, K = qa.shape
     N = qw.shape[0]
     y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device) if y is None else y
-    ws, wsb = _workspace(lib().gemm_w8a8_workspace_bytes(M, N, K), qa.device, ws)
+    ws, wsb = _workspace(0, qa.device, ws)  # row-major weights: no workspace
     _check("gemm_w8a8",
            lib().gemm_w8a8(_ptr(qa), _ptr(sa), M, K, qa.stride(0), _ptr(qw), _ptr(sw), N,
                            qw.stride(0), _ptr(y), y.stride(0), _ptr(ws), wsb,
@@ -174,7 +174,7 @@ def gemm_w8a8_i32acc(qa, qw, acc: torch.Tensor | None = None, ws: torch.Tensor |
     M, K = qa.shape
     N = qw.shape[0]
     acc = torch.empty((M, N), dtype=torch.int32, device=qa.device) if acc is None else acc
-    ws, wsb = _workspace(lib().gemm_w8a8_workspace_bytes(M, N, K), qa.device, ws)
+    ws, wsb = _workspace(0, qa.device, ws)  # row-major weights: no workspace
     _check("gemm_w8a8_i32acc",
            lib().gemm_w8a8_i32acc(_ptr(qa), M, K, qa.stride(0), _ptr(qw), N, qw.stride(0),
                                   _ptr(acc), acc.stride(0), _ptr(ws), wsb, _stream(qa.device)))

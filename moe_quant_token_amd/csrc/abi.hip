@@ -103,14 +103,15 @@ int gemm_common(const int8_t* qa, const float* sa, int64_t M, int64_t K, int64_t
   if (!qa || !sa || !qw || !sw || !y) return W8A8_INVALID_ARG;
   if (!al16(qa) || !al16(qw) || !al4(sa) || !al4(sw) || !al4(y) || ldy % 2 != 0)
     return W8A8_MISALIGNED;
-  if (ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  // only the packed-weight path uses the workspace
+  if (packed && ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  if (packed && M > 16 && (!ws || !al16(ws))) return ws ? W8A8_MISALIGNED : W8A8_INVALID_ARG;
   if ((r = check_device()) != W8A8_OK) return r;
   hipStream_t st = as_stream(stream);
   if (packed && M > 16) {
     // the tiled GEMM reads its activation operand as contiguous 1 KiB tiles:
     // the row-major codes are repacked into the workspace first (row-major
     // operand loads fetch 16 half-line pieces per 1 KiB)
-    if (!ws || !al16(ws)) return ws ? W8A8_MISALIGNED : W8A8_INVALID_ARG;
     int8_t* qp = static_cast<int8_t*>(ws);
     hipError_t e = launch_pack_rows(qa, M, K, lda, qp, st);
     if (e != hipSuccess) return hip_fail(e);
@@ -128,12 +129,12 @@ int gemm_i32_common(const int8_t* qa, int64_t M, int64_t K, int64_t lda, const i
   if (M == 0) return W8A8_OK;
   if (!qa || !qw || !acc) return W8A8_INVALID_ARG;
   if (!al16(qa) || !al16(qw) || !al4(acc)) return W8A8_MISALIGNED;
-  if (ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  if (packed && ws_bytes < gemm_w8a8_workspace_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
+  if (packed && M > 16 && (!ws || !al16(ws))) return ws ? W8A8_MISALIGNED : W8A8_INVALID_ARG;
   if ((r = check_device()) != W8A8_OK) return r;
   hipStream_t st = as_stream(stream);
   if (packed && M > 16) {
     // as gemm_common: repacked activation codes, the same tiled kernel
-    if (!ws || !al16(ws)) return ws ? W8A8_MISALIGNED : W8A8_INVALID_ARG;
     int8_t* qp = static_cast<int8_t*>(ws);
     hipError_t e = launch_pack_rows(qa, M, K, lda, qp, st);
     if (e != hipSuccess) return hip_fail(e);
@@ -212,7 +213,8 @@ int quant_per_token_i8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t
 }
 
 size_t gemm_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  // the tile-layout copy of the activation codes for the tiled GEMM
+  // the tile-layout copy of the activation codes for the tiled GEMM (packed
+  // weights; the row-major-weight calls use none)
   if (M <= 16 || N <= 0 || K <= 0) return 0;
   return act_codes_bytes(M, K);
 }

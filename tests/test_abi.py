@@ -58,6 +58,18 @@ def test_gemm_validation(L):
     g = L.gemm_w8a8_i32acc
     assert g(A, 4, 96, 96, A, 64, 96, A, 64, None, 0, None) == SHAPE
     assert g(A, 4, 128, 128, None, 64, 128, A, 64, None, 0, None) == INVALID
+    # packed weights, more than 16 rows: the activation codes are repacked
+    # into a caller workspace of ceil(M/16)*16*K bytes
+    assert L.gemm_w8a8_workspace_bytes(16, 64, 128) == 0
+    need = L.gemm_w8a8_workspace_bytes(20, 64, 128)
+    assert need >= 32 * 128
+    p = L.gemm_w8a8_packed
+    assert p(A, A, 20, 128, 128, A, A, 64, A, 64, A, need - 1, None) == WS_SMALL
+    assert p(A, A, 20, 128, 128, A, A, 64, A, 64, None, need, None) == INVALID
+    assert p(A, A, 20, 128, 128, A, A, 64, A, 64, A + 8, need, None) == MISALIGNED
+    q = L.gemm_w8a8_packed_i32acc
+    assert q(A, 20, 128, 128, A, 64, A, 64, A, need - 1, None) == WS_SMALL
+    assert q(A, 20, 128, 128, A, 64, A, 64, None, need, None) == INVALID
 
 
 def test_linear_validation(L):
