@@ -461,25 +461,34 @@ static hipError_t launch_tile_impl(const int8_t* qa, const float* sa, int64_t M,
     return launch_256<MODE, BPACKED, APACKED>(qa, sa, M, K, lda, qw, sw, ldw, out, ldo, 0, N,
                                               stream);
   }
-  if (BPACKED && APACKED && M < 1024) {
-    // mid-size problems, both operands in the tile layout (measured on
-    // MI355X with the weights coming from HBM; the first figure is the
-    // 64 x 64 one-chunk tiling below):
-    //  - M >= 128 and K >= 4096: 128 x 128 tiles (512x5120x5120 33.1 -> 28.0
-    //    us, 128x5120x17408 40.0 -> 29.6 us);
-    //  - M >= 128, shorter K: 128 x 64 tiles of 8 waves, two chunks a step
-    //    (256x2048x8192 11.6 -> 10.6 us);
-    //  - fewer rows: 64 x 64 tiles, two chunks a step, two workgroups a CU
-    //    (64x8704x5120 31.8 -> 22.7 us, 32x5120x17408 27.2 -> 26.1 us).
-    if (M >= 128 && K >= 4096)
-      return launch_cols<128, 128, 4, 2, 4, MODE, BPACKED, APACKED, 1, 1>(
-          qa, sa, M, K, lda, qw, sw, ldw, out, ldo, 0, N, stream);
-    if (K % 128 == 0) {
-      if (M >= 128)
-        return launch_cols<128, 64, 4, 2, 4, MODE, BPACKED, APACKED, 2, 1>(
+  if constexpr (BPACKED && APACKED) {
+    if (M < 1024) {
+      // mid-size problems, both operands in the tile layout (measured on
+      // MI355X with the weights coming from HBM; the first figure is the
+      // 64 x 64 one-chunk tiling below):
+      //  - M >= 128 and K >= 4096: 128 x 128 tiles (512x5120x5120 33.1 -> 28.0
+      //    us, 128x5120x17408 40.0 -> 29.6 us);
+      //  - M >= 128, shorter K: 128 x 64 tiles of 8 waves, two chunks a step
+      //    (256x2048x8192 11.6 -> 10.6 us);
+      //  - 33 to 127 rows: 64 x 64 tiles, two chunks a step, two workgroups a
+      //    CU (64x8704x5120 31.8 -> 22.7 us);
+      //  - up to 32 rows: one-wave 32 x 32 tiles, two chunks a step, up to
+      //    five workgroups a CU (32 KiB of LDS each), so a CU has many weight
+      //    streams in flight (32x5120x17408 27.2 -> 20.7 us, 17x5120x17408
+      //    25.6 -> 20.6 us, 32x8704x5120 21.6 -> 19.1 us).
+      if (M >= 128 && K >= 4096)
+        return launch_cols<128, 128, 4, 2, 4, MODE, BPACKED, APACKED, 1, 1>(
             qa, sa, M, K, lda, qw, sw, ldw, out, ldo, 0, N, stream);
-      return launch_cols<64, 64, 2, 2, 4, MODE, BPACKED, APACKED, 2, 2>(
-          qa, sa, M, K, lda, qw, sw, ldw, out, ldo, 0, N, stream);
+      if (K % 128 == 0) {
+        if (M >= 128)
+          return launch_cols<128, 64, 4, 2, 4, MODE, BPACKED, APACKED, 2, 1>(
+              qa, sa, M, K, lda, qw, sw, ldw, out, ldo, 0, N, stream);
+        if (M <= 32)
+          return launch_cols<32, 32, 1, 1, 4, MODE, BPACKED, APACKED, 2, 2>(
+              qa, sa, M, K, lda, qw, sw, ldw, out, ldo, 0, N, stream);
+        return launch_cols<64, 64, 2, 2, 4, MODE, BPACKED, APACKED, 2, 2>(
+            qa, sa, M, K, lda, qw, sw, ldw, out, ldo, 0, N, stream);
+      }
     }
   }
   return launch_cols<64, 64, 2, 2, 4, MODE, BPACKED, APACKED, 1, 1>(
