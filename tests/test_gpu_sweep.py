@@ -29,8 +29,8 @@ def _gpu():
 
 def test_sweep_dense_linear(orc):
     r = np.random.default_rng(71)
-    for i in range(28):
-        M = int(r.choice([1, 1, 2, 2, 3, 5, 8, 13, 16, 17, 33, 70]))
+    for i in range(36):
+        M = int(r.choice([1, 1, 2, 2, 3, 5, 8, 13, 16, 17, 24, 32, 33, 70, 100, 130, 200]))
         K = 64 * int(r.integers(1, 41))
         N = 16 * int(r.integers(1, 49))
         packed = bool(r.integers(0, 2))
