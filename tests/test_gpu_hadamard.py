@@ -150,7 +150,7 @@ def test_linear_g256_ragged_stride(orc):
 def test_g256_small_all_edges(orc, packed):
     r = np.random.default_rng(3)
     for (M, K, N) in [(1, 256, 16), (5, 512, 48), (40, 768, 80), (16, 16384, 32),
-                      (70, 2304, 144)]:
+                      (70, 2304, 144), (17, 1280, 48), (32, 2048, 112)]:
         qa = r.integers(-127, 128, (M, K)).astype(np.int8)
         qw = r.integers(-127, 128, (N, K)).astype(np.int8)
         qa[0] = 127
