@@ -392,11 +392,14 @@ def moe_cases(torch, np, mq, synth, dev, timer, bf16_dev):
         b = torch.from_numpy(synth.expert_weights(cfg["wkey"], e, H, I, synth.T_W2)).to(dev)
         mq.quant_per_token_i8(b, q=w2[e], s=s2[e])
     w13, w2 = mq.pack_moe_weights(w13, w2)  # MFMA tile layout, untimed
+    # two copies of the layer's weights, used alternately, and routing inputs
+    # rotating over seeded sets: a call reuses an expert's weights only after
+    # far more than the 256 MB Infinity Cache has streamed by (at T=1 a call
+    # touches 8 experts, 25 MB; the larger batches 700-800 MB per call, most
+    # of the experts, which without a second copy the next call would partly
+    # find in the cache)
+    copies = [(w13, s13, w2, s2), (w13.clone(), s13.clone(), w2.clone(), s2.clone())]
     res = {}
-    # Routing inputs rotate over seeded sets so that consecutive calls route to
-    # different experts: a call reuses an expert's weights only after far more
-    # than the 256 MB Infinity Cache has streamed by (at T=1 a call touches
-    # 8 experts, 25 MB; the larger batches touch 700-800 MB per call).
     for T, nsets, it in ((1, 64, 64), (64, 4, 20), (2048, 2, 10)):
         c = synth.moe(T)
         ws = torch.empty(mq.moe_w8a8_workspace_bytes(T, H, E, I, k), dtype=torch.uint8,
@@ -413,7 +416,8 @@ def moe_cases(torch, np, mq, synth, dev, timer, bf16_dev):
 
         def fn(i):
             x, logits, ids, wt, out = sets[i % nsets]
-            mq.moe_w8a8_forward(x, logits, w13, s13, w2, s2, k, topk_ids=ids, topk_w=wt,
+            a13, b13, a2, b2 = copies[i % len(copies)]
+            mq.moe_w8a8_forward(x, logits, a13, b13, a2, b2, k, topk_ids=ids, topk_w=wt,
                                 out=out, ws=ws, packed=True)
 
         for r in range(nsets):  # every set routed once (ids filled), untimed
@@ -432,7 +436,9 @@ def moe_cases(torch, np, mq, synth, dev, timer, bf16_dev):
             "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "tops": round(ops / (t * 1e-3) / 1e12, 2),
             "routing_sets": nsets,
+            "weight_copies": len(copies),
         }
+    del copies
     return res
 
 
