@@ -1,5 +1,6 @@
-// Weight packing into MFMA operand tiles (done once, at load, like the weight
-// quantisation itself).
+// Packing into MFMA operand tiles: the weights once, at load (like the weight
+// quantisation itself), and the activation codes of the packed-weight GEMM
+// entry point for more than 16 rows.
 //
 // Packed layout of an int8 [N, K] weight (N % 16 == 0, K % 64 == 0): tile t
 // holds rows 16t..16t+15; its 64-byte k step c is one contiguous 1 KiB block
