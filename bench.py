@@ -16,8 +16,8 @@ Extra cases on the same JSON line (``cases``): prefill M=4096 TOPS, the
 routed MoE layer tokens/s at T in {1, 64, 2048}, and the Hadamard-domain
 linear at M in {1, 256}, each with its fraction of the relevant roofline.
 Prefill and Hadamard weights rotate over copies as above; the MoE cases
-rotate over seeded routing inputs, so consecutive calls read different
-experts' weights.
+rotate over seeded routing inputs and alternate two copies of the layer's
+weights, so consecutive calls read different experts or another copy.
 
 Timing: the stream is first parked on a short spin kernel while the host
 enqueues the timed launches, so HIP events measure GPU time rather than
@@ -162,8 +162,8 @@ def main():
         traffic_from_counters(*args.traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this "
-              "single-GPU build (the path is sharded by design, not run across GPUs here)",
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the "
+              "kernels run on one GPU's share of a layer; nothing here spans GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
