@@ -59,6 +59,11 @@ def threads() -> int:
     return int(_load().orc_threads())
 
 
+def set_threads(n: int) -> None:
+    """OpenMP threads for the oracle's parallel loops (results do not depend on it)."""
+    _load().orc_set_threads(ctypes.c_int(int(n)))
+
+
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -226,6 +231,42 @@ def moe_forward(x_bf16, ids, w, w13, s13, w2, s2, debug: bool = False):
                             g("qx"), g("sx"), g("acc1"), g("act"), g("qa"), g("sa2"),
                             g("acc2"), g("y2"))
     return (out, dbg) if debug else out
+
+
+def mlp_forward(x_bf16, wgu, sgu, wd, sd, debug: bool = False):
+    """O14: dense W8A8 MLP block.
+
+    "[gfx1151] Online INT8 W8A8 ..." (ATOM pull request): A8W8 for all dense
+    GEMMs (intro); the gated-SiLU and requant order of its Changes,
+    fused_moe_triton.py bullet, on the dense gate_up and down linears:
+    per-token int8 quant -> gate_up GEMM (rows 2i = gate, 2i+1 = up) ->
+    SiLU(gate) * up in fp32 -> per-token int8 requant -> down GEMM -> bf16.
+    Shapes: x [M, K] bf16, wgu [2I, K] int8, sgu [2I] fp32, wd [N, I] int8,
+    sd [N] fp32.  Returns y bf16 [M, N], plus a dict of intermediates when
+    ``debug``.
+    """
+    x_bf16 = np.ascontiguousarray(x_bf16, np.uint16)
+    wgu = np.ascontiguousarray(wgu, np.int8)
+    sgu = np.ascontiguousarray(sgu, np.float32)
+    wd = np.ascontiguousarray(wd, np.int8)
+    sd = np.ascontiguousarray(sd, np.float32)
+    M, K = x_bf16.shape
+    I2, K2 = wgu.shape
+    I = I2 // 2
+    N = wd.shape[0]
+    assert K2 == K and wd.shape == (N, I) and sgu.shape == (I2,) and sd.shape == (N,)
+    y = np.empty((M, N), np.uint16)
+    dbg = None
+    if debug:
+        dbg = dict(qx=np.empty((M, K), np.int8), sx=np.empty((M,), np.float32),
+                   acc1=np.empty((M, I2), np.int32), act=np.empty((M, I), np.float32),
+                   qa=np.empty((M, I), np.int8), sa=np.empty((M,), np.float32),
+                   acc2=np.empty((M, N), np.int32))
+    g = (lambda name: _p(dbg[name])) if debug else (lambda name: ctypes.c_void_p(0))
+    _load().orc_mlp_forward(_p(x_bf16), _i64(M), _i64(K), _p(wgu), _p(sgu), _i64(I), _p(wd),
+                            _p(sd), _i64(N), _p(y), g("qx"), g("sx"), g("acc1"), g("act"),
+                            g("qa"), g("sa"), g("acc2"))
+    return (y, dbg) if debug else y
 
 
 def fwht128_rows(v: np.ndarray) -> np.ndarray:

@@ -68,6 +68,16 @@ EXPORT int orc_threads(void)
 #endif
 }
 
+/* Threads for the parallel loops that follow (the results do not depend on it). */
+EXPORT void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
 EXPORT void orc_bf16_round(const float *x, int64_t n, uint16_t *y)
 {
     for (int64_t i = 0; i < n; i++) y[i] = f32_to_bf16(x[i]);
@@ -351,6 +361,71 @@ EXPORT void orc_moe_forward(const uint16_t *x, const int32_t *ids, const float *
     free(qx);
     free(sx);
     free(y2);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O14: dense W8A8 MLP block.  [ATOM] intro (A8W8 for all dense GEMMs of the   */
+/* 27B dense model) with the gated-SiLU / requant order of its "Changes",     */
+/* fused_moe_triton.py bullet, applied to the dense gate_up and down linears:  */
+/*   per-token int8 quant of x -> gate_up GEMM (rows interleaved: 2i = gate_i, */
+/*   2i+1 = up_i) dequantised in fp32 -> act_i = SiLU(gate_i) * up_i ->         */
+/*   per-token int8 requant of the act row -> down GEMM -> bf16.               */
+/* Layouts: x [M,K] bf16; wgu [2I,K] int8, sgu [2I]; wd [N,I] int8, sd [N];    */
+/* y [M,N] bf16.  Optional intermediates (NULL to skip): qx [M,K], sx [M],     */
+/* acc1 [M,2I], act [M,I], qa [M,I], sa [M], acc2 [M,N].                       */
+/* ------------------------------------------------------------------------ */
+EXPORT void orc_mlp_forward(const uint16_t *x, int64_t M, int64_t K, const int8_t *wgu,
+                            const float *sgu, int64_t I, const int8_t *wd, const float *sd,
+                            int64_t N, uint16_t *y, int8_t *qx_out, float *sx_out,
+                            int32_t *acc1_out, float *act_out, int8_t *qa_out, float *sa_out,
+                            int32_t *acc2_out)
+{
+    const int64_t I2 = 2 * I;
+    int8_t *qx = (int8_t *)malloc((size_t)(M * K));
+    float *sx = (float *)malloc((size_t)M * sizeof(float));
+
+    /* per-token quant of the input rows */
+    orc_quant_rows_bf16(x, M, K, K, qx, K, sx);
+
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t m = 0; m < M; m++) {
+        float *h = (float *)malloc((size_t)I2 * sizeof(float));
+        float *act = (float *)malloc((size_t)I * sizeof(float));
+        int8_t *qa = (int8_t *)malloc((size_t)I);
+        float sa;
+
+        /* gate_up GEMM, dequantised */
+        for (int64_t c = 0; c < I2; c++) {
+            int32_t acc = (int32_t)dot_i8(qx + m * K, wgu + c * K, K);
+            if (acc1_out) acc1_out[m * I2 + c] = acc;
+            float v = (float)acc;
+            v = v * sx[m];
+            v = v * sgu[c];
+            h[c] = v;
+        }
+        /* SiLU(gate) * up over the interleaved rows */
+        for (int64_t i = 0; i < I; i++) act[i] = silu_times_up(h[2 * i], h[2 * i + 1]);
+        if (act_out) memcpy(act_out + m * I, act, (size_t)I * sizeof(float));
+
+        /* per-token requant of the activation row */
+        quant_row_f32(act, I, qa, &sa);
+        if (qa_out) memcpy(qa_out + m * I, qa, (size_t)I);
+        if (sa_out) sa_out[m] = sa;
+
+        /* down GEMM and the bf16 epilogue */
+        for (int64_t n = 0; n < N; n++) {
+            int32_t acc = (int32_t)dot_i8(qa, wd + n * I, I);
+            if (acc2_out) acc2_out[m * N + n] = acc;
+            y[m * N + n] = epilogue_bf16(acc, sa, sd[n]);
+        }
+        free(h);
+        free(act);
+        free(qa);
+    }
+    if (qx_out) memcpy(qx_out, qx, (size_t)(M * K));
+    if (sx_out) memcpy(sx_out, sx, (size_t)M * sizeof(float));
+    free(qx);
+    free(sx);
 }
 
 /* ------------------------------------------------------------------------ */
