@@ -269,6 +269,36 @@ def mlp_forward(x_bf16, wgu, sgu, wd, sd, debug: bool = False):
     return (y, dbg) if debug else y
 
 
+def f32_to_f16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> IEEE binary16 bit patterns (uint16), round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, np.uint16)
+    _load().orc_f32_to_f16(_p(x), _i64(x.size), _p(y))
+    return y
+
+
+def kv_quant_i8(x_bf16: np.ndarray, slots: np.ndarray | None = None, rows: int | None = None):
+    """O15: int8 KV-cache quantisation with an f16 scale per token and head.
+
+    "Qwen3.6-35B-A3B IQ8R - radiance container", Serve: kv-cache-dtype i8
+    stores the attention cache as int8 with an f16 scale per token and head.
+    s = f16(amax / 127), code = round-half-even(x / s) clamped to +-127 (0 for
+    a zero scale).  ``x_bf16`` [T, Hk, D] (uint16 bf16 bits); token t goes to
+    cache row ``slots[t]`` (row t without slots; negative skips), ``rows``
+    cache rows (default T).  Returns (q int8 [rows, Hk, D], s f16 bits
+    uint16 [rows, Hk]); rows no token writes stay zero.
+    """
+    x_bf16 = np.ascontiguousarray(x_bf16, np.uint16)
+    T, Hk, D = x_bf16.shape
+    rows = T if rows is None else rows
+    q = np.zeros((rows, Hk, D), np.int8)
+    s = np.zeros((rows, Hk), np.uint16)
+    sl = None if slots is None else np.ascontiguousarray(slots, np.int32)
+    _load().orc_kv_quant_i8(_p(x_bf16), _i64(T), _i64(Hk), _i64(D), _i64(Hk * D), _p(sl),
+                            _p(q), _i64(Hk * D), _p(s), _i64(Hk))
+    return q, s
+
+
 def fwht128_rows(v: np.ndarray) -> np.ndarray:
     """O11: fp32 fast Walsh-Hadamard transform of every 128-block of each row.
 

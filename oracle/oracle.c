@@ -429,6 +429,91 @@ EXPORT void orc_mlp_forward(const uint16_t *x, int64_t M, int64_t K, const int8_
 }
 
 /* ------------------------------------------------------------------------ */
+/* fp32 -> IEEE binary16 bit pattern, round to nearest even (finite inputs;  */
+/* magnitudes from 65520 up become infinity, below 2^-14 subnormal).          */
+/* ------------------------------------------------------------------------ */
+static uint16_t f32_to_f16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    float a = fabsf(f);
+    if (a >= 65520.0f) return (uint16_t)(sign | 0x7c00u);
+    if (a < 0x1p-14f) {
+        /* subnormal: units of 2^-24 (the scaling is exact), rounded to even */
+        float m = nearbyintf(a * 0x1p24f);
+        return (uint16_t)(sign | (uint16_t)m);
+    }
+    uint32_t au = u & 0x7fffffffu;
+    uint32_t e = (au >> 23) - 127u + 15u;   /* 1 .. 30 */
+    uint32_t m = au & 0x7fffffu;
+    uint32_t h = (e << 10) | (m >> 13);
+    uint32_t rest = m & 0x1fffu;          /* the 13 dropped mantissa bits */
+    if (rest > 0x1000u || (rest == 0x1000u && (h & 1u))) h += 1u; /* may carry into e */
+    return (uint16_t)(sign | h);
+}
+
+static float f16_to_f32(uint16_t h)
+{
+    uint32_t e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+    float v;
+    if (e == 0) v = ldexpf((float)m, -24);
+    else if (e == 31) v = INFINITY;
+    else v = ldexpf((float)(m | 0x400u), (int)e - 25);
+    return (h & 0x8000u) ? -v : v;
+}
+
+EXPORT void orc_f32_to_f16(const float *x, int64_t n, uint16_t *y)
+{
+    for (int64_t i = 0; i < n; i++) y[i] = f32_to_f16(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O15: int8 KV-cache quantisation with an f16 scale per token and head.     */
+/* [IQ8R] "Serve": kv-cache-dtype i8 stores the attention cache as int8 with  */
+/* an f16 scale per token and head.  Per (token t, head h), the D values      */
+/* x[t, h, :] (bf16):                                                         */
+/*   s = f16(amax / 127)  (amax/127 in fp32, then rounded to f16, even ties); */
+/*   code = clamp(round_half_even(x / float(s)), -127, 127), 0 where s == 0.  */
+/* The codes are formed against the stored f16 scale, so code * s is the     */
+/* value the cache holds.  Precondition: amax / 127 < 65520 (finite scale).  */
+/* Token t goes to cache row slots[t] (slots NULL: row t; a negative slot    */
+/* skips the token).  x rows have stride ldt elements (heads contiguous);    */
+/* q rows stride ldq, s rows stride lds.                                      */
+/* ------------------------------------------------------------------------ */
+EXPORT void orc_kv_quant_i8(const uint16_t *x, int64_t T, int64_t Hk, int64_t D, int64_t ldt,
+                            const int32_t *slots, int8_t *q, int64_t ldq, uint16_t *s,
+                            int64_t lds)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        int64_t row = slots ? (int64_t)slots[t] : t;
+        if (row < 0) continue;
+        for (int64_t h = 0; h < Hk; h++) {
+            const uint16_t *xr = x + t * ldt + h * D;
+            float amax = 0.0f;
+            for (int64_t d = 0; d < D; d++) {
+                float a = fabsf(bf16_to_f32(xr[d]));
+                if (a > amax) amax = a;
+            }
+            uint16_t sh = f32_to_f16(amax / 127.0f);
+            float sf = f16_to_f32(sh);
+            s[row * lds + h] = sh;
+            for (int64_t d = 0; d < D; d++) {
+                int8_t c = 0;
+                if (sf != 0.0f) {
+                    float r = nearbyintf(bf16_to_f32(xr[d]) / sf);
+                    if (r > 127.0f) r = 127.0f;
+                    if (r < -127.0f) r = -127.0f;
+                    c = (int8_t)r;
+                }
+                q[row * ldq + h * D + d] = c;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* O11: fwht128.  [IQ8R] "Trunk" row: each 128 of K rotated by the            */
 /* unnormalised Hadamard; recipe transform=fwht128.  Fast Walsh-Hadamard      */
 /* butterfly in fp32, natural (Sylvester) order, stages h = 1, 2, ..., 64;    */
