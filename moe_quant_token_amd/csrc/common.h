@@ -121,6 +121,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Orders one wave's LDS stores before the same wave's later LDS loads of
+// another lane's data (and its earlier loads before later stores): a release
+// and an acquire fence at wavefront scope around a wave barrier.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // Marks v as needed here: the compiler can neither sink the load that
 // produces it below this point nor defer the wait for that load past it.
 __device__ __forceinline__ void keep_live(float v) { asm volatile("" ::"v"(v)); }

@@ -1024,7 +1024,9 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm2(
     const float am = __uint_as_float(mb);
     const float sc = am != 0.0f ? am / 127.0f : 0.0f;
     // the row's codes, four per lane at a time, into this wave's LDS row
+    // (after the previous slot's reads of that row)
     int8_t* qrow = qa_lds[wv];
+    wave_lds_sync();
     for (int i = lane * 4; i < I; i += 256) {
       const v4f v = *reinterpret_cast<const v4f*>(act + (int64_t)sl * I + i);
       uint32_t wd = 0u;
@@ -1034,6 +1036,7 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm2(
       *reinterpret_cast<uint32_t*>(qrow + i) = wd;
       if (dbg_qa && tile == 0) *reinterpret_cast<uint32_t*>(dbg_qa + (int64_t)sl * I + i) = wd;
     }
+    wave_lds_sync();  // lanes j == 0 read codes other lanes stored
     v4i acc = {0, 0, 0, 0};
     for (int c0 = 0; c0 < nk; c0 += U) {
       v4i b[U], a[U];
@@ -1326,12 +1329,15 @@ __global__ __launch_bounds__(256) void k_moe_requant(const float* __restrict__ a
 
 // Weighted combine: out[t, c] = bf16( sum_j w[t,j] * y2[t*k + j, c] ), fp32,
 // slot order, one product and one sum per slot (no fused multiply-add).
+// Workgroup b covers token b / nbh, columns 1024 * (b % nbh) .. +1023 (the
+// tokens sit on grid.x, whose range covers every accepted T).
 __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ y2,
                                                      const int32_t* __restrict__ ids,
                                                      const float* __restrict__ w, int T, int H,
-                                                     int E, int k, uint16_t* __restrict__ out) {
-  const int t = blockIdx.y;
-  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+                                                     int E, int k, int nbh,
+                                                     uint16_t* __restrict__ out) {
+  const int t = blockIdx.x / nbh;
+  const int c = ((blockIdx.x - t * nbh) * 256 + threadIdx.x) * 4;
   if (c >= H) return;
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int s = 0; s < k; s++) {
@@ -1493,8 +1499,9 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
       return err;
   }
   if (!t1) {  // the single-token path combined inside its gemm2
-    hipLaunchKernelGGL(k_moe_combine, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, stream,
-                       ws.y2, a.topk_ids, a.topk_w, a.T, a.H, a.E, a.k, a.out);
+    const int nbh = (a.H / 4 + 255) / 256;
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((int64_t)nbh * a.T)), dim3(256), 0, stream,
+                       ws.y2, a.topk_ids, a.topk_w, a.T, a.H, a.E, a.k, nbh, a.out);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
 
