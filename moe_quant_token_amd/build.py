@@ -1,15 +1,21 @@
-"""Build libw8a8.so (the gfx950 HIP kernels and the C-ABI) in-tree with hipcc."""
+"""Build libw8a8.so (the gfx950 HIP kernels and the C-ABI) in-tree with hipcc.
+
+Each .hip source is compiled to its own object (in parallel, under _build/),
+then the objects are linked into the shared library.
+"""
 from __future__ import annotations
 
 import glob
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libw8a8.so")
+OBJDIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -18,7 +24,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # every fp expression is evaluated as written (no fused multiply-add), so
     # the epilogues round exactly like the reference definition
     "-ffp-contract=off",
@@ -33,10 +38,24 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-c", "-o", obj, src]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
     """Compile every .hip source of the package into libw8a8.so (always rebuilds)."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = sources()
+    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources()]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
