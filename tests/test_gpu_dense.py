@@ -270,35 +270,116 @@ def test_decode_linear_full(orc, shape_idx):
         assert assert_bf16_close(bf16_host(yp), y_ref, "linear_w8a8_packed") == 0
 
 
+def test_quant_rows_read_twice(orc):
+    # rows too long to hold in registers are read a second time for the codes:
+    # bf16 with more than 16 rows and K > 16384 (256-thread kernel), fp32 rows
+    # with K > 16384
+    xb = synth.activations((7, 30), 20, 16448, 160, 10.0)
+    xb[3] = 0
+    q_ref, s_ref = orc.quant_rows(xb)
+    q, s = mq.quant_per_token_i8(bf16_dev(xb))
+    Wf = synth.weights((8, 31), 3, 20000)
+    qf_ref, sf_ref = orc.quant_rows(Wf)
+    qf, sf = mq.quant_per_token_i8(dev(Wf))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(q), q_ref)
+    np.testing.assert_array_equal(host(s), s_ref)
+    np.testing.assert_array_equal(host(qf), qf_ref)
+    np.testing.assert_array_equal(host(sf), sf_ref)
+
+
+@pytest.mark.parametrize("M,K", [(40, 8704), (20, 16448)])
+def test_packed_linear_long_rows(orc, M, K):
+    # packed linear with more than 16 rows and K > 8192: the 256-thread
+    # quantiser writes the tile layout (rows held, then read twice)
+    say(f"packed linear long rows M={M} K={K}")
+    N = 64
+    x, W = _inputs((12, M, K), (12, K), M, K, N, max(1, K // 100), 10.0)
+    x[1] = 0
+    qw, sw = orc.quant_rows(W)
+    y_ref = orc.linear_w8a8(x, qw, sw)
+    y = mq.linear_w8a8_packed(bf16_dev(x), mq.pack_weights(dev(qw)), dev(sw), N)
+    np.testing.assert_array_equal(bf16_host(y), y_ref)
+
+
+def test_tile_gemm_global_load_feed(orc):
+    # an activation row stride so large that a workgroup's operand range
+    # spans more than 2 GiB: the tiled kernel feeds LDS with global loads
+    # instead of buffer loads (row-major operands only)
+    M, K, N = 17, 128, 64
+    lda = 35 << 20
+    assert 63 * lda + K >= 1 << 31
+    r = np.random.default_rng(17)
+    qa = r.integers(-127, 128, (M, K)).astype(np.int8)
+    sa = (r.random(M) * 0.01).astype(np.float32)
+    qw = r.integers(-127, 128, (N, K)).astype(np.int8)
+    sw = (r.random(N) * 0.01).astype(np.float32)
+    big = torch.zeros((M, lda), dtype=torch.int8, device=DEV)
+    big[:, :K] = dev(qa)
+    qa_d = big[:, :K]
+    acc = mq.gemm_w8a8_i32acc(qa_d, dev(qw))
+    y = mq.gemm_w8a8(qa_d, dev(sa), dev(qw), dev(sw))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(acc), orc.gemm_i32(qa, qw))
+    np.testing.assert_array_equal(bf16_host(y), orc.gemm_w8a8(qa, sa, qw, sw))
+    del big
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_tile_256x160_plan_full(orc, packed):
+    # 4 x 5 = 20 tiles of 256 x 256 would leave most of a round idle and N is
+    # a multiple of 160: the 256 x 160 plan (two workgroups a CU), compared in
+    # full
+    M, K, N = 1024, 512, 1280
+    x, W = _inputs((13, 1), (13, 2), M, K, N, 4, 20.0)
+    x[7] = 0
+    qa, sa = orc.quant_rows(x)
+    qw, sw = orc.quant_rows(W)
+    acc_ref = orc.gemm_i32(qa, qw)
+    y_ref = orc.epilogue(acc_ref, sa, sw)
+    qw_d = mq.pack_weights(dev(qw)) if packed else dev(qw)
+    if packed:
+        acc = mq.gemm_w8a8_packed_i32acc(dev(qa), qw_d, N)
+        y = mq.gemm_w8a8_packed(dev(qa), dev(sa), qw_d, dev(sw), N)
+        y2 = mq.linear_w8a8_packed(bf16_dev(x), qw_d, dev(sw), N)
+    else:
+        acc = mq.gemm_w8a8_i32acc(dev(qa), qw_d)
+        y = mq.gemm_w8a8(dev(qa), dev(sa), qw_d, dev(sw))
+        y2 = mq.linear_w8a8(bf16_dev(x), qw_d, dev(sw))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    np.testing.assert_array_equal(bf16_host(y), y_ref)
+    np.testing.assert_array_equal(bf16_host(y2), y_ref)
+
+
 # ----------------------------------------------------- prefill, full size
 @pytest.mark.parametrize("N", [5120, 17408])
-def test_prefill_full_sampled(orc, N):
+def test_prefill_full(orc, N):
+    # every output of the prefill workload against the oracle: the int32 sums
+    # of the packed GEMM, the GEMM-only call, the linear entry the benchmark
+    # times (its quantiser writes the tile layout) and the linear on
+    # row-major weights
     cfg = synth.prefill_linear(N)
     M, K = cfg["M"], cfg["K"]
-    say(f"prefill M={M} K={K} N={N}")
+    say(f"prefill full M={M} K={K} N={N}")
     x, W = _inputs(cfg["xkey"], cfg["wkey"], M, K, N, cfg["n_outliers"], cfg["outlier_scale"])
     qa, sa = orc.quant_rows(x)
     qw, sw = orc.quant_rows(W)
     del W
     x_d, qw_d, sw_d = bf16_dev(x), dev(qw), dev(sw)
-    # quant on the GPU (bit-exact), then both the gemm-only and the fused call
     q_d, s_d = mq.quant_per_token_i8(x_d)
-    np.testing.assert_array_equal(host(s_d), sa)
-    assert np.array_equal(host(q_d), qa)
     qp_d = mq.pack_weights(qw_d)
-    y = mq.gemm_w8a8_packed(q_d, s_d, qp_d, sw_d, N)
-    y2 = mq.linear_w8a8(x_d, qw_d, sw_d)
-    acc = mq.gemm_w8a8_packed_i32acc(q_d, qp_d, N)
+    acc = host(mq.gemm_w8a8_packed_i32acc(q_d, qp_d, N))
+    y = bf16_host(mq.gemm_w8a8_packed(q_d, s_d, qp_d, sw_d, N))
+    yl = bf16_host(mq.linear_w8a8_packed(x_d, qp_d, sw_d, N))
+    yu = bf16_host(mq.linear_w8a8(x_d, qw_d, sw_d))  # row-major weights
     torch.cuda.synchronize()
-    r = np.random.default_rng(N)
-    ms = np.concatenate([r.integers(0, M, 4000), np.full(N // 64, M - 1), np.arange(0, M, 64)])
-    ns = np.concatenate([r.integers(0, N, 4000), np.arange(0, N, 64), np.full(M // 64, N - 1)])
-    acc_ref, y_ref = orc.gemm_w8a8_points(qa, sa, qw, sw, ms, ns)
-    np.testing.assert_array_equal(host(acc)[ms, ns], acc_ref)
-    yh = bf16_host(y)
-    assert assert_bf16_close(yh[ms, ns], y_ref, "gemm_w8a8 sampled") == 0
-    np.testing.assert_array_equal(bf16_host(y2), yh)
-    # property at full size: every output is its int32 sum through the fp32
-    # epilogue (torch: int32 -> fp32, two fp32 products, bf16 rounding)
-    full = ((acc.to(torch.float32) * s_d[:, None]) * sw_d[None, :]).to(torch.bfloat16)
-    assert torch.equal(full.view(torch.int16), y.view(torch.int16))
+    np.testing.assert_array_equal(host(q_d), qa)
+    np.testing.assert_array_equal(host(s_d), sa)
+    say("  oracle GEMM")
+    acc_ref = orc.gemm_i32(qa, qw)
+    np.testing.assert_array_equal(acc, acc_ref)
+    y_ref = orc.epilogue(acc_ref, sa, sw)
+    np.testing.assert_array_equal(y, y_ref)
+    np.testing.assert_array_equal(yl, y_ref)
+    np.testing.assert_array_equal(yu, y_ref)

@@ -270,22 +270,40 @@ def test_full_size_all_tokens(orc, full_moe, T):
     _check_full(orc, x, logits, cfg["k"], W, T, f"moe T={T}", packed=True, Wd=Wd)
 
 
-def test_full_size_t2048_sampled_tokens(orc, full_moe):
+def test_full_size_t2048_all_tokens(orc, full_moe):
+    # every token and every intermediate of the large-batch path at full size
     cfg = synth.moe(2048)
     T, k = 2048, cfg["k"]
-    say("moe full size T=2048 (sampled tokens)")
+    say("moe full size T=2048 (all tokens, all intermediates)")
     W, Wd = full_moe
     x = synth.activations(cfg["xkey"], T, cfg["H"], 0, 1.0)
     logits = synth.router_logits(cfg["xkey"], T, cfg["E"])
     assert _tie_free(logits, k)
-    out, ids, w = mq.moe_w8a8_forward(bf16_dev(x), dev(logits), *Wd, topk=k, packed=True)
-    torch.cuda.synchronize()
-    ids_ref, w_ref = orc.route_topk(logits, k)
-    np.testing.assert_array_equal(host(ids), ids_ref)
-    # tokens are independent given the routing: the oracle runs a sample of them
-    sample = np.sort(np.random.default_rng(7).choice(T, 48, replace=False))
-    out_ref = orc.moe_forward(np.ascontiguousarray(x[sample]), ids_ref[sample], w_ref[sample], *W)
-    assert_bf16_close(bf16_host(out)[sample], out_ref, "moe T=2048 sampled")
-    # property at any size: every expert's count equals its routed pairs
-    counts = np.bincount(host(ids).ravel(), minlength=cfg["E"])
-    assert counts.sum() == T * k
+    _check_full(orc, x, logits, k, W, T, "moe T=2048", packed=True, Wd=Wd)
+
+
+@pytest.mark.parametrize("T", [1, 5, 40, 600])
+def test_hidden_above_4096(orc, T):
+    # H > 4096: the token rows no longer fit the registers the routing/quant
+    # waves hold them in and are read a second time (single token, one-
+    # workgroup prep, wave-per-token routing + quant, large path)
+    E, H, I, k = 16, 4160, 64, 4
+    key = (56, T)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    logits = synth.router_logits(key, T, E)
+    assert _tie_free(logits, k)
+    _check_full(orc, x, logits, k, W, T, f"moe H=4160 T={T}", packed=True)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_few_pairs_wide_intermediate(orc, packed):
+    # few routed pairs but I > 2048: too wide for the small-batch gemm2's LDS
+    # rows, so the large-batch kernels run on a handful of pairs
+    T, E, H, I, k = 3, 4, 128, 2112, 2
+    key = (57, 1)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    logits = synth.router_logits(key, T, E)
+    assert _tie_free(logits, k)
+    _check_full(orc, x, logits, k, W, T, "moe I=2112 T=3", packed=packed)
