@@ -145,6 +145,42 @@ int linear_w8a8_packed(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                        int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Dense W8A8 MLP block.  [ATOM] intro: A8W8 for all dense GEMMs (the 27B    */
+/* dense model of its "Performance" section); the order of its "Changes",    */
+/* fused_moe_triton.py bullet (gemm1 with the gated SiLU over interleaved    */
+/* gate/up rows, per-token int8 requant, gemm2) on the dense gate_up and     */
+/* down linears:                                                             */
+/*   qx, sx = per-token quant of x (as quant_per_token_i8)                    */
+/*   h[m,c]   = (float(sum_k qx[m,k] wgu[c,k]) * sx[m]) * sgu[c],  c < 2I     */
+/*   act[m,i] = silu(h[m,2i]) * h[m,2i+1]   (row 2i = gate_i, 2i+1 = up_i;   */
+/*              silu(g) = g / (1 + exp(-g)) in fp64, rounded to fp32)       */
+/*   qa, sa   = per-token quant of the fp32 act rows                         */
+/*   y[m,n]   = bf16_rne((float(sum_i qa[m,i] wd[n,i]) * sa[m]) * sd[n])      */
+/* x: bf16 [M, K] (ldx); wgu_packed: int8 [2I, K] in the packed tile layout  */
+/* (w8a8_pack_weights), sgu fp32 [2I]; wd_packed: int8 [N, I] packed, sd     */
+/* fp32 [N]; y: bf16 [M, N] (ldy).  A checkpoint with concatenated [gate;    */
+/* up] rows is permuted to the interleaved order at load.                    */
+/* Workspace: mlp_w8a8_workspace_bytes(M, K, I, N) (codes, scales and the    */
+/* fp32 activation rows).  Requires K % 64 == 0, K <= 131072, I % 64 == 0,   */
+/* I <= 65536, N % 16 == 0; x, weights, ws 16-byte aligned, ldx a multiple  */
+/* of 16, y 4-byte aligned with even ldy.                                    */
+/* dbg (nullable; each member nullable, 16-byte aligned): row-major copies   */
+/* of the intermediates act fp32 [M, I], qa int8 [M, I], sa fp32 [M].        */
+/* ------------------------------------------------------------------------ */
+typedef struct mlp_w8a8_debug {
+    float *act;  /* [M, I] */
+    int8_t *qa;  /* [M, I] */
+    float *sa;   /* [M] */
+} mlp_w8a8_debug;
+
+size_t mlp_w8a8_workspace_bytes(int64_t M, int64_t K, int64_t I, int64_t N);
+int mlp_w8a8_packed(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                    const int8_t *wgu_packed, const float *sgu, int64_t I,
+                    const int8_t *wd_packed, const float *sd, int64_t N, uint16_t *y,
+                    int64_t ldy, void *ws, size_t ws_bytes, const mlp_w8a8_debug *dbg,
+                    void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Routed int8 MoE layer.                                                    */
 /* [ATOM] Changes, fused_moe_triton.py bullet: routing -> per-token int8     */
 /* quant -> gemm1 with fused gated SiLU over interleaved w13 -> per-token    */

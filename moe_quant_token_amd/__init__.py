@@ -43,6 +43,10 @@ class MoeDebug(ctypes.Structure):
                 ("sa2", _vp), ("acc2", _vp)]
 
 
+class MlpDebug(ctypes.Structure):
+    _fields_ = [("act", _vp), ("qa", _vp), ("sa", _vp)]
+
+
 _SIGS = {
     "w8a8_status_string": ([_i32], ctypes.c_char_p),
     "w8a8_last_hip_error": ([], _i32),
@@ -63,6 +67,9 @@ _SIGS = {
                                 _i32),
     "linear_w8a8_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp],
                            _i32),
+    "mlp_w8a8_workspace_bytes": ([_i64, _i64, _i64, _i64], _sz),
+    "mlp_w8a8_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
+                         _sz, ctypes.POINTER(MlpDebug), _vp], _i32),
     "moe_w8a8_workspace_bytes": ([_i64, _i64, _i64, _i64, _i32], _sz),
     "moe_w8a8_forward": ([_vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _vp, _sz, ctypes.POINTER(MoeDebug), _vp], _i32),
@@ -252,6 +259,34 @@ def linear_w8a8_packed(x, qw_packed, sw, N: int, y: torch.Tensor | None = None,
     return y
 
 
+def mlp_w8a8_workspace_bytes(M: int, K: int, I: int, N: int) -> int:
+    return int(lib().mlp_w8a8_workspace_bytes(M, K, I, N))
+
+
+def mlp_w8a8_packed(x, wgu_packed, sgu, wd_packed, sd, I: int, N: int,
+                    y: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                    debug: bool = False):
+    """Dense W8A8 MLP block: gate_up (interleaved rows) -> SiLU(gate)*up ->
+    per-token requant -> down, weights from ``pack_weights``.  Returns y
+    (bf16 [M, N]) and, with ``debug``, a dict of intermediates."""
+    _req(x, torch.bfloat16, "x")
+    M, K = x.shape
+    dev = x.device
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if y is None else y
+    ws, wsb = _workspace(mlp_w8a8_workspace_bytes(M, K, I, N), dev, ws)
+    dbg_t = dbg_p = None
+    if debug:
+        dbg_t = dict(act=torch.empty((M, I), dtype=torch.float32, device=dev),
+                     qa=torch.empty((M, I), dtype=torch.int8, device=dev),
+                     sa=torch.empty((M,), dtype=torch.float32, device=dev))
+        dbg_p = ctypes.pointer(MlpDebug(**{k: v.data_ptr() for k, v in dbg_t.items()}))
+    _check("mlp_w8a8_packed",
+           lib().mlp_w8a8_packed(_ptr(x), M, K, x.stride(0), _ptr(wgu_packed), _ptr(sgu), I,
+                                 _ptr(wd_packed), _ptr(sd), N, _ptr(y), y.stride(0), _ptr(ws),
+                                 wsb, dbg_p, _stream(dev)))
+    return (y, dbg_t) if debug else y
+
+
 def moe_w8a8_workspace_bytes(T: int, H: int, E: int, I: int, topk: int) -> int:
     return int(lib().moe_w8a8_workspace_bytes(T, H, E, I, topk))
 
@@ -344,6 +379,10 @@ def gemm_w8a8_g256(qa, sa, qw, su8, s2, y: torch.Tensor | None = None,
     _check(fn, getattr(lib(), fn)(_ptr(qa), _ptr(sa), M, K, _ptr(qw), _ptr(su8), _ptr(s2), N,
                                   _ptr(y), y.stride(0), _ptr(ws), wsb, _stream(qa.device)))
     return y
+
+
+def gemm_w8a8_g256_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().gemm_w8a8_g256_workspace_bytes(M, N, K))
 
 
 def linear_w8a8_g256_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -202,7 +202,7 @@ int quant_per_token_i8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t
                        int64_t ldq, float* s, void* stream) {
   if (M < 0 || K <= 0 || ldx < K || ldq < K) return W8A8_INVALID_ARG;
   if (x_dtype != 0 && x_dtype != 1) return W8A8_INVALID_ARG;
-  if (K % 16 != 0 || K > 65536 || M > (int64_t)1 << 31) return W8A8_UNSUPPORTED_SHAPE;
+  if (K % 16 != 0 || K > 65536 || M > INT32_MAX) return W8A8_UNSUPPORTED_SHAPE;
   if (M == 0) return W8A8_OK;
   if (!x || !q || !s) return W8A8_INVALID_ARG;
   if (!al16(x) || !al16(q) || !al4(s) || ldx % 16 != 0 || ldq % 16 != 0) return W8A8_MISALIGNED;
@@ -275,6 +275,55 @@ int linear_w8a8_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                        const int8_t* qw_packed, const float* sw, int64_t N, uint16_t* y,
                        int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   return linear_common(x, M, K, ldx, qw_packed, sw, N, K, true, y, ldy, ws, ws_bytes, stream);
+}
+
+size_t mlp_w8a8_workspace_bytes(int64_t M, int64_t K, int64_t I, int64_t N) {
+  if (M <= 0 || K <= 0 || I <= 0 || N <= 0) return 0;
+  return mlp_workspace_bytes(M, K, I);
+}
+
+int mlp_w8a8_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                    const int8_t* wgu_packed, const float* sgu, int64_t I,
+                    const int8_t* wd_packed, const float* sd, int64_t N, uint16_t* y, int64_t ldy,
+                    void* ws, size_t ws_bytes, const mlp_w8a8_debug* dbg, void* stream) {
+  if (M < 0 || K <= 0 || I <= 0 || N <= 0 || ldx < K || ldy < N) return W8A8_INVALID_ARG;
+  if (K % 64 != 0 || K > 131072 || I % 64 != 0 || I > 65536 || N % 16 != 0 ||
+      N > (int64_t)1 << 30 || M > (int64_t)1 << 30)
+    return W8A8_UNSUPPORTED_SHAPE;
+  if (M == 0) return W8A8_OK;
+  if (!x || !wgu_packed || !sgu || !wd_packed || !sd || !y) return W8A8_INVALID_ARG;
+  if (!al16(x) || ldx % 16 != 0 || !al16(wgu_packed) || !al16(wd_packed) || !al4(sgu) ||
+      !al4(sd) || !al4(y) || ldy % 2 != 0)
+    return W8A8_MISALIGNED;
+  if (dbg && ((dbg->act && !al16(dbg->act)) || (dbg->qa && !al16(dbg->qa)) ||
+              (dbg->sa && !al4(dbg->sa))))
+    return W8A8_MISALIGNED;
+  if (ws_bytes < mlp_w8a8_workspace_bytes(M, K, I, N)) return W8A8_WORKSPACE_TOO_SMALL;
+  if (!ws) return W8A8_INVALID_ARG;
+  if (!al16(ws)) return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  MlpArgs a{};
+  a.x = x;
+  a.M = M;
+  a.K = K;
+  a.ldx = ldx;
+  a.I = I;
+  a.N = N;
+  a.ldy = ldy;
+  a.wgu = wgu_packed;
+  a.sgu = sgu;
+  a.wd = wd_packed;
+  a.sd = sd;
+  a.y = y;
+  a.ws = ws;
+  if (dbg) {
+    a.dbg_act = dbg->act;
+    a.dbg_qa = dbg->qa;
+    a.dbg_sa = dbg->sa;
+  }
+  hipError_t e = launch_mlp(a, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
 }
 
 size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int topk) {
@@ -352,7 +401,7 @@ int moe_w8a8_forward_packed(const uint16_t* x, const float* logits, int64_t T, i
 int fwht128_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
                   float* s, void* stream) {
   if (M < 0 || K <= 0 || ldx < K || ldq < K) return W8A8_INVALID_ARG;
-  if (K % 128 != 0 || K > 16384 || M > (int64_t)1 << 31) return W8A8_UNSUPPORTED_SHAPE;
+  if (K % 128 != 0 || K > 16384 || M > INT32_MAX) return W8A8_UNSUPPORTED_SHAPE;
   if (M == 0) return W8A8_OK;
   if (!x || !q || !s) return W8A8_INVALID_ARG;
   if (!al16(x) || !al16(q) || !al4(s) || ldx % 16 != 0 || ldq % 16 != 0) return W8A8_MISALIGNED;
@@ -365,7 +414,7 @@ int fwht128_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* 
 int fwht128_weight_prep_g256(const float* W, int64_t N, int64_t K, int8_t* qw, uint8_t* su8,
                              uint16_t* s2, void* stream) {
   if (N < 0 || K <= 0) return W8A8_INVALID_ARG;
-  if (K % 256 != 0 || K > 16384 || N > (int64_t)1 << 31) return W8A8_UNSUPPORTED_SHAPE;
+  if (K % 256 != 0 || K > 16384 || N > INT32_MAX) return W8A8_UNSUPPORTED_SHAPE;
   if (N == 0) return W8A8_OK;
   if (!W || !qw || !su8 || !s2) return W8A8_INVALID_ARG;
   if (!al16(W) || !al16(qw)) return W8A8_MISALIGNED;

@@ -27,7 +27,18 @@
 
 namespace w8a8 {
 
-template <int WAVES, int U, bool PACKED, bool STORE_I32>
+// Epilogues of the decode GEMM: bf16 y = (float(acc) * sa) * sw; the int32
+// sums; or the gated SiLU of an interleaved gate/up weight (rows 2i = gate_i,
+// 2i+1 = up_i): act[m, i] = silu(h[m, 2i]) * h[m, 2i+1] in fp32 with h the
+// fp32-dequantised sums (SiLU in fp64, rounded once).
+enum { kSkEpiBf16 = 0, kSkEpiI32 = 1, kSkEpiSilu = 2 };
+
+__device__ __forceinline__ float silu_times(float gate, float up) {
+  const float sg = (float)((double)gate / (1.0 + exp(-(double)gate)));
+  return sg * up;
+}
+
+template <int WAVES, int U, bool PACKED, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
     const int8_t* __restrict__ qa, const float* __restrict__ sa, int M, int K, int64_t lda,
     const int8_t* __restrict__ qw, const float* __restrict__ sw, int64_t ldw,
@@ -65,6 +76,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
   // (row index clamped into range) and waited for once, so no store waits
   // on a scale load (a load between two stores would also wait for the
   // earlier store)
+  constexpr bool STORE_I32 = EPI == kSkEpiI32;
   const int64_t n = tile * 16 + j;
   float sam[4] = {0.0f, 0.0f, 0.0f, 0.0f}, swn = 0.0f;
   if (!STORE_I32 && wv == 0) {
@@ -81,6 +93,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
 #pragma unroll
     for (int v = 0; v < 4; v++) keep_live(sam[v]);
     keep_live(swn);
+  }
+  if (EPI == kSkEpiSilu) {
+    // lanes j and j ^ 1 hold the gate and up rows of one channel for the same
+    // tokens; the even lane forms the activation
+    float h[4], up[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      h[v] = (float)acc[v];
+      h[v] = h[v] * sam[v];
+      h[v] = h[v] * swn;
+      up[v] = __shfl_xor(h[v], 1, 64);
+    }
+    if ((j & 1) == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int m = 4 * g + v;
+        if (m >= M) break;
+        static_cast<float*>(out)[(int64_t)m * ldo + (n >> 1)] = silu_times(h[v], up[v]);
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int v = 0; v < 4; v++) {
@@ -284,11 +317,11 @@ hipError_t launch_linear_skinny_fused(const uint16_t* x, int64_t ldx, int64_t M,
   return hipGetLastError();
 }
 
-template <bool PACKED, bool STORE_I32>
+template <bool PACKED, int EPI>
 static hipError_t launch_skinny_impl(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                                      int64_t lda, const int8_t* qw, const float* sw, int64_t N,
                                      int64_t ldw, void* out, int64_t ldo, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_skinny<kSkinnyWaves, kSkinnyU, PACKED, STORE_I32>),
+  hipLaunchKernelGGL((k_gemm_skinny<kSkinnyWaves, kSkinnyU, PACKED, EPI>),
                      dim3((unsigned)(N / 16)), dim3(kSkinnyWaves * 64), 0, stream, qa, sa, (int)M,
                      (int)K, lda, qw, sw, ldw, out, ldo);
   return hipGetLastError();
@@ -298,19 +331,26 @@ hipError_t launch_gemm_skinny(const int8_t* qa, const float* sa, int64_t M, int6
                               int64_t lda, const int8_t* qw, const float* sw, int64_t N,
                               int64_t ldw, bool packed, uint16_t* y, int64_t ldy,
                               hipStream_t stream) {
-  return packed ? launch_skinny_impl<true, false>(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy,
-                                                  stream)
-                : launch_skinny_impl<false, false>(qa, sa, M, K, lda, qw, sw, N, ldw, y, ldy,
-                                                   stream);
+  return packed ? launch_skinny_impl<true, kSkEpiBf16>(qa, sa, M, K, lda, qw, sw, N, ldw, y,
+                                                        ldy, stream)
+                : launch_skinny_impl<false, kSkEpiBf16>(qa, sa, M, K, lda, qw, sw, N, ldw, y,
+                                                         ldy, stream);
+}
+
+hipError_t launch_gemm_skinny_silu(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                                   int64_t lda, const int8_t* qw_packed, const float* sw,
+                                   int64_t N, float* act, int64_t ldact, hipStream_t stream) {
+  return launch_skinny_impl<true, kSkEpiSilu>(qa, sa, M, K, lda, qw_packed, sw, N, K, act,
+                                              ldact, stream);
 }
 
 hipError_t launch_gemm_skinny_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
                                   const int8_t* qw, int64_t N, int64_t ldw, bool packed,
                                   int32_t* acc, int64_t ldacc, hipStream_t stream) {
-  return packed ? launch_skinny_impl<true, true>(qa, nullptr, M, K, lda, qw, nullptr, N, ldw,
-                                                 acc, ldacc, stream)
-                : launch_skinny_impl<false, true>(qa, nullptr, M, K, lda, qw, nullptr, N, ldw,
-                                                  acc, ldacc, stream);
+  return packed ? launch_skinny_impl<true, kSkEpiI32>(qa, nullptr, M, K, lda, qw, nullptr, N,
+                                                       ldw, acc, ldacc, stream)
+                : launch_skinny_impl<false, kSkEpiI32>(qa, nullptr, M, K, lda, qw, nullptr, N,
+                                                        ldw, acc, ldacc, stream);
 }
 
 }  // namespace w8a8

@@ -32,8 +32,11 @@ namespace w8a8 {
 
 // MODE 0: bf16 epilogue (float(acc) * sa[m]) * sw[n]; MODE 1: store the int32
 // sums; MODE 2: Hadamard-domain g256 epilogue (every four k steps = one group
-// of 256, the exact int32 sum is scaled by su8[n, group] into an int64 sum).
-enum { kEpiBf16 = 0, kEpiI32 = 1, kEpiG256 = 2 };
+// of 256, the exact int32 sum is scaled by su8[n, group] into an int64 sum);
+// MODE 3: gated SiLU over an interleaved gate/up weight (columns 2i = gate_i,
+// 2i+1 = up_i of the product): out[m, i] = silu(h[m, 2i]) * h[m, 2i+1] in
+// fp32, h = (float(acc) * sa[m]) * sw[n], SiLU in fp64 rounded once.
+enum { kEpiBf16 = 0, kEpiI32 = 1, kEpiG256 = 2, kEpiSilu = 3 };
 
 constexpr int kXcds = 8;
 
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
 #pragma unroll
     for (int n = 0; n < TN; n++) {
       const int c = min(col0 + n * 32, N - 1);
-      scol[n] = MODE == kEpiBf16 ? sw[c] : __uint_as_float((uint32_t)s2[c] << 16);
+      scol[n] = MODE == kEpiG256 ? __uint_as_float((uint32_t)s2[c] << 16) : sw[c];
     }
     // one wait for all of them: the stores below sit in per-element
     // branches, across which the compiler would otherwise wait again
@@ -308,6 +311,33 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
       for (int v = 0; v < 16; v++) keep_live(sar[i][v]);
 #pragma unroll
     for (int n = 0; n < TN; n++) keep_live(scol[n]);
+  }
+  if (MODE == kEpiSilu) {
+    // lanes l and l ^ 1 hold adjacent product columns (gate, up) of the same
+    // rows; the even lane stores the activation.  N is even, so both lanes of
+    // a pair are in range or out of range together.
+#pragma unroll
+    for (int n = 0; n < TN; n++) {
+      const int col = col0 + n * 32;
+      const bool store = col < N && (col & 1) == 0;
+#pragma unroll
+      for (int i = 0; i < TM; i++) {
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const int row = row0 + i * 32 + 8 * (v >> 2) + (v & 3);
+          float h = (float)acc[i][n][v];
+          h = h * sar[i][v];
+          h = h * scol[n];
+          const float up = __shfl_xor(h, 1, 64);
+          if (store && row < M) {
+            const float sg = (float)((double)h / (1.0 + exp(-(double)h)));
+            static_cast<float*>(out)[(int64_t)row * ldo + (col >> 1)] = sg * up;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int n = 0; n < TN; n++) {
@@ -379,10 +409,12 @@ static hipError_t launch_cols(const int8_t* qa, const float* sa, int64_t M, int6
                               int64_t lda, const int8_t* qw, const float* sw, int64_t ldw,
                               void* out, int64_t ldo, int64_t n0, int64_t nn,
                               hipStream_t stream) {
-  const size_t esz = MODE == kEpiI32 ? 4 : 2;
+  // bytes per product column of the output: int32, bf16, or half an fp32
+  // activation (two product columns make one)
+  const int64_t off = MODE == kEpiI32 ? n0 * 4 : MODE == kEpiSilu ? n0 / 2 * 4 : n0 * 2;
   return launch_tile_cfg<BM, BN, WAVES_M, WAVES_N, NSTAGE, MODE, BPACKED, APACKED, KSUB, MINB>(
       qa, sa, M, K, lda, qw + n0 * (BPACKED ? K : ldw), sw ? sw + n0 : nullptr, nn, ldw,
-      static_cast<char*>(out) + n0 * esz, ldo, nullptr, nullptr, stream);
+      static_cast<char*>(out) + off, ldo, nullptr, nullptr, stream);
 }
 
 static int64_t gcd64(int64_t a, int64_t b) {
@@ -500,6 +532,14 @@ hipError_t launch_gemm_tile_apacked(const int8_t* qa_packed, const float* sa, in
                                     int64_t N, uint16_t* y, int64_t ldy, hipStream_t stream) {
   return launch_tile_impl<kEpiBf16, true, true>(qa_packed, sa, M, K, K, qw_packed, sw, N, K, y,
                                                 ldy, stream);
+}
+
+hipError_t launch_gemm_tile_apacked_silu(const int8_t* qa_packed, const float* sa, int64_t M,
+                                         int64_t K, const int8_t* qw_packed, const float* sw,
+                                         int64_t N, float* act, int64_t ldact,
+                                         hipStream_t stream) {
+  return launch_tile_impl<kEpiSilu, true, true>(qa_packed, sa, M, K, K, qw_packed, sw, N, K, act,
+                                                ldact, stream);
 }
 
 hipError_t launch_gemm_tile_apacked_i32(const int8_t* qa_packed, int64_t M, int64_t K,

@@ -19,6 +19,11 @@ hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t M, int64_t K, i
 hipError_t launch_quant_rows_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                     int8_t* q, float* s, hipStream_t stream);
 
+// fp32 rows (the dense MLP's activation requant): codes row-major (ldq) or,
+// with `packed`, in the tile layout.
+hipError_t launch_quant_rows_f32(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                 int64_t ldq, float* s, bool packed, hipStream_t stream);
+
 // `packed`: weights in the MFMA tile layout of pack.hip instead of row-major.
 hipError_t launch_pack_weights(const int8_t* qw, int64_t N, int64_t K, int64_t ldw,
                                int8_t* out, hipStream_t stream);
@@ -31,6 +36,11 @@ hipError_t launch_gemm_skinny(const int8_t* qa, const float* sa, int64_t M, int6
                               int64_t lda, const int8_t* qw, const float* sw, int64_t N,
                               int64_t ldw, bool packed, uint16_t* y, int64_t ldy,
                               hipStream_t stream);
+// Gated SiLU epilogue over an interleaved gate/up weight of 2I = N packed rows:
+// act [M, N/2] fp32 (row stride ldact).
+hipError_t launch_gemm_skinny_silu(const int8_t* qa, const float* sa, int64_t M, int64_t K,
+                                   int64_t lda, const int8_t* qw_packed, const float* sw,
+                                   int64_t N, float* act, int64_t ldact, hipStream_t stream);
 hipError_t launch_gemm_skinny_i32(const int8_t* qa, int64_t M, int64_t K, int64_t lda,
                                   const int8_t* qw, int64_t N, int64_t ldw, bool packed,
                                   int32_t* acc, int64_t ldacc, hipStream_t stream);
@@ -52,6 +62,10 @@ hipError_t launch_gemm_tile_i32(const int8_t* qa, int64_t M, int64_t K, int64_t 
 hipError_t launch_gemm_tile_apacked(const int8_t* qa_packed, const float* sa, int64_t M,
                                     int64_t K, const int8_t* qw_packed, const float* sw,
                                     int64_t N, uint16_t* y, int64_t ldy, hipStream_t stream);
+hipError_t launch_gemm_tile_apacked_silu(const int8_t* qa_packed, const float* sa, int64_t M,
+                                         int64_t K, const int8_t* qw_packed, const float* sw,
+                                         int64_t N, float* act, int64_t ldact,
+                                         hipStream_t stream);
 hipError_t launch_gemm_tile_apacked_i32(const int8_t* qa_packed, int64_t M, int64_t K,
                                         const int8_t* qw_packed, int64_t N, int32_t* acc,
                                         int64_t ldacc, hipStream_t stream);
@@ -80,6 +94,23 @@ struct MoeArgs {
 };
 size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int k);
 hipError_t launch_moe_forward(const MoeArgs& a, hipStream_t stream);
+
+// Dense MLP block.  Workspace layout is owned by mlp.hip.
+struct MlpArgs {
+  const uint16_t* x;
+  int64_t M, K, ldx, I, N, ldy;
+  const int8_t* wgu;  // packed [2I, K], rows 2i = gate_i, 2i+1 = up_i
+  const float* sgu;
+  const int8_t* wd;   // packed [N, I]
+  const float* sd;
+  uint16_t* y;
+  void* ws;
+  float* dbg_act;
+  int8_t* dbg_qa;
+  float* dbg_sa;
+};
+size_t mlp_workspace_bytes(int64_t M, int64_t K, int64_t I);
+hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream);
 
 // Hadamard-domain variant.
 hipError_t launch_fwht128_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,

@@ -229,6 +229,20 @@ hipError_t launch_quant_rows_packed(const uint16_t* x, int64_t M, int64_t K, int
   return hipGetLastError();
 }
 
+hipError_t launch_quant_rows_f32(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                 int64_t ldq, float* s, bool packed, hipStream_t stream) {
+  if (packed)
+    hipLaunchKernelGGL((k_quant_rows<float, true>), dim3((unsigned)M), dim3(256), 0, stream, x,
+                       ldx, (int)K, q, (int64_t)0, s);
+  else if (M <= 16)
+    hipLaunchKernelGGL((k_quant_rows<float, false, 1024>), dim3((unsigned)M), dim3(1024), 0,
+                       stream, x, ldx, (int)K, q, ldq, s);
+  else
+    hipLaunchKernelGGL((k_quant_rows<float, false>), dim3((unsigned)M), dim3(256), 0, stream, x,
+                       ldx, (int)K, q, ldq, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                              int8_t* q, int64_t ldq, float* s, hipStream_t stream) {
   dim3 grid((unsigned)M), block(256);
