@@ -181,6 +181,27 @@ int mlp_w8a8_packed(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                     void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* int8 KV-cache quantisation.  [IQ8R] Serve: kv-cache-dtype i8 stores the   */
+/* attention cache as int8 with an f16 scale per token and head.  For every  */
+/* token t and head h, the D values x[t, h, :] (bf16):                       */
+/*   s = f16_rne(max_d |x| / 127)        (fp32 quotient, then binary16)      */
+/*   q = clamp(round_half_even(x / float(s)), -127, 127); q = 0 if s == 0     */
+/* (codes against the stored f16 scale: code * s is the cached value).      */
+/* Token t is written to cache row slots[t] (slots NULL: row t); a slot      */
+/* outside [0, cache_rows) skips the token.  Precondition: max |x| / 127     */
+/* below 65520 (a finite f16 scale; an infinite one gives zero codes).      */
+/* x: bf16 [T, Hk, D], token stride ldx >= Hk*D elements (heads contiguous); */
+/* q_cache: int8 [cache_rows, Hk, D], row stride ldq >= Hk*D;                */
+/* s_cache: f16 bits [cache_rows, Hk], row stride lds >= Hk.  No workspace.  */
+/* Requires D % 8 == 0, D <= 4096; x 16-byte aligned with ldx % 8 == 0,      */
+/* q_cache 8-byte aligned with ldq % 8 == 0, s_cache 2-byte aligned; without */
+/* slots cache_rows >= T.                                                    */
+/* ------------------------------------------------------------------------ */
+int kv_quant_i8(const uint16_t *x, int64_t T, int64_t Hk, int64_t D, int64_t ldx,
+                const int32_t *slots, int64_t cache_rows, int8_t *q_cache, int64_t ldq,
+                uint16_t *s_cache, int64_t lds, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Routed int8 MoE layer.                                                    */
 /* [ATOM] Changes, fused_moe_triton.py bullet: routing -> per-token int8     */
 /* quant -> gemm1 with fused gated SiLU over interleaved w13 -> per-token    */

@@ -70,6 +70,7 @@ _SIGS = {
     "mlp_w8a8_workspace_bytes": ([_i64, _i64, _i64, _i64], _sz),
     "mlp_w8a8_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
                          _sz, ctypes.POINTER(MlpDebug), _vp], _i32),
+    "kv_quant_i8": ([_vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp], _i32),
     "moe_w8a8_workspace_bytes": ([_i64, _i64, _i64, _i64, _i32], _sz),
     "moe_w8a8_forward": ([_vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _vp, _sz, ctypes.POINTER(MoeDebug), _vp], _i32),
@@ -285,6 +286,30 @@ def mlp_w8a8_packed(x, wgu_packed, sgu, wd_packed, sd, I: int, N: int,
                                  _ptr(wd_packed), _ptr(sd), N, _ptr(y), y.stride(0), _ptr(ws),
                                  wsb, dbg_p, _stream(dev)))
     return (y, dbg_t) if debug else y
+
+
+def kv_quant_i8(x, q_cache: torch.Tensor | None = None, s_cache: torch.Tensor | None = None,
+                slots: torch.Tensor | None = None):
+    """int8 KV-cache quant with an f16 scale per token and head.
+
+    ``x`` bf16 [T, Hk, D]; token t goes to cache row ``slots[t]`` (row t
+    without slots).  Returns (q_cache int8 [rows, Hk, D], s_cache f16
+    [rows, Hk])."""
+    _req(x, torch.bfloat16, "x")
+    T, Hk, D = x.shape
+    if x.stride(1) != D:
+        raise ValueError("x: heads must be contiguous within a token")
+    if q_cache is None:
+        q_cache = torch.zeros((T, Hk, D), dtype=torch.int8, device=x.device)
+    if s_cache is None:
+        s_cache = torch.zeros((q_cache.shape[0], Hk), dtype=torch.float16, device=x.device)
+    if slots is not None and slots.dtype != torch.int32:
+        raise TypeError("slots: expected int32")
+    _check("kv_quant_i8",
+           lib().kv_quant_i8(_ptr(x), T, Hk, D, x.stride(0), _ptr(slots), q_cache.shape[0],
+                             _ptr(q_cache), q_cache.stride(0), _ptr(s_cache), s_cache.stride(0),
+                             _stream(x.device)))
+    return q_cache, s_cache
 
 
 def moe_w8a8_workspace_bytes(T: int, H: int, E: int, I: int, topk: int) -> int:

@@ -326,6 +326,28 @@ int mlp_w8a8_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
   return e == hipSuccess ? W8A8_OK : hip_fail(e);
 }
 
+int kv_quant_i8(const uint16_t* x, int64_t T, int64_t Hk, int64_t D, int64_t ldx,
+                const int32_t* slots, int64_t cache_rows, int8_t* q_cache, int64_t ldq,
+                uint16_t* s_cache, int64_t lds, void* stream) {
+  if (T < 0 || Hk <= 0 || D <= 0 || cache_rows < 0 || ldx < Hk * D || ldq < Hk * D ||
+      lds < Hk)
+    return W8A8_INVALID_ARG;
+  if (D % 8 != 0 || D > 4096 || Hk > 65536 || T > INT32_MAX || T * Hk > ((int64_t)1 << 32))
+    return W8A8_UNSUPPORTED_SHAPE;
+  if (!slots && cache_rows < T) return W8A8_INVALID_ARG;
+  if (T == 0 || cache_rows == 0) return W8A8_OK;
+  if (!x || !q_cache || !s_cache) return W8A8_INVALID_ARG;
+  if (!al16(x) || ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(q_cache) & 7u) != 0 ||
+      ldq % 8 != 0 || (reinterpret_cast<uintptr_t>(s_cache) & 1u) != 0 ||
+      (slots && !al4(slots)))
+    return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  hipError_t e = launch_kv_quant_i8(x, T, Hk, D, ldx, slots, cache_rows, q_cache, ldq, s_cache,
+                                    lds, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
 size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int topk) {
   if (T <= 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0) return 0;
   return moe_workspace_bytes(T, H, E, I, topk);

@@ -112,6 +112,11 @@ struct MlpArgs {
 size_t mlp_workspace_bytes(int64_t M, int64_t K, int64_t I);
 hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream);
 
+// int8 KV-cache quantisation (f16 scale per token and head), D <= 4096.
+hipError_t launch_kv_quant_i8(const uint16_t* x, int64_t T, int64_t Hk, int64_t D, int64_t ldx,
+                              const int32_t* slots, int64_t cache_rows, int8_t* q, int64_t ldq,
+                              uint16_t* s, int64_t lds, hipStream_t stream);
+
 // Hadamard-domain variant.
 hipError_t launch_fwht128_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                 int64_t ldq, float* s, hipStream_t stream);
