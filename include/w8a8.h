@@ -145,6 +145,26 @@ int linear_w8a8_packed(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                        int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* linear_w8a8_packed for callers that cannot allocate device memory (code   */
+/* under HIP-graph capture, tight serving loops, harnesses that forbid       */
+/* allocation): the same kernels and results, but the activation codes and  */
+/* scales go to scratch memory the library itself holds -- a static device  */
+/* array of W8A8_NOALLOC_SCRATCH_BYTES (32 MiB) on every GPU it runs on,     */
+/* kept until the process ends -- instead of a caller workspace.  No         */
+/* allocation happens in the call.  Shapes whose                             */
+/* linear_w8a8_workspace_bytes(M, N, K) exceeds that size (e.g. 4096 tokens  */
+/* at K = 5120 fit, 4096 at K = 8704 do not) return W8A8_UNSUPPORTED_SHAPE   */
+/* and launch nothing.  Every call on one GPU shares that GPU's scratch: two */
+/* calls that can overlap on one GPU (different streams without ordering,   */
+/* different threads) race and give undefined results; calls ordered on one */
+/* stream are safe.  Other arguments and rules as linear_w8a8_packed.        */
+/* ------------------------------------------------------------------------ */
+#define W8A8_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int linear_w8a8_packed_noalloc(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                               const int8_t *qw_packed, const float *sw, int64_t N,
+                               uint16_t *y, int64_t ldy, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Dense W8A8 MLP block.  [ATOM] intro: A8W8 for all dense GEMMs (the 27B    */
 /* dense model of its "Performance" section); the order of its "Changes",    */
 /* fused_moe_triton.py bullet (gemm1 with the gated SiLU over interleaved    */

@@ -67,6 +67,8 @@ _SIGS = {
                                 _i32),
     "linear_w8a8_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp],
                            _i32),
+    "linear_w8a8_packed_noalloc": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp],
+                                   _i32),
     "mlp_w8a8_workspace_bytes": ([_i64, _i64, _i64, _i64], _sz),
     "mlp_w8a8_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp,
                          _sz, ctypes.POINTER(MlpDebug), _vp], _i32),
@@ -257,6 +259,21 @@ def linear_w8a8_packed(x, qw_packed, sw, N: int, y: torch.Tensor | None = None,
     _check("linear_w8a8_packed",
            lib().linear_w8a8_packed(_ptr(x), M, K, x.stride(0), _ptr(qw_packed), _ptr(sw), N,
                                     _ptr(y), y.stride(0), _ptr(ws), wsb, _stream(x.device)))
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def linear_w8a8_packed_noalloc(x, qw_packed, sw, N: int, y: torch.Tensor | None = None):
+    """linear_w8a8_packed with the library's own static scratch (no workspace)."""
+    _req(x, torch.bfloat16, "x")
+    M, K = x.shape
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _check("linear_w8a8_packed_noalloc",
+           lib().linear_w8a8_packed_noalloc(_ptr(x), M, K, x.stride(0), _ptr(qw_packed),
+                                            _ptr(sw), N, _ptr(y), y.stride(0),
+                                            _stream(x.device)))
     return y
 
 

@@ -41,6 +41,31 @@ int check_device() {
   return st == 1 ? W8A8_OK : W8A8_UNSUPPORTED_DEVICE;
 }
 
+// Scratch of linear_w8a8_packed_noalloc: device memory of the library itself,
+// one copy per GPU (each at its own address), held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it only
+// names the symbol): the per-device address comes from hipGetSymbolAddress,
+// taken once per device on the first call with that device current.
+constexpr size_t kNoallocScratchBytes = W8A8_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) int8_t scratch[kNoallocScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (check_device() ran before).
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (p == nullptr) return W8A8_HIP_ERROR;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return W8A8_OK;
+}
+
 }  // namespace
 
 int w8a8::device_cus() {
@@ -275,6 +300,22 @@ int linear_w8a8_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                        const int8_t* qw_packed, const float* sw, int64_t N, uint16_t* y,
                        int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   return linear_common(x, M, K, ldx, qw_packed, sw, N, K, true, y, ldy, ws, ws_bytes, stream);
+}
+
+int linear_w8a8_packed_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               const int8_t* qw_packed, const float* sw, int64_t N, uint16_t* y,
+                               int64_t ldy, void* stream) {
+  int r = check_gemm_shape(M, K, ldx, N, K, ldy);
+  if (r != W8A8_OK) return r;
+  if (M == 0) return W8A8_OK;
+  // the codes and scales linear_w8a8_packed keeps in its workspace must fit
+  // the static scratch
+  if (linear_w8a8_workspace_bytes(M, N, K) > kNoallocScratchBytes) return W8A8_UNSUPPORTED_SHAPE;
+  if ((r = check_device()) != W8A8_OK) return r;
+  void* ws = nullptr;
+  if ((r = noalloc_scratch(&ws)) != W8A8_OK) return r;
+  return linear_common(x, M, K, ldx, qw_packed, sw, N, K, true, y, ldy, ws,
+                       kNoallocScratchBytes, stream);
 }
 
 size_t mlp_w8a8_workspace_bytes(int64_t M, int64_t K, int64_t I, int64_t N) {
