@@ -349,6 +349,121 @@ def weight_prep_g256(W: np.ndarray):
     return qw, su8, s2
 
 
+def weight_prep_g128(W: np.ndarray):
+    """O16: rotated int8 weights with a bf16 scale per row per 128 of K.
+
+    "Qwen3.6-35B-A3B IQ8R - radiance container", Experts row and the recipe
+    (group=128 scale=bf16 transform=fwht128 clamp=sym).  s = bf16(amax/127)
+    per 128-block of the rotated row, codes against the stored bf16 scale.
+    Returns (qw int8 [N, K], s bf16 bits uint16 [N, K/128]).
+    """
+    W = np.ascontiguousarray(W, np.float32)
+    N, K = W.shape
+    assert K % 128 == 0
+    qw = np.empty((N, K), np.int8)
+    s = np.empty((N, K // 128), np.uint16)
+    _load().orc_weight_prep_g128(_p(W), _i64(N), _i64(K), _p(qw), _p(s))
+    return qw, s
+
+
+def gemm_g128(qa, sa, qw, s):
+    """O17: rotated-domain GEMM with a bf16 scale per row per 128 of K, fp32 out.
+
+    y = float(((sum over groups, in order, of acc_g * s_g) * sa) * 2^-7) in
+    fp64 (acc_g the exact int32 group sums)."""
+    qa = np.ascontiguousarray(qa, np.int8)
+    sa = np.ascontiguousarray(sa, np.float32)
+    qw = np.ascontiguousarray(qw, np.int8)
+    s = np.ascontiguousarray(s, np.uint16)
+    M, K = qa.shape
+    N = qw.shape[0]
+    y = np.empty((M, N), np.float32)
+    _load().orc_gemm_g128(_p(qa), _p(sa), _i64(M), _i64(K), _p(qw), _p(s), _i64(N), _p(y))
+    return y
+
+
+def rot_quant_rows(x: np.ndarray):
+    """O18: fwht128 of each 128-block of fp32 rows, then per-row int8 quant."""
+    x = np.ascontiguousarray(x, np.float32)
+    M, K = x.shape
+    q = np.empty((M, K), np.int8)
+    s = np.empty((M,), np.float32)
+    _load().orc_rot_quant_rows_f32(_p(x), _i64(M), _i64(K), _p(q), _p(s))
+    return q, s
+
+
+def moe_rot_forward(x_bf16, ids, w, w13, s13, w2, s2, shared=None, debug: bool = False):
+    """O19: routed int8 MoE with the experts on the rotated grid (g128 bf16).
+
+    "Qwen3.6-35B-A3B IQ8R - radiance container", Experts and Activations rows:
+    experts int8 on the rotated grid with a bf16 scale per row and 128 of K,
+    reading the trunk quantiser's codes; the routed order of the ATOM pull
+    request's fused_moe_triton.py bullet.  w13 [E, 2I, H] int8 with s13 bf16
+    [E, 2I, H/128]; w2 [E, H, I] with s2 [E, H, I/128]; ``shared`` fp32
+    [T, H] (the shared expert's output) is added to the fp32 combine.
+    """
+    x_bf16 = np.ascontiguousarray(x_bf16, np.uint16)
+    ids = np.ascontiguousarray(ids, np.int32)
+    w = np.ascontiguousarray(w, np.float32)
+    w13 = np.ascontiguousarray(w13, np.int8)
+    s13 = np.ascontiguousarray(s13, np.uint16)
+    w2 = np.ascontiguousarray(w2, np.int8)
+    s2 = np.ascontiguousarray(s2, np.uint16)
+    T, H = x_bf16.shape
+    k = ids.shape[1]
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    assert w2.shape == (E, H, I) and s13.shape == (E, I2, H // 128) and s2.shape == (E, H, I // 128)
+    sh = None if shared is None else np.ascontiguousarray(shared, np.float32)
+    out = np.empty((T, H), np.uint16)
+    dbg = None
+    if debug:
+        R = T * k
+        dbg = dict(qx=np.empty((T, H), np.int8), sx=np.empty((T,), np.float32),
+                   act=np.empty((R, I), np.float32), qa=np.empty((R, I), np.int8),
+                   sa2=np.empty((R,), np.float32), y2=np.empty((R, H), np.float32))
+    g = (lambda name: _p(dbg[name])) if debug else (lambda name: ctypes.c_void_p(0))
+    _load().orc_moe_rot_forward(_p(x_bf16), _p(ids), _p(w), _p(w13), _p(s13), _p(w2), _p(s2),
+                                _i64(T), _i64(H), _i64(E), _i64(I), _i64(k), _p(sh), _p(out),
+                                g("qx"), g("sx"), g("act"), g("qa"), g("sa2"), g("y2"))
+    return (out, dbg) if debug else out
+
+
+def shared_expert(x_bf16, wgu, su8, s2, wd, sd, debug: bool = False):
+    """O20: the shared expert in the Hadamard domain, fp32 out [T, H].
+
+    "Qwen3.6-35B-A3B IQ8R - radiance container", Experts row and recipe:
+    gate/up as the trunk's linears (g256: wgu [2Is, H] int8, su8 [2Is, H/256],
+    s2 bf16 [2Is], rows 2i = gate_i), down g128 bf16 (wd [H, Is], sd [H, Is/128]).
+    """
+    x_bf16 = np.ascontiguousarray(x_bf16, np.uint16)
+    T, H = x_bf16.shape
+    I2 = wgu.shape[0]
+    Is = I2 // 2
+    args = [np.ascontiguousarray(a, dt) for a, dt in ((wgu, np.int8), (su8, np.uint8),
+                                                     (s2, np.uint16), (wd, np.int8),
+                                                     (sd, np.uint16))]
+    assert args[0].shape == (I2, H) and args[3].shape == (H, Is)
+    y = np.empty((T, H), np.float32)
+    act = np.empty((T, Is), np.float32) if debug else None
+    _load().orc_shared_expert(_p(x_bf16), _i64(T), _i64(H), _i64(Is), *[_p(a) for a in args],
+                              _p(y), _p(act))
+    return (y, act) if debug else y
+
+
+def router_gate_bf16(x_bf16, wg_bf16) -> np.ndarray:
+    """O21: router logits from the bf16 gate: fp64 sums of exact products,
+    rounded once to fp32.  "[gfx1151] Online INT8 W8A8 ..." (ATOM pull
+    request), intro: the router gate stays BF16."""
+    x_bf16 = np.ascontiguousarray(x_bf16, np.uint16)
+    wg_bf16 = np.ascontiguousarray(wg_bf16, np.uint16)
+    T, H = x_bf16.shape
+    E = wg_bf16.shape[0]
+    out = np.empty((T, E), np.float32)
+    _load().orc_router_gate_bf16(_p(x_bf16), _p(wg_bf16), _i64(T), _i64(H), _i64(E), _p(out))
+    return out
+
+
 def gemm_g256(qa, sa, qw, su8, s2, return_tsum: bool = False):
     """O13: rotated-domain GEMM with per-256 u8 group scales and a bf16 row scale.
 

@@ -617,6 +617,235 @@ EXPORT void orc_weight_prep_g256(const float *W, int64_t N, int64_t K, int8_t *q
 }
 
 /* ------------------------------------------------------------------------ */
+/* O16: rotated weight preparation with a bf16 scale per row per 128 of K    */
+/* (the routed experts and the shared expert's down projection).  [IQ8R]     */
+/* "Experts" row (int8 on the same rotated grid with a bf16 scale per row    */
+/* and 128 of K) and the recipe lines ffn_gate_up_exps / ffn_down_exps /     */
+/* ffn_down_shexp (codes=i8 group=128 scale=bf16 transform=fwht128 clamp=sym).*/
+/* Per row n of W [N, K] (fp32): w' = fwht128 of each 128-block (a group is   */
+/* one block); s_g = bf16(max |w'| over the group / 127); code =              */
+/* clamp(round(w' / float(s_g)), -127, 127), 0 where s_g is 0.  The codes are  */
+/* formed against the stored bf16 scale.                                      */
+/* ------------------------------------------------------------------------ */
+EXPORT void orc_weight_prep_g128(const float *W, int64_t N, int64_t K, int8_t *qw, uint16_t *s)
+{
+    const int64_t G = K / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+        memcpy(row, W + n * K, (size_t)K * sizeof(float));
+        for (int64_t b = 0; b < K; b += 128) fwht128_block(row + b);
+        for (int64_t g = 0; g < G; g++) {
+            float a = 0.0f;
+            for (int64_t k = g * 128; k < (g + 1) * 128; k++) {
+                float v = fabsf(row[k]);
+                if (v > a) a = v;
+            }
+            uint16_t sb = f32_to_bf16(a / 127.0f);
+            float sf = bf16_to_f32(sb);
+            s[n * G + g] = sb;
+            for (int64_t k = g * 128; k < (g + 1) * 128; k++) {
+                int8_t c = 0;
+                if (sf != 0.0f) {
+                    float r = nearbyintf(row[k] / sf);
+                    if (r > 127.0f) r = 127.0f;
+                    if (r < -127.0f) r = -127.0f;
+                    c = (int8_t)r;
+                }
+                qw[n * K + k] = c;
+            }
+        }
+        free(row);
+    }
+}
+
+/* O17: g128 GEMM, one output: the exact int32 sum of each 128-group times   */
+/* that group's bf16 scale, summed in fp64 in group order, then times the    */
+/* activation row scale and 2^-7 (undoing <Hx, Hw> = 128 <x, w>), in fp64,    */
+/* rounded once to fp32.                                                      */
+static float g128_one(const int8_t *a, const int8_t *wrow, const uint16_t *srow, int64_t K,
+                      float sa)
+{
+    double t = 0.0;
+    for (int64_t g = 0; g < K / 128; g++) {
+        int64_t accg = dot_i8(a + g * 128, wrow + g * 128, 128);
+        t = t + (double)accg * (double)bf16_to_f32(srow[g]);
+    }
+    t = t * (double)sa;
+    t = t * 0.0078125;
+    return (float)t;
+}
+
+EXPORT void orc_gemm_g128(const int8_t *qa, const float *sa, int64_t M, int64_t K,
+                          const int8_t *qw, const uint16_t *s, int64_t N, float *y)
+{
+    const int64_t G = K / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++)
+            y[m * N + n] = g128_one(qa + m * K, qw + n * K, s + n * G, K, sa[m]);
+}
+
+/* O18: rotated requant of an fp32 row: fwht128 of each 128-block, then the   */
+/* per-row quant O1 over the whole rotated row.  [IQ8R] "Activations" row     */
+/* (int8 activations under the same rotation): the down projection's input   */
+/* lives on the rotated grid of its weights.                                  */
+static void rot_quant_row_f32(const float *v, int64_t K, int8_t *q, float *s_out)
+{
+    float *row = (float *)malloc((size_t)K * sizeof(float));
+    memcpy(row, v, (size_t)K * sizeof(float));
+    for (int64_t b = 0; b < K; b += 128) fwht128_block(row + b);
+    quant_row_f32(row, K, q, s_out);
+    free(row);
+}
+
+EXPORT void orc_rot_quant_rows_f32(const float *x, int64_t M, int64_t K, int8_t *q, float *s)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) rot_quant_row_f32(x + m * K, K, q + m * K, s + m);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O19: routed experts in the Hadamard domain.  [IQ8R] "Experts" and         */
+/* "Activations" rows: the 256 routed experts int8 on the rotated grid with a */
+/* bf16 scale per row and 128 of K, reading the codes the trunk's quantisers  */
+/* write; with the [ATOM] order (routing given) -> quant -> gemm1 with the     */
+/* gated SiLU over interleaved w13 -> per-token requant -> gemm2 -> combine:  */
+/*   qx, sx = fwht128 + per-token quant of x (O11 + O1, the trunk's codes);    */
+/*   per pair r = t*k + j, e = ids[t,j]:                                       */
+/*     h[c] = g128(qx[t], w13[e,c], s13[e,c], sx[t])   (O17), c < 2I;          */
+/*     act_i = silu(h[2i]) * h[2i+1];                                         */
+/*     qa, sa2 = fwht128 + per-row quant of act (O18);                        */
+/*     y2[c] = g128(qa, w2[e,c], s2[e,c], sa2), c < H;                        */
+/*   out[t,h] = bf16( (sum_j w[t,j] * y2[(t,j),h], fp32, slot order)          */
+/*                    + shared[t,h] )   (shared: the shared expert, O20, or    */
+/*                                       no term when NULL)                   */
+/* Layouts: w13 [E, 2I, H] int8, s13 bf16 [E, 2I, H/128]; w2 [E, H, I],        */
+/* s2 bf16 [E, H, I/128]; shared fp32 [T, H].  Intermediates as O6..O10        */
+/* (NULL to skip): qx, sx, act, qa, sa2, y2.                                  */
+/* ------------------------------------------------------------------------ */
+EXPORT void orc_moe_rot_forward(const uint16_t *x, const int32_t *ids, const float *w,
+                                const int8_t *w13, const uint16_t *s13, const int8_t *w2,
+                                const uint16_t *s2, int64_t T, int64_t H, int64_t E, int64_t I,
+                                int64_t k, const float *shared, uint16_t *out, int8_t *qx_out,
+                                float *sx_out, float *act_out, int8_t *qa_out, float *sa2_out,
+                                float *y2_out)
+{
+    (void)E;
+    const int64_t I2 = 2 * I, GH = H / 128, GI = I / 128;
+    int8_t *qx = (int8_t *)malloc((size_t)(T * H));
+    float *sx = (float *)malloc((size_t)T * sizeof(float));
+    float *y2 = (float *)malloc((size_t)(T * k * H) * sizeof(float));
+    orc_fwht128_quant(x, T, H, H, qx, H, sx);
+
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t r = 0; r < T * k; r++) {
+        int64_t t = r / k;
+        int64_t e = ids[r];
+        float *h = (float *)malloc((size_t)I2 * sizeof(float));
+        float *act = (float *)malloc((size_t)I * sizeof(float));
+        int8_t *qa = (int8_t *)malloc((size_t)I);
+        float sa2;
+        for (int64_t c = 0; c < I2; c++)
+            h[c] = g128_one(qx + t * H, w13 + (e * I2 + c) * H, s13 + (e * I2 + c) * GH, H,
+                            sx[t]);
+        for (int64_t i = 0; i < I; i++) act[i] = silu_times_up(h[2 * i], h[2 * i + 1]);
+        if (act_out) memcpy(act_out + r * I, act, (size_t)I * sizeof(float));
+        rot_quant_row_f32(act, I, qa, &sa2);
+        if (qa_out) memcpy(qa_out + r * I, qa, (size_t)I);
+        if (sa2_out) sa2_out[r] = sa2;
+        for (int64_t c = 0; c < H; c++)
+            y2[r * H + c] = g128_one(qa, w2 + (e * H + c) * I, s2 + (e * H + c) * GI, I, sa2);
+        free(h);
+        free(act);
+        free(qa);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t c = 0; c < H; c++) {
+            float acc = 0.0f;
+            for (int64_t j = 0; j < k; j++) {
+                float term = w[t * k + j] * y2[(t * k + j) * H + c];
+                acc = acc + term;
+            }
+            if (shared) acc = acc + shared[t * H + c];
+            out[t * H + c] = f32_to_bf16(acc);
+        }
+    if (qx_out) memcpy(qx_out, qx, (size_t)(T * H));
+    if (sx_out) memcpy(sx_out, sx, (size_t)T * sizeof(float));
+    if (y2_out) memcpy(y2_out, y2, (size_t)(T * k * H) * sizeof(float));
+    free(qx);
+    free(sx);
+    free(y2);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O20: the shared expert in the Hadamard domain.  [IQ8R] "Experts" row: the  */
+/* shared expert like the routed ones, its gate/up projection as the trunk's  */
+/* linears; recipe ffn_gate_up_shexp (group=256 scale=u8 scale2=bf16, as O12)  */
+/* and ffn_down_shexp (group=128 scale=bf16, as O16):                          */
+/*   qx, sx = fwht128 + per-token quant of x (the trunk's codes);              */
+/*   h[c] = float( sum_g su8[c,g] acc_g * sx * s2[c] * 2^-7 )  (O13 in fp64,    */
+/*          rounded to fp32 instead of bf16), c < 2Is, rows 2i = gate_i;      */
+/*   act_i = silu(h[2i]) * h[2i+1]; qa, sa = O18(act);                        */
+/*   y[t,n] = g128(qa, wd[n], sd[n], sa)   (fp32 [T, H]).                      */
+/* ------------------------------------------------------------------------ */
+EXPORT void orc_shared_expert(const uint16_t *x, int64_t T, int64_t H, int64_t Is,
+                              const int8_t *wgu, const uint8_t *su8, const uint16_t *s2,
+                              const int8_t *wd, const uint16_t *sd, float *y, float *act_out)
+{
+    const int64_t I2 = 2 * Is, G = H / 256, GI = Is / 128;
+    int8_t *qx = (int8_t *)malloc((size_t)(T * H));
+    float *sx = (float *)malloc((size_t)T * sizeof(float));
+    orc_fwht128_quant(x, T, H, H, qx, H, sx);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        float *h = (float *)malloc((size_t)I2 * sizeof(float));
+        float *act = (float *)malloc((size_t)Is * sizeof(float));
+        int8_t *qa = (int8_t *)malloc((size_t)Is);
+        float sa;
+        for (int64_t c = 0; c < I2; c++) {
+            int64_t tsum = 0;
+            for (int64_t g = 0; g < G; g++)
+                tsum += (int64_t)su8[c * G + g] *
+                        dot_i8(qx + t * H + g * 256, wgu + c * H + g * 256, 256);
+            double v = (double)tsum * (double)sx[t];
+            v = v * (double)bf16_to_f32(s2[c]);
+            v = v * 0.0078125;
+            h[c] = (float)v;
+        }
+        for (int64_t i = 0; i < Is; i++) act[i] = silu_times_up(h[2 * i], h[2 * i + 1]);
+        if (act_out) memcpy(act_out + t * Is, act, (size_t)Is * sizeof(float));
+        rot_quant_row_f32(act, Is, qa, &sa);
+        for (int64_t n = 0; n < H; n++) y[t * H + n] = g128_one(qa, wd + n * Is, sd + n * GI, Is, sa);
+        free(h);
+        free(act);
+        free(qa);
+    }
+    free(qx);
+    free(sx);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O21: the router gate in bf16.  [ATOM] intro (precision split): the router  */
+/* gate stays BF16.  logits[t,e] = sum_h x[t,h] * wg[e,h] with bf16 operands; */
+/* the products are exact in fp64 and are summed in fp64 in index order,      */
+/* then rounded once to fp32.                                                 */
+/* ------------------------------------------------------------------------ */
+EXPORT void orc_router_gate_bf16(const uint16_t *x, const uint16_t *wg, int64_t T, int64_t H,
+                                 int64_t E, float *logits)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t e = 0; e < E; e++) {
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; h++)
+                acc = acc + (double)bf16_to_f32(x[t * H + h]) * (double)bf16_to_f32(wg[e * H + h]);
+            logits[t * E + e] = (float)acc;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* O13: g256 GEMM in the rotated domain.  Per output (m, n):                  */
 /*   acc_g = sum over the 256 k of group g of qa[m,k] * qw[n,k]  (exact);     */
 /*   T = sum_g su8[n,g] * acc_g                                  (int64);     */

@@ -24,7 +24,8 @@ def _gpu():
     mq.lib()
 
 
-@pytest.mark.parametrize("M,K", [(1, 2048), (256, 2048), (7, 128), (3, 16384), (33, 640)])
+@pytest.mark.parametrize("M,K", [(1, 2048), (256, 2048), (7, 128), (3, 16384), (33, 640),
+                                 (40, 4096), (17, 4224), (21, 384)])
 def test_fwht128_quant_bit_exact(orc, M, K):
     say(f"fwht128_quant M={M} K={K}")
     x = synth.activations((50, M, K), M, K, max(1, K // 100), 10.0, heavy_tail=True)
@@ -115,6 +116,24 @@ def test_linear_g256_single_token(orc, K, N, zero):
     np.testing.assert_array_equal(bf16_host(y), orc.gemm_g256(qa, sa, qw, su8, s2))
     if zero:
         assert not bf16_host(y).any()
+
+
+@pytest.mark.parametrize("M,K,N", [(33, 1024, 128), (64, 2048, 256), (100, 2048, 1152),
+                                   (200, 1024, 384), (256, 2048, 8192)])
+def test_linear_g256_mid_batches(orc, M, K, N):
+    # 33 to 256 rows through the fused entry (tile-layout codes, the g256 tile
+    # kernel), ragged last row tile, an all-zero row
+    say(f"linear g256 mid batches M={M} K={K} N={N}")
+    W = synth.weights((58, K, N), N, K)
+    qw, su8, s2 = orc.weight_prep_g256(W)
+    x = synth.activations((59, M, K), M, K, max(1, K // 100), 10.0, heavy_tail=True)
+    x[M // 2] = 0
+    qa, sa = orc.fwht128_quant(x)
+    y = mq.linear_w8a8_g256_packed(bf16_dev(x), mq.pack_weights(dev(qw)), dev(su8),
+                                   dev(s2.view(np.int16)).view(torch.bfloat16))
+    got = bf16_host(y)
+    np.testing.assert_array_equal(got, orc.gemm_g256(qa, sa, qw, su8, s2))
+    assert not got[M // 2].any()
 
 
 def test_linear_g256_ragged_stride(orc):
