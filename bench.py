@@ -241,6 +241,7 @@ def traffic_from_counters(fetch_dir: str, write_dir: str, out_name: str) -> None
         out[key + "_scale"] = scale
         per = {}
         for n, v in rows:
+            n = n[5:] if n.startswith("void ") else n
             if "neg" in n or not n.startswith("w8a8::"):
                 continue
             name = n.split("(")[0]
