@@ -52,7 +52,7 @@ I8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA (5.0 POPS)
 MALL_BYTES = 256 << 20     # Infinity Cache
 PROBE_ELEMS = 1 << 28      # --probe-copy: 1 GiB of fp32 read and 1 GiB written
 DECODE_KERNEL = "k_gemm_skinny"
-CASE_GROUPS = ("decode", "small", "prefill", "moe", "hadamard", "mlp", "kv")
+CASE_GROUPS = ("decode", "small", "prefill", "moe", "rot_moe", "hadamard", "mlp", "kv")
 
 
 def parse():
@@ -447,6 +447,8 @@ def main():
         cases.update(prefill_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes))
     if "moe" in groups:
         cases.update(moe_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes))
+    if "rot_moe" in groups:
+        cases.update(rot_moe_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes))
     if "hadamard" in groups:
         cases.update(hadamard_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes))
     if "mlp" in groups:
@@ -699,6 +701,109 @@ def moe_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes):
             "weight_copies": len(copies),
         }
     del copies
+    return res
+
+
+def rot_moe_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes):
+    """The MoE layer in the Hadamard domain at the routed-MoE shapes (256
+    experts, top-8, hidden 2048, expert and shared intermediate 512): the bf16
+    router gate, the shared expert (g256 gate/up, g128 down) and the routed
+    experts on the rotated grid (g128 bf16 scales) with the shared term in the
+    combine.  Each piece is timed alone and the three in sequence ("layer").
+    HBM-graded on the weights the call touches plus activations in and out."""
+    cfg = synth.moe(1)
+    E, H, I, k = cfg["E"], cfg["H"], cfg["I"], cfg["k"]
+    Is = I
+    w13 = torch.empty((E, 2 * I, H), dtype=torch.int8, device=dev)
+    s13 = torch.empty((E, 2 * I, H // 128), dtype=torch.bfloat16, device=dev)
+    w2 = torch.empty((E, H, I), dtype=torch.int8, device=dev)
+    s2 = torch.empty((E, H, I // 128), dtype=torch.bfloat16, device=dev)
+    wh = hashlib.sha256()
+    for e in range(E):  # rotated weight preparation on the GPU (untimed)
+        ah = synth.expert_weights(cfg["wkey"], e, 2 * I, H, synth.T_W)
+        bh = synth.expert_weights(cfg["wkey"], e, H, I, synth.T_W2)
+        wh.update(memoryview(ah).cast("B"))
+        wh.update(memoryview(bh).cast("B"))
+        w13[e], s13[e] = mq.fwht128_weight_prep_g128(torch.from_numpy(ah).to(dev))
+        w2[e], s2[e] = mq.fwht128_weight_prep_g128(torch.from_numpy(bh).to(dev))
+    w13, w2 = mq.pack_moe_weights(w13, w2)
+    gh = synth.weights((101, 0), 2 * Is, H)
+    dh = synth.weights((101, 0), H, Is, tensor_id=synth.T_W2)
+    rh = synth.to_bf16_bits(synth.weights((101, 1), E, H))
+    wh.update(memoryview(gh).cast("B"))
+    wh.update(memoryview(dh).cast("B"))
+    wh.update(memoryview(rh).cast("B"))
+    hashes["rot_moe_weights_fp32"] = wh.hexdigest()
+    qgu, su8, sgu = mq.fwht128_weight_prep_g256(torch.from_numpy(gh).to(dev))
+    qd, sd = mq.fwht128_weight_prep_g128(torch.from_numpy(dh).to(dev))
+    shared_w = (mq.pack_weights(qgu), su8, sgu, mq.pack_weights(qd), sd)
+    wg = bf16_dev(rh)
+    copies = [(w13, s13, w2, s2), (w13.clone(), s13.clone(), w2.clone(), s2.clone())]
+    expert_bytes = 2 * I * H + H * I + 2 * (2 * I * H // 128 + H * I // 128)
+    shared_bytes = 2 * Is * H + 2 * Is * H // 256 + 4 * Is + H * Is + 2 * H * Is // 128
+    router_bytes = E * H * 2
+    res = {}
+    for T, nsets, it in ((1, 64, 64), (64, 4, 20), (2048, 2, 10)):
+        c = synth.moe(T)
+        ws = torch.empty(mq.moe_w8a8_workspace_bytes(T, H, E, I, k), dtype=torch.uint8,
+                         device=dev)
+        wss = torch.empty(mq.shared_expert_w8a8_rot_workspace_bytes(T, H, Is),
+                          dtype=torch.uint8, device=dev)
+        sets = []
+        ih = hashlib.sha256()
+        for r in range(nsets):
+            key = (*c["xkey"], 7) if r == 0 else (*c["xkey"], 7, r)
+            xh = synth.activations(key, T, H, 0, 1.0)
+            ih.update(memoryview(xh).cast("B"))
+            sets.append(dict(x=bf16_dev(xh),
+                             logits=torch.empty((T, E), dtype=torch.float32, device=dev),
+                             ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+                             wt=torch.empty((T, k), dtype=torch.float32, device=dev),
+                             y=torch.empty((T, H), dtype=torch.float32, device=dev),
+                             out=torch.empty((T, H), dtype=torch.bfloat16, device=dev)))
+        hashes[f"rot_moe_T{T}_inputs"] = ih.hexdigest()
+
+        def router(i):
+            st = sets[i % nsets]
+            mq.router_gate_bf16(st["x"], wg, logits=st["logits"])
+
+        def shared(i):
+            st = sets[i % nsets]
+            mq.shared_expert_w8a8_rot(st["x"], *shared_w, y=st["y"], ws=wss)
+
+        def routed(i):
+            st = sets[i % nsets]
+            a13, b13, a2, b2 = copies[i % len(copies)]
+            mq.moe_w8a8_rot_forward(st["x"], st["logits"], a13, b13, a2, b2, k,
+                                    shared=st["y"], topk_ids=st["ids"], topk_w=st["wt"],
+                                    out=st["out"], ws=ws)
+
+        def layer(i):
+            router(i)
+            shared(i)
+            routed(i)
+
+        for r in range(nsets):  # every set through the layer once (untimed)
+            layer(r)
+        torch.cuda.synchronize()
+        touched = sum(int(torch.unique(st["ids"]).numel()) for st in sets) / nsets
+        io = T * H * 2 + T * H * 2
+        parts = {"router": (router, router_bytes + T * H * 2 + T * E * 4),
+                 "shared": (shared, shared_bytes + T * H * 2 + T * H * 4),
+                 "routed": (routed, touched * expert_bytes + io + T * H * 4 + T * E * 4),
+                 "layer": (layer, touched * expert_bytes + shared_bytes + router_bytes + io)}
+        for name, (fn, nbytes) in parts.items():
+            _, each = timer.run(fn, it, groups=min(it, 8))
+            t = pct(each, 50)
+            r = {**timer.stats_us(each), "alg_bytes": int(nbytes),
+                 "gbs": round(nbytes / (t * 1e-3) / 1e9, 1),
+                 "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if name in ("routed", "layer"):
+                r["tokens_per_s"] = round(T / (t * 1e-3), 1)
+                r["experts_touched"] = round(touched, 1)
+            res[f"rot_moe_T{T}_{name}"] = r
+    del copies
+    torch.cuda.empty_cache()
     return res
 
 

@@ -337,6 +337,99 @@ int linear_w8a8_g256_packed(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
                             int64_t N, uint16_t *y, int64_t ldy, void *ws, size_t ws_bytes,
                             void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* Rotated weight preparation with a bf16 scale per row per 128 of K (done   */
+/* once, at load; the routed experts and the shared expert's down            */
+/* projection).  [IQ8R] Experts row and the recipe lines for the expert      */
+/* gate/up, expert down and shared down tensors (i8 codes, group 128, bf16   */
+/* scale, fwht128, symmetric clamp).  Per row n of W (fp32 [N, K],           */
+/* contiguous), per 128-block g (one group):                                 */
+/*   w' = fwht128 of the block (as fwht128_quant);                           */
+/*   s[n,g] = bf16_rne(max |w'| / 127);                                      */
+/*   qw[n,k] = clamp(round_half_even(w' / float(s[n,g])), -127, 127), and 0  */
+/*   where s[n,g] is 0 (the codes are taken against the stored bf16 scale).  */
+/* qw: int8 [N, K] row-major (pack it with w8a8_pack_weights for the GEMMs); */
+/* s: bf16 [N, K/128].  Requires K % 128 == 0, K <= 16384.                   */
+/* ------------------------------------------------------------------------ */
+int fwht128_weight_prep_g128(const float *W, int64_t N, int64_t K, int8_t *qw, uint16_t *s,
+                             void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* The MoE router gate in bf16.  [ATOM] intro: the precision split keeps the */
+/* router gate in BF16 (the experts run A8W8).                               */
+/*   logits[t,e] = sum_h x[t,h] * wg[e,h]  (bf16 operands, fp32 accumulate,  */
+/*   fixed order: repeated calls give identical bits).                       */
+/* x: bf16 [T, H] (ldx, multiple of 8, 16-byte aligned rows); wg: bf16       */
+/* [E, H] contiguous; logits: fp32 [T, E] (ldl >= E).  Requires H % 32 == 0, */
+/* H <= 16384, E % 16 == 0, E <= 4096, T <= 2^22.  The result differs from   */
+/* the exact sum by at most the fp32 summation bound.                        */
+/* ------------------------------------------------------------------------ */
+int router_gate_bf16(const uint16_t *x, int64_t T, int64_t H, int64_t ldx, const uint16_t *wg,
+                     int64_t E, float *logits, int64_t ldl, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Routed MoE layer in the Hadamard domain.  [IQ8R] Experts row (the routed  */
+/* experts int8 on the rotated grid with a bf16 scale per row and 128 of K)  */
+/* and Activations row (the experts read the rotated codes the trunk's       */
+/* quantisers write); the routed order of [ATOM] Changes, fused_moe_triton.py */
+/* bullet.  Routing as moe_w8a8_forward (logits NULL: topk_ids/topk_w are    */
+/* inputs).  Then, with g128(a, w, s, sa) = float( (sum over 128-groups g,   */
+/* in order, of double(acc_g) * double(s_g)) * sa * 2^-7 ) in fp64 (acc_g    */
+/* the exact int32 group sum; 2^-7 undoes <Hx, Hw> = 128 <x, w>):            */
+/*   qx, sx = fwht128 + per-token quant of x (as fwht128_quant);             */
+/*   per pair r = t*k + j, e = topk_ids[t,j]:                                */
+/*     h[c]   = g128(qx[t], w13[e,c], s13[e,c], sx[t]),  c < 2I              */
+/*     act[i] = silu(h[2i]) * h[2i+1]    (silu in fp64, rounded to fp32)     */
+/*     qa, sa2 = fwht128 of each 128-block of act, then per-row quant        */
+/*     y2[c]  = g128(qa, w2[e,c], s2[e,c], sa2),  c < H                      */
+/*   out[t,c] = bf16_rne( (sum_j topk_w[t,j] * y2[(t,j),c], fp32, j order)    */
+/*                        + shared[t,c] )    (no shared term when NULL)      */
+/* x: bf16 [T, H] contiguous; w13_packed: the prepared codes (as             */
+/* fwht128_weight_prep_g128) of [E, 2I, H] packed as one [E*2I, H] matrix;   */
+/* s13: bf16 [E, 2I, H/128]; w2_packed: [E, H, I] packed as [E*H, I]; s2:    */
+/* bf16 [E, H, I/128]; shared: fp32 [T, H] or NULL (the shared expert's      */
+/* output, shared_expert_w8a8_rot_packed); out: bf16 [T, H].  Workspace:     */
+/* moe_w8a8_workspace_bytes(T, H, E, I, topk).  dbg: qx, sx, act, qa, sa2    */
+/* are written (acc1, acc2 are not).  Requires H % 256 == 0, H <= 4096,      */
+/* I % 128 == 0, I <= 2048, 1 <= k <= 16, k <= E <= 1024, T*k <= 2^24.        */
+/* ------------------------------------------------------------------------ */
+int moe_w8a8_rot_forward_packed(const uint16_t *x, const float *logits, int64_t T, int64_t H,
+                                int64_t E, int64_t I, int topk, const int8_t *w13_packed,
+                                const uint16_t *s13, const int8_t *w2_packed,
+                                const uint16_t *s2, const float *shared, int32_t *topk_ids,
+                                float *topk_w, uint16_t *out, void *ws, size_t ws_bytes,
+                                const moe_w8a8_debug *dbg, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* The shared expert in the Hadamard domain.  [IQ8R] Experts row: the shared */
+/* expert like the routed ones, its gate/up projection as the trunk's        */
+/* linears (g256 u8 under a bf16 row scale) and its down projection g128.    */
+/*   qx, sx = fwht128 + per-token quant of x;                                */
+/*   h[c] = float( (sum_g su8[c,g] * acc_g, exact) * sx * s2[c] * 2^-7 )     */
+/*          (fp64; 256-groups), c < 2Is, rows 2i = gate_i, 2i+1 = up_i;      */
+/*   act_i = silu(h[2i]) * h[2i+1]; qa, sa = fwht128 + per-row quant of act; */
+/*   y[t,n] = g128(qa, wd[n], sd[n], sa)   (fp32, as above).                 */
+/* x: bf16 [T, H] contiguous; wgu_packed: prepared codes (as                 */
+/* fwht128_weight_prep_g256) of [2Is, H], packed; su8: uint8 [2Is, H/256];   */
+/* s2: bf16 [2Is]; wd_packed: prepared codes (as fwht128_weight_prep_g128)   */
+/* of [H, Is], packed; sd: bf16 [H, Is/128]; y: fp32 [T, H].  Requires       */
+/* H % 256 == 0, H <= 4096, Is % 128 == 0, Is <= 2048, T <= 2^24.            */
+/* dbg (nullable; each member nullable): act fp32 [T, Is], qa int8 [T, Is],  */
+/* sa fp32 [T].                                                              */
+/* ------------------------------------------------------------------------ */
+typedef struct shared_expert_debug {
+    float *act;  /* [T, Is] */
+    int8_t *qa;  /* [T, Is] */
+    float *sa;   /* [T] */
+} shared_expert_debug;
+
+size_t shared_expert_w8a8_rot_workspace_bytes(int64_t T, int64_t H, int64_t Is);
+int shared_expert_w8a8_rot_packed(const uint16_t *x, int64_t T, int64_t H, int64_t Is,
+                                  const int8_t *wgu_packed, const uint8_t *su8,
+                                  const uint16_t *s2, const int8_t *wd_packed,
+                                  const uint16_t *sd, float *y, void *ws, size_t ws_bytes,
+                                  const shared_expert_debug *dbg, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

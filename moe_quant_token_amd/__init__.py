@@ -47,6 +47,10 @@ class MlpDebug(ctypes.Structure):
     _fields_ = [("act", _vp), ("qa", _vp), ("sa", _vp)]
 
 
+class SharedDebug(ctypes.Structure):
+    _fields_ = [("act", _vp), ("qa", _vp), ("sa", _vp)]
+
+
 _SIGS = {
     "w8a8_status_string": ([_i32], ctypes.c_char_p),
     "w8a8_last_hip_error": ([], _i32),
@@ -88,6 +92,14 @@ _SIGS = {
                                _vp], _i32),
     "gemm_w8a8_g256": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp],
                        _i32),
+    "fwht128_weight_prep_g128": ([_vp, _i64, _i64, _vp, _vp, _vp], _i32),
+    "router_gate_bf16": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp], _i32),
+    "moe_w8a8_rot_forward_packed": ([_vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
+                                     _vp, _vp, _vp, _vp, _vp, _sz, ctypes.POINTER(MoeDebug),
+                                     _vp], _i32),
+    "shared_expert_w8a8_rot_workspace_bytes": ([_i64, _i64, _i64], _sz),
+    "shared_expert_w8a8_rot_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _sz, ctypes.POINTER(SharedDebug), _vp], _i32),
 }
 
 
@@ -445,3 +457,117 @@ def linear_w8a8_g256_packed(x, qw_packed, su8, s2, y: torch.Tensor | None = None
                                          _ptr(s2), N, _ptr(y), y.stride(0), _ptr(ws), wsb,
                                          _stream(x.device)))
     return y
+
+
+def fwht128_weight_prep_g128(W):
+    """Rotated int8 weights with a bf16 scale per row per 128 of K.
+
+    Returns (qw int8 [N, K] row-major, s bf16 [N, K/128])."""
+    _req(W, torch.float32, "W")
+    W = W.contiguous()
+    N, K = W.shape
+    qw = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    s = torch.empty((N, K // 128), dtype=torch.bfloat16, device=W.device)
+    _check("fwht128_weight_prep_g128",
+           lib().fwht128_weight_prep_g128(_ptr(W), N, K, _ptr(qw), _ptr(s), _stream(W.device)))
+    return qw, s
+
+
+def router_gate_bf16(x, wg, logits: torch.Tensor | None = None):
+    """fp32 router logits [T, E] = x [T, H] . wg [E, H]^T, bf16 operands."""
+    _req(x, torch.bfloat16, "x")
+    _req(wg, torch.bfloat16, "wg")
+    T, H = x.shape
+    E = wg.shape[0]
+    if not wg.is_contiguous():
+        raise ValueError("wg: expected a contiguous [E, H] tensor")
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check("router_gate_bf16",
+           lib().router_gate_bf16(_ptr(x), T, H, x.stride(0), _ptr(wg), E, _ptr(logits),
+                                  logits.stride(0), _stream(x.device)))
+    return logits
+
+
+def moe_w8a8_rot_forward(x, logits, w13_packed, s13, w2_packed, s2, topk: int, shared=None,
+                         topk_ids=None, topk_w=None, out=None, ws=None, debug: bool = False):
+    """Routed MoE layer in the Hadamard domain (experts with bf16 scales per 128 of K).
+
+    ``w13_packed`` [E, 2I, H] and ``w2_packed`` [E, H, I] are prepared codes
+    (``fwht128_weight_prep_g128``) packed with ``pack_moe_weights``; ``s13``
+    bf16 [E, 2I, H/128], ``s2`` bf16 [E, H, I/128]; ``shared`` fp32 [T, H]
+    (the shared expert's output) or None.  Returns out, topk_ids, topk_w
+    (and the intermediates qx, sx, act, qa, sa2 with ``debug``)."""
+    _req(x, torch.bfloat16, "x")
+    _req(s13, torch.bfloat16, "s13")
+    _req(s2, torch.bfloat16, "s2")
+    if not x.is_contiguous():
+        raise ValueError("x: expected a contiguous [T, H] tensor")
+    T, H = x.shape
+    E, I2, _ = w13_packed.shape
+    I = I2 // 2
+    dev = x.device
+    if shared is not None:
+        _req(shared, torch.float32, "shared")
+        if not shared.is_contiguous() or tuple(shared.shape) != (T, H):
+            raise ValueError("shared: expected a contiguous fp32 [T, H] tensor")
+    if topk_ids is None:
+        topk_ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    ws, wsb = _workspace(moe_w8a8_workspace_bytes(T, H, E, I, topk), dev, ws)
+    dbg_t = None
+    dbg_p = None
+    if debug:
+        R = T * topk
+        dbg_t = dict(qx=torch.empty((T, H), dtype=torch.int8, device=dev),
+                     sx=torch.empty((T,), dtype=torch.float32, device=dev),
+                     act=torch.empty((R, I), dtype=torch.float32, device=dev),
+                     qa=torch.empty((R, I), dtype=torch.int8, device=dev),
+                     sa2=torch.empty((R,), dtype=torch.float32, device=dev))
+        dbg_p = ctypes.pointer(MoeDebug(**{k: v.data_ptr() for k, v in dbg_t.items()}))
+    _check("moe_w8a8_rot_forward_packed",
+           lib().moe_w8a8_rot_forward_packed(_ptr(x), _ptr(logits), T, H, E, I, topk,
+                                             _ptr(w13_packed), _ptr(s13), _ptr(w2_packed),
+                                             _ptr(s2), _ptr(shared), _ptr(topk_ids),
+                                             _ptr(topk_w), _ptr(out), _ptr(ws), wsb, dbg_p,
+                                             _stream(dev)))
+    if debug:
+        return out, topk_ids, topk_w, dbg_t
+    return out, topk_ids, topk_w
+
+
+def shared_expert_w8a8_rot_workspace_bytes(T: int, H: int, Is: int) -> int:
+    return int(lib().shared_expert_w8a8_rot_workspace_bytes(T, H, Is))
+
+
+def shared_expert_w8a8_rot(x, wgu_packed, su8, s2, wd_packed, sd, y=None, ws=None,
+                           debug: bool = False):
+    """The shared expert in the Hadamard domain: fp32 y [T, H].
+
+    ``wgu_packed`` [2Is, H] (g256 codes, ``fwht128_weight_prep_g256``, packed)
+    with ``su8`` [2Is, H/256] and ``s2`` bf16 [2Is]; ``wd_packed`` [H, Is]
+    (g128 codes, packed) with ``sd`` bf16 [H, Is/128]."""
+    _req(x, torch.bfloat16, "x")
+    _req(s2, torch.bfloat16, "s2")
+    _req(sd, torch.bfloat16, "sd")
+    if not x.is_contiguous():
+        raise ValueError("x: expected a contiguous [T, H] tensor")
+    T, H = x.shape
+    Is = su8.shape[0] // 2
+    dev = x.device
+    y = torch.empty((T, H), dtype=torch.float32, device=dev) if y is None else y
+    ws, wsb = _workspace(shared_expert_w8a8_rot_workspace_bytes(T, H, Is), dev, ws)
+    dbg_t = None
+    dbg_p = None
+    if debug:
+        dbg_t = dict(act=torch.empty((T, Is), dtype=torch.float32, device=dev),
+                     qa=torch.empty((T, Is), dtype=torch.int8, device=dev),
+                     sa=torch.empty((T,), dtype=torch.float32, device=dev))
+        dbg_p = ctypes.pointer(SharedDebug(**{k: v.data_ptr() for k, v in dbg_t.items()}))
+    _check("shared_expert_w8a8_rot_packed",
+           lib().shared_expert_w8a8_rot_packed(_ptr(x), T, H, Is, _ptr(wgu_packed), _ptr(su8),
+                                               _ptr(s2), _ptr(wd_packed), _ptr(sd), _ptr(y),
+                                               _ptr(ws), wsb, dbg_p, _stream(dev)))
+    return (y, dbg_t) if debug else y

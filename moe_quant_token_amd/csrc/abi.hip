@@ -487,6 +487,125 @@ int fwht128_weight_prep_g256(const float* W, int64_t N, int64_t K, int8_t* qw, u
   return e == hipSuccess ? W8A8_OK : hip_fail(e);
 }
 
+int fwht128_weight_prep_g128(const float* W, int64_t N, int64_t K, int8_t* qw, uint16_t* s,
+                             void* stream) {
+  if (N < 0 || K <= 0) return W8A8_INVALID_ARG;
+  if (K % 128 != 0 || K > 16384 || N > INT32_MAX) return W8A8_UNSUPPORTED_SHAPE;
+  if (N == 0) return W8A8_OK;
+  if (!W || !qw || !s) return W8A8_INVALID_ARG;
+  if (!al16(W) || !al16(qw) || !al4(s)) return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  hipError_t e = launch_fwht128_weight_prep_g128(W, N, K, qw, s, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+int router_gate_bf16(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, const uint16_t* wg,
+                     int64_t E, float* logits, int64_t ldl, void* stream) {
+  if (T < 0 || H <= 0 || E <= 0 || ldx < H || ldl < E) return W8A8_INVALID_ARG;
+  if (H % 32 != 0 || H > 16384 || E % 16 != 0 || E > 4096 || T > ((int64_t)1 << 22))
+    return W8A8_UNSUPPORTED_SHAPE;
+  if (T == 0) return W8A8_OK;
+  if (!x || !wg || !logits) return W8A8_INVALID_ARG;
+  if (!al16(x) || !al16(wg) || !al4(logits) || ldx % 8 != 0) return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  hipError_t e = launch_router_gate_bf16(x, T, H, ldx, wg, E, logits, ldl, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+int moe_w8a8_rot_forward_packed(const uint16_t* x, const float* logits, int64_t T, int64_t H,
+                                int64_t E, int64_t I, int topk, const int8_t* w13_packed,
+                                const uint16_t* s13, const int8_t* w2_packed,
+                                const uint16_t* s2, const float* shared, int32_t* topk_ids,
+                                float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                                const moe_w8a8_debug* dbg, void* stream) {
+  if (T < 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0) return W8A8_INVALID_ARG;
+  if (H % 256 != 0 || I % 128 != 0 || H > 4096 || I > 2048 || topk > 16 || topk > E ||
+      E > 1024 || T * topk > ((int64_t)1 << 24))
+    return W8A8_UNSUPPORTED_SHAPE;
+  if (T == 0) return W8A8_OK;
+  if (!x || !w13_packed || !s13 || !w2_packed || !s2 || !topk_ids || !topk_w || !out)
+    return W8A8_INVALID_ARG;
+  if (!al16(x) || !al16(w13_packed) || !al16(w2_packed) || !al4(s13) || !al4(s2) ||
+      !al4(topk_ids) || !al4(topk_w) || !al16(out) || (logits && !al4(logits)) ||
+      (shared && !al16(shared)))
+    return W8A8_MISALIGNED;
+  if (ws_bytes < moe_w8a8_workspace_bytes(T, H, E, I, topk)) return W8A8_WORKSPACE_TOO_SMALL;
+  if (!ws) return W8A8_INVALID_ARG;
+  if (!al16(ws)) return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  MoeArgs a{};
+  a.x = x;
+  a.logits = logits;
+  a.T = (int)T;
+  a.H = (int)H;
+  a.E = (int)E;
+  a.I = (int)I;
+  a.k = topk;
+  a.w13 = w13_packed;
+  a.w2 = w2_packed;
+  a.topk_ids = topk_ids;
+  a.topk_w = topk_w;
+  a.out = out;
+  a.ws = ws;
+  a.packed = true;
+  if (dbg) {
+    a.dbg_qx = dbg->qx;
+    a.dbg_sx = dbg->sx;
+    a.dbg_act = dbg->act;
+    a.dbg_qa = dbg->qa;
+    a.dbg_sa2 = dbg->sa2;
+  }
+  hipError_t e = launch_moe_rot_forward(a, s13, s2, shared, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
+size_t shared_expert_w8a8_rot_workspace_bytes(int64_t T, int64_t H, int64_t Is) {
+  if (T <= 0 || H <= 0 || Is <= 0) return 0;
+  return shared_expert_workspace_bytes(T, H, Is);
+}
+
+int shared_expert_w8a8_rot_packed(const uint16_t* x, int64_t T, int64_t H, int64_t Is,
+                                  const int8_t* wgu_packed, const uint8_t* su8,
+                                  const uint16_t* s2, const int8_t* wd_packed,
+                                  const uint16_t* sd, float* y, void* ws, size_t ws_bytes,
+                                  const shared_expert_debug* dbg, void* stream) {
+  if (T < 0 || H <= 0 || Is <= 0) return W8A8_INVALID_ARG;
+  if (H % 256 != 0 || Is % 128 != 0 || H > 4096 || Is > 2048 || T > ((int64_t)1 << 24))
+    return W8A8_UNSUPPORTED_SHAPE;
+  if (T == 0) return W8A8_OK;
+  if (!x || !wgu_packed || !su8 || !s2 || !wd_packed || !sd || !y) return W8A8_INVALID_ARG;
+  if (!al16(x) || !al16(wgu_packed) || !al16(wd_packed) || !al4(sd) || !al16(y))
+    return W8A8_MISALIGNED;
+  if (ws_bytes < shared_expert_w8a8_rot_workspace_bytes(T, H, Is))
+    return W8A8_WORKSPACE_TOO_SMALL;
+  if (!ws) return W8A8_INVALID_ARG;
+  if (!al16(ws)) return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  SharedArgs a{};
+  a.x = x;
+  a.T = T;
+  a.H = H;
+  a.Is = Is;
+  a.wgu = wgu_packed;
+  a.su8 = su8;
+  a.s2 = s2;
+  a.wd = wd_packed;
+  a.sd = sd;
+  a.y = y;
+  a.ws = ws;
+  if (dbg) {
+    a.dbg_act = dbg->act;
+    a.dbg_qa = dbg->qa;
+    a.dbg_sa = dbg->sa;
+  }
+  hipError_t e = launch_shared_expert(a, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
 size_t gemm_w8a8_g256_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return g256_workspace_bytes(M, N, K);
 }

@@ -21,49 +21,6 @@ namespace w8a8 {
 
 namespace {
 
-struct Block8 {
-  float v[8];
-};
-
-// The value of lane (lane ^ m), m in {1, 2, 4, 8}: DPP quad permutations for
-// 1 and 2, a swizzle (xor mode, no LDS access) for 4 and 8.
-__device__ __forceinline__ float lane_xor(float v, int m) {
-  const int i = __float_as_int(v);
-  int r;
-  if (m == 1)
-    r = __builtin_amdgcn_mov_dpp(i, 0xb1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
-  else if (m == 2)
-    r = __builtin_amdgcn_mov_dpp(i, 0x4e, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
-  else if (m == 4)
-    r = __builtin_amdgcn_ds_swizzle(i, 0x1f | (4 << 10));  // and 0x1f, xor 4
-  else
-    r = __builtin_amdgcn_ds_swizzle(i, 0x1f | (8 << 10));  // and 0x1f, xor 8
-  return __int_as_float(r);
-}
-
-// In-place butterfly of a 128-block spread over 16 lanes (l16 = lane % 16).
-__device__ __forceinline__ void fwht128_lanes(Block8& b, int l16) {
-#pragma unroll
-  for (int h = 1; h < 8; h <<= 1)
-#pragma unroll
-    for (int c = 0; c < 8; c++)
-      if ((c & h) == 0) {
-        const float lo = b.v[c], hi = b.v[c + h];
-        b.v[c] = lo + hi;
-        b.v[c + h] = lo - hi;
-      }
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    const bool upper = (l16 & m) != 0;
-#pragma unroll
-    for (int c = 0; c < 8; c++) {
-      const float mine = b.v[c];
-      const float other = lane_xor(mine, m);
-      b.v[c] = upper ? (other - mine) : (mine + other);
-    }
-  }
-}
-
 __device__ __forceinline__ float block_max_256(float v, float* part) {
   v = wave_max(v);
   __syncthreads();
@@ -220,6 +177,47 @@ __global__ __launch_bounds__(256) void k_fwht128_wprep(const float* __restrict__
       w[i] = pack4_i8(a[0], a[1], a[2], a[3]);
     }
     *reinterpret_cast<v4u*>(qw + row * K + c16 * 16) = v4u{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// Rotated weight preparation with a bf16 scale per row per 128 of K (each
+// 128-group is one rotated block): one 16-lane group owns a block, so the
+// block maximum is a 16-lane reduction and no LDS is needed.  s = bf16(amax /
+// 127) rounded to nearest even; the codes are taken against the stored bf16
+// scale (zero codes where it is zero).  Workgroup b takes rows 16 b .. (one
+// 16-lane group per row, the row's blocks in turn); W fp32 [N, K], qw
+// row-major [N, K], s [N, K / 128].
+__global__ __launch_bounds__(256) void k_fwht128_wprep_g128(const float* __restrict__ W,
+                                                            int64_t N, int K,
+                                                            int8_t* __restrict__ qw,
+                                                            uint16_t* __restrict__ s) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (row >= N) return;  // 16-lane-uniform; the shuffles below stay within a group
+  const int l16 = threadIdx.x & 15;
+  const float* wr = W + row * K;
+  const int G = K >> 7;
+  for (int blk = 0; blk < G; blk++) {
+    Block8 b;
+    const v4f lo = *reinterpret_cast<const v4f*>(wr + blk * 128 + l16 * 8);
+    const v4f hi = *reinterpret_cast<const v4f*>(wr + blk * 128 + l16 * 8 + 4);
+    b.v[0] = lo.x; b.v[1] = lo.y; b.v[2] = lo.z; b.v[3] = lo.w;
+    b.v[4] = hi.x; b.v[5] = hi.y; b.v[6] = hi.z; b.v[7] = hi.w;
+    fwht128_lanes(b, l16);
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; c++) m = fmaxf(m, fabsf(b.v[c]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+    const uint32_t sb = f32_to_bf16_bits(m / 127.0f);
+    const float sf = bf16_bits_to_f32(sb);
+    int a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (sf != 0.0f) {
+#pragma unroll
+      for (int c = 0; c < 8; c++) a[c] = quant_code(b.v[c], sf);
+    }
+    *reinterpret_cast<uint2*>(qw + row * K + blk * 128 + l16 * 8) =
+        make_uint2(pack4_i8(a[0], a[1], a[2], a[3]), pack4_i8(a[4], a[5], a[6], a[7]));
+    if (l16 == 0) s[row * G + blk] = (uint16_t)sb;
   }
 }
 
@@ -452,6 +450,13 @@ hipError_t launch_fwht128_weight_prep(const float* W, int64_t N, int64_t K, int8
                                       uint8_t* su8, uint16_t* s2, hipStream_t stream) {
   hipLaunchKernelGGL(k_fwht128_wprep, dim3((unsigned)N), dim3(256), 0, stream, W, (int)K, qw,
                      su8, s2);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwht128_weight_prep_g128(const float* W, int64_t N, int64_t K, int8_t* qw,
+                                           uint16_t* s, hipStream_t stream) {
+  hipLaunchKernelGGL(k_fwht128_wprep_g128, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream,
+                     W, N, (int)K, qw, s);
   return hipGetLastError();
 }
 

@@ -94,6 +94,29 @@ struct MoeArgs {
 };
 size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int k);
 hipError_t launch_moe_forward(const MoeArgs& a, hipStream_t stream);
+// Hadamard-domain routed experts: w13 / w2 packed, s13 bf16 [E, 2I, H/128],
+// s2 bf16 [E, H, I/128]; shared fp32 [T, H] or nullptr.  Same workspace as
+// launch_moe_forward.
+hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const uint16_t* s2,
+                                  const float* shared, hipStream_t stream);
+
+// The shared expert in the Hadamard domain (dense: every token).
+struct SharedArgs {
+  const uint16_t* x;  // bf16 [T, H], rows contiguous
+  int64_t T, H, Is;
+  const int8_t* wgu;  // packed [2Is, H], rows 2i = gate_i, 2i+1 = up_i (rotated codes)
+  const uint8_t* su8;  // [2Is, H/256]
+  const uint16_t* s2;  // bf16 [2Is]
+  const int8_t* wd;   // packed [H, Is] (rotated codes)
+  const uint16_t* sd;  // bf16 [H, Is/128]
+  float* y;           // fp32 [T, H]
+  void* ws;
+  float* dbg_act;     // optional [T, Is]
+  int8_t* dbg_qa;     // optional [T, Is]
+  float* dbg_sa;      // optional [T]
+};
+size_t shared_expert_workspace_bytes(int64_t T, int64_t H, int64_t Is);
+hipError_t launch_shared_expert(const SharedArgs& a, hipStream_t stream);
 
 // Dense MLP block.  Workspace layout is owned by mlp.hip.
 struct MlpArgs {
@@ -122,6 +145,11 @@ hipError_t launch_fwht128_quant(const uint16_t* x, int64_t M, int64_t K, int64_t
                                 int64_t ldq, float* s, hipStream_t stream);
 hipError_t launch_fwht128_weight_prep(const float* W, int64_t N, int64_t K, int8_t* qw,
                                       uint8_t* su8, uint16_t* s2, hipStream_t stream);
+hipError_t launch_fwht128_weight_prep_g128(const float* W, int64_t N, int64_t K, int8_t* qw,
+                                           uint16_t* s, hipStream_t stream);
+hipError_t launch_router_gate_bf16(const uint16_t* x, int64_t T, int64_t H, int64_t ldx,
+                                   const uint16_t* wg, int64_t E, float* logits, int64_t ldl,
+                                   hipStream_t stream);
 size_t g256_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fwht128_quant_packed(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                        int8_t* q, float* s, hipStream_t stream);

@@ -1335,6 +1335,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ y
                                                      const int32_t* __restrict__ ids,
                                                      const float* __restrict__ w, int T, int H,
                                                      int E, int k, int nbh,
+                                                     const float* __restrict__ shared,
                                                      uint16_t* __restrict__ out) {
   const int t = blockIdx.x / nbh;
   const int c = ((blockIdx.x - t * nbh) * 256 + threadIdx.x) * 4;
@@ -1351,11 +1352,593 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ y
     acc.z = acc.z + ws * y.z;
     acc.w = acc.w + ws * y.w;
   }
+  if (shared) {  // the shared expert's output, after the routed sum
+    const v4f y = *reinterpret_cast<const v4f*>(shared + (int64_t)t * H + c);
+    acc.x = acc.x + y.x;
+    acc.y = acc.y + y.y;
+    acc.z = acc.z + y.z;
+    acc.w = acc.w + y.w;
+  }
   const uint32_t lo = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
   const uint32_t hi = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
   uint32_t* o = reinterpret_cast<uint32_t*>(out + (int64_t)t * H + c);
   o[0] = lo;
   o[1] = hi;
+}
+
+// ---------------------------------------------------------------------------
+// Hadamard-domain routed experts and shared expert (the IQ8R container's
+// format).  Source: "Qwen3.6-35B-A3B IQ8R - radiance container", Experts
+// row (the routed experts int8 on the rotated grid with a bf16 scale per row
+// and 128 of K; the shared expert likewise, its gate/up projection as the
+// trunk's linears) and Activations row (int8 under the same rotation, the
+// experts reading the codes the trunk's quantisers write); the routed order
+// of the ATOM pull request's fused_moe_triton.py bullet.
+//   - x is quantised under the fwht128 rotation, once per token;
+//   - a g128 GEMM output is the sum over the 128-groups, in group order, of
+//     the exact int32 group sum times the group's bf16 scale, in fp64, times
+//     the row scale and 2^-7 (undoing <Hx, Hw> = 128 <x, w>), rounded to fp32;
+//   - the gemm1 activation row is rotated by fwht128 before its per-row
+//     requant (the down weights are rotated along their K);
+//   - the combine adds the shared expert's fp32 output after the routed sum.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void load8_f32(const uint16_t* __restrict__ p, float* v) {
+  const v4u raw = *reinterpret_cast<const v4u*>(p);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+    v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+}
+
+__device__ __forceinline__ void load8_f32(const float* __restrict__ p, float* v) {
+  const v4f lo = *reinterpret_cast<const v4f*>(p);
+  const v4f hi = *reinterpret_cast<const v4f*>(p + 4);
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+}
+
+// One wave rotates a row of K values (K % 128 == 0, K <= 512 NR): round rd
+// holds 128-blocks 4 rd .. 4 rd + 3, 16 lanes a block, 8 values a lane (the
+// lane's values are k = 128 blk + 8 (lane % 16) + 0..7).  fp32 butterflies as
+// k_fwht128_quant; returns the wave-wide maximum |value| of the rotated row.
+template <int NR, typename TIn>
+__device__ __forceinline__ float rot_row_wave(const TIn* __restrict__ x, int K, Block8 (&b)[NR],
+                                              int lane) {
+  const int l16 = lane & 15;
+  const int nblk = K >> 7;
+  float amax = 0.0f;
+#pragma unroll
+  for (int rd = 0; rd < NR; rd++) {
+    const int blk = rd * 4 + (lane >> 4);
+    if (blk < nblk) {
+      load8_f32(x + blk * 128 + l16 * 8, b[rd].v);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; c++) b[rd].v[c] = 0.0f;
+    }
+    if (rd * 4 < nblk) {  // wave-uniform: every lane joins the butterflies
+      fwht128_lanes(b[rd], l16);
+#pragma unroll
+      for (int c = 0; c < 8; c++) amax = fmaxf(amax, fabsf(b[rd].v[c]));
+    }
+  }
+  return wave_max(amax);
+}
+
+// The int8 codes of one lane's 8 rotated values against s = amax / 127
+// (all zero for a zero row), packed little-endian.
+__device__ __forceinline__ uint2 rot_codes8(const Block8& b, float amax, float sc) {
+  int cd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (amax != 0.0f) {
+#pragma unroll
+    for (int c = 0; c < 8; c++) cd[c] = quant_code(b.v[c], sc);
+  }
+  return make_uint2(pack4_i8(cd[0], cd[1], cd[2], cd[3]), pack4_i8(cd[4], cd[5], cd[6], cd[7]));
+}
+
+// One wave rotates and quantises one row (bf16 or fp32) into row-major codes.
+template <int NR, typename TIn>
+__device__ __forceinline__ void rot_quant_row_wave(const TIn* __restrict__ x, int K,
+                                                   int8_t* __restrict__ q,
+                                                   float* __restrict__ s, int lane) {
+  Block8 b[NR];
+  const float amax = rot_row_wave<NR>(x, K, b, lane);
+  const float sc = amax / 127.0f;
+  const int nblk = K >> 7;
+#pragma unroll
+  for (int rd = 0; rd < NR; rd++) {
+    const int blk = rd * 4 + (lane >> 4);
+    if (blk < nblk)
+      *reinterpret_cast<uint2*>(q + blk * 128 + (lane & 15) * 8) = rot_codes8(b[rd], amax, sc);
+  }
+  if (lane == 0) s[0] = amax != 0.0f ? sc : 0.0f;
+}
+
+// Routing and the rotated per-token quant of x (H <= 4096): workgroup b takes
+// tokens 4b..4b+3; waves 0-3 route them (when logits are given) while waves
+// 4-7 rotate and quantise them.
+__global__ __launch_bounds__(512) void k_rot_route_quant(
+    const uint16_t* __restrict__ x, const float* __restrict__ logits, int T, int H, int E, int k,
+    int32_t* __restrict__ ids, float* __restrict__ w, int8_t* __restrict__ qx,
+    float* __restrict__ sx) {
+  const int wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + (wv & 3);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  if (wv < 4) {
+    if (logits)
+      route_token(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k, lane);
+  } else {
+    rot_quant_row_wave<8>(x + (int64_t)t * H, H, qx + (int64_t)t * H, sx + t, lane);
+  }
+}
+
+// Rotated requant of fp32 activation rows (K <= 2048), one wave a row.
+__global__ __launch_bounds__(512) void k_rot_requant(const float* __restrict__ act, int64_t P,
+                                                     int K, int8_t* __restrict__ qa,
+                                                     float* __restrict__ sa) {
+  const int64_t r = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 6);
+  if (r >= P) return;
+  rot_quant_row_wave<4>(act + r * K, K, qa + r * K, sa + r, threadIdx.x & 63);
+}
+
+// The epilogues of the rotated-expert GEMMs.
+enum { kRotSilu = 1, kRotActRot = 2, kRotG256Silu = 3, kRotCodes = 4 };
+
+// Which input rows a workgroup's pair block reads: expert slot grouping (the
+// sorted pairs of one expert) or, in the dense form (expert_list == nullptr),
+// rows [64 blockIdx.y, +64) of a plain matrix (pair p = row p).
+struct RotRows {
+  int e, begin, end;
+};
+
+__device__ __forceinline__ bool rot_rows(const int32_t* __restrict__ expert_list,
+                                         const int32_t* __restrict__ seg_off,
+                                         const int32_t* __restrict__ n_active, int dense_rows,
+                                         int rows_per_y, RotRows& rr) {
+  if (expert_list == nullptr) {
+    rr.e = 0;
+    rr.begin = blockIdx.y * rows_per_y;
+    rr.end = min(dense_rows, rr.begin + rows_per_y);
+    return true;
+  }
+  const int slot = blockIdx.y;
+  if (slot >= n_active[0]) return false;
+  rr.e = expert_list[slot];
+  rr.begin = seg_off[slot];
+  rr.end = seg_off[slot + 1];
+  return true;
+}
+
+// SiLU(gate) * up over the interleaved columns (even = gate, odd = up), the
+// pair sharing lanes j and j ^ 1; every lane must call it (it shuffles).
+__device__ __forceinline__ float rot_silu_pair(float h) {
+  const float partner = __shfl_xor(h, 1, 64);
+  const float sg = (float)((double)h / (1.0 + exp(-(double)h)));
+  return sg * partner;
+}
+
+// Grouped GEMM with per-group scales, split over K (small batches).  The
+// workgroup takes one 16-column tile of one weight matrix (blockIdx.x) and
+// its pair rows in blocks of 16; wave w computes the exact int32 sums of the
+// 128-groups w, w + WAVES, ... (two 16x16x64 MFMA steps each) into LDS, and
+// wave 0 folds them in group order (fixed order: deterministic, and equal to
+// the definition):
+//   kRotSilu:     t = sum_g acc_g s[c, g] (fp64); h = (float)(t sx 2^-7);
+//                 SiLU(gate) * up -> fp32 activation [pair, c / 2];
+//   kRotActRot:   the prologue rotates each pair's fp32 activation row, takes
+//                 its per-row scale and writes its codes into LDS in the
+//                 packed operand layout; y = (float)(t sa 2^-7) -> fp32;
+//   kRotG256Silu: T = sum over 256-groups of su8 (acc_2g + acc_2g+1), exact
+//                 in int64; h = (float)(T sx s2 2^-7); SiLU(gate) * up.
+// W is packed (16-row tiles of 1 KiB k-steps), as [E * Nw, K].
+template <int MODE, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, const float* __restrict__ act,
+    int k, const int8_t* __restrict__ W, const uint16_t* __restrict__ sW,
+    const uint8_t* __restrict__ su8, int Nw, int K, const int32_t* __restrict__ expert_list,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ n_active,
+    const int32_t* __restrict__ sorted_pairs, int dense_rows, float* __restrict__ out, int ldo,
+    int8_t* __restrict__ qa_rec, float* __restrict__ sa_rec) {
+  constexpr int MAXG = 32;  // K <= 4096
+  constexpr int GW = MAXG / WAVES;
+  __shared__ v4i red[MAXG][64];
+  __shared__ float s_lds[MODE == kRotG256Silu ? 1 : 16][MAXG];
+  __shared__ __attribute__((aligned(16))) int8_t a_lds[MODE == kRotActRot ? 16 * 2048 : 16];
+  __shared__ float sa_lds[16];
+  __shared__ int pair_lds[16];
+  RotRows rr;
+  if (!rot_rows(expert_list, seg_off, n_active, dense_rows, 64, rr)) return;
+  const bool dense = expert_list == nullptr;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int nk = K >> 6;
+  const int G = K >> 7;
+  const int tile = blockIdx.x;
+  const int col = tile * 16 + j;
+  const int8_t* wbase = W + ((int64_t)rr.e * (Nw >> 4) + tile) * nk * 1024 + lane * 16;
+
+  if (MODE != kRotG256Silu) {
+    for (int i = threadIdx.x; i < 16 * G; i += WAVES * 64) {
+      const int cc = i / G, gg = i - cc * G;
+      s_lds[cc][gg] = bf16_bits_to_f32(sW[((int64_t)rr.e * Nw + tile * 16 + cc) * G + gg]);
+    }
+  }
+  v4i bw[GW][2];
+#pragma unroll
+  for (int i = 0; i < GW; i++) {
+    const int gg = wv + i * WAVES;
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+      bw[i][h] = gg < G ? ld_stream(wbase + (int64_t)(2 * gg + h) * 1024) : v4i{0, 0, 0, 0};
+  }
+
+  for (int pb = rr.begin; pb < rr.end; pb += 16) {
+    const int nrows = min(16, rr.end - pb);
+    __syncthreads();  // the previous block's LDS consumed
+    if (threadIdx.x < 16)
+      pair_lds[threadIdx.x] = threadIdx.x < nrows
+                                  ? (dense ? pb + (int)threadIdx.x : sorted_pairs[pb + threadIdx.x])
+                                  : 0;
+    __syncthreads();
+    if (MODE == kRotActRot) {
+      for (int r = wv; r < nrows; r += WAVES) {
+        Block8 bb[4];
+        const float am = rot_row_wave<4>(act + (int64_t)pair_lds[r] * K, K, bb, lane);
+        const float sc = am / 127.0f;
+#pragma unroll
+        for (int rd = 0; rd < 4; rd++) {
+          const int blk = rd * 4 + g;
+          if (blk >= G) continue;
+          const uint2 wd = rot_codes8(bb[rd], am, sc);
+          const int kk = blk * 128 + j * 8;  // first of the lane's 8 values
+          *reinterpret_cast<uint2*>(a_lds + (kk >> 6) * 1024 + (r + 16 * ((kk & 63) >> 4)) * 16 +
+                                    (kk & 15)) = wd;
+          if (tile == 0 && qa_rec)
+            *reinterpret_cast<uint2*>(qa_rec + (int64_t)pair_lds[r] * K + kk) = wd;
+        }
+        if (lane == 0) {
+          const float sv = am != 0.0f ? sc : 0.0f;
+          sa_lds[r] = sv;
+          if (tile == 0 && sa_rec) sa_rec[pair_lds[r]] = sv;
+        }
+      }
+      __syncthreads();
+    }
+
+    const bool a_ok = j < nrows;
+    const int8_t* ap = qx + (int64_t)(pair_lds[a_ok ? j : 0] / k) * K + g * 16;
+#pragma unroll
+    for (int i = 0; i < GW; i++) {
+      const int gg = wv + i * WAVES;
+      if (gg < G) {
+        v4i acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const int c = 2 * gg + h;
+          v4i a;
+          if (MODE == kRotActRot)
+            a = *reinterpret_cast<const v4i*>(&a_lds[c * 1024 + lane * 16]);
+          else
+            a = a_ok ? *reinterpret_cast<const v4i*>(ap + (int64_t)c * 64) : v4i{0, 0, 0, 0};
+          acc = mfma_16x16x64_i8(a, bw[i][h], acc);
+        }
+        red[gg][lane] = acc;
+      }
+    }
+    __syncthreads();
+    if (wv != 0) continue;
+    // lane holds rows 4 g + v of column col
+    float hv[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int r = min(4 * g + v, nrows - 1);
+      const float rs = MODE == kRotActRot ? sa_lds[r] : sx[pair_lds[r] / k];
+      double t;
+      if (MODE == kRotG256Silu) {
+        const int G2 = K >> 8;
+        const uint8_t* sp = su8 + (int64_t)col * G2;
+        long long ts = 0;
+        for (int gg = 0; gg < G2; gg++)
+          ts += (long long)sp[gg] * (long long)(red[2 * gg][lane][v] + red[2 * gg + 1][lane][v]);
+        t = (double)ts * (double)rs;
+        t = t * (double)bf16_bits_to_f32(sW[col]);
+      } else {
+        t = 0.0;
+        for (int gg = 0; gg < G; gg++) t = t + (double)red[gg][lane][v] * (double)s_lds[j][gg];
+        t = t * (double)rs;
+      }
+      t = t * 0.0078125;
+      hv[v] = (float)t;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int r = 4 * g + v;
+      const bool valid = r < nrows;
+      const int p = pair_lds[valid ? r : 0];
+      if (MODE == kRotActRot) {
+        if (valid) out[(int64_t)p * ldo + col] = hv[v];
+      } else {
+        const float a = rot_silu_pair(hv[v]);
+        if ((j & 1) == 0 && valid) out[(int64_t)p * ldo + (col >> 1)] = a;
+      }
+    }
+  }
+}
+
+// Grouped GEMM with per-group scales, row-blocked (large batches).  The
+// workgroup takes 16 WAVES columns of one weight matrix (wave w: columns
+// 16 (WAVES blockIdx.x + w) + 0..15) and its pair rows in blocks of 32; each
+// wave walks all of K for two 16-row blocks and folds every group into fp64
+// (int64 for kRotG256Silu) accumulators as it goes, in group order — the same
+// arithmetic as k_rot_gemm_splitk.  kRotCodes reads the rotated codes and
+// scales of each pair row (qa [P, K], sa [P]) and writes fp32 y rows.
+template <int MODE, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_rows(
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, int k,
+    const int8_t* __restrict__ W, const uint16_t* __restrict__ sW,
+    const uint8_t* __restrict__ su8, int Nw, int K, const int32_t* __restrict__ expert_list,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ n_active,
+    const int32_t* __restrict__ sorted_pairs, int dense_rows, float* __restrict__ out,
+    int ldo) {
+  constexpr int RB = 2;  // 16-row blocks per pass
+  __shared__ int pair_lds[RB * 16];
+  RotRows rr;
+  if (!rot_rows(expert_list, seg_off, n_active, dense_rows, 128, rr)) return;
+  const bool dense = expert_list == nullptr;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int nk = K >> 6;
+  const int G = K >> 7;
+  const int tile = blockIdx.x * WAVES + wv;
+  const int col = tile * 16 + j;
+  const int8_t* wbase = W + ((int64_t)rr.e * (Nw >> 4) + tile) * nk * 1024 + lane * 16;
+  const uint16_t* srow = sW + ((int64_t)rr.e * Nw + col) * (MODE == kRotG256Silu ? 1 : G);
+  const uint8_t* sp = MODE == kRotG256Silu ? su8 + (int64_t)col * (K >> 8) : nullptr;
+
+  for (int pb = rr.begin; pb < rr.end; pb += RB * 16) {
+    const int nrows = min(RB * 16, rr.end - pb);
+    __syncthreads();
+    if (threadIdx.x < RB * 16)
+      pair_lds[threadIdx.x] = threadIdx.x < nrows
+                                  ? (dense ? pb + (int)threadIdx.x : sorted_pairs[pb + threadIdx.x])
+                                  : 0;
+    __syncthreads();
+    const int8_t* ap[RB];
+    bool aok[RB];
+#pragma unroll
+    for (int b = 0; b < RB; b++) {
+      const int r = b * 16 + j;
+      aok[b] = r < nrows;
+      const int p = pair_lds[aok[b] ? r : 0];
+      ap[b] = (MODE == kRotCodes ? qx + (int64_t)p * K : qx + (int64_t)(p / k) * K) + g * 16;
+    }
+    double t[RB][4];
+    long long ts[RB][4];
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        t[b][v] = 0.0;
+        ts[b][v] = 0;
+      }
+    for (int gg = 0; gg < G; gg++) {
+      const v4i b0 = ld_stream(wbase + (int64_t)(2 * gg) * 1024);
+      const v4i b1 = ld_stream(wbase + (int64_t)(2 * gg + 1) * 1024);
+      v4i acc[RB];
+#pragma unroll
+      for (int b = 0; b < RB; b++) {
+        const v4i a0 = aok[b] ? *reinterpret_cast<const v4i*>(ap[b] + (int64_t)(2 * gg) * 64)
+                              : v4i{0, 0, 0, 0};
+        const v4i a1 = aok[b] ? *reinterpret_cast<const v4i*>(ap[b] + (int64_t)(2 * gg + 1) * 64)
+                              : v4i{0, 0, 0, 0};
+        acc[b] = mfma_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0});
+        acc[b] = mfma_16x16x64_i8(a1, b1, acc[b]);
+      }
+      if (MODE == kRotG256Silu) {
+        // both 128-halves of a 256-group take its u8 scale; exact in int64
+        const long long u = (long long)sp[gg >> 1];
+#pragma unroll
+        for (int b = 0; b < RB; b++)
+#pragma unroll
+          for (int v = 0; v < 4; v++) ts[b][v] += u * (long long)acc[b][v];
+      } else {
+        const double s = (double)bf16_bits_to_f32(srow[gg]);
+#pragma unroll
+        for (int b = 0; b < RB; b++)
+#pragma unroll
+          for (int v = 0; v < 4; v++) t[b][v] = t[b][v] + (double)acc[b][v] * s;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < RB; b++) {
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int r = b * 16 + 4 * g + v;
+        const bool valid = r < nrows;
+        const int p = pair_lds[valid ? r : 0];
+        const float rs = MODE == kRotCodes ? sx[p] : sx[p / k];
+        double tv;
+        if (MODE == kRotG256Silu) {
+          tv = (double)ts[b][v] * (double)rs;
+          tv = tv * (double)bf16_bits_to_f32(srow[0]);
+        } else {
+          tv = t[b][v] * (double)rs;
+        }
+        tv = tv * 0.0078125;
+        const float h = (float)tv;
+        if (MODE == kRotCodes) {
+          if (valid) out[(int64_t)p * ldo + col] = h;
+        } else {
+          const float a = rot_silu_pair(h);
+          if ((j & 1) == 0 && valid) out[(int64_t)p * ldo + (col >> 1)] = a;
+        }
+      }
+    }
+  }
+}
+
+// pair counts up to this take the split-K GEMMs (and fuse the rotated requant
+// into gemm2's prologue); beyond it the row-blocked GEMMs and k_rot_requant.
+constexpr int64_t kRotSplitMaxPairs = 256;
+
+hipError_t launch_rot_sort(const MoeArgs& a, const MoeWs& ws, int64_t P, hipStream_t stream) {
+  if (P <= kMoeSortOneWg) {
+    hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
+                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax);
+    return hipGetLastError();
+  }
+  const int chunk = (int)std::max<int64_t>(1024, (P + kMoeSortChunks - 1) / kMoeSortChunks);
+  const int nchunks = (int)((P + chunk - 1) / chunk);
+  hipLaunchKernelGGL(k_moe_sort_hist, dim3(nchunks), dim3(1024), 0, stream, a.topk_ids, (int)P,
+                     a.E, chunk, ws.hist, ws.rank);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_moe_sort_scatter, dim3(nchunks), dim3(1024), 0, stream, a.topk_ids,
+                     (int)P, a.E, chunk, nchunks, ws.hist, ws.rank, ws.expert_list, ws.seg_off,
+                     ws.n_active, ws.sorted_pairs, ws.blk_slot, ws.blk_row0, ws.n_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const uint16_t* s2,
+                                  const float* shared, hipStream_t stream) {
+  const int64_t P = (int64_t)a.T * a.k;
+  MoeWs ws = carve(a.ws, a.T, a.H, a.E, a.I, a.k);
+  const unsigned slots = (unsigned)std::min<int64_t>(a.E, P);
+  const int I2 = 2 * a.I;
+  hipError_t err;
+  hipLaunchKernelGGL(k_rot_route_quant, dim3((a.T + 3) / 4), dim3(512), 0, stream, a.x, a.logits,
+                     a.T, a.H, a.E, a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = launch_rot_sort(a, ws, P, stream)) != hipSuccess) return err;
+  if (P <= kRotSplitMaxPairs) {
+    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotSilu, 8>), dim3(I2 / 16, slots), dim3(512), 0,
+                       stream, ws.qx, ws.sx, nullptr, a.k, a.w13, s13, nullptr, I2, a.H,
+                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.act, a.I,
+                       nullptr, nullptr);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotActRot, 4>), dim3(a.H / 16, slots), dim3(256), 0,
+                       stream, nullptr, nullptr, ws.act, a.k, a.w2, s2, nullptr, a.H, a.I,
+                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.y2, a.H,
+                       a.dbg_qa, a.dbg_sa2);
+  } else {
+    hipLaunchKernelGGL((k_rot_gemm_rows<kRotSilu, 4>), dim3(I2 / 64, slots), dim3(256), 0,
+                       stream, ws.qx, ws.sx, a.k, a.w13, s13, nullptr, I2, a.H, ws.expert_list,
+                       ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.act, a.I);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_rot_requant, dim3((unsigned)((P + 7) / 8)), dim3(512), 0, stream,
+                       ws.act, P, a.I, ws.qa, ws.sa2);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((k_rot_gemm_rows<kRotCodes, 4>), dim3(a.H / 64, slots), dim3(256), 0,
+                       stream, ws.qa, ws.sa2, 1, a.w2, s2, nullptr, a.H, a.I, ws.expert_list,
+                       ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.y2, a.H);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)(P * a.I),
+                                          hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+      return err;
+    if (a.dbg_sa2 && (err = hipMemcpyAsync(a.dbg_sa2, ws.sa2, (size_t)P * 4,
+                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+      return err;
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int nbh = (a.H / 4 + 255) / 256;
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((int64_t)nbh * a.T)), dim3(256), 0, stream,
+                     ws.y2, a.topk_ids, a.topk_w, a.T, a.H, a.E, a.k, nbh, shared, a.out);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (a.dbg_qx && (err = hipMemcpyAsync(a.dbg_qx, ws.qx, (size_t)a.T * a.H,
+                                        hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+    return err;
+  if (a.dbg_sx && (err = hipMemcpyAsync(a.dbg_sx, ws.sx, (size_t)a.T * 4,
+                                        hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+    return err;
+  if (a.dbg_act && (err = hipMemcpyAsync(a.dbg_act, ws.act, (size_t)P * a.I * 4,
+                                         hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+    return err;
+  return hipSuccess;
+}
+
+// The shared expert: rotated codes of x, the g256 gate/up GEMM with the SiLU
+// epilogue, then the rotated requant and the g128 down GEMM (dense forms).
+namespace {
+struct SharedWs {
+  int8_t* qx;
+  float* sx;
+  float* act;
+  int8_t* qa;
+  float* sa;
+  size_t bytes;
+};
+
+SharedWs carve_shared(void* base, int64_t T, int64_t H, int64_t Is) {
+  SharedWs w;
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t bytes) {
+    char* p = b ? b + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  w.qx = reinterpret_cast<int8_t*>(take(T * H));
+  w.sx = reinterpret_cast<float*>(take(T * 4));
+  w.act = reinterpret_cast<float*>(take(T * Is * 4));
+  w.qa = reinterpret_cast<int8_t*>(take(T * Is));
+  w.sa = reinterpret_cast<float*>(take(T * 4));
+  w.bytes = off;
+  return w;
+}
+}  // namespace
+
+size_t shared_expert_workspace_bytes(int64_t T, int64_t H, int64_t Is) {
+  return carve_shared(nullptr, T, H, Is).bytes;
+}
+
+hipError_t launch_shared_expert(const SharedArgs& a, hipStream_t stream) {
+  const SharedWs ws = carve_shared(a.ws, a.T, a.H, a.Is);
+  const int T = (int)a.T, H = (int)a.H, Is = (int)a.Is;
+  hipError_t err;
+  hipLaunchKernelGGL(k_rot_route_quant, dim3((unsigned)((T + 3) / 4)), dim3(512), 0, stream, a.x,
+                     nullptr, T, H, 1, 1, nullptr, nullptr, ws.qx, ws.sx);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (a.T <= 64) {
+    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotG256Silu, 8>), dim3(2 * Is / 16, 1), dim3(512), 0,
+                       stream, ws.qx, ws.sx, nullptr, 1, a.wgu, a.s2, a.su8, 2 * Is, H, nullptr,
+                       nullptr, nullptr, nullptr, T, ws.act, Is, nullptr, nullptr);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotActRot, 4>), dim3(H / 16, 1), dim3(256), 0, stream,
+                       nullptr, nullptr, ws.act, 1, a.wd, a.sd, nullptr, H, Is, nullptr, nullptr,
+                       nullptr, nullptr, T, a.y, H, a.dbg_qa, a.dbg_sa);
+  } else {
+    const unsigned rb = (unsigned)((a.T + 127) / 128);
+    hipLaunchKernelGGL((k_rot_gemm_rows<kRotG256Silu, 4>), dim3(2 * Is / 64, rb), dim3(256), 0,
+                       stream, ws.qx, ws.sx, 1, a.wgu, a.s2, a.su8, 2 * Is, H, nullptr, nullptr,
+                       nullptr, nullptr, T, ws.act, Is);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_rot_requant, dim3((unsigned)((a.T + 7) / 8)), dim3(512), 0, stream,
+                       ws.act, a.T, Is, ws.qa, ws.sa);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((k_rot_gemm_rows<kRotCodes, 4>), dim3(H / 64, rb), dim3(256), 0, stream,
+                       ws.qa, ws.sa, 1, a.wd, a.sd, nullptr, H, Is, nullptr, nullptr, nullptr,
+                       nullptr, T, a.y, H);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)(a.T * a.Is),
+                                          hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+      return err;
+    if (a.dbg_sa && (err = hipMemcpyAsync(a.dbg_sa, ws.sa, (size_t)a.T * 4,
+                                          hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+      return err;
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (a.dbg_act && (err = hipMemcpyAsync(a.dbg_act, ws.act, (size_t)(a.T * a.Is) * 4,
+                                         hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+    return err;
+  return hipSuccess;
 }
 
 size_t moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int k) {
@@ -1501,7 +2084,7 @@ static hipError_t moe_forward_impl(const MoeArgs& a, hipStream_t stream) {
   if (!t1) {  // the single-token path combined inside its gemm2
     const int nbh = (a.H / 4 + 255) / 256;
     hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((int64_t)nbh * a.T)), dim3(256), 0, stream,
-                       ws.y2, a.topk_ids, a.topk_w, a.T, a.H, a.E, a.k, nbh, a.out);
+                       ws.y2, a.topk_ids, a.topk_w, a.T, a.H, a.E, a.k, nbh, nullptr, a.out);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
 

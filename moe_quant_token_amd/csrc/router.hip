@@ -1,0 +1,123 @@
+// The MoE router gate in bf16: logits[t, e] = sum_h x[t, h] wg[e, h], bf16
+// operands, fp32 accumulation, fp32 logits (the input of routing).
+//
+// Source: "Online INT8 W8A8 for Qwen3.6 27B / 35B-A3B" (ATOM pull request),
+// intro: the precision split keeps the router gate in BF16 while the experts
+// and dense GEMMs run A8W8.
+//
+// Two forms, both with a fixed summation order (bit-reproducible):
+//   - up to 16 tokens: one wave per expert row; each lane walks its 8-value
+//     chunks of the row (h = 512 c + 8 lane + 0..7) with fp32 FMAs (a bf16
+//     product is exact in fp32) for every token, then a butterfly reduction
+//     over the wave.  The weight row is read once for all tokens;
+//   - more tokens: bf16 MFMA (v_mfma_f32_16x16x32_bf16) tiles of 64 tokens x
+//     16 experts, one wave per 16 tokens walking all of H.
+// Layouts: x bf16 [T, H] with row stride ldx; wg bf16 [E, H] contiguous;
+// logits fp32 [T, E] with row stride ldl.
+#include "kernels.h"
+
+namespace w8a8 {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kRouterWaveTokens = 16;
+
+__device__ __forceinline__ void unpack_bf16x8(const v4u raw, float* v) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+    v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_router_wave(const uint16_t* __restrict__ x, int T, int H,
+                                                     int64_t ldx, const uint16_t* __restrict__ wg,
+                                                     int E, float* __restrict__ logits,
+                                                     int64_t ldl) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (e >= E) return;  // wave-uniform
+  float acc[kRouterWaveTokens];
+#pragma unroll
+  for (int t = 0; t < kRouterWaveTokens; t++) acc[t] = 0.0f;
+  const uint16_t* wr = wg + (int64_t)e * H;
+  for (int h0 = lane * 8; h0 < H; h0 += 512) {
+    float wv[8];
+    unpack_bf16x8(*reinterpret_cast<const v4u*>(wr + h0), wv);
+#pragma unroll
+    for (int t = 0; t < kRouterWaveTokens; t++) {
+      if (t < T) {
+        float xv[8];
+        unpack_bf16x8(*reinterpret_cast<const v4u*>(x + t * ldx + h0), xv);
+#pragma unroll
+        for (int c = 0; c < 8; c++) acc[t] = fmaf(xv[c], wv[c], acc[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kRouterWaveTokens; t++) {
+    if (t < T) {
+      float v = acc[t];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_xor(v, off, 64);
+      if (lane == 0) logits[t * ldl + e] = v;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict__ x, int T, int H,
+                                                     int64_t ldx, const uint16_t* __restrict__ wg,
+                                                     float* __restrict__ logits, int64_t ldl) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int e0 = blockIdx.x * 16;
+  const int t0 = blockIdx.y * 64 + wv * 16;
+  if (t0 >= T) return;  // wave-uniform
+  const int ta = min(t0 + j, T - 1);  // rows past T read a valid row; not stored
+  const uint16_t* ap = x + (int64_t)ta * ldx + g * 8;
+  const uint16_t* bp = wg + (int64_t)(e0 + j) * H + g * 8;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int U = 4;
+  int k0 = 0;
+  for (; k0 + 32 * U <= H; k0 += 32 * U) {
+    v4u a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      a[u] = *reinterpret_cast<const v4u*>(ap + k0 + 32 * u);
+      b[u] = *reinterpret_cast<const v4u*>(bp + k0 + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[u]),
+                                                    __builtin_bit_cast(v8bf, b[u]), acc, 0, 0, 0);
+  }
+  for (; k0 < H; k0 += 32) {
+    const v4u a = *reinterpret_cast<const v4u*>(ap + k0);
+    const v4u b = *reinterpret_cast<const v4u*>(bp + k0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                  __builtin_bit_cast(v8bf, b), acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; v++) {
+    const int t = t0 + 4 * g + v;
+    if (t < T) logits[(int64_t)t * ldl + e0 + j] = acc[v];
+  }
+}
+
+hipError_t launch_router_gate_bf16(const uint16_t* x, int64_t T, int64_t H, int64_t ldx,
+                                   const uint16_t* wg, int64_t E, float* logits, int64_t ldl,
+                                   hipStream_t stream) {
+  if (T <= kRouterWaveTokens) {
+    hipLaunchKernelGGL(k_router_wave, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, stream, x,
+                       (int)T, (int)H, ldx, wg, (int)E, logits, ldl);
+  } else {
+    hipLaunchKernelGGL(k_router_mfma, dim3((unsigned)(E / 16), (unsigned)((T + 63) / 64)),
+                       dim3(256), 0, stream, x, (int)T, (int)H, ldx, wg, logits, ldl);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace w8a8

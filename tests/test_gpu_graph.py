@@ -229,3 +229,183 @@ def test_moe_graph(orc, T):
         assert np.all(np.abs(g - r) <= 1e-3 + 1e-2 * np.abs(r))
 
     _graph_check(call, [x, lg], [(bf16_dev(a), dev(b)) for a, b in sets_h], [out, ids, wt], check)
+
+
+@pytest.mark.parametrize("M", [2, 100])
+def test_mlp_graph(orc, M):
+    K, I, N = 512, 192, 128
+    key = (74, M)
+    qgu, sgu = orc.quant_rows(synth.weights(key, 2 * I, K))
+    qd, sd = orc.quant_rows(synth.weights(key, N, I, tensor_id=synth.T_W2))
+    wgu_d, wd_d = mq.pack_weights(dev(qgu)), mq.pack_weights(dev(qd))
+    sgu_d, sd_d = dev(sgu), dev(sd)
+    sets_h = [synth.activations((*key, i), M, K, 4, 20.0) for i in range(2)]
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mq.mlp_w8a8_workspace_bytes(M, K, I, N), dtype=torch.uint8, device="cuda")
+
+    def call():
+        mq.mlp_w8a8_packed(x, wgu_d, sgu_d, wd_d, sd_d, I, N, y=y, ws=ws)
+
+    def check(inp):
+        want = orc.mlp_forward(bf16_host(inp[0]), qgu, sgu, qd, sd)
+        g = orc.bf16_to_f32(bf16_host(y)).astype(np.float64)
+        r = orc.bf16_to_f32(want).astype(np.float64)
+        assert np.all(np.abs(g - r) <= 1e-3 + 1e-2 * np.abs(r))
+
+    _graph_check(call, [x], [(bf16_dev(a),) for a in sets_h], [y], check)
+
+
+def test_kv_quant_graph(orc):
+    T, Hk, D, rows = 9, 4, 256, 64
+    sets_h = [synth.activations((75, i), T, Hk * D, 10, 10.0).reshape(T, Hk, D)
+              for i in range(2)]
+    slots_h = np.random.default_rng(75).permutation(rows)[:T].astype(np.int32)
+    x = torch.empty((T, Hk, D), dtype=torch.bfloat16, device="cuda")
+    slots = dev(slots_h)
+    q = torch.zeros((rows, Hk, D), dtype=torch.int8, device="cuda")
+    s = torch.zeros((rows, Hk), dtype=torch.float16, device="cuda")
+
+    def call():
+        mq.kv_quant_i8(x, q, s, slots=slots)
+
+    def check(inp):
+        q_ref, s_ref = orc.kv_quant_i8(bf16_host(inp[0]).reshape(T, Hk, D), slots_h, rows)
+        np.testing.assert_array_equal(host(q)[slots_h], q_ref[slots_h])
+        np.testing.assert_array_equal(host(s).view(np.uint16)[slots_h], s_ref[slots_h])
+
+    _graph_check(call, [x], [(bf16_dev(a),) for a in sets_h], [q, s], check)
+
+
+def test_router_and_g128_prep_graph(orc):
+    T, H, E = 20, 512, 32
+    wg_h = synth.to_bf16_bits(synth.weights((76, 0), E, H))
+    wg = bf16_dev(wg_h)
+    sets_h = [(synth.activations((76, i), T, H, 4, 10.0), synth.weights((76, i + 1), 24, H))
+              for i in range(2)]
+    x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    W = torch.empty((24, H), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    qw = torch.empty((24, H), dtype=torch.int8, device="cuda")
+    sw = torch.empty((24, H // 128), dtype=torch.bfloat16, device="cuda")
+    L = mq.lib()
+
+    def call():
+        mq.router_gate_bf16(x, wg, logits=lg)
+        st = L.fwht128_weight_prep_g128(W.data_ptr(), 24, H, qw.data_ptr(), sw.data_ptr(),
+                                        torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+
+    def check(inp):
+        ref = orc.router_gate_bf16(bf16_host(inp[0]), wg_h)
+        xf = orc.bf16_to_f32(bf16_host(inp[0])).astype(np.float64)
+        bound = H * 2.0 ** -24 * (np.abs(xf) @ np.abs(orc.bf16_to_f32(wg_h)).astype(
+            np.float64).T)
+        assert np.all(np.abs(host(lg) - ref) <= bound + 1e-30)
+        q_ref, s_ref = orc.weight_prep_g128(host(inp[1]))
+        np.testing.assert_array_equal(host(qw), q_ref)
+        np.testing.assert_array_equal(bf16_host(sw), s_ref)
+
+    _graph_check(call, [x, W], [(bf16_dev(a), dev(b)) for a, b in sets_h], [lg, qw, sw], check)
+
+
+@pytest.mark.parametrize("T", [2, 40, 200])
+def test_rot_moe_and_shared_graph(orc, T):
+    # split-K forms (up to 256 pairs / 64 tokens) and the row-blocked forms
+    E, H, I, k, Is = 8, 256, 128, 4, 128
+    key = (77, T)
+    q13 = np.empty((E, 2 * I, H), np.int8)
+    s13 = np.empty((E, 2 * I, H // 128), np.uint16)
+    q2 = np.empty((E, H, I), np.int8)
+    s2 = np.empty((E, H, I // 128), np.uint16)
+    for e in range(E):
+        q13[e], s13[e] = orc.weight_prep_g128(synth.expert_weights(key, e, 2 * I, H, synth.T_W))
+        q2[e], s2[e] = orc.weight_prep_g128(synth.expert_weights(key, e, H, I, synth.T_W2))
+    S = (*orc.weight_prep_g256(synth.weights(key, 2 * Is, H)),
+         *orc.weight_prep_g128(synth.weights(key, H, Is, tensor_id=synth.T_W2)))
+    w13, w2 = mq.pack_moe_weights(dev(q13), dev(q2))
+    Wd = (w13, bf16_dev(s13), w2, bf16_dev(s2))
+    Sd = (mq.pack_weights(dev(S[0])), dev(S[1]), bf16_dev(S[2]), mq.pack_weights(dev(S[3])),
+          bf16_dev(S[4]))
+    sets_h = [(synth.activations((*key, i), T, H, 0, 1.0), synth.router_logits((*key, i), T, E))
+              for i in range(2)]
+    x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(mq.moe_w8a8_workspace_bytes(T, H, E, I, k), dtype=torch.uint8, device="cuda")
+    wss = torch.empty(mq.shared_expert_w8a8_rot_workspace_bytes(T, H, Is), dtype=torch.uint8,
+                      device="cuda")
+
+    def call():
+        mq.shared_expert_w8a8_rot(x, *Sd, y=y, ws=wss)
+        mq.moe_w8a8_rot_forward(x, lg, *Wd, topk=k, shared=y, topk_ids=ids, topk_w=wt, out=out,
+                                ws=ws)
+
+    def check(inp):
+        xh, lh = bf16_host(inp[0]), host(inp[1])
+        y_ref = orc.shared_expert(xh, *S)
+        ids_ref, w_ref = orc.route_topk(lh, k)
+        np.testing.assert_array_equal(host(ids), ids_ref)
+        want = orc.moe_rot_forward(xh, ids_ref, w_ref, q13, s13, q2, s2, shared=y_ref)
+        g = orc.bf16_to_f32(bf16_host(out)).astype(np.float64)
+        r = orc.bf16_to_f32(want).astype(np.float64)
+        assert np.all(np.abs(g - r) <= 1e-3 + 1e-2 * np.abs(r))
+
+    _graph_check(call, [x, lg], [(bf16_dev(a), dev(b)) for a, b in sets_h], [y, out, ids, wt],
+                 check)
+
+
+@pytest.mark.parametrize("M", [3, 300])
+def test_unpacked_linear_pack_and_noalloc_graph(orc, M):
+    # linear_w8a8 (row-major weights), w8a8_pack_weights, the allocation-free
+    # linear and the g256 preparation + packed g256 GEMM, in one graph
+    K, N = 1024, 1280
+    xs, qw, sw = _dense(orc, M, K, N, 200 + M)
+    Wg = synth.weights((78, M), 256, K)
+    qg_ref, su_ref, s2_ref = orc.weight_prep_g256(Wg)
+    qw_d, sw_d, Wg_d = dev(qw), dev(sw), dev(Wg)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    yg = torch.empty((M, 256), dtype=torch.bfloat16, device="cuda")
+    qp = torch.empty((N * K,), dtype=torch.int8, device="cuda")
+    qg = torch.empty((256, K), dtype=torch.int8, device="cuda")
+    su = torch.empty((256, K // 256), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((256,), dtype=torch.bfloat16, device="cuda")
+    qgp = torch.empty((256 * K,), dtype=torch.int8, device="cuda")
+    qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sa = torch.empty((M,), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, mq.linear_w8a8_workspace_bytes(M, N, K)), dtype=torch.uint8,
+                     device="cuda")
+    wsg = torch.empty(max(256, mq.gemm_w8a8_g256_workspace_bytes(M, 256, K)), dtype=torch.uint8,
+                      device="cuda")
+    L = mq.lib()
+
+    def call():
+        st = torch.cuda.current_stream().cuda_stream
+        mq.linear_w8a8(x, qw_d, sw_d, y=y, ws=ws)
+        assert L.w8a8_pack_weights(qw_d.data_ptr(), N, K, K, qp.data_ptr(), st) == 0
+        mq.linear_w8a8_packed_noalloc(x, qp, sw_d, N, y=y2)
+        assert L.fwht128_weight_prep_g256(Wg_d.data_ptr(), 256, K, qg.data_ptr(), su.data_ptr(),
+                                          s2.data_ptr(), st) == 0
+        assert L.w8a8_pack_weights(qg.data_ptr(), 256, K, K, qgp.data_ptr(), st) == 0
+        mq.fwht128_quant(x, q=qa, s=sa)
+        mq.gemm_w8a8_g256(qa, sa, qgp, su, s2, y=yg, ws=wsg, packed=True)
+
+    def check(inp):
+        xh = bf16_host(inp[0])
+        want = orc.linear_w8a8(xh, qw, sw)
+        np.testing.assert_array_equal(bf16_host(y), want)
+        np.testing.assert_array_equal(bf16_host(y2), want)
+        np.testing.assert_array_equal(host(qg), qg_ref)
+        np.testing.assert_array_equal(host(su), su_ref)
+        np.testing.assert_array_equal(bf16_host(s2), s2_ref)
+        qr, sr = orc.fwht128_quant(xh)
+        np.testing.assert_array_equal(bf16_host(yg), orc.gemm_g256(qr, sr, qg_ref, su_ref,
+                                                                    s2_ref))
+
+    _graph_check(call, [x], [(bf16_dev(v),) for v in xs], [y, y2, qp, qg, su, s2, qgp, yg],
+                 check)
