@@ -730,7 +730,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_moe_skinny(
     __syncthreads();
 
     const bool a_ok = j < nrows;
-    const int8_t* ap = qx + (int64_t)(pair_lds[a_ok ? j : 0] / k) * K + g * 16;
+    const int8_t* ap = qx + (int64_t)(pair_lds[a_ok ? j : 0] / k) * K + g * 16;  // k = 1: qa rows
     // gemm1: the token scales of the lane's four pair rows (rows past the
     // block read pair id 0), loaded before the k loop
     float sxv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1521,20 +1521,95 @@ __device__ __forceinline__ float rot_silu_pair(float h) {
   return sg * partner;
 }
 
+// Decodes a bf16 scale as m * 2^x with m a signed integer (|m| <= 255);
+// returns false for Inf / NaN.
+__device__ __forceinline__ bool bf16_int_exp(uint32_t bits, int& m, int& x) {
+  const int ef = (bits >> 7) & 0xff;
+  const int f = bits & 0x7f;
+  if (ef == 0xff) return false;
+  m = ef == 0 ? f : 128 + f;
+  x = ef == 0 ? -133 : ef - 134;
+  if (bits & 0x8000u) m = -m;
+  return true;
+}
+
+// The exact integer form of one column's g128 fold.  The definition sums
+// double(acc_g) * double(s_g) over the 128-groups in order, in fp64.  With
+// s_g = m_g 2^x_g (m_g an integer, |m_g| <= 255) and xm the least x_g of the
+// column's non-zero scales, every term is an integer multiple of 2^xm; if
+// D = sum_g |m_g| 2^(x_g - xm) < 2^31, every partial sum is an integer of
+// magnitude below 2^21 D < 2^52 times 2^xm (|acc_g| <= 128^3), so each fp64
+// addition is exact and the sum equals S 2^xm with S = sum_g acc_g M_g,
+// M_g = m_g 2^(x_g - xm), exact in int64 in any order.  Writes M_g and the
+// fp32 scales of the column's G (<= MAXG) groups, 2^xm, and whether the
+// integer form applies.  The scales come in with independent loads.
+template <int MAXG>
+__device__ __forceinline__ void rot_col_scales(const uint16_t* __restrict__ sp, int G,
+                                               int32_t* m_out, float* s_out, float& cs,
+                                               bool& ok) {
+  uint32_t bits[MAXG];
+#pragma unroll
+  for (int gg = 0; gg < MAXG; gg++) bits[gg] = gg < G ? sp[gg] : 0u;
+  int mm[MAXG], xx[MAXG];
+  int xm = 1 << 20;
+  ok = true;
+#pragma unroll
+  for (int gg = 0; gg < MAXG; gg++) {
+    mm[gg] = 0;
+    xx[gg] = 0;
+    if (gg < G) {
+      s_out[gg] = bf16_bits_to_f32(bits[gg]);
+      if (!bf16_int_exp(bits[gg], mm[gg], xx[gg])) {
+        ok = false;
+        mm[gg] = 0;
+      } else if (mm[gg] != 0) {
+        xm = min(xm, xx[gg]);
+      }
+    }
+  }
+  if (xm == (1 << 20)) xm = 0;
+  long long D = 0;
+#pragma unroll
+  for (int gg = 0; gg < MAXG; gg++) {
+    if (gg < G) {
+      int Mg = 0;
+      if (mm[gg] != 0) {
+        const int sh = xx[gg] - xm;
+        if (sh > 23) {
+          ok = false;
+        } else {
+          Mg = mm[gg] * (1 << sh);
+          D += Mg < 0 ? -(long long)Mg : (long long)Mg;
+        }
+      }
+      m_out[gg] = Mg;
+    }
+  }
+  if (D >= (1LL << 31)) ok = false;
+  cs = ldexpf(1.0f, xm);
+}
+
 // Grouped GEMM with per-group scales, split over K (small batches).  The
 // workgroup takes one 16-column tile of one weight matrix (blockIdx.x) and
-// its pair rows in blocks of 16; wave w computes the exact int32 sums of the
-// 128-groups w, w + WAVES, ... (two 16x16x64 MFMA steps each) into LDS, and
-// wave 0 folds them in group order (fixed order: deterministic, and equal to
-// the definition):
-//   kRotSilu:     t = sum_g acc_g s[c, g] (fp64); h = (float)(t sx 2^-7);
-//                 SiLU(gate) * up -> fp32 activation [pair, c / 2];
+// its pair rows in blocks of 16; wave w takes the 128-groups w, w + WAVES, ...
+// (two 16x16x64 MFMA steps each).  For g128 the waves leave every group's
+// int32 sums in LDS and the fold walks the groups in order in fp64, as
+// defined; for g256 each wave adds su8 * acc into int64 sums as its groups
+// complete and the waves' sums are added through LDS (exact, so the order is
+// free).  The epilogue runs on four waves, one output row of each lane's
+// four a wave:
+//   kRotSilu:     h = (float)(t sx 2^-7), t the fold; SiLU(gate) * up ->
+//                 fp32 activation [pair, c / 2];
 //   kRotActRot:   the prologue rotates each pair's fp32 activation row, takes
 //                 its per-row scale and writes its codes into LDS in the
 //                 packed operand layout; y = (float)(t sa 2^-7) -> fp32;
+//   kRotCodes:    as kRotActRot with the rotated codes and scales given
+//                 (qx = qa [P, K], sx = sa [P], k = 1);
 //   kRotG256Silu: T = sum over 256-groups of su8 (acc_2g + acc_2g+1), exact
 //                 in int64; h = (float)(T sx s2 2^-7); SiLU(gate) * up.
-// W is packed (16-row tiles of 1 KiB k-steps), as [E * Nw, K].
+// W is packed (16-row tiles of 1 KiB k-steps), as [E * Nw, K].  In the dense
+// form (expert_list == nullptr) the rows are [64 blockIdx.y, +64) of a
+// plain matrix (pair p = row p).
 template <int MODE, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
     const int8_t* __restrict__ qx, const float* __restrict__ sx, const float* __restrict__ act,
@@ -1545,8 +1620,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
     int8_t* __restrict__ qa_rec, float* __restrict__ sa_rec) {
   constexpr int MAXG = 32;  // K <= 4096
   constexpr int GW = MAXG / WAVES;
+  constexpr bool G256 = MODE == kRotG256Silu;
   __shared__ v4i red[MAXG][64];
-  __shared__ float s_lds[MODE == kRotG256Silu ? 1 : 16][MAXG];
+  __shared__ long long sred[WAVES][4][64];
+  __shared__ int32_t m_lds[16][MAXG];
+  __shared__ float s_lds[16][MAXG];
+  __shared__ float cs_lds[16];
   __shared__ __attribute__((aligned(16))) int8_t a_lds[MODE == kRotActRot ? 16 * 2048 : 16];
   __shared__ float sa_lds[16];
   __shared__ int pair_lds[16];
@@ -1560,15 +1639,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
   const int nk = K >> 6;
   const int G = K >> 7;
   const int tile = blockIdx.x;
-  const int col = tile * 16 + j;
   const int8_t* wbase = W + ((int64_t)rr.e * (Nw >> 4) + tile) * nk * 1024 + lane * 16;
 
-  if (MODE != kRotG256Silu) {
-    for (int i = threadIdx.x; i < 16 * G; i += WAVES * 64) {
-      const int cc = i / G, gg = i - cc * G;
-      s_lds[cc][gg] = bf16_bits_to_f32(sW[((int64_t)rr.e * Nw + tile * 16 + cc) * G + gg]);
-    }
-  }
   v4i bw[GW][2];
 #pragma unroll
   for (int i = 0; i < GW; i++) {
@@ -1577,14 +1649,37 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
     for (int h = 0; h < 2; h++)
       bw[i][h] = gg < G ? ld_stream(wbase + (int64_t)(2 * gg + h) * 1024) : v4i{0, 0, 0, 0};
   }
+  if (G256) {
+    if (threadIdx.x < 16) {
+      const int c = threadIdx.x;
+      const int col = tile * 16 + c;
+      const uint8_t* sp = su8 + (int64_t)col * (K >> 8);
+      uint32_t u[MAXG / 2];
+#pragma unroll
+      for (int i = 0; i < MAXG / 2; i++) u[i] = 2 * i < G ? sp[i] : 0u;
+#pragma unroll
+      for (int gg = 0; gg < MAXG; gg++)
+        if (gg < G) m_lds[c][gg] = (int32_t)u[gg >> 1];
+      cs_lds[c] = bf16_bits_to_f32(sW[col]);
+    }
+  } else {
+    for (int i = threadIdx.x; i < 16 * G; i += WAVES * 64) {
+      const int cc = i / G, gg = i - cc * G;
+      s_lds[cc][gg] = bf16_bits_to_f32(sW[((int64_t)rr.e * Nw + tile * 16 + cc) * G + gg]);
+    }
+  }
+  // g256 folds su8 * acc in int64 (exact, its definition) as each wave's
+  // groups complete; g128 leaves the group sums in LDS for the fp64 fold in
+  // group order (few outputs per workgroup here: the fold is cheap)
+  constexpr bool fast = G256;
 
   for (int pb = rr.begin; pb < rr.end; pb += 16) {
     const int nrows = min(16, rr.end - pb);
     __syncthreads();  // the previous block's LDS consumed
     if (threadIdx.x < 16)
-      pair_lds[threadIdx.x] = threadIdx.x < nrows
-                                  ? (dense ? pb + (int)threadIdx.x : sorted_pairs[pb + threadIdx.x])
-                                  : 0;
+      pair_lds[threadIdx.x] =
+          threadIdx.x < nrows ? (dense ? pb + (int)threadIdx.x : sorted_pairs[pb + threadIdx.x])
+                              : 0;
     __syncthreads();
     if (MODE == kRotActRot) {
       for (int r = wv; r < nrows; r += WAVES) {
@@ -1608,11 +1703,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
           if (tile == 0 && sa_rec) sa_rec[pair_lds[r]] = sv;
         }
       }
-      __syncthreads();
     }
+    if (MODE != kRotActRot && threadIdx.x < 16)
+      sa_lds[threadIdx.x] = sx[pair_lds[threadIdx.x < nrows ? threadIdx.x : 0] / k];
+    __syncthreads();
 
     const bool a_ok = j < nrows;
     const int8_t* ap = qx + (int64_t)(pair_lds[a_ok ? j : 0] / k) * K + g * 16;
+    long long S[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < GW; i++) {
       const int gg = wv + i * WAVES;
@@ -1628,169 +1726,570 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
             a = a_ok ? *reinterpret_cast<const v4i*>(ap + (int64_t)c * 64) : v4i{0, 0, 0, 0};
           acc = mfma_16x16x64_i8(a, bw[i][h], acc);
         }
-        red[gg][lane] = acc;
+        if (fast) {
+          const long long M = m_lds[j][gg];
+#pragma unroll
+          for (int v = 0; v < 4; v++) S[v] += (long long)acc[v] * M;
+        } else {
+          red[gg][lane] = acc;
+        }
       }
+    }
+    if (fast) {
+#pragma unroll
+      for (int v = 0; v < 4; v++) sred[wv][v][lane] = S[v];
     }
     __syncthreads();
-    if (wv != 0) continue;
-    // lane holds rows 4 g + v of column col
-    float hv[4];
+    if (wv >= 4) continue;
+    // wave v finishes element v of every lane: row 4 (lane / 16) + v, column
+    // tile * 16 + lane % 16
+    const int v = wv;
+    const int r = 4 * g + v;
+    const int rc = min(r, nrows - 1);
+    double t;
+    if (fast) {
+      long long tot = 0;
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-      const int r = min(4 * g + v, nrows - 1);
-      const float rs = MODE == kRotActRot ? sa_lds[r] : sx[pair_lds[r] / k];
-      double t;
-      if (MODE == kRotG256Silu) {
-        const int G2 = K >> 8;
-        const uint8_t* sp = su8 + (int64_t)col * G2;
-        long long ts = 0;
-        for (int gg = 0; gg < G2; gg++)
-          ts += (long long)sp[gg] * (long long)(red[2 * gg][lane][v] + red[2 * gg + 1][lane][v]);
-        t = (double)ts * (double)rs;
-        t = t * (double)bf16_bits_to_f32(sW[col]);
-      } else {
-        t = 0.0;
-        for (int gg = 0; gg < G; gg++) t = t + (double)red[gg][lane][v] * (double)s_lds[j][gg];
-        t = t * (double)rs;
-      }
-      t = t * 0.0078125;
-      hv[v] = (float)t;
+      for (int w = 0; w < WAVES; w++) tot += sred[w][v][lane];
+      t = G256 ? (double)tot : (double)tot * (double)cs_lds[j];
+    } else {
+      t = 0.0;
+      for (int gg = 0; gg < G; gg++) t = t + (double)red[gg][lane][v] * (double)s_lds[j][gg];
     }
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-      const int r = 4 * g + v;
-      const bool valid = r < nrows;
-      const int p = pair_lds[valid ? r : 0];
-      if (MODE == kRotActRot) {
-        if (valid) out[(int64_t)p * ldo + col] = hv[v];
-      } else {
-        const float a = rot_silu_pair(hv[v]);
-        if ((j & 1) == 0 && valid) out[(int64_t)p * ldo + (col >> 1)] = a;
-      }
+    t = t * (double)sa_lds[rc];
+    if (G256) t = t * (double)cs_lds[j];
+    t = t * 0.0078125;
+    const float hv = (float)t;
+    const int p = pair_lds[rc];
+    const int col = tile * 16 + j;
+    if (MODE == kRotActRot || MODE == kRotCodes) {
+      if (r < nrows) out[(int64_t)p * ldo + col] = hv;
+    } else {
+      const float a = rot_silu_pair(hv);
+      if ((j & 1) == 0 && r < nrows) out[(int64_t)p * ldo + (col >> 1)] = a;
     }
   }
 }
 
-// Grouped GEMM with per-group scales, row-blocked (large batches).  The
-// workgroup takes 16 WAVES columns of one weight matrix (wave w: columns
-// 16 (WAVES blockIdx.x + w) + 0..15) and its pair rows in blocks of 32; each
-// wave walks all of K for two 16-row blocks and folds every group into fp64
-// (int64 for kRotG256Silu) accumulators as it goes, in group order — the same
-// arithmetic as k_rot_gemm_splitk.  kRotCodes reads the rotated codes and
-// scales of each pair row (qa [P, K], sa [P]) and writes fp32 y rows.
-template <int MODE, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_rows(
-    const int8_t* __restrict__ qx, const float* __restrict__ sx, int k,
+// A single token in the Hadamard domain: two launches.  k_rot_t1_gemm1 fuses
+// the routing and the rotated quant of x into gemm1 (every workgroup repeats
+// them: wave 0 routes, wave 1 rotates and quantises the row into LDS; the
+// first workgroup also writes the routing and the codes out), then folds
+// its pair's 16 columns as k_rot_gemm_splitk.  k_rot_t1_gemm2 takes 16
+// output columns for all k pairs: its prologue rotates and requantises the
+// k activation rows into LDS, each (pair, group) unit runs the two MFMA
+// steps of that pair's expert, the fold gives y2 for every pair, and the
+// epilogue combines them in slot order (plus the shared term) into bf16 out.
+__global__ __launch_bounds__(512) void k_rot_t1_gemm1(
+    const uint16_t* __restrict__ x, const float* __restrict__ logits, int H, int E, int k,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, const int8_t* __restrict__ W,
+    const uint16_t* __restrict__ sW, int Nw, int8_t* __restrict__ qx_rec,
+    float* __restrict__ sx_rec, float* __restrict__ act, int I) {
+  constexpr int WAVES = 8, MAXG = 32, GW = MAXG / WAVES;
+  __shared__ v4i red[MAXG][64];
+  __shared__ float s_lds[16][MAXG];
+  __shared__ __attribute__((aligned(16))) int8_t q_lds[4096];
+  __shared__ float sx_lds;
+  __shared__ int e_lds;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int tile = blockIdx.x, slot = blockIdx.y;
+  const int nk = H >> 6;
+  const int G = H >> 7;
+  const bool first = tile == 0 && slot == 0;
+  if (wv == 0) {
+    int sel_e = 0;
+    float sel_w = 0.0f;
+    if (logits) {
+      route_select(logits, E, k, lane, sel_e, sel_w);
+      if (first && lane < k) {
+        topk_ids[lane] = sel_e;
+        topk_w[lane] = sel_w;
+      }
+    } else {
+      sel_e = lane < k ? topk_ids[lane] : 0;
+    }
+    const int es = __shfl(sel_e, slot, 64);
+    if (lane == 0) e_lds = es;
+  } else if (wv == 1) {
+    rot_quant_row_wave<8>(x, H, q_lds, &sx_lds, lane);
+  }
+  __syncthreads();
+  const int e = __builtin_amdgcn_readfirstlane(e_lds);
+  const int8_t* wbase = W + ((int64_t)e * (Nw >> 4) + tile) * nk * 1024 + lane * 16;
+  v4i bw[GW][2];
+#pragma unroll
+  for (int i = 0; i < GW; i++) {
+    const int gg = wv + i * WAVES;
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+      bw[i][h] = gg < G ? ld_stream(wbase + (int64_t)(2 * gg + h) * 1024) : v4i{0, 0, 0, 0};
+  }
+  for (int i = threadIdx.x; i < 16 * G; i += WAVES * 64) {
+    const int cc = i / G, gg = i - cc * G;
+    s_lds[cc][gg] = bf16_bits_to_f32(sW[((int64_t)e * Nw + tile * 16 + cc) * G + gg]);
+  }
+  if (first && qx_rec) {
+    for (int i = threadIdx.x; i < (H >> 4); i += WAVES * 64)
+      *reinterpret_cast<v4i*>(qx_rec + i * 16) = *reinterpret_cast<const v4i*>(q_lds + i * 16);
+    if (threadIdx.x == 0) sx_rec[0] = sx_lds;
+  }
+  // the token is row 0 of the A tile (lanes with j == 0 feed it)
+#pragma unroll
+  for (int i = 0; i < GW; i++) {
+    const int gg = wv + i * WAVES;
+    if (gg < G) {
+      v4i acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int c = 2 * gg + h;
+        const v4i a = j == 0 ? *reinterpret_cast<const v4i*>(q_lds + c * 64 + g * 16)
+                             : v4i{0, 0, 0, 0};
+        acc = mfma_16x16x64_i8(a, bw[i][h], acc);
+      }
+      red[gg][lane] = acc;
+    }
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  // row 0 of column tile * 16 + j sits in element 0 of lane j (g == 0)
+  double t = 0.0;
+  for (int gg = 0; gg < G; gg++) t = t + (double)red[gg][j][0] * (double)s_lds[j][gg];
+  t = t * (double)sx_lds;
+  t = t * 0.0078125;
+  const float a = rot_silu_pair((float)t);
+  if (g == 0 && (j & 1) == 0) act[(int64_t)slot * I + ((tile * 16 + j) >> 1)] = a;
+}
+
+// k * (I / 128) <= kRotT1MaxUnits (pair, group) units; I <= 1024
+constexpr int kRotT1MaxUnits = 64;
+
+__global__ __launch_bounds__(512) void k_rot_t1_gemm2(
+    const float* __restrict__ act, int I, int k, const int32_t* __restrict__ topk_ids,
+    const float* __restrict__ topk_w, const int8_t* __restrict__ W,
+    const uint16_t* __restrict__ sW, int H, const float* __restrict__ shared,
+    uint16_t* __restrict__ out, int8_t* __restrict__ qa_rec, float* __restrict__ sa_rec) {
+  constexpr int WAVES = 8, UW = kRotT1MaxUnits / WAVES;
+  __shared__ v4i red[kRotT1MaxUnits][64];
+  __shared__ __attribute__((aligned(16))) int8_t a_lds[16 * 1024];
+  __shared__ float s_lds[kRotT1MaxUnits][16];
+  __shared__ float sa_lds[16], w_lds[16], y_lds[16][16];
+  __shared__ int e_lds[16];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int tile = blockIdx.x;
+  const int nk = I >> 6;
+  const int G = I >> 7;
+  const int U = k * G;
+  if (threadIdx.x < k) {
+    e_lds[threadIdx.x] = topk_ids[threadIdx.x];
+    w_lds[threadIdx.x] = topk_w[threadIdx.x];
+  }
+  __syncthreads();
+  // the weight fragments of this wave's (pair, group) units
+  v4i bw[UW][2];
+#pragma unroll
+  for (int i = 0; i < UW; i++) {
+    const int u = wv + i * WAVES;
+    const int pr = u / G, gg = u - (u / G) * G;
+    const int8_t* wb = W + ((int64_t)e_lds[u < U ? pr : 0] * (H >> 4) + tile) * nk * 1024 +
+                       lane * 16 + (int64_t)(2 * gg) * 1024;
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+      bw[i][h] = u < U ? ld_stream(wb + h * 1024) : v4i{0, 0, 0, 0};
+  }
+  for (int i = threadIdx.x; i < U * 16; i += WAVES * 64) {
+    const int u = i >> 4, c = i & 15;
+    const int pr = u / G, gg = u - pr * G;
+    s_lds[u][c] = bf16_bits_to_f32(sW[((int64_t)e_lds[pr] * H + tile * 16 + c) * G + gg]);
+  }
+  // rotated requant of the k activation rows into LDS (packed operand rows)
+  for (int r = wv; r < k; r += WAVES) {
+    Block8 bb[2];
+    const float am = rot_row_wave<2>(act + (int64_t)r * I, I, bb, lane);
+    const float sc = am / 127.0f;
+#pragma unroll
+    for (int rd = 0; rd < 2; rd++) {
+      const int blk = rd * 4 + g;
+      if (blk >= G) continue;
+      const uint2 wd = rot_codes8(bb[rd], am, sc);
+      const int kk = blk * 128 + j * 8;
+      *reinterpret_cast<uint2*>(a_lds + (kk >> 6) * 1024 + (r + 16 * ((kk & 63) >> 4)) * 16 +
+                                (kk & 15)) = wd;
+      if (tile == 0 && qa_rec) *reinterpret_cast<uint2*>(qa_rec + (int64_t)r * I + kk) = wd;
+    }
+    if (lane == 0) {
+      const float sv = am != 0.0f ? sc : 0.0f;
+      sa_lds[r] = sv;
+      if (tile == 0 && sa_rec) sa_rec[r] = sv;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < UW; i++) {
+    const int u = wv + i * WAVES;
+    if (u < U) {
+      const int gg = u % G;
+      v4i acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+        acc = mfma_16x16x64_i8(*reinterpret_cast<const v4i*>(&a_lds[(2 * gg + h) * 1024 +
+                                                                       lane * 16]),
+                               bw[i][h], acc);
+      red[u][lane] = acc;
+    }
+  }
+  __syncthreads();
+  // y2 of pair pr, column c: row pr of the pair's own units (lane 16 (pr / 4)
+  // + c, element pr % 4), folded in group order
+  if (threadIdx.x < k * 16) {
+    const int pr = threadIdx.x >> 4, c = threadIdx.x & 15;
+    const int L = (pr >> 2) * 16 + c;
+    double t = 0.0;
+    for (int gg = 0; gg < G; gg++)
+      t = t + (double)red[pr * G + gg][L][pr & 3] * (double)s_lds[pr * G + gg][c];
+    t = t * (double)sa_lds[pr];
+    t = t * 0.0078125;
+    y_lds[pr][c] = (float)t;
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int c = threadIdx.x;
+    float acc = 0.0f;
+    for (int pr = 0; pr < k; pr++) {
+      const float term = w_lds[pr] * y_lds[pr][c];
+      acc = acc + term;
+    }
+    if (shared) acc = acc + shared[tile * 16 + c];
+    out[tile * 16 + c] = (uint16_t)f32_to_bf16_bits(acc);
+  }
+}
+
+// Grouped GEMM with per-group scales, LDS-tiled (large batches).  Workgroup =
+// 64 pair rows (half of one 128-row m-block of the expert sort, or rows
+// [128 mb + 64 half, +64) of a plain matrix in the DENSE form) x 128 weight
+// rows; wave w takes weight rows 32 w .. 32 w + 31 (two 16-row tiles) of
+// all 64 pair rows (four 16-row blocks, 16x16x64 MFMA).  The activation rows
+// are gathered into LDS (packed operand layout, two buffers), the weights
+// stream from HBM PF k steps ahead.
+//
+// The fold after every 128-group: a wave whose 32 columns all have the
+// integer form of the fold (rot_col_scales) adds acc_g M_g into int64 sums;
+// any other wave folds in fp64 in group order, as defined.  kRotG256Silu
+// folds su8 * acc in int64 (exact, as its definition).
+template <int MODE, bool DENSE>
+__global__ __launch_bounds__(256, 2) void k_rot_tile(
+    const int8_t* __restrict__ A, const float* __restrict__ sA, int a_div,
     const int8_t* __restrict__ W, const uint16_t* __restrict__ sW,
     const uint8_t* __restrict__ su8, int Nw, int K, const int32_t* __restrict__ expert_list,
-    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ n_active,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ blk_slot,
+    const int32_t* __restrict__ blk_row0, const int32_t* __restrict__ n_blocks,
     const int32_t* __restrict__ sorted_pairs, int dense_rows, float* __restrict__ out,
-    int ldo) {
-  constexpr int RB = 2;  // 16-row blocks per pass
-  __shared__ int pair_lds[RB * 16];
-  RotRows rr;
-  if (!rot_rows(expert_list, seg_off, n_active, dense_rows, 128, rr)) return;
-  const bool dense = expert_list == nullptr;
+    int ldo, int ncb) {
+  constexpr int BM = 64, BN = 128, MAXG = 32, CH = 4;
+  constexpr bool G256 = MODE == kRotG256Silu;
+  __shared__ __attribute__((aligned(1024))) int8_t a_lds[2][CH][4 * 1024];
+  __shared__ int pair_lds[BM];
+  __shared__ float sa_lds[BM];
+  __shared__ int32_t m_lds[BN][MAXG + 1];  // rows padded: lanes read 16 rows at once
+  __shared__ float s_lds[G256 ? 1 : BN][MAXG + 1];
+  __shared__ float cs_lds[BN];  // 2^xm (g128) or the bf16 row scale (g256)
+  __shared__ int ok_lds[BN];
+
+  const int ngrp = Nw / (BN * ncb);  // workgroups across the weight rows
+  const int xcd = blockIdx.x & 7;
+  const int tq = blockIdx.x >> 3;
+  const int nper = 2 * ngrp;
+  const int mb = (tq / nper) * 8 + xcd;
+  const int rem = tq - (tq / nper) * nper;
+  const int half = rem & 1;
+  const int nfirst0 = (rem >> 1) * BN * ncb;
+  int e = 0, row0, rows;
+  if (DENSE) {
+    row0 = mb * 128 + half * 64;
+    rows = min(BM, dense_rows - row0);
+  } else {
+    if (mb >= n_blocks[0]) return;
+    const int slot = blk_slot[mb];
+    const int r0 = blk_row0[mb];
+    row0 = r0 + half * 64;
+    rows = min(r0 + 128, seg_off[slot + 1]) - row0;
+    e = expert_list[slot];
+  }
+  if (rows <= 0) return;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int j = lane & 15;
   const int g = lane >> 4;
   const int nk = K >> 6;
   const int G = K >> 7;
-  const int tile = blockIdx.x * WAVES + wv;
-  const int col = tile * 16 + j;
-  const int8_t* wbase = W + ((int64_t)rr.e * (Nw >> 4) + tile) * nk * 1024 + lane * 16;
-  const uint16_t* srow = sW + ((int64_t)rr.e * Nw + col) * (MODE == kRotG256Silu ? 1 : G);
-  const uint8_t* sp = MODE == kRotG256Silu ? su8 + (int64_t)col * (K >> 8) : nullptr;
+  const int nsteps = (nk + 2 * CH - 1) / (2 * CH) * (2 * CH);
 
-  for (int pb = rr.begin; pb < rr.end; pb += RB * 16) {
-    const int nrows = min(RB * 16, rr.end - pb);
-    __syncthreads();
-    if (threadIdx.x < RB * 16)
-      pair_lds[threadIdx.x] = threadIdx.x < nrows
-                                  ? (dense ? pb + (int)threadIdx.x : sorted_pairs[pb + threadIdx.x])
-                                  : 0;
-    __syncthreads();
-    const int8_t* ap[RB];
-    bool aok[RB];
+  if (threadIdx.x < BM) {
+    const int r = min((int)threadIdx.x, rows - 1);
+    const int p = DENSE ? row0 + r : sorted_pairs[row0 + r];
+    pair_lds[threadIdx.x] = p;
+    sa_lds[threadIdx.x] = sA[p / a_div];
+  }
+
+  // ncb blocks of BN weight rows in turn: the pair rows, their scales and
+  // the gathered activation rows' addresses are read once for all of them
+  for (int cbk = 0; cbk < ncb; cbk++) {
+    const int nfirst = nfirst0 + cbk * BN;
+    // weight fragments: tiles nfirst / 16 + 2 wv + cb
+    const int8_t* bsrc = W + ((int64_t)e * (Nw >> 4) + (nfirst >> 4) + 2 * wv) * nk * 1024 +
+                         lane * 16;
+    const int64_t tstride = (int64_t)nk * 1024;
+    // plain loads: the two 64-row halves of an m-block read the same weight
+    // rows back to back on one XCD, the second from L2
+    auto load_b = [&](int st, v4i* b) __attribute__((always_inline)) {
+      const int c = st < nk ? st : 0;
+      b[0] = *reinterpret_cast<const v4i*>(bsrc + (int64_t)c * 1024);
+      b[1] = *reinterpret_cast<const v4i*>(bsrc + tstride + (int64_t)c * 1024);
+    };
+    if (G256) {
+      if (threadIdx.x < BN) {
+        const int c = threadIdx.x;
+        const int col = nfirst + c;
+        const uint8_t* sp = su8 + (int64_t)col * (K >> 8);
+        uint32_t u[MAXG / 2];
 #pragma unroll
-    for (int b = 0; b < RB; b++) {
-      const int r = b * 16 + j;
-      aok[b] = r < nrows;
-      const int p = pair_lds[aok[b] ? r : 0];
-      ap[b] = (MODE == kRotCodes ? qx + (int64_t)p * K : qx + (int64_t)(p / k) * K) + g * 16;
-    }
-    double t[RB][4];
-    long long ts[RB][4];
+        for (int i = 0; i < MAXG / 2; i++) u[i] = 2 * i < G ? sp[i] : 0u;
 #pragma unroll
-    for (int b = 0; b < RB; b++)
-#pragma unroll
-      for (int v = 0; v < 4; v++) {
-        t[b][v] = 0.0;
-        ts[b][v] = 0;
+        for (int gg = 0; gg < MAXG; gg++)
+          if (gg < G) m_lds[c][gg] = (int32_t)u[gg >> 1];
+        cs_lds[c] = bf16_bits_to_f32(sW[col]);
+        ok_lds[c] = 1;
       }
-    for (int gg = 0; gg < G; gg++) {
-      const v4i b0 = ld_stream(wbase + (int64_t)(2 * gg) * 1024);
-      const v4i b1 = ld_stream(wbase + (int64_t)(2 * gg + 1) * 1024);
-      v4i acc[RB];
-#pragma unroll
-      for (int b = 0; b < RB; b++) {
-        const v4i a0 = aok[b] ? *reinterpret_cast<const v4i*>(ap[b] + (int64_t)(2 * gg) * 64)
-                              : v4i{0, 0, 0, 0};
-        const v4i a1 = aok[b] ? *reinterpret_cast<const v4i*>(ap[b] + (int64_t)(2 * gg + 1) * 64)
-                              : v4i{0, 0, 0, 0};
-        acc[b] = mfma_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0});
-        acc[b] = mfma_16x16x64_i8(a1, b1, acc[b]);
+    } else {
+      // the tile's BN x G scales (contiguous) decoded element-wise, the
+      // exponents held in the activation buffer until the main loop
+      int* x_tmp = reinterpret_cast<int*>(&a_lds[0][0][0]);  // [BN][MAXG + 1]
+      const uint16_t* sp = sW + ((int64_t)e * Nw + nfirst) * G;
+      const int n = BN * G;
+#pragma unroll 8
+      for (int i = threadIdx.x; i < n; i += 256) {
+        const uint32_t bits = sp[i];
+        const int c = i / G, gg = i - c * G;
+        int m = 0, x = 0;
+        const bool fin = bf16_int_exp(bits, m, x);
+        s_lds[c][gg] = bf16_bits_to_f32(bits);
+        m_lds[c][gg] = fin ? m : 0;
+        x_tmp[c * (MAXG + 1) + gg] = fin ? x : (1 << 20);  // 1 << 20 marks Inf / NaN
       }
-      if (MODE == kRotG256Silu) {
-        // both 128-halves of a 256-group take its u8 scale; exact in int64
-        const long long u = (long long)sp[gg >> 1];
-#pragma unroll
-        for (int b = 0; b < RB; b++)
-#pragma unroll
-          for (int v = 0; v < 4; v++) ts[b][v] += u * (long long)acc[b][v];
-      } else {
-        const double s = (double)bf16_bits_to_f32(srow[gg]);
-#pragma unroll
-        for (int b = 0; b < RB; b++)
-#pragma unroll
-          for (int v = 0; v < 4; v++) t[b][v] = t[b][v] + (double)acc[b][v] * s;
+      lds_barrier();
+      // two threads a column, alternate groups: least exponent, multipliers,
+      // the bound D and the check, combined across the pair
+      const int c = threadIdx.x >> 1, h = threadIdx.x & 1;
+      int xm = 1 << 20;
+      bool ok = true;
+      for (int gg = h; gg < G; gg += 2) {
+        const int x = x_tmp[c * (MAXG + 1) + gg];
+        if (x == (1 << 20)) ok = false;
+        else if (m_lds[c][gg] != 0) xm = min(xm, x);
       }
-    }
-#pragma unroll
-    for (int b = 0; b < RB; b++) {
-#pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int r = b * 16 + 4 * g + v;
-        const bool valid = r < nrows;
-        const int p = pair_lds[valid ? r : 0];
-        const float rs = MODE == kRotCodes ? sx[p] : sx[p / k];
-        double tv;
-        if (MODE == kRotG256Silu) {
-          tv = (double)ts[b][v] * (double)rs;
-          tv = tv * (double)bf16_bits_to_f32(srow[0]);
-        } else {
-          tv = t[b][v] * (double)rs;
+      xm = min(xm, __shfl_xor(xm, 1, 64));
+      if (xm == (1 << 20)) xm = 0;
+      long long D = 0;
+      for (int gg = h; gg < G; gg += 2) {
+        const int m = m_lds[c][gg];
+        int Mg = 0;
+        if (m != 0) {
+          const int sh = x_tmp[c * (MAXG + 1) + gg] - xm;
+          if (sh > 23 || sh < 0) {
+            ok = false;
+          } else {
+            Mg = m * (1 << sh);
+            D += Mg < 0 ? -(long long)Mg : (long long)Mg;
+          }
         }
-        tv = tv * 0.0078125;
-        const float h = (float)tv;
-        if (MODE == kRotCodes) {
-          if (valid) out[(int64_t)p * ldo + col] = h;
-        } else {
-          const float a = rot_silu_pair(h);
-          if ((j & 1) == 0 && valid) out[(int64_t)p * ldo + (col >> 1)] = a;
+        m_lds[c][gg] = Mg;
+      }
+      // both shuffles run on every lane (a shuffle inside a short-circuited
+      // expression would read an inactive partner)
+      D += __shfl_xor(D, 1, 64);
+      const int ok_pair = __shfl_xor(ok ? 1 : 0, 1, 64);
+      ok = ok && ok_pair != 0 && D < (1LL << 31);
+      if (h == 0) {
+        cs_lds[c] = ldexpf(1.0f, xm);
+        ok_lds[c] = ok ? 1 : 0;
+      }
+    }
+    lds_barrier();
+
+    // activation rows: wave wv gathers 16-row block wv of each k step
+    const int8_t* asrc = A + (int64_t)(pair_lds[16 * wv + j] / a_div) * K + g * 16;
+    auto load_a = [&](int st) __attribute__((always_inline)) {
+      const int c = st < nk ? st : 0;
+      return *reinterpret_cast<const v4i*>(asrc + (int64_t)c * 64);
+    };
+    // this wave folds with integers when all of its 32 columns allow it
+    const bool fast = __all(ok_lds[32 * wv + (lane & 31)] != 0);
+
+    long long acc64[4][2][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+      for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) acc64[rb][cb][v] = 0;
+    v4i acc[4][2];
+
+    // The k steps go in chunks of CH, double-buffered: while a chunk is
+    // multiplied (its weights in one register set, its activation rows in one
+    // LDS buffer), the next chunk's loads are in flight (weights into the other
+    // register set, activation rows into staging registers).  The only waits
+    // are where the staged rows are stored into LDS, once per chunk: by then
+    // the whole chunk's compute has covered the loads' latency.  (A ring
+    // carried in registers from step to step makes the compiler wait for
+    // nearly every load at the loop head instead.)
+    v4i b0[CH][2], b1[CH][2];
+    v4i at[CH];
+    auto issue = [&](int c0, v4i (*bq)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < CH; u++) load_b(c0 + u, bq[u]);
+#pragma unroll
+      for (int u = 0; u < CH; u++) at[u] = load_a(c0 + u);  // last: their wait covers all
+    };
+    auto stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < CH; u++)
+        *reinterpret_cast<v4i*>(&a_lds[buf][u][wv * 1024 + lane * 16]) = at[u];
+    };
+    auto compute = [&](int c0, int buf, v4i (*bq)[2], auto fast_c) __attribute__((always_inline)) {
+      constexpr bool FAST = decltype(fast_c)::value;
+#pragma unroll
+      for (int u = 0; u < CH; u++) {
+        const int st = c0 + u;
+        v4i fa[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++)
+          fa[rb] = *reinterpret_cast<const v4i*>(&a_lds[buf][u][rb * 1024 + lane * 16]);
+        const bool kin = st < nk;
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++) {
+          const v4i bf = kin ? bq[u][cb] : v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int rb = 0; rb < 4; rb++)
+            acc[rb][cb] = mfma_16x16x64_i8(fa[rb], bf, (u & 1) ? acc[rb][cb] : v4i{0, 0, 0, 0});
+        }
+        if ((u & 1) && kin) {  // a 128-group is complete: fold it
+          const int gg = st >> 1;
+#pragma unroll
+          for (int cb = 0; cb < 2; cb++) {
+            const int c = 32 * wv + 16 * cb + j;
+            if (FAST) {
+              const long long M = m_lds[c][gg];
+#pragma unroll
+              for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+                for (int v = 0; v < 4; v++) acc64[rb][cb][v] += (long long)acc[rb][cb][v] * M;
+            } else {
+              const double sv = (double)s_lds[G256 ? 0 : c][gg];
+#pragma unroll
+              for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                  double t = __longlong_as_double(acc64[rb][cb][v]);
+                  t = t + (double)acc[rb][cb][v] * sv;
+                  acc64[rb][cb][v] = __double_as_longlong(t);
+                }
+            }
+          }
+        }
+      }
+    };
+
+    // the empty asm statements keep the compiler from moving a chunk's loads
+    // across the compute or the staging (scheduling barriers)
+    // the fold's form is fixed per wave before the loop, so each loop carries
+    // one form only (a branch inside it gets if-converted into both)
+    auto mainloop = [&](auto fast_c) __attribute__((always_inline)) {
+      issue(0, b0);
+      asm volatile("" ::: "memory");
+      stage(0);
+      lds_barrier();
+      for (int c0 = 0; c0 < nsteps; c0 += 2 * CH) {
+        issue(c0 + CH, b1);
+        asm volatile("" ::: "memory");
+        compute(c0, 0, b0, fast_c);
+        asm volatile("" ::: "memory");
+        stage(1);
+        lds_barrier();
+        issue(c0 + 2 * CH, b0);
+        asm volatile("" ::: "memory");
+        compute(c0 + CH, 1, b1, fast_c);
+        asm volatile("" ::: "memory");
+        stage(0);
+        lds_barrier();
+      }
+    };
+    if (G256 || fast)
+      mainloop(std::true_type{});
+    else
+      mainloop(std::false_type{});
+
+    // epilogue: lane holds rows 16 rb + 4 g + v of columns nfirst + 32 wv + 16 cb + j
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++) {
+      const int c = 32 * wv + 16 * cb + j;
+      const int col = nfirst + c;
+      const double cs = (double)cs_lds[c];
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++) {
+        float hv[4];
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          const int r = 16 * rb + 4 * g + v;
+          double t;
+          if (G256) {
+            t = (double)acc64[rb][cb][v] * (double)sa_lds[r];
+            t = t * cs;
+          } else {
+            t = fast ? (double)acc64[rb][cb][v] * cs : __longlong_as_double(acc64[rb][cb][v]);
+            t = t * (double)sa_lds[r];
+          }
+          t = t * 0.0078125;
+          hv[v] = (float)t;
+          if (MODE == kRotCodes && r < rows) out[(int64_t)pair_lds[r] * ldo + col] = hv[v];
+        }
+        if (MODE != kRotCodes) {
+          // gate = even column, up = the odd one in the neighbouring lane; the
+          // lane pair splits the rows: the even lane finishes v = 0, 1, the
+          // odd lane v = 2, 3 (one exp per output, not two)
+          float xv[4];
+#pragma unroll
+          for (int v = 0; v < 4; v++) xv[v] = __shfl_xor(hv[v], 1, 64);
+          const bool odd = j & 1;
+#pragma unroll
+          for (int q = 0; q < 2; q++) {
+            const int v = odd ? q + 2 : q;
+            const float gate = odd ? xv[q + 2] : hv[q];
+            const float up = odd ? hv[q + 2] : xv[q];
+            const float sg = (float)((double)gate / (1.0 + exp(-(double)gate)));
+            const int r = 16 * rb + 4 * g + v;
+            if (r < rows) out[(int64_t)pair_lds[r] * ldo + (col >> 1)] = sg * up;
+          }
         }
       }
     }
+    lds_barrier();  // LDS reused by the next weight-row block
   }
 }
 
-// pair counts up to this take the split-K GEMMs (and fuse the rotated requant
-// into gemm2's prologue); beyond it the row-blocked GEMMs and k_rot_requant.
+// pair counts up to kRotSplitMaxPairs take the split-K GEMMs with the rotated
+// requant fused into gemm2's prologue; up to kRotTileMinPairs the split-K
+// GEMMs around k_rot_requant; beyond it the LDS-tiled GEMMs.
 constexpr int64_t kRotSplitMaxPairs = 256;
+constexpr int64_t kRotTileMinPairs = 4096;
 
-hipError_t launch_rot_sort(const MoeArgs& a, const MoeWs& ws, int64_t P, hipStream_t stream) {
-  if (P <= kMoeSortOneWg) {
+hipError_t launch_rot_sort(const MoeArgs& a, const MoeWs& ws, int64_t P, bool blocks,
+                           hipStream_t stream) {
+  if (!blocks && P <= kMoeSortOneWg) {
     hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
                        ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax);
     return hipGetLastError();
@@ -1814,31 +2313,73 @@ hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const u
   const unsigned slots = (unsigned)std::min<int64_t>(a.E, P);
   const int I2 = 2 * a.I;
   hipError_t err;
+  if (a.T == 1 && a.k <= 16 && a.I <= 1024 && a.k * (a.I / 128) <= kRotT1MaxUnits) {
+    hipLaunchKernelGGL(k_rot_t1_gemm1, dim3(I2 / 16, a.k), dim3(512), 0, stream, a.x, a.logits,
+                       a.H, a.E, a.k, a.topk_ids, a.topk_w, a.w13, s13, I2, a.dbg_qx, a.dbg_sx,
+                       ws.act, a.I);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_rot_t1_gemm2, dim3(a.H / 16), dim3(512), 0, stream, ws.act, a.I, a.k,
+                       a.topk_ids, a.topk_w, a.w2, s2, a.H, shared, a.out, a.dbg_qa, a.dbg_sa2);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.dbg_act && (err = hipMemcpyAsync(a.dbg_act, ws.act, (size_t)P * a.I * 4,
+                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+      return err;
+    return hipSuccess;
+  }
   hipLaunchKernelGGL(k_rot_route_quant, dim3((a.T + 3) / 4), dim3(512), 0, stream, a.x, a.logits,
                      a.T, a.H, a.E, a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if ((err = launch_rot_sort(a, ws, P, stream)) != hipSuccess) return err;
-  if (P <= kRotSplitMaxPairs) {
+  const bool split = P <= kRotSplitMaxPairs;
+  const bool tiled = P > kRotTileMinPairs;
+  if ((err = launch_rot_sort(a, ws, P, tiled, stream)) != hipSuccess) return err;
+  if (!tiled) {
     hipLaunchKernelGGL((k_rot_gemm_splitk<kRotSilu, 8>), dim3(I2 / 16, slots), dim3(512), 0,
                        stream, ws.qx, ws.sx, nullptr, a.k, a.w13, s13, nullptr, I2, a.H,
                        ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.act, a.I,
                        nullptr, nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (split) {
     hipLaunchKernelGGL((k_rot_gemm_splitk<kRotActRot, 4>), dim3(a.H / 16, slots), dim3(256), 0,
                        stream, nullptr, nullptr, ws.act, a.k, a.w2, s2, nullptr, a.H, a.I,
                        ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.y2, a.H,
                        a.dbg_qa, a.dbg_sa2);
+  } else if (!tiled) {
+    hipLaunchKernelGGL(k_rot_requant, dim3((unsigned)((P + 7) / 8)), dim3(512), 0, stream,
+                       ws.act, P, a.I, ws.qa, ws.sa2);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotCodes, 4>), dim3(a.H / 16, slots), dim3(256), 0,
+                       stream, ws.qa, ws.sa2, nullptr, 1, a.w2, s2, nullptr, a.H, a.I,
+                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.y2, a.H,
+                       nullptr, nullptr);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)(P * a.I),
+                                          hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+      return err;
+    if (a.dbg_sa2 && (err = hipMemcpyAsync(a.dbg_sa2, ws.sa2, (size_t)P * 4,
+                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+      return err;
   } else {
-    hipLaunchKernelGGL((k_rot_gemm_rows<kRotSilu, 4>), dim3(I2 / 64, slots), dim3(256), 0,
-                       stream, ws.qx, ws.sx, a.k, a.w13, s13, nullptr, I2, a.H, ws.expert_list,
-                       ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.act, a.I);
+    // m-blocks of 128 pairs (at most one partial block per expert), two
+    // 64-row halves each, rounded up to the 8 XCDs
+    const unsigned max_blocks = (unsigned)((P / kMoeBM + slots + 7) / 8 * 8);
+    // one 128-row weight block a workgroup (measured on MI355X at 2048 tokens,
+    // 256 experts, H=2048, I=512: four blocks a workgroup, 300 / 195 us for
+    // gemm1 / gemm2, against 237 / 192 us with one)
+    const int ncb1 = 1, ncb2 = 1;
+    hipLaunchKernelGGL((k_rot_tile<kRotSilu, false>), dim3(max_blocks * 2 * (I2 / 128 / ncb1)),
+                       dim3(256), 0, stream, ws.qx, ws.sx, a.k, a.w13, s13, nullptr, I2, a.H,
+                       ws.expert_list, ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks,
+                       ws.sorted_pairs, 0, ws.act, a.I, ncb1);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_rot_requant, dim3((unsigned)((P + 7) / 8)), dim3(512), 0, stream,
                        ws.act, P, a.I, ws.qa, ws.sa2);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_rot_gemm_rows<kRotCodes, 4>), dim3(a.H / 64, slots), dim3(256), 0,
-                       stream, ws.qa, ws.sa2, 1, a.w2, s2, nullptr, a.H, a.I, ws.expert_list,
-                       ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.y2, a.H);
+    hipLaunchKernelGGL((k_rot_tile<kRotCodes, false>),
+                       dim3(max_blocks * 2 * (a.H / 128 / ncb2)), dim3(256), 0, stream, ws.qa,
+                       ws.sa2, 1, a.w2, s2, nullptr, a.H, a.I,
+                       ws.expert_list, ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks,
+                       ws.sorted_pairs, 0, ws.y2, a.H, ncb2);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)(P * a.I),
                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)
@@ -1915,17 +2456,17 @@ hipError_t launch_shared_expert(const SharedArgs& a, hipStream_t stream) {
                        nullptr, nullptr, ws.act, 1, a.wd, a.sd, nullptr, H, Is, nullptr, nullptr,
                        nullptr, nullptr, T, a.y, H, a.dbg_qa, a.dbg_sa);
   } else {
-    const unsigned rb = (unsigned)((a.T + 127) / 128);
-    hipLaunchKernelGGL((k_rot_gemm_rows<kRotG256Silu, 4>), dim3(2 * Is / 64, rb), dim3(256), 0,
-                       stream, ws.qx, ws.sx, 1, a.wgu, a.s2, a.su8, 2 * Is, H, nullptr, nullptr,
-                       nullptr, nullptr, T, ws.act, Is);
+    const unsigned mbs = (unsigned)((a.T + 1023) / 1024 * 8);  // 128-row blocks, x 8 XCDs
+    hipLaunchKernelGGL((k_rot_tile<kRotG256Silu, true>), dim3(mbs * 2 * (2 * Is / 128)),
+                       dim3(256), 0, stream, ws.qx, ws.sx, 1, a.wgu, a.s2, a.su8, 2 * Is, H,
+                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, T, ws.act, Is, 1);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_rot_requant, dim3((unsigned)((a.T + 7) / 8)), dim3(512), 0, stream,
                        ws.act, a.T, Is, ws.qa, ws.sa);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_rot_gemm_rows<kRotCodes, 4>), dim3(H / 64, rb), dim3(256), 0, stream,
-                       ws.qa, ws.sa, 1, a.wd, a.sd, nullptr, H, Is, nullptr, nullptr, nullptr,
-                       nullptr, T, a.y, H);
+    hipLaunchKernelGGL((k_rot_tile<kRotCodes, true>), dim3(mbs * 2 * (H / 128)), dim3(256), 0,
+                       stream, ws.qa, ws.sa, 1, a.wd, a.sd, nullptr, H, Is, nullptr, nullptr,
+                       nullptr, nullptr, nullptr, nullptr, T, a.y, H, 1);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)(a.T * a.Is),
                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)

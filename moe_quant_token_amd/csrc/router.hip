@@ -10,8 +10,10 @@
 //     chunks of the row (h = 512 c + 8 lane + 0..7) with fp32 FMAs (a bf16
 //     product is exact in fp32) for every token, then a butterfly reduction
 //     over the wave.  The weight row is read once for all tokens;
-//   - more tokens: bf16 MFMA (v_mfma_f32_16x16x32_bf16) tiles of 64 tokens x
-//     16 experts, one wave per 16 tokens walking all of H.
+//   - more tokens: bf16 MFMA (v_mfma_f32_16x16x32_bf16) tiles of 16 tokens x
+//     16 experts per wave, H split over 8 waves (up to 256 tokens) or 2
+//     waves (beyond, four token blocks a workgroup), the slices' partial sums
+//     added in slice order.
 // Layouts: x bf16 [T, H] with row stride ldx; wg bf16 [E, H] contiguous;
 // logits fp32 [T, E] with row stride ldl.
 #include "kernels.h"
@@ -66,44 +68,65 @@ __global__ __launch_bounds__(256) void k_router_wave(const uint16_t* __restrict_
   }
 }
 
-__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict__ x, int T, int H,
-                                                     int64_t ldx, const uint16_t* __restrict__ wg,
-                                                     float* __restrict__ logits, int64_t ldl) {
+// Workgroup = TB 16-token blocks x one 16-expert block; wave (tb, ks) takes
+// token block tb and the ks-th of KS equal slices of H (H / KS a multiple of
+// 32).  The KS partial sums are added in slice order by the first slice's
+// wave (fixed order).
+template <int TB, int KS>
+__global__ __launch_bounds__(TB * KS * 64) void k_router_mfma(
+    const uint16_t* __restrict__ x, int T, int H, int64_t ldx, const uint16_t* __restrict__ wg,
+    float* __restrict__ logits, int64_t ldl) {
+  __shared__ v4f red[TB][KS][64];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
+  const int tb = wv / KS, ks = wv - (wv / KS) * KS;
   const int j = lane & 15;
   const int g = lane >> 4;
   const int e0 = blockIdx.x * 16;
-  const int t0 = blockIdx.y * 64 + wv * 16;
-  if (t0 >= T) return;  // wave-uniform
+  const int t0 = (blockIdx.y * TB + tb) * 16;
   const int ta = min(t0 + j, T - 1);  // rows past T read a valid row; not stored
-  const uint16_t* ap = x + (int64_t)ta * ldx + g * 8;
-  const uint16_t* bp = wg + (int64_t)(e0 + j) * H + g * 8;
+  const int hs = H / KS;
+  const uint16_t* ap = x + (int64_t)ta * ldx + ks * hs + g * 8;
+  const uint16_t* bp = wg + (int64_t)(e0 + j) * H + ks * hs + g * 8;
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  constexpr int U = 4;
-  int k0 = 0;
-  for (; k0 + 32 * U <= H; k0 += 32 * U) {
-    v4u a[U], b[U];
+  if (t0 < T) {
+    constexpr int U = 4;
+    int k0 = 0;
+    for (; k0 + 32 * U <= hs; k0 += 32 * U) {
+      v4u a[U], b[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      a[u] = *reinterpret_cast<const v4u*>(ap + k0 + 32 * u);
-      b[u] = *reinterpret_cast<const v4u*>(bp + k0 + 32 * u);
+      for (int u = 0; u < U; u++) {
+        a[u] = *reinterpret_cast<const v4u*>(ap + k0 + 32 * u);
+        b[u] = *reinterpret_cast<const v4u*>(bp + k0 + 32 * u);
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[u]),
+                                                      __builtin_bit_cast(v8bf, b[u]), acc, 0, 0,
+                                                      0);
     }
-#pragma unroll
-    for (int u = 0; u < U; u++)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[u]),
-                                                    __builtin_bit_cast(v8bf, b[u]), acc, 0, 0, 0);
+    for (; k0 < hs; k0 += 32) {
+      const v4u a = *reinterpret_cast<const v4u*>(ap + k0);
+      const v4u b = *reinterpret_cast<const v4u*>(bp + k0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                    __builtin_bit_cast(v8bf, b), acc, 0, 0, 0);
+    }
   }
-  for (; k0 < H; k0 += 32) {
-    const v4u a = *reinterpret_cast<const v4u*>(ap + k0);
-    const v4u b = *reinterpret_cast<const v4u*>(bp + k0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
-                                                  __builtin_bit_cast(v8bf, b), acc, 0, 0, 0);
+  red[tb][ks][lane] = acc;
+  __syncthreads();
+  if (ks != 0 || t0 >= T) return;
+  v4f sum = red[tb][0][lane];
+  for (int i = 1; i < KS; i++) {
+    const v4f p = red[tb][i][lane];
+    sum.x = sum.x + p.x;
+    sum.y = sum.y + p.y;
+    sum.z = sum.z + p.z;
+    sum.w = sum.w + p.w;
   }
 #pragma unroll
   for (int v = 0; v < 4; v++) {
     const int t = t0 + 4 * g + v;
-    if (t < T) logits[(int64_t)t * ldl + e0 + j] = acc[v];
+    if (t < T) logits[(int64_t)t * ldl + e0 + j] = sum[v];
   }
 }
 
@@ -113,8 +136,14 @@ hipError_t launch_router_gate_bf16(const uint16_t* x, int64_t T, int64_t H, int6
   if (T <= kRouterWaveTokens) {
     hipLaunchKernelGGL(k_router_wave, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, stream, x,
                        (int)T, (int)H, ldx, wg, (int)E, logits, ldl);
+  } else if (T <= 256 && H % 256 == 0) {
+    hipLaunchKernelGGL((k_router_mfma<1, 8>), dim3((unsigned)(E / 16), (unsigned)((T + 15) / 16)),
+                       dim3(512), 0, stream, x, (int)T, (int)H, ldx, wg, logits, ldl);
+  } else if (H % 64 == 0) {
+    hipLaunchKernelGGL((k_router_mfma<4, 2>), dim3((unsigned)(E / 16), (unsigned)((T + 63) / 64)),
+                       dim3(512), 0, stream, x, (int)T, (int)H, ldx, wg, logits, ldl);
   } else {
-    hipLaunchKernelGGL(k_router_mfma, dim3((unsigned)(E / 16), (unsigned)((T + 63) / 64)),
+    hipLaunchKernelGGL((k_router_mfma<4, 1>), dim3((unsigned)(E / 16), (unsigned)((T + 63) / 64)),
                        dim3(256), 0, stream, x, (int)T, (int)H, ldx, wg, logits, ldl);
   }
   return hipGetLastError();

@@ -172,9 +172,10 @@ def _check_rot(orc, x, logits, k, W, Wd, label, shared=None, tokens=None):
     return out
 
 
-# small shapes: both GEMM forms (split-K up to 256 pairs, row-blocked beyond),
-# ragged expert segments, a zero token, given ids, the shared term
-@pytest.mark.parametrize("T,k", [(1, 2), (5, 2), (32, 8), (33, 8), (300, 2)])
+# small shapes: the single-token path, the split-K GEMMs (with the requant in
+# gemm2's prologue up to 256 pairs, around the requant kernel up to 4096),
+# the LDS-tiled GEMMs beyond; ragged expert segments, a zero token
+@pytest.mark.parametrize("T,k", [(1, 2), (5, 2), (32, 8), (33, 8), (300, 2), (600, 8)])
 def test_rot_moe_small(orc, T, k):
     E, H, I = 8, 256, 128
     W = _rot_weights(orc, (94, 0), E, H, I)
@@ -197,9 +198,10 @@ def test_rot_moe_with_shared_term(orc, T):
     _check_rot(orc, x, logits, k, W, Wd, f"rot moe + shared T={T}", shared=shared)
 
 
-def test_rot_moe_given_ids_and_skew(orc):
+@pytest.mark.parametrize("T", [1, 90])
+def test_rot_moe_given_ids_and_skew(orc, T):
     # every token picks expert 0 first: one long segment, the rest short
-    E, H, I, k, T = 8, 256, 256, 3, 90
+    E, H, I, k = 8, 256, 256, 3
     W = _rot_weights(orc, (96, 0), E, H, I)
     Wd = _dev_rot_weights(W)
     x = synth.activations((96, T), T, H, 3, 10.0)
@@ -216,6 +218,30 @@ def test_rot_moe_given_ids_and_skew(orc):
     out_ref, dref = orc.moe_rot_forward(x, ids, w, *W, debug=True)
     assert ulp_diff_f32(host(dbg["act"]), dref["act"]).max() <= 1
     assert_bf16_close(bf16_host(out), out_ref, "rot moe given ids")
+
+
+def test_rot_moe_wide_scale_range(orc):
+    # some weight rows have one 128-group scaled down by 2^-28: their scales
+    # span more than the integer fold allows, so those waves of the tiled
+    # GEMMs fold in fp64 group by group while the others take the integer fold
+    E, H, I, k, T = 4, 256, 256, 4, 1100
+    key = (97, 0)
+    q13 = np.empty((E, 2 * I, H), np.int8)
+    s13 = np.empty((E, 2 * I, H // 128), np.uint16)
+    q2 = np.empty((E, H, I), np.int8)
+    s2 = np.empty((E, H, I // 128), np.uint16)
+    for e in range(E):
+        a = synth.expert_weights(key, e, 2 * I, H, synth.T_W)
+        b = synth.expert_weights(key, e, H, I, synth.T_W2)
+        a[:32, :128] *= np.float32(2.0 ** -28)
+        a[200:203, 128:] *= np.float32(2.0 ** -26)
+        b[64:96, 128:256] *= np.float32(2.0 ** -30)
+        q13[e], s13[e] = orc.weight_prep_g128(a)
+        q2[e], s2[e] = orc.weight_prep_g128(b)
+    W = (q13, s13, q2, s2)
+    x = synth.activations((97, T), T, H, 3, 10.0)
+    logits = synth.router_logits((97, T), T, E)
+    _check_rot(orc, x, logits, k, W, _dev_rot_weights(W), "rot moe wide scale range")
 
 
 @pytest.fixture(scope="module")
