@@ -437,6 +437,13 @@ def main():
         probe["step_us"] = round(probe.pop("replay_us") / 8, 2)
         clocks["decode_step_graph"] = probe
 
+    # ------------------------------------------------------------ what HBM delivers
+    # torch's own copy and sum kernels over 1 GiB buffers: the streaming rates
+    # of this box at this moment, beside which the roofline fractions (against
+    # the published 8 TB/s) can be read
+    if not args.probe_copy:
+        out["hbm_stream"] = stream_ceiling(torch, timer)
+
     # ------------------------------------------------------------ extra cases
     cases = {}
     if "decode" in groups:
@@ -483,6 +490,25 @@ def main():
         out["cpu_baseline"] = cpu_baseline(np, synth, args.cpu_seconds, step_bytes)
 
     print(json.dumps(out), flush=True)
+
+
+def stream_ceiling(torch, timer):
+    """Streaming rates of torch's copy (1 GiB read + 1 GiB written) and sum
+    (1 GiB read) kernels, median of 10 launches each, in GB/s of bytes moved."""
+    n = 1 << 28  # fp32 elements: 1 GiB
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    r = torch.empty((), dtype=torch.float32, device="cuda")
+    b.copy_(a)
+    torch.sum(a, out=r)
+    _, cp = timer.run(lambda i: b.copy_(a), 10, groups=10)
+    _, sm = timer.run(lambda i: torch.sum(a, out=r), 10, groups=10)
+    res = {"copy_gbs": round(2 * 4 * n / (pct(cp, 50) * 1e-3) / 1e9, 1),
+           "read_gbs": round(4 * n / (pct(sm, 50) * 1e-3) / 1e9, 1),
+           "source": "torch copy_ and sum over 1 GiB fp32, median of 10"}
+    del a, b, r
+    torch.cuda.empty_cache()
+    return res
 
 
 def clock_probe(torch, clock, capture, seconds):
