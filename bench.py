@@ -500,9 +500,9 @@ def stream_ceiling(torch, timer):
     b = torch.empty_like(a)
     r = torch.empty((), dtype=torch.float32, device="cuda")
     b.copy_(a)
-    torch.sum(a, out=r)
+    torch.sum(a, dim=(0,), out=r)
     _, cp = timer.run(lambda i: b.copy_(a), 10, groups=10)
-    _, sm = timer.run(lambda i: torch.sum(a, out=r), 10, groups=10)
+    _, sm = timer.run(lambda i: torch.sum(a, dim=(0,), out=r), 10, groups=10)
     res = {"copy_gbs": round(2 * 4 * n / (pct(cp, 50) * 1e-3) / 1e9, 1),
            "read_gbs": round(4 * n / (pct(sm, 50) * 1e-3) / 1e9, 1),
            "source": "torch copy_ and sum over 1 GiB fp32, median of 10"}

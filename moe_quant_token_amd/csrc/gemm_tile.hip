@@ -314,25 +314,35 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, MINB) void k_gemm_tile(
   }
   if (MODE == kEpiSilu) {
     // lanes l and l ^ 1 hold adjacent product columns (gate, up) of the same
-    // rows; the even lane stores the activation.  N is even, so both lanes of
-    // a pair are in range or out of range together.
+    // 16 rows; the pair splits the rows so that each lane forms 8 of the 16
+    // activations (the even lane rows v < 8, the odd lane v >= 8): one fp64
+    // exp per output instead of two lanes' worth.  N is even, so both lanes
+    // of a pair are in range or out of range together.
+    const bool odd = (lane & 1) != 0;
 #pragma unroll
     for (int n = 0; n < TN; n++) {
       const int col = col0 + n * 32;
-      const bool store = col < N && (col & 1) == 0;
+      const bool col_ok = col < N;
 #pragma unroll
       for (int i = 0; i < TM; i++) {
+        float h[16], x[16];
 #pragma unroll
         for (int v = 0; v < 16; v++) {
+          h[v] = (float)acc[i][n][v];
+          h[v] = h[v] * sar[i][v];
+          h[v] = h[v] * scol[n];
+        }
+#pragma unroll
+        for (int v = 0; v < 16; v++) x[v] = __shfl_xor(h[v], 1, 64);
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+          const float gate = odd ? x[q + 8] : h[q];
+          const float up = odd ? h[q + 8] : x[q];
+          const int v = odd ? q + 8 : q;
           const int row = row0 + i * 32 + 8 * (v >> 2) + (v & 3);
-          float h = (float)acc[i][n][v];
-          h = h * sar[i][v];
-          h = h * scol[n];
-          const float up = __shfl_xor(h, 1, 64);
-          if (store && row < M) {
-            const float sg = (float)((double)h / (1.0 + exp(-(double)h)));
+          const float sg = (float)((double)gate / (1.0 + exp(-(double)gate)));
+          if (col_ok && row < M)
             static_cast<float*>(out)[(int64_t)row * ldo + (col >> 1)] = sg * up;
-          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }

@@ -1610,7 +1610,7 @@ __device__ __forceinline__ void rot_col_scales(const uint16_t* __restrict__ sp, 
 // W is packed (16-row tiles of 1 KiB k-steps), as [E * Nw, K].  In the dense
 // form (expert_list == nullptr) the rows are [64 blockIdx.y, +64) of a
 // plain matrix (pair p = row p).
-template <int MODE, int WAVES>
+template <int MODE, int WAVES, int NT, int MAXG>
 __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
     const int8_t* __restrict__ qx, const float* __restrict__ sx, const float* __restrict__ act,
     int k, const int8_t* __restrict__ W, const uint16_t* __restrict__ sW,
@@ -1618,17 +1618,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
     const int32_t* __restrict__ seg_off, const int32_t* __restrict__ n_active,
     const int32_t* __restrict__ sorted_pairs, int dense_rows, float* __restrict__ out, int ldo,
     int8_t* __restrict__ qa_rec, float* __restrict__ sa_rec) {
-  constexpr int MAXG = 32;  // K <= 4096
-  constexpr int GW = MAXG / WAVES;
+  constexpr int GW = (MAXG + WAVES - 1) / WAVES;  // groups a wave takes
   constexpr bool G256 = MODE == kRotG256Silu;
-  __shared__ v4i red[MAXG][64];
-  __shared__ long long sred[WAVES][4][64];
-  __shared__ int32_t m_lds[16][MAXG];
-  __shared__ float s_lds[16][MAXG];
+  __shared__ v4i red[G256 ? 1 : NT][G256 ? 1 : MAXG][64];
+  __shared__ long long sred[G256 ? WAVES : 1][4][64];
+  __shared__ int32_t m_lds[G256 ? 16 : 1][MAXG + 1];
+  __shared__ float s_lds[NT * 16][MAXG + 1];
   __shared__ float cs_lds[16];
   __shared__ __attribute__((aligned(16))) int8_t a_lds[MODE == kRotActRot ? 16 * 2048 : 16];
   __shared__ float sa_lds[16];
   __shared__ int pair_lds[16];
+  static_assert(!G256 || NT == 1, "the g256 form takes one tile a workgroup");
   RotRows rr;
   if (!rot_rows(expert_list, seg_off, n_active, dense_rows, 64, rr)) return;
   const bool dense = expert_list == nullptr;
@@ -1638,21 +1638,26 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
   const int g = lane >> 4;
   const int nk = K >> 6;
   const int G = K >> 7;
-  const int tile = blockIdx.x;
-  const int8_t* wbase = W + ((int64_t)rr.e * (Nw >> 4) + tile) * nk * 1024 + lane * 16;
+  const int tile0 = blockIdx.x * NT;
+  const int8_t* wbase = W + ((int64_t)rr.e * (Nw >> 4) + tile0) * nk * 1024 + lane * 16;
+  const int64_t tstride = (int64_t)nk * 1024;
 
-  v4i bw[GW][2];
+  // all of the workgroup's weight bytes go out at once
+  v4i bw[NT][GW][2];
 #pragma unroll
-  for (int i = 0; i < GW; i++) {
-    const int gg = wv + i * WAVES;
+  for (int t = 0; t < NT; t++)
 #pragma unroll
-    for (int h = 0; h < 2; h++)
-      bw[i][h] = gg < G ? ld_stream(wbase + (int64_t)(2 * gg + h) * 1024) : v4i{0, 0, 0, 0};
-  }
+    for (int i = 0; i < GW; i++) {
+      const int gg = wv + i * WAVES;
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+        bw[t][i][h] = gg < G ? ld_stream(wbase + t * tstride + (int64_t)(2 * gg + h) * 1024)
+                             : v4i{0, 0, 0, 0};
+    }
   if (G256) {
     if (threadIdx.x < 16) {
       const int c = threadIdx.x;
-      const int col = tile * 16 + c;
+      const int col = tile0 * 16 + c;
       const uint8_t* sp = su8 + (int64_t)col * (K >> 8);
       uint32_t u[MAXG / 2];
 #pragma unroll
@@ -1663,15 +1668,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
       cs_lds[c] = bf16_bits_to_f32(sW[col]);
     }
   } else {
-    for (int i = threadIdx.x; i < 16 * G; i += WAVES * 64) {
+    // the tiles' scales are contiguous: NT * 16 rows of G
+    const uint16_t* sp = sW + ((int64_t)rr.e * Nw + tile0 * 16) * G;
+    for (int i = threadIdx.x; i < NT * 16 * G; i += WAVES * 64) {
       const int cc = i / G, gg = i - cc * G;
-      s_lds[cc][gg] = bf16_bits_to_f32(sW[((int64_t)rr.e * Nw + tile * 16 + cc) * G + gg]);
+      s_lds[cc][gg] = bf16_bits_to_f32(sp[i]);
     }
   }
-  // g256 folds su8 * acc in int64 (exact, its definition) as each wave's
-  // groups complete; g128 leaves the group sums in LDS for the fp64 fold in
-  // group order (few outputs per workgroup here: the fold is cheap)
-  constexpr bool fast = G256;
 
   for (int pb = rr.begin; pb < rr.end; pb += 16) {
     const int nrows = min(16, rr.end - pb);
@@ -1694,13 +1697,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
           const int kk = blk * 128 + j * 8;  // first of the lane's 8 values
           *reinterpret_cast<uint2*>(a_lds + (kk >> 6) * 1024 + (r + 16 * ((kk & 63) >> 4)) * 16 +
                                     (kk & 15)) = wd;
-          if (tile == 0 && qa_rec)
+          if (blockIdx.x == 0 && qa_rec)
             *reinterpret_cast<uint2*>(qa_rec + (int64_t)pair_lds[r] * K + kk) = wd;
         }
         if (lane == 0) {
           const float sv = am != 0.0f ? sc : 0.0f;
           sa_lds[r] = sv;
-          if (tile == 0 && sa_rec) sa_rec[pair_lds[r]] = sv;
+          if (blockIdx.x == 0 && sa_rec) sa_rec[pair_lds[r]] = sv;
         }
       }
     }
@@ -1708,6 +1711,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
       sa_lds[threadIdx.x] = sx[pair_lds[threadIdx.x < nrows ? threadIdx.x : 0] / k];
     __syncthreads();
 
+    // this wave's groups: the activation slices once, every tile's MFMAs
     const bool a_ok = j < nrows;
     const int8_t* ap = qx + (int64_t)(pair_lds[a_ok ? j : 0] / k) * K + g * 16;
     long long S[4] = {0, 0, 0, 0};
@@ -1715,58 +1719,64 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
     for (int i = 0; i < GW; i++) {
       const int gg = wv + i * WAVES;
       if (gg < G) {
-        v4i acc = {0, 0, 0, 0};
+        v4i a[2];
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const int c = 2 * gg + h;
-          v4i a;
           if (MODE == kRotActRot)
-            a = *reinterpret_cast<const v4i*>(&a_lds[c * 1024 + lane * 16]);
+            a[h] = *reinterpret_cast<const v4i*>(&a_lds[c * 1024 + lane * 16]);
           else
-            a = a_ok ? *reinterpret_cast<const v4i*>(ap + (int64_t)c * 64) : v4i{0, 0, 0, 0};
-          acc = mfma_16x16x64_i8(a, bw[i][h], acc);
+            a[h] = a_ok ? *reinterpret_cast<const v4i*>(ap + (int64_t)c * 64) : v4i{0, 0, 0, 0};
         }
-        if (fast) {
-          const long long M = m_lds[j][gg];
 #pragma unroll
-          for (int v = 0; v < 4; v++) S[v] += (long long)acc[v] * M;
-        } else {
-          red[gg][lane] = acc;
+        for (int t = 0; t < NT; t++) {
+          v4i acc = {0, 0, 0, 0};
+#pragma unroll
+          for (int h = 0; h < 2; h++) acc = mfma_16x16x64_i8(a[h], bw[t][i][h], acc);
+          if (G256) {
+            const long long M = m_lds[j][gg];
+#pragma unroll
+            for (int v = 0; v < 4; v++) S[v] += (long long)acc[v] * M;
+          } else {
+            red[t][gg][lane] = acc;
+          }
         }
       }
     }
-    if (fast) {
+    if (G256) {
 #pragma unroll
       for (int v = 0; v < 4; v++) sred[wv][v][lane] = S[v];
     }
     __syncthreads();
-    if (wv >= 4) continue;
-    // wave v finishes element v of every lane: row 4 (lane / 16) + v, column
-    // tile * 16 + lane % 16
-    const int v = wv;
-    const int r = 4 * g + v;
-    const int rc = min(r, nrows - 1);
-    double t;
-    if (fast) {
-      long long tot = 0;
+    // (tile, element) units over the waves: element v of every lane is row
+    // 4 (lane / 16) + v, column 16 (tile0 + t) + lane % 16
+    for (int u = wv; u < NT * 4; u += WAVES) {
+      const int t = u >> 2, v = u & 3;
+      const int r = 4 * g + v;
+      const int rc = min(r, nrows - 1);
+      const int col = (tile0 + t) * 16 + j;
+      double tt;
+      if (G256) {
+        long long tot = 0;
 #pragma unroll
-      for (int w = 0; w < WAVES; w++) tot += sred[w][v][lane];
-      t = G256 ? (double)tot : (double)tot * (double)cs_lds[j];
-    } else {
-      t = 0.0;
-      for (int gg = 0; gg < G; gg++) t = t + (double)red[gg][lane][v] * (double)s_lds[j][gg];
-    }
-    t = t * (double)sa_lds[rc];
-    if (G256) t = t * (double)cs_lds[j];
-    t = t * 0.0078125;
-    const float hv = (float)t;
-    const int p = pair_lds[rc];
-    const int col = tile * 16 + j;
-    if (MODE == kRotActRot || MODE == kRotCodes) {
-      if (r < nrows) out[(int64_t)p * ldo + col] = hv;
-    } else {
-      const float a = rot_silu_pair(hv);
-      if ((j & 1) == 0 && r < nrows) out[(int64_t)p * ldo + (col >> 1)] = a;
+        for (int w = 0; w < WAVES; w++) tot += sred[w][v][lane];
+        tt = (double)tot * (double)sa_lds[rc];
+        tt = tt * (double)cs_lds[j];
+      } else {
+        tt = 0.0;
+        for (int gg = 0; gg < G; gg++)
+          tt = tt + (double)red[t][gg][lane][v] * (double)s_lds[t * 16 + j][gg];
+        tt = tt * (double)sa_lds[rc];
+      }
+      tt = tt * 0.0078125;
+      const float hv = (float)tt;
+      const int p = pair_lds[rc];
+      if (MODE == kRotActRot || MODE == kRotCodes) {
+        if (r < nrows) out[(int64_t)p * ldo + col] = hv;
+      } else {
+        const float a = rot_silu_pair(hv);
+        if ((j & 1) == 0 && r < nrows) out[(int64_t)p * ldo + (col >> 1)] = a;
+      }
     }
   }
 }
@@ -1969,27 +1979,23 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm2(
   }
 }
 
-// Grouped GEMM with per-group scales, LDS-tiled (large batches).  Workgroup =
-// 64 pair rows (half of one 128-row m-block of the expert sort, or rows
-// [128 mb + 64 half, +64) of a plain matrix in the DENSE form) x 128 weight
-// rows; wave w takes weight rows 32 w .. 32 w + 31 (two 16-row tiles) of
-// all 64 pair rows (four 16-row blocks, 16x16x64 MFMA).  The activation rows
-// are gathered into LDS (packed operand layout, two buffers), the weights
-// stream from HBM PF k steps ahead.
+// The shared expert's GEMMs for large batches, LDS-tiled.  Workgroup = 64
+// token rows (rows [128 mb + 64 half, +64)) x 128 weight rows; wave w takes
+// weight rows 32 w .. 32 w + 31 (two 16-row tiles) of all 64 token rows
+// (four 16-row blocks, 16x16x64 MFMA).
 //
 // The fold after every 128-group: a wave whose 32 columns all have the
 // integer form of the fold (rot_col_scales) adds acc_g M_g into int64 sums;
 // any other wave folds in fp64 in group order, as defined.  kRotG256Silu
 // folds su8 * acc in int64 (exact, as its definition).
-template <int MODE, bool DENSE>
-__global__ __launch_bounds__(256, 2) void k_rot_tile(
-    const int8_t* __restrict__ A, const float* __restrict__ sA, int a_div,
-    const int8_t* __restrict__ W, const uint16_t* __restrict__ sW,
-    const uint8_t* __restrict__ su8, int Nw, int K, const int32_t* __restrict__ expert_list,
-    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ blk_slot,
-    const int32_t* __restrict__ blk_row0, const int32_t* __restrict__ n_blocks,
-    const int32_t* __restrict__ sorted_pairs, int dense_rows, float* __restrict__ out,
-    int ldo, int ncb) {
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void k_rot_tile(const int8_t* __restrict__ A,
+                                                     const float* __restrict__ sA,
+                                                     const int8_t* __restrict__ W,
+                                                     const uint16_t* __restrict__ sW,
+                                                     const uint8_t* __restrict__ su8, int Nw,
+                                                     int K, int dense_rows,
+                                                     float* __restrict__ out, int ldo) {
   constexpr int BM = 64, BN = 128, MAXG = 32, CH = 4;
   constexpr bool G256 = MODE == kRotG256Silu;
   __shared__ __attribute__((aligned(1024))) int8_t a_lds[2][CH][4 * 1024];
@@ -2000,26 +2006,16 @@ __global__ __launch_bounds__(256, 2) void k_rot_tile(
   __shared__ float cs_lds[BN];  // 2^xm (g128) or the bf16 row scale (g256)
   __shared__ int ok_lds[BN];
 
-  const int ngrp = Nw / (BN * ncb);  // workgroups across the weight rows
+  const int ngrp = Nw / BN;  // workgroups across the weight rows
   const int xcd = blockIdx.x & 7;
   const int tq = blockIdx.x >> 3;
   const int nper = 2 * ngrp;
   const int mb = (tq / nper) * 8 + xcd;
   const int rem = tq - (tq / nper) * nper;
   const int half = rem & 1;
-  const int nfirst0 = (rem >> 1) * BN * ncb;
-  int e = 0, row0, rows;
-  if (DENSE) {
-    row0 = mb * 128 + half * 64;
-    rows = min(BM, dense_rows - row0);
-  } else {
-    if (mb >= n_blocks[0]) return;
-    const int slot = blk_slot[mb];
-    const int r0 = blk_row0[mb];
-    row0 = r0 + half * 64;
-    rows = min(r0 + 128, seg_off[slot + 1]) - row0;
-    e = expert_list[slot];
-  }
+  const int nfirst = (rem >> 1) * BN;
+  const int row0 = mb * 128 + half * 64;
+  const int rows = min(BM, dense_rows - row0);
   if (rows <= 0) return;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -2030,266 +2026,259 @@ __global__ __launch_bounds__(256, 2) void k_rot_tile(
   const int nsteps = (nk + 2 * CH - 1) / (2 * CH) * (2 * CH);
 
   if (threadIdx.x < BM) {
-    const int r = min((int)threadIdx.x, rows - 1);
-    const int p = DENSE ? row0 + r : sorted_pairs[row0 + r];
+    const int p = row0 + min((int)threadIdx.x, rows - 1);
     pair_lds[threadIdx.x] = p;
-    sa_lds[threadIdx.x] = sA[p / a_div];
+    sa_lds[threadIdx.x] = sA[p];
   }
 
-  // ncb blocks of BN weight rows in turn: the pair rows, their scales and
-  // the gathered activation rows' addresses are read once for all of them
-  for (int cbk = 0; cbk < ncb; cbk++) {
-    const int nfirst = nfirst0 + cbk * BN;
-    // weight fragments: tiles nfirst / 16 + 2 wv + cb
-    const int8_t* bsrc = W + ((int64_t)e * (Nw >> 4) + (nfirst >> 4) + 2 * wv) * nk * 1024 +
-                         lane * 16;
-    const int64_t tstride = (int64_t)nk * 1024;
-    // plain loads: the two 64-row halves of an m-block read the same weight
-    // rows back to back on one XCD, the second from L2
-    auto load_b = [&](int st, v4i* b) __attribute__((always_inline)) {
-      const int c = st < nk ? st : 0;
-      b[0] = *reinterpret_cast<const v4i*>(bsrc + (int64_t)c * 1024);
-      b[1] = *reinterpret_cast<const v4i*>(bsrc + tstride + (int64_t)c * 1024);
-    };
-    if (G256) {
-      if (threadIdx.x < BN) {
-        const int c = threadIdx.x;
-        const int col = nfirst + c;
-        const uint8_t* sp = su8 + (int64_t)col * (K >> 8);
-        uint32_t u[MAXG / 2];
+  // weight fragments: tiles nfirst / 16 + 2 wv + cb
+  const int8_t* bsrc = W + ((int64_t)(nfirst >> 4) + 2 * wv) * nk * 1024 +
+                       lane * 16;
+  const int64_t tstride = (int64_t)nk * 1024;
+  // plain loads: the two 64-row halves of an m-block read the same weight
+  // rows back to back on one XCD, the second from L2
+  auto load_b = [&](int st, v4i* b) __attribute__((always_inline)) {
+    const int c = st < nk ? st : 0;
+    b[0] = *reinterpret_cast<const v4i*>(bsrc + (int64_t)c * 1024);
+    b[1] = *reinterpret_cast<const v4i*>(bsrc + tstride + (int64_t)c * 1024);
+  };
+  if (G256) {
+    if (threadIdx.x < BN) {
+      const int c = threadIdx.x;
+      const int col = nfirst + c;
+      const uint8_t* sp = su8 + (int64_t)col * (K >> 8);
+      uint32_t u[MAXG / 2];
 #pragma unroll
-        for (int i = 0; i < MAXG / 2; i++) u[i] = 2 * i < G ? sp[i] : 0u;
+      for (int i = 0; i < MAXG / 2; i++) u[i] = 2 * i < G ? sp[i] : 0u;
 #pragma unroll
-        for (int gg = 0; gg < MAXG; gg++)
-          if (gg < G) m_lds[c][gg] = (int32_t)u[gg >> 1];
-        cs_lds[c] = bf16_bits_to_f32(sW[col]);
-        ok_lds[c] = 1;
-      }
-    } else {
-      // the tile's BN x G scales (contiguous) decoded element-wise, the
-      // exponents held in the activation buffer until the main loop
-      int* x_tmp = reinterpret_cast<int*>(&a_lds[0][0][0]);  // [BN][MAXG + 1]
-      const uint16_t* sp = sW + ((int64_t)e * Nw + nfirst) * G;
-      const int n = BN * G;
+      for (int gg = 0; gg < MAXG; gg++)
+        if (gg < G) m_lds[c][gg] = (int32_t)u[gg >> 1];
+      cs_lds[c] = bf16_bits_to_f32(sW[col]);
+      ok_lds[c] = 1;
+    }
+  } else {
+    // the tile's BN x G scales (contiguous) decoded element-wise, the
+    // exponents held in the activation buffer until the main loop
+    int* x_tmp = reinterpret_cast<int*>(&a_lds[0][0][0]);  // [BN][MAXG + 1]
+    const uint16_t* sp = sW + (int64_t)nfirst * G;
+    const int n = BN * G;
 #pragma unroll 8
-      for (int i = threadIdx.x; i < n; i += 256) {
-        const uint32_t bits = sp[i];
-        const int c = i / G, gg = i - c * G;
-        int m = 0, x = 0;
-        const bool fin = bf16_int_exp(bits, m, x);
-        s_lds[c][gg] = bf16_bits_to_f32(bits);
-        m_lds[c][gg] = fin ? m : 0;
-        x_tmp[c * (MAXG + 1) + gg] = fin ? x : (1 << 20);  // 1 << 20 marks Inf / NaN
-      }
-      lds_barrier();
-      // two threads a column, alternate groups: least exponent, multipliers,
-      // the bound D and the check, combined across the pair
-      const int c = threadIdx.x >> 1, h = threadIdx.x & 1;
-      int xm = 1 << 20;
-      bool ok = true;
-      for (int gg = h; gg < G; gg += 2) {
-        const int x = x_tmp[c * (MAXG + 1) + gg];
-        if (x == (1 << 20)) ok = false;
-        else if (m_lds[c][gg] != 0) xm = min(xm, x);
-      }
-      xm = min(xm, __shfl_xor(xm, 1, 64));
-      if (xm == (1 << 20)) xm = 0;
-      long long D = 0;
-      for (int gg = h; gg < G; gg += 2) {
-        const int m = m_lds[c][gg];
-        int Mg = 0;
-        if (m != 0) {
-          const int sh = x_tmp[c * (MAXG + 1) + gg] - xm;
-          if (sh > 23 || sh < 0) {
-            ok = false;
-          } else {
-            Mg = m * (1 << sh);
-            D += Mg < 0 ? -(long long)Mg : (long long)Mg;
-          }
-        }
-        m_lds[c][gg] = Mg;
-      }
-      // both shuffles run on every lane (a shuffle inside a short-circuited
-      // expression would read an inactive partner)
-      D += __shfl_xor(D, 1, 64);
-      const int ok_pair = __shfl_xor(ok ? 1 : 0, 1, 64);
-      ok = ok && ok_pair != 0 && D < (1LL << 31);
-      if (h == 0) {
-        cs_lds[c] = ldexpf(1.0f, xm);
-        ok_lds[c] = ok ? 1 : 0;
-      }
+    for (int i = threadIdx.x; i < n; i += 256) {
+      const uint32_t bits = sp[i];
+      const int c = i / G, gg = i - c * G;
+      int m = 0, x = 0;
+      const bool fin = bf16_int_exp(bits, m, x);
+      s_lds[c][gg] = bf16_bits_to_f32(bits);
+      m_lds[c][gg] = fin ? m : 0;
+      x_tmp[c * (MAXG + 1) + gg] = fin ? x : (1 << 20);  // 1 << 20 marks Inf / NaN
     }
     lds_barrier();
+    // two threads a column, alternate groups: least exponent, multipliers,
+    // the bound D and the check, combined across the pair
+    const int c = threadIdx.x >> 1, h = threadIdx.x & 1;
+    int xm = 1 << 20;
+    bool ok = true;
+    for (int gg = h; gg < G; gg += 2) {
+      const int x = x_tmp[c * (MAXG + 1) + gg];
+      if (x == (1 << 20)) ok = false;
+      else if (m_lds[c][gg] != 0) xm = min(xm, x);
+    }
+    xm = min(xm, __shfl_xor(xm, 1, 64));
+    if (xm == (1 << 20)) xm = 0;
+    long long D = 0;
+    for (int gg = h; gg < G; gg += 2) {
+      const int m = m_lds[c][gg];
+      int Mg = 0;
+      if (m != 0) {
+        const int sh = x_tmp[c * (MAXG + 1) + gg] - xm;
+        if (sh > 23 || sh < 0) {
+          ok = false;
+        } else {
+          Mg = m * (1 << sh);
+          D += Mg < 0 ? -(long long)Mg : (long long)Mg;
+        }
+      }
+      m_lds[c][gg] = Mg;
+    }
+    // both shuffles run on every lane (a shuffle inside a short-circuited
+    // expression would read an inactive partner)
+    D += __shfl_xor(D, 1, 64);
+    const int ok_pair = __shfl_xor(ok ? 1 : 0, 1, 64);
+    ok = ok && ok_pair != 0 && D < (1LL << 31);
+    if (h == 0) {
+      cs_lds[c] = ldexpf(1.0f, xm);
+      ok_lds[c] = ok ? 1 : 0;
+    }
+  }
+  lds_barrier();
 
-    // activation rows: wave wv gathers 16-row block wv of each k step
-    const int8_t* asrc = A + (int64_t)(pair_lds[16 * wv + j] / a_div) * K + g * 16;
-    auto load_a = [&](int st) __attribute__((always_inline)) {
-      const int c = st < nk ? st : 0;
-      return *reinterpret_cast<const v4i*>(asrc + (int64_t)c * 64);
-    };
-    // this wave folds with integers when all of its 32 columns allow it
-    const bool fast = __all(ok_lds[32 * wv + (lane & 31)] != 0);
+  // activation rows: wave wv gathers 16-row block wv of each k step
+  const int8_t* asrc = A + (int64_t)pair_lds[16 * wv + j] * K + g * 16;
+  auto load_a = [&](int st) __attribute__((always_inline)) {
+    const int c = st < nk ? st : 0;
+    return *reinterpret_cast<const v4i*>(asrc + (int64_t)c * 64);
+  };
+  // this wave folds with integers when all of its 32 columns allow it
+  const bool fast = __all(ok_lds[32 * wv + (lane & 31)] != 0);
 
-    long long acc64[4][2][4];
+  long long acc64[4][2][4];
 #pragma unroll
-    for (int rb = 0; rb < 4; rb++)
+  for (int rb = 0; rb < 4; rb++)
 #pragma unroll
-      for (int cb = 0; cb < 2; cb++)
+    for (int cb = 0; cb < 2; cb++)
 #pragma unroll
-        for (int v = 0; v < 4; v++) acc64[rb][cb][v] = 0;
-    v4i acc[4][2];
+      for (int v = 0; v < 4; v++) acc64[rb][cb][v] = 0;
+  v4i acc[4][2];
 
-    // The k steps go in chunks of CH, double-buffered: while a chunk is
-    // multiplied (its weights in one register set, its activation rows in one
-    // LDS buffer), the next chunk's loads are in flight (weights into the other
-    // register set, activation rows into staging registers).  The only waits
-    // are where the staged rows are stored into LDS, once per chunk: by then
-    // the whole chunk's compute has covered the loads' latency.  (A ring
-    // carried in registers from step to step makes the compiler wait for
-    // nearly every load at the loop head instead.)
-    v4i b0[CH][2], b1[CH][2];
-    v4i at[CH];
-    auto issue = [&](int c0, v4i (*bq)[2]) __attribute__((always_inline)) {
+  // The k steps go in chunks of CH, double-buffered: while a chunk is
+  // multiplied (its weights in one register set, its activation rows in one
+  // LDS buffer), the next chunk's loads are in flight (weights into the other
+  // register set, activation rows into staging registers).  The only waits
+  // are where the staged rows are stored into LDS, once per chunk: by then
+  // the whole chunk's compute has covered the loads' latency.  (A ring
+  // carried in registers from step to step makes the compiler wait for
+  // nearly every load at the loop head instead.)
+  v4i b0[CH][2], b1[CH][2];
+  v4i at[CH];
+  auto issue = [&](int c0, v4i (*bq)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < CH; u++) load_b(c0 + u, bq[u]);
+    for (int u = 0; u < CH; u++) load_b(c0 + u, bq[u]);
 #pragma unroll
-      for (int u = 0; u < CH; u++) at[u] = load_a(c0 + u);  // last: their wait covers all
-    };
-    auto stage = [&](int buf) __attribute__((always_inline)) {
+    for (int u = 0; u < CH; u++) at[u] = load_a(c0 + u);  // last: their wait covers all
+  };
+  auto stage = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < CH; u++)
-        *reinterpret_cast<v4i*>(&a_lds[buf][u][wv * 1024 + lane * 16]) = at[u];
-    };
-    auto compute = [&](int c0, int buf, v4i (*bq)[2], auto fast_c) __attribute__((always_inline)) {
-      constexpr bool FAST = decltype(fast_c)::value;
+    for (int u = 0; u < CH; u++)
+      *reinterpret_cast<v4i*>(&a_lds[buf][u][wv * 1024 + lane * 16]) = at[u];
+  };
+  auto compute = [&](int c0, int buf, v4i (*bq)[2], auto fast_c) __attribute__((always_inline)) {
+    constexpr bool FAST = decltype(fast_c)::value;
 #pragma unroll
-      for (int u = 0; u < CH; u++) {
-        const int st = c0 + u;
-        v4i fa[4];
+    for (int u = 0; u < CH; u++) {
+      const int st = c0 + u;
+      v4i fa[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++)
+        fa[rb] = *reinterpret_cast<const v4i*>(&a_lds[buf][u][rb * 1024 + lane * 16]);
+      const bool kin = st < nk;
+#pragma unroll
+      for (int cb = 0; cb < 2; cb++) {
+        const v4i bf = kin ? bq[u][cb] : v4i{0, 0, 0, 0};
 #pragma unroll
         for (int rb = 0; rb < 4; rb++)
-          fa[rb] = *reinterpret_cast<const v4i*>(&a_lds[buf][u][rb * 1024 + lane * 16]);
-        const bool kin = st < nk;
+          acc[rb][cb] = mfma_16x16x64_i8(fa[rb], bf, (u & 1) ? acc[rb][cb] : v4i{0, 0, 0, 0});
+      }
+      if ((u & 1) && kin) {  // a 128-group is complete: fold it
+        const int gg = st >> 1;
 #pragma unroll
         for (int cb = 0; cb < 2; cb++) {
-          const v4i bf = kin ? bq[u][cb] : v4i{0, 0, 0, 0};
+          const int c = 32 * wv + 16 * cb + j;
+          if (FAST) {
+            const long long M = m_lds[c][gg];
 #pragma unroll
-          for (int rb = 0; rb < 4; rb++)
-            acc[rb][cb] = mfma_16x16x64_i8(fa[rb], bf, (u & 1) ? acc[rb][cb] : v4i{0, 0, 0, 0});
-        }
-        if ((u & 1) && kin) {  // a 128-group is complete: fold it
-          const int gg = st >> 1;
+            for (int rb = 0; rb < 4; rb++)
 #pragma unroll
-          for (int cb = 0; cb < 2; cb++) {
-            const int c = 32 * wv + 16 * cb + j;
-            if (FAST) {
-              const long long M = m_lds[c][gg];
+              for (int v = 0; v < 4; v++) acc64[rb][cb][v] += (long long)acc[rb][cb][v] * M;
+          } else {
+            const double sv = (double)s_lds[G256 ? 0 : c][gg];
 #pragma unroll
-              for (int rb = 0; rb < 4; rb++)
+            for (int rb = 0; rb < 4; rb++)
 #pragma unroll
-                for (int v = 0; v < 4; v++) acc64[rb][cb][v] += (long long)acc[rb][cb][v] * M;
-            } else {
-              const double sv = (double)s_lds[G256 ? 0 : c][gg];
-#pragma unroll
-              for (int rb = 0; rb < 4; rb++)
-#pragma unroll
-                for (int v = 0; v < 4; v++) {
-                  double t = __longlong_as_double(acc64[rb][cb][v]);
-                  t = t + (double)acc[rb][cb][v] * sv;
-                  acc64[rb][cb][v] = __double_as_longlong(t);
-                }
-            }
+              for (int v = 0; v < 4; v++) {
+                double t = __longlong_as_double(acc64[rb][cb][v]);
+                t = t + (double)acc[rb][cb][v] * sv;
+                acc64[rb][cb][v] = __double_as_longlong(t);
+              }
           }
         }
       }
-    };
+    }
+  };
 
-    // the empty asm statements keep the compiler from moving a chunk's loads
-    // across the compute or the staging (scheduling barriers)
-    // the fold's form is fixed per wave before the loop, so each loop carries
-    // one form only (a branch inside it gets if-converted into both)
-    auto mainloop = [&](auto fast_c) __attribute__((always_inline)) {
-      issue(0, b0);
+  // the empty asm statements keep the compiler from moving a chunk's loads
+  // across the compute or the staging (scheduling barriers)
+  // the fold's form is fixed per wave before the loop, so each loop carries
+  // one form only (a branch inside it gets if-converted into both)
+  auto mainloop = [&](auto fast_c) __attribute__((always_inline)) {
+    issue(0, b0);
+    asm volatile("" ::: "memory");
+    stage(0);
+    lds_barrier();
+    for (int c0 = 0; c0 < nsteps; c0 += 2 * CH) {
+      issue(c0 + CH, b1);
+      asm volatile("" ::: "memory");
+      compute(c0, 0, b0, fast_c);
+      asm volatile("" ::: "memory");
+      stage(1);
+      lds_barrier();
+      issue(c0 + 2 * CH, b0);
+      asm volatile("" ::: "memory");
+      compute(c0 + CH, 1, b1, fast_c);
       asm volatile("" ::: "memory");
       stage(0);
       lds_barrier();
-      for (int c0 = 0; c0 < nsteps; c0 += 2 * CH) {
-        issue(c0 + CH, b1);
-        asm volatile("" ::: "memory");
-        compute(c0, 0, b0, fast_c);
-        asm volatile("" ::: "memory");
-        stage(1);
-        lds_barrier();
-        issue(c0 + 2 * CH, b0);
-        asm volatile("" ::: "memory");
-        compute(c0 + CH, 1, b1, fast_c);
-        asm volatile("" ::: "memory");
-        stage(0);
-        lds_barrier();
-      }
-    };
-    if (G256 || fast)
-      mainloop(std::true_type{});
-    else
-      mainloop(std::false_type{});
+    }
+  };
+  if (G256 || fast)
+    mainloop(std::true_type{});
+  else
+    mainloop(std::false_type{});
 
-    // epilogue: lane holds rows 16 rb + 4 g + v of columns nfirst + 32 wv + 16 cb + j
+  // epilogue: lane holds rows 16 rb + 4 g + v of columns nfirst + 32 wv + 16 cb + j
 #pragma unroll
-    for (int cb = 0; cb < 2; cb++) {
-      const int c = 32 * wv + 16 * cb + j;
-      const int col = nfirst + c;
-      const double cs = (double)cs_lds[c];
+  for (int cb = 0; cb < 2; cb++) {
+    const int c = 32 * wv + 16 * cb + j;
+    const int col = nfirst + c;
+    const double cs = (double)cs_lds[c];
 #pragma unroll
-      for (int rb = 0; rb < 4; rb++) {
-        float hv[4];
+    for (int rb = 0; rb < 4; rb++) {
+      float hv[4];
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-          const int r = 16 * rb + 4 * g + v;
-          double t;
-          if (G256) {
-            t = (double)acc64[rb][cb][v] * (double)sa_lds[r];
-            t = t * cs;
-          } else {
-            t = fast ? (double)acc64[rb][cb][v] * cs : __longlong_as_double(acc64[rb][cb][v]);
-            t = t * (double)sa_lds[r];
-          }
-          t = t * 0.0078125;
-          hv[v] = (float)t;
-          if (MODE == kRotCodes && r < rows) out[(int64_t)pair_lds[r] * ldo + col] = hv[v];
+      for (int v = 0; v < 4; v++) {
+        const int r = 16 * rb + 4 * g + v;
+        double t;
+        if (G256) {
+          t = (double)acc64[rb][cb][v] * (double)sa_lds[r];
+          t = t * cs;
+        } else {
+          t = fast ? (double)acc64[rb][cb][v] * cs : __longlong_as_double(acc64[rb][cb][v]);
+          t = t * (double)sa_lds[r];
         }
-        if (MODE != kRotCodes) {
-          // gate = even column, up = the odd one in the neighbouring lane; the
-          // lane pair splits the rows: the even lane finishes v = 0, 1, the
-          // odd lane v = 2, 3 (one exp per output, not two)
-          float xv[4];
+        t = t * 0.0078125;
+        hv[v] = (float)t;
+        if (MODE == kRotCodes && r < rows) out[(int64_t)pair_lds[r] * ldo + col] = hv[v];
+      }
+      if (MODE != kRotCodes) {
+        // gate = even column, up = the odd one in the neighbouring lane; the
+        // lane pair splits the rows: the even lane finishes v = 0, 1, the
+        // odd lane v = 2, 3 (one exp per output, not two)
+        float xv[4];
 #pragma unroll
-          for (int v = 0; v < 4; v++) xv[v] = __shfl_xor(hv[v], 1, 64);
-          const bool odd = j & 1;
+        for (int v = 0; v < 4; v++) xv[v] = __shfl_xor(hv[v], 1, 64);
+        const bool odd = j & 1;
 #pragma unroll
-          for (int q = 0; q < 2; q++) {
-            const int v = odd ? q + 2 : q;
-            const float gate = odd ? xv[q + 2] : hv[q];
-            const float up = odd ? hv[q + 2] : xv[q];
-            const float sg = (float)((double)gate / (1.0 + exp(-(double)gate)));
-            const int r = 16 * rb + 4 * g + v;
-            if (r < rows) out[(int64_t)pair_lds[r] * ldo + (col >> 1)] = sg * up;
-          }
+        for (int q = 0; q < 2; q++) {
+          const int v = odd ? q + 2 : q;
+          const float gate = odd ? xv[q + 2] : hv[q];
+          const float up = odd ? hv[q + 2] : xv[q];
+          const float sg = (float)((double)gate / (1.0 + exp(-(double)gate)));
+          const int r = 16 * rb + 4 * g + v;
+          if (r < rows) out[(int64_t)pair_lds[r] * ldo + (col >> 1)] = sg * up;
         }
       }
     }
-    lds_barrier();  // LDS reused by the next weight-row block
   }
 }
 
 // pair counts up to kRotSplitMaxPairs take the split-K GEMMs with the rotated
-// requant fused into gemm2's prologue; up to kRotTileMinPairs the split-K
-// GEMMs around k_rot_requant; beyond it the LDS-tiled GEMMs.
+// requant fused into gemm2's prologue; beyond, the split-K GEMMs around
+// k_rot_requant (measured on MI355X at 2048 tokens, 256 experts, H=2048,
+// I=512: gemm1 / gemm2 259 / 121 us, against 303 / 205 us for the LDS-tiled
+// kernel, which the shared expert's large batches use)
 constexpr int64_t kRotSplitMaxPairs = 256;
-constexpr int64_t kRotTileMinPairs = 4096;
 
-hipError_t launch_rot_sort(const MoeArgs& a, const MoeWs& ws, int64_t P, bool blocks,
-                           hipStream_t stream) {
-  if (!blocks && P <= kMoeSortOneWg) {
+hipError_t launch_rot_sort(const MoeArgs& a, const MoeWs& ws, int64_t P, hipStream_t stream) {
+  if (P <= kMoeSortOneWg) {
     hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
                        ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax);
     return hipGetLastError();
@@ -2329,57 +2318,32 @@ hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const u
   hipLaunchKernelGGL(k_rot_route_quant, dim3((a.T + 3) / 4), dim3(512), 0, stream, a.x, a.logits,
                      a.T, a.H, a.E, a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const bool split = P <= kRotSplitMaxPairs;
-  const bool tiled = P > kRotTileMinPairs;
-  if ((err = launch_rot_sort(a, ws, P, tiled, stream)) != hipSuccess) return err;
-  if (!tiled) {
-    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotSilu, 8>), dim3(I2 / 16, slots), dim3(512), 0,
-                       stream, ws.qx, ws.sx, nullptr, a.k, a.w13, s13, nullptr, I2, a.H,
-                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.act, a.I,
-                       nullptr, nullptr);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  if (split) {
-    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotActRot, 4>), dim3(a.H / 16, slots), dim3(256), 0,
-                       stream, nullptr, nullptr, ws.act, a.k, a.w2, s2, nullptr, a.H, a.I,
-                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.y2, a.H,
-                       a.dbg_qa, a.dbg_sa2);
-  } else if (!tiled) {
-    hipLaunchKernelGGL(k_rot_requant, dim3((unsigned)((P + 7) / 8)), dim3(512), 0, stream,
-                       ws.act, P, a.I, ws.qa, ws.sa2);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotCodes, 4>), dim3(a.H / 16, slots), dim3(256), 0,
-                       stream, ws.qa, ws.sa2, nullptr, 1, a.w2, s2, nullptr, a.H, a.I,
-                       ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, 0, ws.y2, a.H,
-                       nullptr, nullptr);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)(P * a.I),
-                                          hipMemcpyDeviceToDevice, stream)) != hipSuccess)
-      return err;
-    if (a.dbg_sa2 && (err = hipMemcpyAsync(a.dbg_sa2, ws.sa2, (size_t)P * 4,
-                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)
-      return err;
+  if ((err = launch_rot_sort(a, ws, P, stream)) != hipSuccess) return err;
+  // four (H <= 2048) or two 16-row weight tiles a workgroup: the activation
+  // slices loaded once for all, more weight bytes in flight; LDS sized for H
+  auto g1 = a.H <= 2048 ? k_rot_gemm_splitk<kRotSilu, 8, 4, 16>
+                        : k_rot_gemm_splitk<kRotSilu, 8, 2, 32>;
+  const unsigned t1 = a.H <= 2048 ? I2 / 64 : I2 / 32;
+  hipLaunchKernelGGL(g1, dim3(t1, slots), dim3(512), 0, stream, ws.qx, ws.sx, nullptr, a.k,
+                     a.w13, s13, nullptr, I2, a.H, ws.expert_list, ws.seg_off, ws.n_active,
+                     ws.sorted_pairs, 0, ws.act, a.I, nullptr, nullptr);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (P <= kRotSplitMaxPairs) {
+    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotActRot, 4, 1, 16>), dim3(a.H / 16, slots),
+                       dim3(256), 0, stream, nullptr, nullptr, ws.act, a.k, a.w2, s2, nullptr,
+                       a.H, a.I, ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, 0,
+                       ws.y2, a.H, a.dbg_qa, a.dbg_sa2);
   } else {
-    // m-blocks of 128 pairs (at most one partial block per expert), two
-    // 64-row halves each, rounded up to the 8 XCDs
-    const unsigned max_blocks = (unsigned)((P / kMoeBM + slots + 7) / 8 * 8);
-    // one 128-row weight block a workgroup (measured on MI355X at 2048 tokens,
-    // 256 experts, H=2048, I=512: four blocks a workgroup, 300 / 195 us for
-    // gemm1 / gemm2, against 237 / 192 us with one)
-    const int ncb1 = 1, ncb2 = 1;
-    hipLaunchKernelGGL((k_rot_tile<kRotSilu, false>), dim3(max_blocks * 2 * (I2 / 128 / ncb1)),
-                       dim3(256), 0, stream, ws.qx, ws.sx, a.k, a.w13, s13, nullptr, I2, a.H,
-                       ws.expert_list, ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks,
-                       ws.sorted_pairs, 0, ws.act, a.I, ncb1);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_rot_requant, dim3((unsigned)((P + 7) / 8)), dim3(512), 0, stream,
                        ws.act, P, a.I, ws.qa, ws.sa2);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_rot_tile<kRotCodes, false>),
-                       dim3(max_blocks * 2 * (a.H / 128 / ncb2)), dim3(256), 0, stream, ws.qa,
-                       ws.sa2, 1, a.w2, s2, nullptr, a.H, a.I,
-                       ws.expert_list, ws.seg_off, ws.blk_slot, ws.blk_row0, ws.n_blocks,
-                       ws.sorted_pairs, 0, ws.y2, a.H, ncb2);
+    // four 16-row weight tiles a workgroup; LDS sized for I
+    auto g2 = a.I <= 512    ? k_rot_gemm_splitk<kRotCodes, 4, 4, 4>
+              : a.I <= 1024 ? k_rot_gemm_splitk<kRotCodes, 4, 4, 8>
+                            : k_rot_gemm_splitk<kRotCodes, 4, 4, 16>;
+    hipLaunchKernelGGL(g2, dim3(a.H / 64, slots), dim3(256), 0, stream, ws.qa, ws.sa2, nullptr,
+                       1, a.w2, s2, nullptr, a.H, a.I, ws.expert_list, ws.seg_off, ws.n_active,
+                       ws.sorted_pairs, 0, ws.y2, a.H, nullptr, nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)(P * a.I),
                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)
@@ -2448,25 +2412,24 @@ hipError_t launch_shared_expert(const SharedArgs& a, hipStream_t stream) {
                      nullptr, T, H, 1, 1, nullptr, nullptr, ws.qx, ws.sx);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.T <= 64) {
-    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotG256Silu, 8>), dim3(2 * Is / 16, 1), dim3(512), 0,
-                       stream, ws.qx, ws.sx, nullptr, 1, a.wgu, a.s2, a.su8, 2 * Is, H, nullptr,
-                       nullptr, nullptr, nullptr, T, ws.act, Is, nullptr, nullptr);
+    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotG256Silu, 8, 1, 32>), dim3(2 * Is / 16, 1),
+                       dim3(512), 0, stream, ws.qx, ws.sx, nullptr, 1, a.wgu, a.s2, a.su8, 2 * Is,
+                       H, nullptr, nullptr, nullptr, nullptr, T, ws.act, Is, nullptr, nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotActRot, 4>), dim3(H / 16, 1), dim3(256), 0, stream,
+    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotActRot, 4, 1, 16>), dim3(H / 16, 1), dim3(256), 0,
+                       stream,
                        nullptr, nullptr, ws.act, 1, a.wd, a.sd, nullptr, H, Is, nullptr, nullptr,
                        nullptr, nullptr, T, a.y, H, a.dbg_qa, a.dbg_sa);
   } else {
     const unsigned mbs = (unsigned)((a.T + 1023) / 1024 * 8);  // 128-row blocks, x 8 XCDs
-    hipLaunchKernelGGL((k_rot_tile<kRotG256Silu, true>), dim3(mbs * 2 * (2 * Is / 128)),
-                       dim3(256), 0, stream, ws.qx, ws.sx, 1, a.wgu, a.s2, a.su8, 2 * Is, H,
-                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, T, ws.act, Is, 1);
+    hipLaunchKernelGGL(k_rot_tile<kRotG256Silu>, dim3(mbs * 2 * (2 * Is / 128)), dim3(256), 0,
+                       stream, ws.qx, ws.sx, a.wgu, a.s2, a.su8, 2 * Is, H, T, ws.act, Is);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_rot_requant, dim3((unsigned)((a.T + 7) / 8)), dim3(512), 0, stream,
                        ws.act, a.T, Is, ws.qa, ws.sa);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_rot_tile<kRotCodes, true>), dim3(mbs * 2 * (H / 128)), dim3(256), 0,
-                       stream, ws.qa, ws.sa, 1, a.wd, a.sd, nullptr, H, Is, nullptr, nullptr,
-                       nullptr, nullptr, nullptr, nullptr, T, a.y, H, 1);
+    hipLaunchKernelGGL(k_rot_tile<kRotCodes>, dim3(mbs * 2 * (H / 128)), dim3(256), 0, stream,
+                       ws.qa, ws.sa, a.wd, a.sd, nullptr, H, Is, T, a.y, H);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)(a.T * a.Is),
                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)

@@ -173,8 +173,8 @@ def _check_rot(orc, x, logits, k, W, Wd, label, shared=None, tokens=None):
 
 
 # small shapes: the single-token path, the split-K GEMMs (with the requant in
-# gemm2's prologue up to 256 pairs, around the requant kernel up to 4096),
-# the LDS-tiled GEMMs beyond; ragged expert segments, a zero token
+# gemm2's prologue up to 256 pairs, around the requant kernel beyond); ragged
+# expert segments, a zero token
 @pytest.mark.parametrize("T,k", [(1, 2), (5, 2), (32, 8), (33, 8), (300, 2), (600, 8)])
 def test_rot_moe_small(orc, T, k):
     E, H, I = 8, 256, 128
@@ -221,9 +221,8 @@ def test_rot_moe_given_ids_and_skew(orc, T):
 
 
 def test_rot_moe_wide_scale_range(orc):
-    # some weight rows have one 128-group scaled down by 2^-28: their scales
-    # span more than the integer fold allows, so those waves of the tiled
-    # GEMMs fold in fp64 group by group while the others take the integer fold
+    # some weight rows have one 128-group scaled down by 2^-28: the fold still
+    # matches the fp64 in-order sum of the definition
     E, H, I, k, T = 4, 256, 256, 4, 1100
     key = (97, 0)
     q13 = np.empty((E, 2 * I, H), np.int8)
@@ -291,6 +290,21 @@ def _check_shared(orc, x, S, Sd, label):
     np.testing.assert_array_equal(yh[rows], y_ref[rows])
     say(f"{label}: rows with equal act {same.mean():.4f}, rows bit-exact {rows.mean():.4f}")
     return y, y_ref
+
+
+def test_shared_expert_wide_scale_range(orc):
+    # the tiled GEMMs (more than 64 rows): down-weight rows with one 128-group
+    # scaled down by 2^-30 span more than the integer fold allows, so those
+    # waves fold in fp64 group by group while the others take the integer fold
+    H, Is, T = 512, 256, 200
+    wgu, su8, s2 = orc.weight_prep_g256(synth.weights((98, 5), 2 * Is, H, tensor_id=synth.T_W))
+    Wd = synth.weights((98, 5), H, Is, tensor_id=synth.T_W2)
+    Wd[:32, :128] *= np.float32(2.0 ** -30)
+    Wd[300:301, 128:] *= np.float32(2.0 ** -25)
+    wd, sd = orc.weight_prep_g128(Wd)
+    S = (wgu, su8, s2, wd, sd)
+    x = synth.activations((98, 6), T, H, 4, 10.0)
+    _check_shared(orc, x, S, _dev_shared_weights(S), "shared wide scale range")
 
 
 @pytest.mark.parametrize("T", [1, 7, 64, 65, 300])
