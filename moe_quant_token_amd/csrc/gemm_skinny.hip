@@ -305,6 +305,8 @@ hipError_t launch_linear_skinny_fused(const uint16_t* x, int64_t ldx, int64_t M,
   const size_t lds = (size_t)(M * K);
   const int64_t need = (M * (K / 8) + kSkinnyWaves * 64 - 1) / (kSkinnyWaves * 64);
   const dim3 grid((unsigned)(N / 16)), block(kSkinnyWaves * 64);
+  // (12 loads a wave for the down projection, as launch_skinny_impl: 12.38 ->
+  // 12.29 us at one token, 13.67 -> 18.66 us at two; kept at 8)
   if (M == 1)
     hipLaunchKernelGGL((k_linear_skinny_fused<1, 4>), grid, block, lds, stream, x, ldx, (int)M,
                        (int)K, qw_packed, sw, y, ldy);
@@ -321,9 +323,23 @@ template <bool PACKED, int EPI>
 static hipError_t launch_skinny_impl(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                                      int64_t lda, const int8_t* qw, const float* sw, int64_t N,
                                      int64_t ldw, void* out, int64_t ldo, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm_skinny<kSkinnyWaves, kSkinnyU, PACKED, EPI>),
-                     dim3((unsigned)(N / 16)), dim3(kSkinnyWaves * 64), 0, stream, qa, sa, (int)M,
-                     (int)K, lda, qw, sw, ldw, out, ldo);
+  // loads in flight per wave by the tile's k-step count: 65..80 steps take one
+  // round of 10 (the gate_up projection, K=5120: 17.0 -> 16.5 us at one
+  // token, 19.3 -> 18.1 at eight), 129..144 steps two rounds of 12 (the down
+  // projection, K=8704: 11.57 -> 11.44 us, 13.6 -> 13.2), else 8 (measured on
+  // MI355X, two interleaved rounds; one round of 17 for the down projection
+  // was slower, 11.8 us)
+  const int64_t nc = K >> 6;
+  const dim3 grid((unsigned)(N / 16)), block(kSkinnyWaves * 64);
+  if (nc > 64 && nc <= 80)
+    hipLaunchKernelGGL((k_gemm_skinny<kSkinnyWaves, 10, PACKED, EPI>), grid, block, 0, stream,
+                       qa, sa, (int)M, (int)K, lda, qw, sw, ldw, out, ldo);
+  else if (nc > 128 && nc <= 144)
+    hipLaunchKernelGGL((k_gemm_skinny<kSkinnyWaves, 12, PACKED, EPI>), grid, block, 0, stream,
+                       qa, sa, (int)M, (int)K, lda, qw, sw, ldw, out, ldo);
+  else
+    hipLaunchKernelGGL((k_gemm_skinny<kSkinnyWaves, kSkinnyU, PACKED, EPI>), grid, block, 0,
+                       stream, qa, sa, (int)M, (int)K, lda, qw, sw, ldw, out, ldo);
   return hipGetLastError();
 }
 
