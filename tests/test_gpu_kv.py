@@ -27,8 +27,11 @@ def _x(T, Hk, D, seed):
     return np.ascontiguousarray(x)
 
 
+# D in {64, 128, 256} with at least 256 rows takes several rows a wave (ragged
+# last wave), everything else one row a wave
 @pytest.mark.parametrize("T,Hk,D", [(1, 4, 256), (8, 4, 256), (4096, 4, 256), (37, 8, 128),
-                                    (5, 2, 4096), (3, 1, 8), (70, 3, 520)])
+                                    (9, 5, 64), (61, 5, 64), (5, 2, 4096), (3, 1, 8),
+                                    (70, 3, 520)])
 def test_kv_quant_bit_exact(orc, T, Hk, D):
     say(f"kv quant T={T} Hk={Hk} D={D}")
     x = _x(T, Hk, D, T * 1000 + D)
@@ -46,10 +49,12 @@ def test_kv_quant_bit_exact(orc, T, Hk, D):
     np.testing.assert_array_equal(host(q), q_ref)
 
 
-def test_kv_quant_slots_and_stride(orc):
-    T, Hk, D, rows = 11, 4, 256, 20
+@pytest.mark.parametrize("T", [11, 100])
+def test_kv_quant_slots_and_stride(orc, T):
+    Hk, D, rows = 4, 256, T + 9
     x = _x(T, Hk, D, 7)
-    slots = np.array([19, 3, -1, 7, 0, 15, 25, 1, 8, -5, 12], np.int32)
+    r = np.random.default_rng(T)
+    slots = r.permutation(rows + 6)[:T].astype(np.int32) - 3  # some negative, some past the end
     ok = (slots >= 0) & (slots < rows)
     q_ref, s_ref = orc.kv_quant_i8(x[ok], slots[ok], rows=rows)
     big = np.zeros((T, Hk * D + 64), np.uint16)
