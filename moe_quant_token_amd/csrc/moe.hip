@@ -1490,7 +1490,7 @@ enum { kRotSilu = 1, kRotActRot = 2, kRotG256Silu = 3, kRotCodes = 4 };
 
 // Which input rows a workgroup's pair block reads: expert slot grouping (the
 // sorted pairs of one expert) or, in the dense form (expert_list == nullptr),
-// rows [64 blockIdx.y, +64) of a plain matrix (pair p = row p).
+// rows [rows_per_y blockIdx.y, +rows_per_y) of a plain matrix (pair p = row p).
 struct RotRows {
   int e, begin, end;
 };
@@ -1608,7 +1608,7 @@ __device__ __forceinline__ void rot_col_scales(const uint16_t* __restrict__ sp, 
 //   kRotG256Silu: T = sum over 256-groups of su8 (acc_2g + acc_2g+1), exact
 //                 in int64; h = (float)(T sx s2 2^-7); SiLU(gate) * up.
 // W is packed (16-row tiles of 1 KiB k-steps), as [E * Nw, K].  In the dense
-// form (expert_list == nullptr) the rows are [64 blockIdx.y, +64) of a
+// form (expert_list == nullptr) the rows are [16 blockIdx.y, +16) of a
 // plain matrix (pair p = row p).
 template <int MODE, int WAVES, int NT, int MAXG>
 __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
@@ -1630,7 +1630,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
   __shared__ int pair_lds[16];
   static_assert(!G256 || NT == 1, "the g256 form takes one tile a workgroup");
   RotRows rr;
-  if (!rot_rows(expert_list, seg_off, n_active, dense_rows, 64, rr)) return;
+  if (!rot_rows(expert_list, seg_off, n_active, dense_rows, 16, rr)) return;
   const bool dense = expert_list == nullptr;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -2412,14 +2412,15 @@ hipError_t launch_shared_expert(const SharedArgs& a, hipStream_t stream) {
                      nullptr, T, H, 1, 1, nullptr, nullptr, ws.qx, ws.sx);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.T <= 64) {
-    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotG256Silu, 8, 1, 32>), dim3(2 * Is / 16, 1),
+    // one 16-row block of tokens a workgroup row (grid.y)
+    const unsigned rb = (unsigned)((a.T + 15) / 16);
+    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotG256Silu, 8, 1, 32>), dim3(2 * Is / 16, rb),
                        dim3(512), 0, stream, ws.qx, ws.sx, nullptr, 1, a.wgu, a.s2, a.su8, 2 * Is,
                        H, nullptr, nullptr, nullptr, nullptr, T, ws.act, Is, nullptr, nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotActRot, 4, 1, 16>), dim3(H / 16, 1), dim3(256), 0,
-                       stream,
-                       nullptr, nullptr, ws.act, 1, a.wd, a.sd, nullptr, H, Is, nullptr, nullptr,
-                       nullptr, nullptr, T, a.y, H, a.dbg_qa, a.dbg_sa);
+    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotActRot, 4, 1, 16>), dim3(H / 16, rb), dim3(256), 0,
+                       stream, nullptr, nullptr, ws.act, 1, a.wd, a.sd, nullptr, H, Is, nullptr,
+                       nullptr, nullptr, nullptr, T, a.y, H, a.dbg_qa, a.dbg_sa);
   } else {
     const unsigned mbs = (unsigned)((a.T + 1023) / 1024 * 8);  // 128-row blocks, x 8 XCDs
     hipLaunchKernelGGL(k_rot_tile<kRotG256Silu>, dim3(mbs * 2 * (2 * Is / 128)), dim3(256), 0,

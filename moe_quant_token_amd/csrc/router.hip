@@ -11,9 +11,10 @@
 //     product is exact in fp32) for every token, then a butterfly reduction
 //     over the wave.  The weight row is read once for all tokens;
 //   - more tokens: bf16 MFMA (v_mfma_f32_16x16x32_bf16) tiles of 16 tokens x
-//     16 experts per wave, H split over 8 waves (up to 256 tokens) or 2
-//     waves (beyond, four token blocks a workgroup), the slices' partial sums
-//     added in slice order.
+//     16 experts per wave, H split over 8 waves (up to 256 tokens); beyond,
+//     16 tokens x 64 experts per wave with H split over 4 waves (or the
+//     16 x 16 tiles over 2 waves where E or H do not divide), the slices'
+//     partial sums added in slice order.
 // Layouts: x bf16 [T, H] with row stride ldx; wg bf16 [E, H] contiguous;
 // logits fp32 [T, E] with row stride ldl.
 #include "kernels.h"
@@ -130,6 +131,72 @@ __global__ __launch_bounds__(TB * KS * 64) void k_router_mfma(
   }
 }
 
+// Larger batches: a wave takes 16 tokens x 16 EB experts (the token
+// fragment of each k step feeds EB MFMAs); workgroup = TB token blocks x KS
+// slices of H, the slices' partial sums added in slice order.  Each weight
+// fragment is read by T / (16 TB) workgroups and each token fragment by
+// E / (16 EB), against E / 16 for the one-expert-block form.
+template <int TB, int KS, int EB>
+__global__ __launch_bounds__(TB * KS * 64) void k_router_mfma_wide(
+    const uint16_t* __restrict__ x, int T, int H, int64_t ldx, const uint16_t* __restrict__ wg,
+    float* __restrict__ logits, int64_t ldl) {
+  __shared__ v4f red[TB][KS][EB][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int tb = wv / KS, ks = wv - (wv / KS) * KS;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int e0 = blockIdx.x * 16 * EB;
+  const int t0 = (blockIdx.y * TB + tb) * 16;
+  const int ta = min(t0 + j, T - 1);  // rows past T read a valid row; not stored
+  const int hs = H / KS;
+  const uint16_t* ap = x + (int64_t)ta * ldx + ks * hs + g * 8;
+  const uint16_t* bp = wg + (int64_t)(e0 + j) * H + ks * hs + g * 8;
+  v4f acc[EB];
+#pragma unroll
+  for (int b = 0; b < EB; b++) acc[b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  if (t0 < T) {
+    constexpr int U = 4;
+    for (int k0 = 0; k0 < hs; k0 += 32 * U) {  // hs is a multiple of 32 U (launcher)
+      v4u a[U], b[U][EB];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        a[u] = *reinterpret_cast<const v4u*>(ap + k0 + 32 * u);
+#pragma unroll
+        for (int e = 0; e < EB; e++)
+          b[u][e] = *reinterpret_cast<const v4u*>(bp + (int64_t)e * 16 * H + k0 + 32 * u);
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++)
+#pragma unroll
+        for (int e = 0; e < EB; e++)
+          acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[u]),
+                                                           __builtin_bit_cast(v8bf, b[u][e]),
+                                                           acc[e], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EB; e++) red[tb][ks][e][lane] = acc[e];
+  __syncthreads();
+  if (ks != 0 || t0 >= T) return;
+#pragma unroll
+  for (int e = 0; e < EB; e++) {
+    v4f sum = red[tb][0][e][lane];
+    for (int i = 1; i < KS; i++) {
+      const v4f p = red[tb][i][e][lane];
+      sum.x = sum.x + p.x;
+      sum.y = sum.y + p.y;
+      sum.z = sum.z + p.z;
+      sum.w = sum.w + p.w;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int t = t0 + 4 * g + v;
+      if (t < T) logits[(int64_t)t * ldl + e0 + 16 * e + j] = sum[v];
+    }
+  }
+}
+
 hipError_t launch_router_gate_bf16(const uint16_t* x, int64_t T, int64_t H, int64_t ldx,
                                    const uint16_t* wg, int64_t E, float* logits, int64_t ldl,
                                    hipStream_t stream) {
@@ -139,6 +206,10 @@ hipError_t launch_router_gate_bf16(const uint16_t* x, int64_t T, int64_t H, int6
   } else if (T <= 256 && H % 256 == 0) {
     hipLaunchKernelGGL((k_router_mfma<1, 8>), dim3((unsigned)(E / 16), (unsigned)((T + 15) / 16)),
                        dim3(512), 0, stream, x, (int)T, (int)H, ldx, wg, logits, ldl);
+  } else if (E % 64 == 0 && H % 512 == 0) {
+    hipLaunchKernelGGL((k_router_mfma_wide<2, 4, 4>),
+                       dim3((unsigned)(E / 64), (unsigned)((T + 31) / 32)), dim3(512), 0, stream,
+                       x, (int)T, (int)H, ldx, wg, logits, ldl);
   } else if (H % 64 == 0) {
     hipLaunchKernelGGL((k_router_mfma<4, 2>), dim3((unsigned)(E / 16), (unsigned)((T + 63) / 64)),
                        dim3(512), 0, stream, x, (int)T, (int)H, ldx, wg, logits, ldl);

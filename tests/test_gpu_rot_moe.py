@@ -84,11 +84,15 @@ def test_weight_prep_g128(orc, N, K):
 
 # ----------------------------------------------------------- router gate --
 
-@pytest.mark.parametrize("T", [1, 3, 16, 17, 100, 2048])
-def test_router_gate(orc, T):
-    H, E = 2048, 256
+# one wave per expert (up to 16 tokens), 16 x 16 tiles over 8 slices of H (up
+# to 256), 16 x 64 tiles over 4 slices beyond (ragged last token block); the
+# 16 x 16 tiles over 2 slices where E is not a multiple of 64
+@pytest.mark.parametrize("T,E", [(1, 256), (3, 256), (16, 256), (17, 256), (100, 256),
+                                 (300, 256), (2048, 256), (300, 48)])
+def test_router_gate(orc, T, E):
+    H = 2048
     x = synth.activations((91, T), T, H, 20, 10.0)
-    wg = synth.to_bf16_bits(synth.weights((91, 0), E, H))
+    wg = synth.to_bf16_bits(synth.weights((91, E), E, H))
     ref = orc.router_gate_bf16(x, wg)
     lg = mq.router_gate_bf16(bf16_dev(x), bf16_dev(wg))
     lg2 = mq.router_gate_bf16(bf16_dev(x), bf16_dev(wg))
@@ -99,8 +103,8 @@ def test_router_gate(orc, T):
     wf = orc.bf16_to_f32(wg).astype(np.float64)
     bound = H * 2.0 ** -24 * (np.abs(xf) @ np.abs(wf).T) + 1e-30
     err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
-    assert (err <= bound).all(), f"router T={T}: max err / bound {(err / bound).max():.3f}"
-    say(f"router T={T}: max err / bound {(err / bound).max():.4f}")
+    assert (err <= bound).all(), f"router T={T} E={E}: max err / bound {(err / bound).max():.3f}"
+    say(f"router T={T} E={E}: max err / bound {(err / bound).max():.4f}")
 
 
 @pytest.mark.parametrize("T", [5, 40])
