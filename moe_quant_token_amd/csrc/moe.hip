@@ -1486,7 +1486,7 @@ __global__ __launch_bounds__(512) void k_rot_requant(const float* __restrict__ a
 }
 
 // The epilogues of the rotated-expert GEMMs.
-enum { kRotSilu = 1, kRotActRot = 2, kRotG256Silu = 3, kRotCodes = 4 };
+enum { kRotSilu = 1, kRotActRot = 2, kRotG256Silu = 3, kRotCodes = 4, kRotG256SiluX = 5 };
 
 // Which input rows a workgroup's pair block reads: expert slot grouping (the
 // sorted pairs of one expert) or, in the dense form (expert_list == nullptr),
@@ -1606,7 +1606,9 @@ __device__ __forceinline__ void rot_col_scales(const uint16_t* __restrict__ sp, 
 //   kRotCodes:    as kRotActRot with the rotated codes and scales given
 //                 (qx = qa [P, K], sx = sa [P], k = 1);
 //   kRotG256Silu: T = sum over 256-groups of su8 (acc_2g + acc_2g+1), exact
-//                 in int64; h = (float)(T sx s2 2^-7); SiLU(gate) * up.
+//                 in int64; h = (float)(T sx s2 2^-7); SiLU(gate) * up;
+//   kRotG256SiluX: as kRotG256Silu with the prologue rotating and
+//                 quantising the bf16 token rows (act = x, K <= 2048) itself.
 // W is packed (16-row tiles of 1 KiB k-steps), as [E * Nw, K].  In the dense
 // form (expert_list == nullptr) the rows are [16 blockIdx.y, +16) of a
 // plain matrix (pair p = row p).
@@ -1619,13 +1621,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
     const int32_t* __restrict__ sorted_pairs, int dense_rows, float* __restrict__ out, int ldo,
     int8_t* __restrict__ qa_rec, float* __restrict__ sa_rec) {
   constexpr int GW = (MAXG + WAVES - 1) / WAVES;  // groups a wave takes
-  constexpr bool G256 = MODE == kRotG256Silu;
+  constexpr bool G256 = MODE == kRotG256Silu || MODE == kRotG256SiluX;
+  constexpr bool ROT_IN = MODE == kRotActRot || MODE == kRotG256SiluX;  // rows rotated here
   __shared__ v4i red[G256 ? 1 : NT][G256 ? 1 : MAXG][64];
   __shared__ long long sred[G256 ? WAVES : 1][4][64];
   __shared__ int32_t m_lds[G256 ? 16 : 1][MAXG + 1];
   __shared__ float s_lds[NT * 16][MAXG + 1];
   __shared__ float cs_lds[16];
-  __shared__ __attribute__((aligned(16))) int8_t a_lds[MODE == kRotActRot ? 16 * 2048 : 16];
+  __shared__ __attribute__((aligned(16))) int8_t a_lds[ROT_IN ? 16 * 2048 : 16];
   __shared__ float sa_lds[16];
   __shared__ int pair_lds[16];
   static_assert(!G256 || NT == 1, "the g256 form takes one tile a workgroup");
@@ -1684,10 +1687,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
           threadIdx.x < nrows ? (dense ? pb + (int)threadIdx.x : sorted_pairs[pb + threadIdx.x])
                               : 0;
     __syncthreads();
-    if (MODE == kRotActRot) {
+    if (ROT_IN) {
       for (int r = wv; r < nrows; r += WAVES) {
         Block8 bb[4];
-        const float am = rot_row_wave<4>(act + (int64_t)pair_lds[r] * K, K, bb, lane);
+        const float am =
+            MODE == kRotG256SiluX
+                ? rot_row_wave<4>(reinterpret_cast<const uint16_t*>(act) + (int64_t)pair_lds[r] * K,
+                                  K, bb, lane)
+                : rot_row_wave<4>(act + (int64_t)pair_lds[r] * K, K, bb, lane);
         const float sc = am / 127.0f;
 #pragma unroll
         for (int rd = 0; rd < 4; rd++) {
@@ -1697,17 +1704,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
           const int kk = blk * 128 + j * 8;  // first of the lane's 8 values
           *reinterpret_cast<uint2*>(a_lds + (kk >> 6) * 1024 + (r + 16 * ((kk & 63) >> 4)) * 16 +
                                     (kk & 15)) = wd;
-          if (blockIdx.x == 0 && qa_rec)
+          if (MODE == kRotActRot && blockIdx.x == 0 && qa_rec)
             *reinterpret_cast<uint2*>(qa_rec + (int64_t)pair_lds[r] * K + kk) = wd;
         }
         if (lane == 0) {
           const float sv = am != 0.0f ? sc : 0.0f;
           sa_lds[r] = sv;
-          if (blockIdx.x == 0 && sa_rec) sa_rec[pair_lds[r]] = sv;
+          if (MODE == kRotActRot && blockIdx.x == 0 && sa_rec) sa_rec[pair_lds[r]] = sv;
         }
       }
     }
-    if (MODE != kRotActRot && threadIdx.x < 16)
+    if (!ROT_IN && threadIdx.x < 16)
       sa_lds[threadIdx.x] = sx[pair_lds[threadIdx.x < nrows ? threadIdx.x : 0] / k];
     __syncthreads();
 
@@ -1723,7 +1730,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const int c = 2 * gg + h;
-          if (MODE == kRotActRot)
+          if (ROT_IN)
             a[h] = *reinterpret_cast<const v4i*>(&a_lds[c * 1024 + lane * 16]);
           else
             a[h] = a_ok ? *reinterpret_cast<const v4i*>(ap + (int64_t)c * 64) : v4i{0, 0, 0, 0};
@@ -2408,15 +2415,27 @@ hipError_t launch_shared_expert(const SharedArgs& a, hipStream_t stream) {
   const SharedWs ws = carve_shared(a.ws, a.T, a.H, a.Is);
   const int T = (int)a.T, H = (int)a.H, Is = (int)a.Is;
   hipError_t err;
-  hipLaunchKernelGGL(k_rot_route_quant, dim3((unsigned)((T + 3) / 4)), dim3(512), 0, stream, a.x,
-                     nullptr, T, H, 1, 1, nullptr, nullptr, ws.qx, ws.sx);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // up to 8 tokens with H <= 2048 the gate/up GEMM rotates and quantises its
+  // token rows itself (one launch less)
+  const bool fused = a.T <= 8 && a.H <= 2048;
+  if (!fused) {
+    hipLaunchKernelGGL(k_rot_route_quant, dim3((unsigned)((T + 3) / 4)), dim3(512), 0, stream,
+                       a.x, nullptr, T, H, 1, 1, nullptr, nullptr, ws.qx, ws.sx);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if (a.T <= 64) {
     // one 16-row block of tokens a workgroup row (grid.y)
     const unsigned rb = (unsigned)((a.T + 15) / 16);
-    hipLaunchKernelGGL((k_rot_gemm_splitk<kRotG256Silu, 8, 1, 32>), dim3(2 * Is / 16, rb),
-                       dim3(512), 0, stream, ws.qx, ws.sx, nullptr, 1, a.wgu, a.s2, a.su8, 2 * Is,
-                       H, nullptr, nullptr, nullptr, nullptr, T, ws.act, Is, nullptr, nullptr);
+    if (fused)  // x passed as the rows to rotate (bf16; the mode reads them as such)
+      hipLaunchKernelGGL((k_rot_gemm_splitk<kRotG256SiluX, 8, 1, 16>), dim3(2 * Is / 16, rb),
+                         dim3(512), 0, stream, nullptr, nullptr,
+                         reinterpret_cast<const float*>(a.x), 1, a.wgu, a.s2, a.su8, 2 * Is, H,
+                         nullptr, nullptr, nullptr, nullptr, T, ws.act, Is, nullptr, nullptr);
+    else
+      hipLaunchKernelGGL((k_rot_gemm_splitk<kRotG256Silu, 8, 1, 32>), dim3(2 * Is / 16, rb),
+                         dim3(512), 0, stream, ws.qx, ws.sx, nullptr, 1, a.wgu, a.s2, a.su8,
+                         2 * Is, H, nullptr, nullptr, nullptr, nullptr, T, ws.act, Is, nullptr,
+                         nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL((k_rot_gemm_splitk<kRotActRot, 4, 1, 16>), dim3(H / 16, rb), dim3(256), 0,
                        stream, nullptr, nullptr, ws.act, 1, a.wd, a.sd, nullptr, H, Is, nullptr,
