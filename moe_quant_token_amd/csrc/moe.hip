@@ -284,6 +284,71 @@ __device__ __forceinline__ void route_select(const float* __restrict__ lt, int E
     route_select_v<16>(lt, E, k, lane, sel_e, sel_w);
 }
 
+// The expert of one slot alone (E <= 256), from the lane's four logits
+// (experts lane + 64 i): the rounds of route_select_sorted4 up to that slot,
+// so the same selection.  A round whose maximum sits on one lane reads the
+// expert there through a ballot; tied maxima take the second reduction.
+// Lane s <= slot keeps round s's expert and logit in my_e, my_l, and mx gets
+// the largest logit, so after k rounds route_slot_weight gives the weights.
+__device__ __forceinline__ int route_slot_expert4(const float (&lv)[4], int E, int slot,
+                                                  int lane, int& my_e, float& my_l,
+                                                  double& mx) {
+  uint32_t q[4];
+  int ee[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    ee[i] = lane + 64 * i;
+    q[i] = ee[i] < E ? float_key(lv[i]) : 0u;
+  }
+  order_pair(q[0], ee[0], q[1], ee[1]);
+  order_pair(q[2], ee[2], q[3], ee[3]);
+  order_pair(q[0], ee[0], q[2], ee[2]);
+  order_pair(q[1], ee[1], q[3], ee[3]);
+  order_pair(q[1], ee[1], q[2], ee[2]);
+  int be = 0;
+  my_e = 0;
+  my_l = 0.0f;
+  for (int s = 0; s <= slot; s++) {
+    const uint32_t mh = wave_max_u32(q[0]);
+    const uint64_t holders = __ballot(q[0] == mh);
+    if (__popcll(holders) == 1)
+      be = __builtin_amdgcn_readlane(ee[0], __ffsll((long long)holders) - 1);
+    else
+      be = (int)(0xffffffffu -
+                 wave_max_u32(q[0] == mh ? 0xffffffffu - (uint32_t)ee[0] : 0u));
+    if (s == 0) mx = (double)key_float(mh);
+    if ((be & 63) == lane) {
+      q[0] = q[1];
+      ee[0] = ee[1];
+      q[1] = q[2];
+      ee[1] = ee[2];
+      q[2] = q[3];
+      ee[2] = ee[3];
+      q[3] = 0u;
+      ee[3] = 0x7fffffff;
+    }
+    if (lane == s) {
+      my_e = be;
+      my_l = key_float(mh);
+    }
+  }
+  return be;
+}
+
+// The renormalised weight of lane s's slot after k rounds of
+// route_slot_expert4: the arithmetic of route_select_sorted4.
+__device__ __forceinline__ float route_slot_weight(float my_l, double mx, int k) {
+  const double myp = exp((double)my_l - mx);
+  const uint64_t pb = (uint64_t)__double_as_longlong(myp);
+  double kept = 0.0;
+  for (int s = 0; s < k; s++) {
+    const uint32_t plo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pb, s);
+    const uint32_t phi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pb >> 32), s);
+    kept += __longlong_as_double((long long)(((uint64_t)phi << 32) | plo));
+  }
+  return (float)(myp / kept);
+}
+
 __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E, int k,
                                             int32_t* __restrict__ ids, float* __restrict__ w,
                                             int lane, int32_t* ids_copy = nullptr) {
@@ -858,15 +923,26 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm1(
     const int c = lane + 64 * u;
     xr[u] = c < nc8 ? *reinterpret_cast<const v4u*>(x + c * 8) : v4u{0u, 0u, 0u, 0u};
   }
-  // wave 0 routes the token (the selection is a chain of k wave-wide
-  // maximum rounds; on every wave it would fill the SIMDs for microseconds);
-  // the others wait at the barrier
+  // wave 0 finds this workgroup's expert (the selection is a chain of
+  // wave-wide maximum rounds, slot + 1 of them up to 256 experts; on every
+  // wave it would fill the SIMDs); the others wait at the barrier
   __shared__ int e_lds;
   int sel_e = 0;
   float sel_w = 0.0f;
+  const bool few = E <= 256;
+  float my_l = 0.0f;
+  double mx = 0.0;
   if (wv == 0) {
-    route_select(logits, E, k, lane, sel_e, sel_w);
-    const int es = __shfl(sel_e, slot, 64);
+    int es;
+    if (few) {
+      float lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) lv[i] = logits[min(lane + 64 * i, E - 1)];
+      es = route_slot_expert4(lv, E, slot, lane, sel_e, my_l, mx);
+    } else {
+      route_select(logits, E, k, lane, sel_e, sel_w);
+      es = __shfl(sel_e, slot, 64);
+    }
     if (lane == 0) e_lds = es;
   }
   __syncthreads();
@@ -886,6 +962,9 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm1(
   load_w(bq, wv);
   const int col = tile * 16 + j;
   const float swc = wv == 0 ? sW[(int64_t)e * Nw + col] : 0.0f;  // wave 0's epilogue
+  // the routing weights (workgroup (0, k - 1), which ran all k rounds), with
+  // the weight loads already out
+  if (few && wv == 0 && tile == 0 && slot == k - 1) sel_w = route_slot_weight(my_l, mx, k);
 
   // the token's scale: maximum of |x| over the row (every wave), as k_quant_rows
   float amax = 0.0f;
@@ -969,16 +1048,14 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm1(
         seg_off[slot] = slot;
         sorted_pairs[slot] = slot;
       }
-      if (slot == 0) {
-        if (lane == 0) {
-          n_active[0] = k;
-          seg_off[k] = k;
-          sx[0] = sxv;
-        }
-        if (lane < k) {
-          topk_ids[lane] = sel_e;
-          topk_w[lane] = sel_w;
-        }
+      if (slot == 0 && lane == 0) {
+        n_active[0] = k;
+        seg_off[k] = k;
+        sx[0] = sxv;
+      }
+      if (slot == k - 1 && lane < k) {
+        topk_ids[lane] = sel_e;
+        topk_w[lane] = sel_w;
       }
     }
   }
@@ -1016,6 +1093,10 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm2(
     constexpr int64_t wstep = PACKED ? 1024 : 64;
     const int col = tile * 16 + j;
     const float swc = s2[(int64_t)e * H + col];
+    // the first U weight steps go out before the requantisation
+    v4i b0[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) b0[u] = u < nk ? ld_stream(wbase + u * wstep) : v4i{0, 0, 0, 0};
     // the pair's |act| maximum from gemm1's partial maxima (non-negative
     // fp32 bit patterns), then its scale
     uint32_t mb = 0u;
@@ -1043,7 +1124,7 @@ __global__ __launch_bounds__(512) void k_moe_t1_gemm2(
 #pragma unroll
       for (int u = 0; u < U; u++) {
         const int c = c0 + u;
-        b[u] = c < nk ? ld_stream(wbase + c * wstep) : v4i{0, 0, 0, 0};
+        b[u] = c0 == 0 ? b0[u] : (c < nk ? ld_stream(wbase + c * wstep) : v4i{0, 0, 0, 0});
       }
 #pragma unroll
       for (int u = 0; u < U; u++) {
@@ -1816,19 +1897,32 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm1(
   const int nk = H >> 6;
   const int G = H >> 7;
   const bool first = tile == 0 && slot == 0;
+  // up to 256 experts each workgroup finds its slot's expert alone; workgroup
+  // (0, k - 1), which ran all k rounds, writes the selection
+  const bool few = logits && E <= 256;
+  int sel_e = 0;
+  float my_l = 0.0f;
+  double mx = 0.0;
   if (wv == 0) {
-    int sel_e = 0;
     float sel_w = 0.0f;
-    if (logits) {
-      route_select(logits, E, k, lane, sel_e, sel_w);
-      if (first && lane < k) {
-        topk_ids[lane] = sel_e;
-        topk_w[lane] = sel_w;
-      }
+    int es;
+    if (few) {
+      float lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) lv[i] = logits[min(lane + 64 * i, E - 1)];
+      es = route_slot_expert4(lv, E, slot, lane, sel_e, my_l, mx);
     } else {
-      sel_e = lane < k ? topk_ids[lane] : 0;
+      if (logits) {
+        route_select(logits, E, k, lane, sel_e, sel_w);
+        if (first && lane < k) {
+          topk_ids[lane] = sel_e;
+          topk_w[lane] = sel_w;
+        }
+      } else {
+        sel_e = lane < k ? topk_ids[lane] : 0;
+      }
+      es = __shfl(sel_e, slot, 64);
     }
-    const int es = __shfl(sel_e, slot, 64);
     if (lane == 0) e_lds = es;
   } else if (wv == 1) {
     rot_quant_row_wave<8>(x, H, q_lds, &sx_lds, lane);
@@ -1847,6 +1941,13 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm1(
   for (int i = threadIdx.x; i < 16 * G; i += WAVES * 64) {
     const int cc = i / G, gg = i - cc * G;
     s_lds[cc][gg] = bf16_bits_to_f32(sW[((int64_t)e * Nw + tile * 16 + cc) * G + gg]);
+  }
+  if (few && tile == 0 && slot == k - 1 && wv == 0) {
+    const float sel_w = route_slot_weight(my_l, mx, k);
+    if (lane < k) {
+      topk_ids[lane] = sel_e;
+      topk_w[lane] = sel_w;
+    }
   }
   if (first && qx_rec) {
     for (int i = threadIdx.x; i < (H >> 4); i += WAVES * 64)

@@ -55,3 +55,20 @@ def ulp_diff_f32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     ai = np.ascontiguousarray(a, np.float32).view(np.int32).astype(np.int64)
     bi = np.ascontiguousarray(b, np.float32).view(np.int32).astype(np.int64)
     return np.abs(ai - bi)
+
+
+def tie_logits(pattern, E):
+    """One token's router logits with ties: at the top, everywhere, across
+    the 8th slot, or in pairs."""
+    lg = np.zeros((1, E), np.float32)
+    if pattern == "top3":      # three-way tie at the top, the rest tied below
+        lg[0, [E - 3, 9, 2]] = 1.0
+    elif pattern == "all":     # every logit equal: experts 0..k-1
+        lg[0, :] = 0.5
+    elif pattern == "boundary":  # ten tied logits straddle the k-th slot
+        lg[0, :] = np.linspace(-1.0, -2.0, E, dtype=np.float32)
+        lg[0, np.arange(3, E, max(1, E // 10))[:10]] = 0.25
+        lg[0, E - 1] = 3.0
+    else:                      # descending values in pairs of equal logits
+        lg[0, ::-1] = (np.arange(E) // 2).astype(np.float32)
+    return lg

@@ -14,7 +14,7 @@ import torch
 import moe_quant_token_amd as mq
 import synth
 from tests._util import (DEV, assert_bf16_close, bf16_dev, bf16_host, dev, host, say,
-                         ulp_diff_f32)
+                         tie_logits, ulp_diff_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -248,6 +248,20 @@ def test_routing_ties_lower_index():
     np.testing.assert_array_equal(ids[3, :2], [30, 31])
     np.testing.assert_allclose(host(w).sum(1), 1.0, atol=1e-6)
     assert not bf16_host(out).any()
+
+
+@pytest.mark.parametrize("E", [32, 256])
+@pytest.mark.parametrize("pattern", ["top3", "all", "boundary", "pairs"])
+def test_single_token_tied_logits(orc, E, pattern):
+    # T=1: each gemm1 workgroup finds its own slot's expert; with tied logits
+    # every slot must still follow the lower-index rule of the full selection
+    # (checked through each slot's int32 sums against the oracle)
+    T, H, I, k = 1, 256, 128, 8
+    key = (49, E)
+    W = _weights(orc, key, E, H, I)
+    x = synth.activations(key, T, H, 0, 1.0)
+    _check_full(orc, x, tie_logits(pattern, E), k, W, T, f"moe T=1 ties {pattern} E={E}",
+                packed=True)
 
 
 @pytest.fixture(scope="module")

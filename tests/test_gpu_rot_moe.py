@@ -24,7 +24,7 @@ import torch
 
 import moe_quant_token_amd as mq
 import synth
-from tests._util import (assert_bf16_close, bf16_dev, bf16_host, dev, host, say,
+from tests._util import (tie_logits, assert_bf16_close, bf16_dev, bf16_host, dev, host, say,
                          ulp_diff_f32)
 
 pytestmark = pytest.mark.gpu
@@ -189,6 +189,17 @@ def test_rot_moe_small(orc, T, k):
         x[2] = 0
     logits = synth.router_logits((94, T), T, E)
     _check_rot(orc, x, logits, k, W, Wd, f"rot moe small T={T} k={k}")
+
+
+@pytest.mark.parametrize("pattern", ["top3", "all", "boundary", "pairs"])
+def test_rot_moe_single_token_tied_logits(orc, pattern):
+    # one token: each gemm1 workgroup finds its own slot's expert; tied logits
+    # must give every slot the expert of the full lower-index selection
+    E, H, I, k = 256, 256, 128, 8
+    W = _rot_weights(orc, (93, 1), E, H, I)
+    Wd = _dev_rot_weights(W)
+    x = synth.activations((93, 1), 1, H, 0, 1.0)
+    _check_rot(orc, x, tie_logits(pattern, E), k, W, Wd, f"rot moe T=1 ties {pattern}")
 
 
 @pytest.mark.parametrize("T", [3, 100])
