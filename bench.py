@@ -438,11 +438,12 @@ def main():
         clocks["decode_step_graph"] = probe
 
     # ------------------------------------------------------------ what HBM delivers
-    # torch's own copy and sum kernels over 1 GiB buffers: the streaming rates
-    # of this box at this moment, beside which the roofline fractions (against
-    # the published 8 TB/s) can be read
+    # torch's own copy and sum kernels over 1 GiB buffers, and the library's
+    # streaming-read kernel over each decode shape's weight bytes: the rates
+    # this box delivers at this moment, beside which the roofline fractions
+    # (against the published 8 TB/s) can be read
     if not args.probe_copy:
-        out["hbm_stream"] = stream_ceiling(torch, timer)
+        out["hbm_stream"] = stream_ceiling(torch, timer, mq, shapes)
 
     # ------------------------------------------------------------ extra cases
     cases = {}
@@ -492,9 +493,13 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def stream_ceiling(torch, timer):
-    """Streaming rates of torch's copy (1 GiB read + 1 GiB written) and sum
-    (1 GiB read) kernels, median of 10 launches each, in GB/s of bytes moved."""
+def stream_ceiling(torch, timer, mq, shapes):
+    """Streaming rates: torch's copy (1 GiB read + 1 GiB written) and sum (1 GiB
+    read) kernels, median of 10 launches each, in GB/s of bytes moved; and the
+    library's streaming-read kernel (w8a8_stream_read) reading exactly the
+    weight bytes of each decode shape with the decode GEMM's access pattern
+    (one workgroup per 16 weight rows, chunk = 16 K bytes), rotating over
+    copies as the step does, median of 48 launches, plus one 713 MB read."""
     n = 1 << 28  # fp32 elements: 1 GiB
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
@@ -507,6 +512,30 @@ def stream_ceiling(torch, timer):
            "read_gbs": round(4 * n / (pct(sm, 50) * 1e-3) / 1e9, 1),
            "source": "torch copy_ and sum over 1 GiB fp32, median of 10"}
     del a, b, r
+    # the streaming-read kernel over one buffer sliced like the weight copies
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    big = max(sh["N"] * sh["K"] for sh in shapes) * 8
+    buf = torch.zeros(big, dtype=torch.int8, device="cuda")
+    probe = {}
+    for sh in shapes:
+        nbytes, chunk = sh["N"] * sh["K"], 16 * sh["K"]
+        nslice = big // nbytes
+        views = [buf[i * nbytes:(i + 1) * nbytes] for i in range(nslice)]
+        for i in range(nslice):
+            mq.stream_read(views[i], chunk, sink)
+        _, each = timer.run(lambda i: mq.stream_read(views[i % nslice], chunk, sink), 48,
+                            groups=8)
+        med = pct(each, 50)
+        probe[sh["name"]] = {"bytes": nbytes, "chunk": chunk, "median_us": round(med * 1e3, 2),
+                             "gbs": round(nbytes / (med * 1e-3) / 1e9, 1)}
+    chunk = 80 * 1024
+    whole = big // chunk * chunk
+    _, each = timer.run(lambda i: mq.stream_read(buf[:whole], chunk, sink), 10, groups=10)
+    probe["whole_buffer"] = {"bytes": whole, "chunk": chunk,
+                             "median_us": round(pct(each, 50) * 1e3, 2),
+                             "gbs": round(whole / (pct(each, 50) * 1e-3) / 1e9, 1)}
+    res["stream_read"] = probe
+    del buf, sink
     torch.cuda.empty_cache()
     return res
 

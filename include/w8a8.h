@@ -222,6 +222,18 @@ int kv_quant_i8(const uint16_t *x, int64_t T, int64_t Hk, int64_t D, int64_t ldx
                 uint16_t *s_cache, int64_t lds, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Measurement helper, not part of the method: reads `bytes` of `buf` once, */
+/* one 512-thread workgroup per `chunk` contiguous bytes, each wave keeping */
+/* ten 1 KiB loads in flight (the access pattern of the decode GEMM).  The  */
+/* time of such a read is the streaming ceiling the GEMM's HBM fraction is  */
+/* compared with.  sink: int32 [1], written only for one bit pattern of the */
+/* data (never for a buffer of zeros).  Requires chunk a positive multiple  */
+/* of 1024, bytes a positive multiple of chunk with bytes / chunk < 2^31;   */
+/* buf 16-byte aligned.  No workspace; buf is not modified.                  */
+/* ------------------------------------------------------------------------ */
+int w8a8_stream_read(const void *buf, int64_t bytes, int64_t chunk, int32_t *sink, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Routed int8 MoE layer.                                                    */
 /* [ATOM] Changes, fused_moe_triton.py bullet: routing -> per-token int8     */
 /* quant -> gemm1 with fused gated SiLU over interleaved w13 -> per-token    */

@@ -55,6 +55,7 @@ _SIGS = {
     "w8a8_status_string": ([_i32], ctypes.c_char_p),
     "w8a8_last_hip_error": ([], _i32),
     "w8a8_version": ([], _i32),
+    "w8a8_stream_read": ([_vp, _i64, _i64, _vp, _vp], _i32),
     "quant_per_token_i8": ([_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _vp], _i32),
     "gemm_w8a8_workspace_bytes": ([_i64, _i64, _i64], _sz),
     "gemm_w8a8": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp],
@@ -339,6 +340,17 @@ def kv_quant_i8(x, q_cache: torch.Tensor | None = None, s_cache: torch.Tensor | 
                              _ptr(q_cache), q_cache.stride(0), _ptr(s_cache), s_cache.stride(0),
                              _stream(x.device)))
     return q_cache, s_cache
+
+
+def stream_read(buf: torch.Tensor, chunk: int, sink: torch.Tensor) -> None:
+    """Measurement helper: read ``buf`` (any dtype, contiguous) once, one
+    workgroup per ``chunk`` bytes (see w8a8_stream_read); ``sink`` int32 [1]."""
+    if not buf.is_contiguous():
+        raise ValueError("buf: must be contiguous")
+    _req(sink, torch.int32, "sink")
+    _check("w8a8_stream_read",
+           lib().w8a8_stream_read(_ptr(buf), buf.numel() * buf.element_size(), chunk,
+                                  _ptr(sink), _stream(buf.device)))
 
 
 def moe_w8a8_workspace_bytes(T: int, H: int, E: int, I: int, topk: int) -> int:

@@ -389,6 +389,20 @@ int kv_quant_i8(const uint16_t* x, int64_t T, int64_t Hk, int64_t D, int64_t ldx
   return e == hipSuccess ? W8A8_OK : hip_fail(e);
 }
 
+int w8a8_stream_read(const void* buf, int64_t bytes, int64_t chunk, int32_t* sink,
+                     void* stream) {
+  if (bytes <= 0 || chunk <= 0 || chunk % 1024 != 0 || bytes % chunk != 0 ||
+      bytes / chunk > INT32_MAX)
+    return W8A8_INVALID_ARG;
+  if (!buf || !sink) return W8A8_INVALID_ARG;
+  if (!al16(buf) || !al4(sink)) return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  hipError_t e = launch_stream_read(static_cast<const int8_t*>(buf), bytes, chunk, sink,
+                                    as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
 size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int topk) {
   if (T <= 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0) return 0;
   return moe_workspace_bytes(T, H, E, I, topk);

@@ -10,9 +10,10 @@
 // (one 16x16x64 MFMA column tile).  Its waves take the tile's 64-byte k
 // steps round-robin (wave w of W: steps w, w+W, ...), so at any moment the
 // workgroup streams one contiguous stretch of the tile; every wave keeps U
-// 1 KiB weight loads in flight.  The waves' int32 partial sums are added
-// exactly through LDS and the fp32 epilogue runs in registers: no workspace
-// and no cross-workgroup traffic.
+// 1 KiB weight loads in flight, non-temporal (the weights are read once:
+// measured on MI355X 7% faster than plain loads over the decode step).  The
+// waves' int32 partial sums are added exactly through LDS and the fp32
+// epilogue runs in registers: no workspace and no cross-workgroup traffic.
 //
 // Weight layouts: row-major [N, K], or the packed tile layout (see pack.hip)
 // in which each 16-row x 64-byte MFMA operand tile is one contiguous 1 KiB
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_skinny(
     for (int u = 0; u < U; u++) {
       const int c = c0 + u * WAVES;
       const bool in = c < nchunk;
-      b[u] = in ? *reinterpret_cast<const v4i*>(wp + c * wstep) : v4i{0, 0, 0, 0};
+      b[u] = in ? ld_stream(wp + c * wstep) : v4i{0, 0, 0, 0};
       a[u] = (in && a_ok) ? *reinterpret_cast<const v4i*>(ap + (int64_t)c * 64)
                           : v4i{0, 0, 0, 0};
     }
@@ -179,8 +180,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_linear_skinny_fused(
 #pragma unroll
   for (int u = 0; u < U; u++) {
     const int c = wv + u * WAVES;
-    b0[u] = c < nchunk ? *reinterpret_cast<const v4i*>(wp + (int64_t)c * 1024)
-                       : v4i{0, 0, 0, 0};
+    b0[u] = c < nchunk ? ld_stream(wp + (int64_t)c * 1024) : v4i{0, 0, 0, 0};
   }
   const int64_t n = tile * 16 + j;
   const float swn = wv == 0 ? sw[n] : 0.0f;
@@ -264,8 +264,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_linear_skinny_fused(
       const int c = c0 + u * WAVES;
       const bool in = c < nchunk;
       b[u] = first ? b0[u]
-                   : (in ? *reinterpret_cast<const v4i*>(wp + (int64_t)c * 1024)
-                         : v4i{0, 0, 0, 0});
+                   : (in ? ld_stream(wp + (int64_t)c * 1024) : v4i{0, 0, 0, 0});
       a[u] = (in && a_ok) ? *reinterpret_cast<const v4i*>(ap + c * 64) : v4i{0, 0, 0, 0};
     }
 #pragma unroll

@@ -161,4 +161,8 @@ hipError_t launch_gemm_g256(const int8_t* qa, const float* sa, int64_t M, int64_
                             const int8_t* qw, const uint8_t* su8, const uint16_t* s2, int64_t N,
                             bool packed, uint16_t* y, int64_t ldy, void* ws, hipStream_t stream);
 
+// Measurement only: reads bytes / chunk contiguous chunks of buf once.
+hipError_t launch_stream_read(const int8_t* buf, int64_t bytes, int64_t chunk, int32_t* sink,
+                              hipStream_t stream);
+
 }  // namespace w8a8

@@ -104,3 +104,14 @@ def test_hadamard_validation(L):
     assert L.fwht128_weight_prep_g256(A, 4, 384, A, A, A, None) == SHAPE
     assert L.gemm_w8a8_g256(A, A, 2, 384, A, A, A, 64, A, 64, None, 0, None) == SHAPE
     assert L.gemm_w8a8_g256(A, A, 2, 512, A, A, A, 40, A, 40, None, 0, None) == SHAPE
+
+
+def test_stream_read_validation(L):
+    f = L.w8a8_stream_read
+    assert f(A, 1 << 20, 1000, A, None) == INVALID        # chunk not a multiple of 1 KiB
+    assert f(A, (1 << 20) + 1024, 1 << 12, A, None) == INVALID  # bytes not whole chunks
+    assert f(A, 0, 1024, A, None) == INVALID
+    assert f(None, 1 << 20, 1024, A, None) == INVALID
+    assert f(A, 1 << 20, 1024, None, None) == INVALID
+    assert f(A + 8, 1 << 20, 1024, A, None) == MISALIGNED
+

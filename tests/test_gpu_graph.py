@@ -277,6 +277,25 @@ def test_kv_quant_graph(orc):
     _graph_check(call, [x], [(bf16_dev(a),) for a in sets_h], [q, s], check)
 
 
+def test_stream_read_probe():
+    # the measurement helper reads its 481 KiB buffer and leaves the sink
+    # alone for zeros (eager and graph-replayed): 37, 13 and 1 chunks, the
+    # last with 481 pieces (several rounds of loads, the final one partial)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    buf = torch.zeros(37 * 13 * 1024, dtype=torch.int8, device="cuda")
+    for chunk in (13 * 1024, 37 * 1024, 481 * 1024):
+        mq.stream_read(buf, chunk, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mq.stream_read(buf, 13 * 1024, sink)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+
+
 def test_router_and_g128_prep_graph(orc):
     T, H, E = 20, 512, 32
     wg_h = synth.to_bf16_bits(synth.weights((76, 0), E, H))
