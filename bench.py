@@ -764,7 +764,9 @@ def rot_moe_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes):
     experts, top-8, hidden 2048, expert and shared intermediate 512): the bf16
     router gate, the shared expert (g256 gate/up, g128 down) and the routed
     experts on the rotated grid (g128 bf16 scales) with the shared term in the
-    combine.  Each piece is timed alone and the three in sequence ("layer").
+    combine.  Each piece is timed alone, the three in sequence ("layer"), and the
+    router followed by the one-call routed layer with its shared expert
+    ("layer_one_call": one token runs it in two launches).
     HBM-graded on the weights the call touches plus activations in and out."""
     cfg = synth.moe(1)
     E, H, I, k = cfg["E"], cfg["H"], cfg["I"], cfg["k"]
@@ -804,6 +806,8 @@ def rot_moe_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes):
                          device=dev)
         wss = torch.empty(mq.shared_expert_w8a8_rot_workspace_bytes(T, H, Is),
                           dtype=torch.uint8, device=dev)
+        wsl = torch.empty(mq.lib().moe_w8a8_rot_shared_workspace_bytes(T, H, E, I, k, Is),
+                          dtype=torch.uint8, device=dev)
         sets = []
         ih = hashlib.sha256()
         for r in range(nsets):
@@ -838,6 +842,14 @@ def rot_moe_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes):
             shared(i)
             routed(i)
 
+        def layer_one_call(i):  # router, then the routed layer with its shared expert
+            router(i)
+            st = sets[i % nsets]
+            a13, b13, a2, b2 = copies[i % len(copies)]
+            mq.moe_w8a8_rot_shared_forward(st["x"], st["logits"], a13, b13, a2, b2, k,
+                                           shared_w=shared_w, topk_ids=st["ids"],
+                                           topk_w=st["wt"], out=st["out"], ws=wsl)
+
         for r in range(nsets):  # every set through the layer once (untimed)
             layer(r)
         torch.cuda.synchronize()
@@ -846,14 +858,16 @@ def rot_moe_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes):
         parts = {"router": (router, router_bytes + T * H * 2 + T * E * 4),
                  "shared": (shared, shared_bytes + T * H * 2 + T * H * 4),
                  "routed": (routed, touched * expert_bytes + io + T * H * 4 + T * E * 4),
-                 "layer": (layer, touched * expert_bytes + shared_bytes + router_bytes + io)}
+                 "layer": (layer, touched * expert_bytes + shared_bytes + router_bytes + io),
+                 "layer_one_call": (layer_one_call,
+                                    touched * expert_bytes + shared_bytes + router_bytes + io)}
         for name, (fn, nbytes) in parts.items():
             _, each = timer.run(fn, it, groups=min(it, 8))
             t = pct(each, 50)
             r = {**timer.stats_us(each), "alg_bytes": int(nbytes),
                  "gbs": round(nbytes / (t * 1e-3) / 1e9, 1),
                  "frac_hbm": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-            if name in ("routed", "layer"):
+            if name in ("routed", "layer", "layer_one_call"):
                 r["tokens_per_s"] = round(T / (t * 1e-3), 1)
                 r["experts_touched"] = round(touched, 1)
             res[f"rot_moe_T{T}_{name}"] = r

@@ -442,6 +442,33 @@ int shared_expert_w8a8_rot_packed(const uint16_t *x, int64_t T, int64_t H, int64
                                   const uint16_t *sd, float *y, void *ws, size_t ws_bytes,
                                   const shared_expert_debug *dbg, void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* The Hadamard-domain MoE layer with its shared expert in one call.  [IQ8R] */
+/* Experts row: routed and shared experts of one layer; [ATOM] Changes,      */
+/* fused_moe_triton.py bullet (the routed order).  The result is exactly     */
+/*   moe_w8a8_rot_forward_packed(..., shared = y) with                        */
+/*   y = shared_expert_w8a8_rot_packed(x, Is, wgu_packed, su8, sgu,          */
+/*                                     wd_packed, sd),                        */
+/* computed together: for one token (k <= 15, I <= 1024, Is <= 1024,         */
+/* k*I/128 + Is/128 <= 64) in two launches, the shared gate/up tiles beside */
+/* the routed gemm1 and the shared down projection as one more pair of      */
+/* gemm2; otherwise the shared expert first, then the routed layer.          */
+/* Arguments as in those two calls (sgu is the shared gate/up's bf16 row     */
+/* scale, there named s2).  Workspace:                                       */
+/* moe_w8a8_rot_shared_workspace_bytes(T, H, E, I, topk, Is).  dbg as in     */
+/* moe_w8a8_rot_forward_packed (the routed pairs' intermediates).  Requires  */
+/* the conditions of both calls.                                             */
+/* ------------------------------------------------------------------------ */
+size_t moe_w8a8_rot_shared_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I,
+                                           int topk, int64_t Is);
+int moe_w8a8_rot_shared_forward_packed(
+    const uint16_t *x, const float *logits, int64_t T, int64_t H, int64_t E, int64_t I,
+    int topk, const int8_t *w13_packed, const uint16_t *s13, const int8_t *w2_packed,
+    const uint16_t *s2, int64_t Is, const int8_t *wgu_packed, const uint8_t *su8,
+    const uint16_t *sgu, const int8_t *wd_packed, const uint16_t *sd, int32_t *topk_ids,
+    float *topk_w, uint16_t *out, void *ws, size_t ws_bytes, const moe_w8a8_debug *dbg,
+    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

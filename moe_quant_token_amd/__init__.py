@@ -99,6 +99,10 @@ _SIGS = {
                                      _vp, _vp, _vp, _vp, _vp, _sz, ctypes.POINTER(MoeDebug),
                                      _vp], _i32),
     "shared_expert_w8a8_rot_workspace_bytes": ([_i64, _i64, _i64], _sz),
+    "moe_w8a8_rot_shared_workspace_bytes": ([_i64, _i64, _i64, _i64, _i32, _i64], _sz),
+    "moe_w8a8_rot_shared_forward_packed": ([_vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp,
+                                            _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _vp, _vp, _sz, ctypes.POINTER(MoeDebug), _vp], _i32),
     "shared_expert_w8a8_rot_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _sz, ctypes.POINTER(SharedDebug), _vp], _i32),
 }
@@ -545,6 +549,58 @@ def moe_w8a8_rot_forward(x, logits, w13_packed, s13, w2_packed, s2, topk: int, s
                                              _ptr(s2), _ptr(shared), _ptr(topk_ids),
                                              _ptr(topk_w), _ptr(out), _ptr(ws), wsb, dbg_p,
                                              _stream(dev)))
+    if debug:
+        return out, topk_ids, topk_w, dbg_t
+    return out, topk_ids, topk_w
+
+
+def moe_w8a8_rot_shared_forward(x, logits, w13_packed, s13, w2_packed, s2, topk: int,
+                                shared_w, topk_ids=None, topk_w=None, out=None, ws=None,
+                                debug: bool = False):
+    """The Hadamard-domain MoE layer with its shared expert in one call.
+
+    ``shared_w`` = (wgu_packed, su8, sgu, wd_packed, sd) as for
+    ``shared_expert_w8a8_rot``; the rest as ``moe_w8a8_rot_forward``.  The
+    result equals ``moe_w8a8_rot_forward(..., shared=shared_expert_w8a8_rot(x,
+    *shared_w))``; one token runs in two launches with the shared expert
+    inside them."""
+    _req(x, torch.bfloat16, "x")
+    _req(s13, torch.bfloat16, "s13")
+    _req(s2, torch.bfloat16, "s2")
+    if not x.is_contiguous():
+        raise ValueError("x: expected a contiguous [T, H] tensor")
+    wgu_packed, su8, sgu, wd_packed, sd = shared_w
+    _req(su8, torch.uint8, "su8")
+    _req(sgu, torch.bfloat16, "sgu")
+    _req(sd, torch.bfloat16, "sd")
+    T, H = x.shape
+    E, I2, _ = w13_packed.shape
+    I = I2 // 2
+    Is = su8.shape[0] // 2
+    dev = x.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if out is None else out
+    ws, wsb = _workspace(lib().moe_w8a8_rot_shared_workspace_bytes(T, H, E, I, topk, Is), dev,
+                         ws)
+    dbg_t = None
+    dbg_p = None
+    if debug:
+        R = T * topk
+        dbg_t = dict(qx=torch.empty((T, H), dtype=torch.int8, device=dev),
+                     sx=torch.empty((T,), dtype=torch.float32, device=dev),
+                     act=torch.empty((R, I), dtype=torch.float32, device=dev),
+                     qa=torch.empty((R, I), dtype=torch.int8, device=dev),
+                     sa2=torch.empty((R,), dtype=torch.float32, device=dev))
+        dbg_p = ctypes.pointer(MoeDebug(**{k: v.data_ptr() for k, v in dbg_t.items()}))
+    _check("moe_w8a8_rot_shared_forward_packed",
+           lib().moe_w8a8_rot_shared_forward_packed(
+               _ptr(x), _ptr(logits), T, H, E, I, topk, _ptr(w13_packed), _ptr(s13),
+               _ptr(w2_packed), _ptr(s2), Is, _ptr(wgu_packed), _ptr(su8), _ptr(sgu),
+               _ptr(wd_packed), _ptr(sd), _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws),
+               wsb, dbg_p, _stream(dev)))
     if debug:
         return out, topk_ids, topk_w, dbg_t
     return out, topk_ids, topk_w

@@ -576,6 +576,64 @@ int moe_w8a8_rot_forward_packed(const uint16_t* x, const float* logits, int64_t 
   return e == hipSuccess ? W8A8_OK : hip_fail(e);
 }
 
+size_t moe_w8a8_rot_shared_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I,
+                                           int topk, int64_t Is) {
+  if (T <= 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0 || Is <= 0) return 0;
+  return moe_rot_shared_workspace_bytes(T, H, E, I, topk, Is);
+}
+
+int moe_w8a8_rot_shared_forward_packed(
+    const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t E, int64_t I,
+    int topk, const int8_t* w13_packed, const uint16_t* s13, const int8_t* w2_packed,
+    const uint16_t* s2, int64_t Is, const int8_t* wgu_packed, const uint8_t* su8,
+    const uint16_t* sgu, const int8_t* wd_packed, const uint16_t* sd, int32_t* topk_ids,
+    float* topk_w, uint16_t* out, void* ws, size_t ws_bytes, const moe_w8a8_debug* dbg,
+    void* stream) {
+  if (T < 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0 || Is <= 0) return W8A8_INVALID_ARG;
+  if (H % 256 != 0 || I % 128 != 0 || Is % 128 != 0 || H > 4096 || I > 2048 || Is > 2048 ||
+      topk > 16 || topk > E || E > 1024 || T * topk > ((int64_t)1 << 24))
+    return W8A8_UNSUPPORTED_SHAPE;
+  if (T == 0) return W8A8_OK;
+  if (!x || !w13_packed || !s13 || !w2_packed || !s2 || !wgu_packed || !su8 || !sgu ||
+      !wd_packed || !sd || !topk_ids || !topk_w || !out)
+    return W8A8_INVALID_ARG;
+  if (!al16(x) || !al16(w13_packed) || !al16(w2_packed) || !al4(s13) || !al4(s2) ||
+      !al16(wgu_packed) || !al16(wd_packed) || !al4(sd) || !al4(topk_ids) || !al4(topk_w) ||
+      !al16(out) || (logits && !al4(logits)))
+    return W8A8_MISALIGNED;
+  if (ws_bytes < moe_w8a8_rot_shared_workspace_bytes(T, H, E, I, topk, Is))
+    return W8A8_WORKSPACE_TOO_SMALL;
+  if (!ws) return W8A8_INVALID_ARG;
+  if (!al16(ws)) return W8A8_MISALIGNED;
+  int r = check_device();
+  if (r != W8A8_OK) return r;
+  MoeArgs a{};
+  a.x = x;
+  a.logits = logits;
+  a.T = (int)T;
+  a.H = (int)H;
+  a.E = (int)E;
+  a.I = (int)I;
+  a.k = topk;
+  a.w13 = w13_packed;
+  a.w2 = w2_packed;
+  a.topk_ids = topk_ids;
+  a.topk_w = topk_w;
+  a.out = out;
+  a.ws = ws;
+  a.packed = true;
+  if (dbg) {
+    a.dbg_qx = dbg->qx;
+    a.dbg_sx = dbg->sx;
+    a.dbg_act = dbg->act;
+    a.dbg_qa = dbg->qa;
+    a.dbg_sa2 = dbg->sa2;
+  }
+  RotSharedW sh{Is, wgu_packed, su8, sgu, wd_packed, sd};
+  hipError_t e = launch_moe_rot_shared_forward(a, s13, s2, sh, as_stream(stream));
+  return e == hipSuccess ? W8A8_OK : hip_fail(e);
+}
+
 size_t shared_expert_w8a8_rot_workspace_bytes(int64_t T, int64_t H, int64_t Is) {
   if (T <= 0 || H <= 0 || Is <= 0) return 0;
   return shared_expert_workspace_bytes(T, H, Is);

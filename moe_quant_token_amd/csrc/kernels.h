@@ -118,6 +118,23 @@ struct SharedArgs {
 size_t shared_expert_workspace_bytes(int64_t T, int64_t H, int64_t Is);
 hipError_t launch_shared_expert(const SharedArgs& a, hipStream_t stream);
 
+// The Hadamard-domain routed layer with its shared expert in one call: one
+// token in two launches (the shared expert inside them), else the shared
+// expert, then the routed layer with its output as the shared term.
+struct RotSharedW {
+  int64_t Is;
+  const int8_t* wgu;   // packed [2Is, H] (g256 codes)
+  const uint8_t* su8;  // [2Is, H/256]
+  const uint16_t* sgu;  // bf16 [2Is]
+  const int8_t* wd;    // packed [H, Is] (g128 codes)
+  const uint16_t* sd;  // bf16 [H, Is/128]
+};
+size_t moe_rot_shared_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int k,
+                                      int64_t Is);
+hipError_t launch_moe_rot_shared_forward(const MoeArgs& a, const uint16_t* s13,
+                                         const uint16_t* s2, const RotSharedW& sh,
+                                         hipStream_t stream);
+
 // Dense MLP block.  Workspace layout is owned by mlp.hip.
 struct MlpArgs {
   const uint16_t* x;

@@ -1878,11 +1878,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
 // k activation rows into LDS, each (pair, group) unit runs the two MFMA
 // steps of that pair's expert, the fold gives y2 for every pair, and the
 // epilogue combines them in slot order (plus the shared term) into bf16 out.
-__global__ __launch_bounds__(512) void k_rot_t1_gemm1(
+// SH: with the shared expert's gate/up tiles as workgroup row k; the
+// register budget then allows six waves a SIMD (three workgroups a CU: the
+// shared tiles come on top of the routed ones)
+template <bool SH>
+__global__ __launch_bounds__(512, SH ? 6 : 1) void k_rot_t1_gemm1(
     const uint16_t* __restrict__ x, const float* __restrict__ logits, int H, int E, int k,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, const int8_t* __restrict__ W,
     const uint16_t* __restrict__ sW, int Nw, int8_t* __restrict__ qx_rec,
-    float* __restrict__ sx_rec, float* __restrict__ act, int I) {
+    float* __restrict__ sx_rec, float* __restrict__ act, int I,
+    const int8_t* __restrict__ Wsh, const uint8_t* __restrict__ su8sh,
+    const uint16_t* __restrict__ s2sh, int Nsh, float* __restrict__ act_sh) {
   constexpr int WAVES = 8, MAXG = 32, GW = MAXG / WAVES;
   __shared__ v4i red[MAXG][64];
   __shared__ float s_lds[16][MAXG];
@@ -1897,13 +1903,17 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm1(
   const int nk = H >> 6;
   const int G = H >> 7;
   const bool first = tile == 0 && slot == 0;
+  // workgroup row k (with Wsh): the shared expert's gate/up (g256), one
+  // 16-row tile a workgroup, beside the routed pairs' tiles
+  const bool sh = SH && slot == k;
+  if (tile >= (sh ? Nsh : Nw) >> 4) return;  // the wider of the two sets the grid
   // up to 256 experts each workgroup finds its slot's expert alone; workgroup
   // (0, k - 1), which ran all k rounds, writes the selection
   const bool few = logits && E <= 256;
   int sel_e = 0;
   float my_l = 0.0f;
   double mx = 0.0;
-  if (wv == 0) {
+  if (wv == 0 && !sh) {
     float sel_w = 0.0f;
     int es;
     if (few) {
@@ -1928,8 +1938,9 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm1(
     rot_quant_row_wave<8>(x, H, q_lds, &sx_lds, lane);
   }
   __syncthreads();
-  const int e = __builtin_amdgcn_readfirstlane(e_lds);
-  const int8_t* wbase = W + ((int64_t)e * (Nw >> 4) + tile) * nk * 1024 + lane * 16;
+  const int e = sh ? 0 : __builtin_amdgcn_readfirstlane(e_lds);
+  const int8_t* wbase = sh ? Wsh + (int64_t)tile * nk * 1024 + lane * 16
+                           : W + ((int64_t)e * (Nw >> 4) + tile) * nk * 1024 + lane * 16;
   v4i bw[GW][2];
 #pragma unroll
   for (int i = 0; i < GW; i++) {
@@ -1938,9 +1949,19 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm1(
     for (int h = 0; h < 2; h++)
       bw[i][h] = gg < G ? ld_stream(wbase + (int64_t)(2 * gg + h) * 1024) : v4i{0, 0, 0, 0};
   }
-  for (int i = threadIdx.x; i < 16 * G; i += WAVES * 64) {
-    const int cc = i / G, gg = i - cc * G;
-    s_lds[cc][gg] = bf16_bits_to_f32(sW[((int64_t)e * Nw + tile * 16 + cc) * G + gg]);
+  if (sh) {
+    // the tile's u8 scales per 256-group (exact as floats) and row scales
+    const int G2 = H >> 8;
+    for (int i = threadIdx.x; i < 16 * G2; i += WAVES * 64) {
+      const int cc = i / G2, gg = i - cc * G2;
+      s_lds[cc][gg] = (float)su8sh[(int64_t)(tile * 16 + cc) * G2 + gg];
+    }
+    if (threadIdx.x < 16) s_lds[threadIdx.x][MAXG - 1] = bf16_bits_to_f32(s2sh[tile * 16 + threadIdx.x]);
+  } else {
+    for (int i = threadIdx.x; i < 16 * G; i += WAVES * 64) {
+      const int cc = i / G, gg = i - cc * G;
+      s_lds[cc][gg] = bf16_bits_to_f32(sW[((int64_t)e * Nw + tile * 16 + cc) * G + gg]);
+    }
   }
   if (few && tile == 0 && slot == k - 1 && wv == 0) {
     const float sel_w = route_slot_weight(my_l, mx, k);
@@ -1974,21 +1995,39 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm1(
   if (wv != 0) return;
   // row 0 of column tile * 16 + j sits in element 0 of lane j (g == 0)
   double t = 0.0;
-  for (int gg = 0; gg < G; gg++) t = t + (double)red[gg][j][0] * (double)s_lds[j][gg];
-  t = t * (double)sx_lds;
+  if (sh) {
+    // g256: each 128-group's exact sum times its 256-group's u8, in int64
+    // (exact, so in any order), then * sx * s2 * 2^-7 in fp64
+    long long tot = 0;
+    for (int gg = 0; gg < G; gg++)
+      tot += (long long)red[gg][j][0] * (long long)s_lds[j][gg >> 1];
+    t = (double)tot * (double)sx_lds;
+    t = t * (double)s_lds[j][MAXG - 1];
+  } else {
+    for (int gg = 0; gg < G; gg++) t = t + (double)red[gg][j][0] * (double)s_lds[j][gg];
+    t = t * (double)sx_lds;
+  }
   t = t * 0.0078125;
   const float a = rot_silu_pair((float)t);
-  if (g == 0 && (j & 1) == 0) act[(int64_t)slot * I + ((tile * 16 + j) >> 1)] = a;
+  if (g == 0 && (j & 1) == 0) {
+    if (sh)
+      act_sh[(tile * 16 + j) >> 1] = a;
+    else
+      act[(int64_t)slot * I + ((tile * 16 + j) >> 1)] = a;
+  }
 }
 
 // k * (I / 128) <= kRotT1MaxUnits (pair, group) units; I <= 1024
 constexpr int kRotT1MaxUnits = 64;
 
+template <bool SH>
 __global__ __launch_bounds__(512) void k_rot_t1_gemm2(
     const float* __restrict__ act, int I, int k, const int32_t* __restrict__ topk_ids,
     const float* __restrict__ topk_w, const int8_t* __restrict__ W,
     const uint16_t* __restrict__ sW, int H, const float* __restrict__ shared,
-    uint16_t* __restrict__ out, int8_t* __restrict__ qa_rec, float* __restrict__ sa_rec) {
+    uint16_t* __restrict__ out, int8_t* __restrict__ qa_rec, float* __restrict__ sa_rec,
+    const float* __restrict__ act_sh, int Is, const int8_t* __restrict__ Wdsh,
+    const uint16_t* __restrict__ sdsh) {
   constexpr int WAVES = 8, UW = kRotT1MaxUnits / WAVES;
   __shared__ v4i red[kRotT1MaxUnits][64];
   __shared__ __attribute__((aligned(16))) int8_t a_lds[16 * 1024];
@@ -2002,7 +2041,13 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm2(
   const int tile = blockIdx.x;
   const int nk = I >> 6;
   const int G = I >> 7;
-  const int U = k * G;
+  // with act_sh: the shared expert's down projection as pair k (its own
+  // weights, scales and row length), its y added after the slot-order sum
+  constexpr bool has_sh = SH;
+  const int Gs = has_sh ? Is >> 7 : 0;
+  const int U0 = k * G;     // the routed pairs' (pair, group) units
+  const int U = U0 + Gs;    // then the shared pair's
+  const int rows = k + (has_sh ? 1 : 0);
   if (threadIdx.x < k) {
     e_lds[threadIdx.x] = topk_ids[threadIdx.x];
     w_lds[threadIdx.x] = topk_w[threadIdx.x];
@@ -2013,37 +2058,50 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm2(
 #pragma unroll
   for (int i = 0; i < UW; i++) {
     const int u = wv + i * WAVES;
-    const int pr = u / G, gg = u - (u / G) * G;
-    const int8_t* wb = W + ((int64_t)e_lds[u < U ? pr : 0] * (H >> 4) + tile) * nk * 1024 +
-                       lane * 16 + (int64_t)(2 * gg) * 1024;
+    const bool routed = u < U0;
+    const int pr = routed ? u / G : 0;
+    const int gg = routed ? u - pr * G : u - U0;
+    const int8_t* wb =
+        routed ? W + ((int64_t)e_lds[pr] * (H >> 4) + tile) * nk * 1024 + lane * 16 +
+                     (int64_t)(2 * gg) * 1024
+               : Wdsh + (int64_t)tile * (Is >> 6) * 1024 + lane * 16 + (int64_t)(2 * gg) * 1024;
 #pragma unroll
     for (int h = 0; h < 2; h++)
       bw[i][h] = u < U ? ld_stream(wb + h * 1024) : v4i{0, 0, 0, 0};
   }
   for (int i = threadIdx.x; i < U * 16; i += WAVES * 64) {
     const int u = i >> 4, c = i & 15;
-    const int pr = u / G, gg = u - pr * G;
-    s_lds[u][c] = bf16_bits_to_f32(sW[((int64_t)e_lds[pr] * H + tile * 16 + c) * G + gg]);
+    if (u < U0) {
+      const int pr = u / G, gg = u - pr * G;
+      s_lds[u][c] = bf16_bits_to_f32(sW[((int64_t)e_lds[pr] * H + tile * 16 + c) * G + gg]);
+    } else {
+      s_lds[u][c] = bf16_bits_to_f32(sdsh[(int64_t)(tile * 16 + c) * Gs + (u - U0)]);
+    }
   }
-  // rotated requant of the k activation rows into LDS (packed operand rows)
-  for (int r = wv; r < k; r += WAVES) {
+  // rotated requant of the k activation rows (and the shared row, row k)
+  // into LDS (packed operand rows)
+  for (int r = wv; r < rows; r += WAVES) {
+    const bool rsh = r == k;
+    const int len = rsh ? Is : I;
+    const int gr = len >> 7;
     Block8 bb[2];
-    const float am = rot_row_wave<2>(act + (int64_t)r * I, I, bb, lane);
+    const float am = rot_row_wave<2>(rsh ? act_sh : act + (int64_t)r * I, len, bb, lane);
     const float sc = am / 127.0f;
 #pragma unroll
     for (int rd = 0; rd < 2; rd++) {
       const int blk = rd * 4 + g;
-      if (blk >= G) continue;
+      if (blk >= gr) continue;
       const uint2 wd = rot_codes8(bb[rd], am, sc);
       const int kk = blk * 128 + j * 8;
       *reinterpret_cast<uint2*>(a_lds + (kk >> 6) * 1024 + (r + 16 * ((kk & 63) >> 4)) * 16 +
                                 (kk & 15)) = wd;
-      if (tile == 0 && qa_rec) *reinterpret_cast<uint2*>(qa_rec + (int64_t)r * I + kk) = wd;
+      if (!rsh && tile == 0 && qa_rec)
+        *reinterpret_cast<uint2*>(qa_rec + (int64_t)r * I + kk) = wd;
     }
     if (lane == 0) {
       const float sv = am != 0.0f ? sc : 0.0f;
       sa_lds[r] = sv;
-      if (tile == 0 && sa_rec) sa_rec[r] = sv;
+      if (!rsh && tile == 0 && sa_rec) sa_rec[r] = sv;
     }
   }
   __syncthreads();
@@ -2051,7 +2109,7 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm2(
   for (int i = 0; i < UW; i++) {
     const int u = wv + i * WAVES;
     if (u < U) {
-      const int gg = u % G;
+      const int gg = u < U0 ? u % G : u - U0;
       v4i acc = {0, 0, 0, 0};
 #pragma unroll
       for (int h = 0; h < 2; h++)
@@ -2064,12 +2122,13 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm2(
   __syncthreads();
   // y2 of pair pr, column c: row pr of the pair's own units (lane 16 (pr / 4)
   // + c, element pr % 4), folded in group order
-  if (threadIdx.x < k * 16) {
+  if (threadIdx.x < rows * 16) {
     const int pr = threadIdx.x >> 4, c = threadIdx.x & 15;
     const int L = (pr >> 2) * 16 + c;
+    const int u0 = pr < k ? pr * G : U0, ng = pr < k ? G : Gs;
     double t = 0.0;
-    for (int gg = 0; gg < G; gg++)
-      t = t + (double)red[pr * G + gg][L][pr & 3] * (double)s_lds[pr * G + gg][c];
+    for (int gg = 0; gg < ng; gg++)
+      t = t + (double)red[u0 + gg][L][pr & 3] * (double)s_lds[u0 + gg][c];
     t = t * (double)sa_lds[pr];
     t = t * 0.0078125;
     y_lds[pr][c] = (float)t;
@@ -2083,6 +2142,7 @@ __global__ __launch_bounds__(512) void k_rot_t1_gemm2(
       acc = acc + term;
     }
     if (shared) acc = acc + shared[tile * 16 + c];
+    else if (has_sh) acc = acc + y_lds[k][c];
     out[tile * 16 + c] = (uint16_t)f32_to_bf16_bits(acc);
   }
 }
@@ -2403,6 +2463,53 @@ hipError_t launch_rot_sort(const MoeArgs& a, const MoeWs& ws, int64_t P, hipStre
   return hipGetLastError();
 }
 
+// One token in two launches.  With sh: the shared expert rides along (its
+// gate/up tiles as workgroup row k of gemm1, its down projection as pair k
+// of gemm2, its y added after the slot-order sum), act_sh holding its
+// activation row.
+static bool rot_t1_fits(const MoeArgs& a, int64_t Is) {
+  if (!(a.T == 1 && a.k <= 16 && a.I <= 1024 && a.k * (a.I / 128) <= kRotT1MaxUnits))
+    return false;
+  return Is == 0 || (a.k <= 15 && Is <= 1024 && a.k * (a.I / 128) + Is / 128 <= kRotT1MaxUnits);
+}
+
+static hipError_t launch_rot_t1(const MoeArgs& a, const MoeWs& ws, const uint16_t* s13,
+                                const uint16_t* s2, const float* shared, const RotSharedW* sh,
+                                float* act_sh, hipStream_t stream) {
+  const int I2 = 2 * a.I;
+  const int Nsh = sh ? (int)(2 * sh->Is) : 0;
+  hipError_t err;
+  // with the shared expert: three workgroups a CU (80 VGPRs), since its
+  // gate/up tiles come on top of the k * 2I / 16 routed ones (measured on
+  // MI355X at one token, 256 experts, top-8, H=2048, I=Is=512: the layer
+  // after the router 23.3 -> 18.8 us; the routed-only kernels keep the wider
+  // budget, 17.3 against 17.9 us with the narrower one)
+  if (sh)
+    hipLaunchKernelGGL(k_rot_t1_gemm1<true>, dim3((unsigned)(std::max(I2, Nsh) / 16), a.k + 1),
+                       dim3(512), 0, stream, a.x, a.logits, a.H, a.E, a.k, a.topk_ids, a.topk_w,
+                       a.w13, s13, I2, a.dbg_qx, a.dbg_sx, ws.act, a.I, sh->wgu, sh->su8,
+                       sh->sgu, Nsh, act_sh);
+  else
+    hipLaunchKernelGGL(k_rot_t1_gemm1<false>, dim3((unsigned)(I2 / 16), a.k), dim3(512), 0, stream,
+                       a.x, a.logits, a.H, a.E, a.k, a.topk_ids, a.topk_w, a.w13, s13, I2,
+                       a.dbg_qx, a.dbg_sx, ws.act, a.I, nullptr, nullptr, nullptr, 0, nullptr);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (sh)
+    hipLaunchKernelGGL(k_rot_t1_gemm2<true>, dim3(a.H / 16), dim3(512), 0, stream, ws.act, a.I,
+                       a.k, a.topk_ids, a.topk_w, a.w2, s2, a.H, shared, a.out, a.dbg_qa,
+                       a.dbg_sa2, act_sh, (int)sh->Is, sh->wd, sh->sd);
+  else
+    hipLaunchKernelGGL(k_rot_t1_gemm2<false>, dim3(a.H / 16), dim3(512), 0, stream, ws.act, a.I,
+                       a.k, a.topk_ids, a.topk_w, a.w2, s2, a.H, shared, a.out, a.dbg_qa,
+                       a.dbg_sa2, nullptr, 0, nullptr, nullptr);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int64_t P = (int64_t)a.T * a.k;
+  if (a.dbg_act && (err = hipMemcpyAsync(a.dbg_act, ws.act, (size_t)P * a.I * 4,
+                                         hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+    return err;
+  return hipSuccess;
+}
+
 hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const uint16_t* s2,
                                   const float* shared, hipStream_t stream) {
   const int64_t P = (int64_t)a.T * a.k;
@@ -2410,19 +2517,7 @@ hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const u
   const unsigned slots = (unsigned)std::min<int64_t>(a.E, P);
   const int I2 = 2 * a.I;
   hipError_t err;
-  if (a.T == 1 && a.k <= 16 && a.I <= 1024 && a.k * (a.I / 128) <= kRotT1MaxUnits) {
-    hipLaunchKernelGGL(k_rot_t1_gemm1, dim3(I2 / 16, a.k), dim3(512), 0, stream, a.x, a.logits,
-                       a.H, a.E, a.k, a.topk_ids, a.topk_w, a.w13, s13, I2, a.dbg_qx, a.dbg_sx,
-                       ws.act, a.I);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_rot_t1_gemm2, dim3(a.H / 16), dim3(512), 0, stream, ws.act, a.I, a.k,
-                       a.topk_ids, a.topk_w, a.w2, s2, a.H, shared, a.out, a.dbg_qa, a.dbg_sa2);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.dbg_act && (err = hipMemcpyAsync(a.dbg_act, ws.act, (size_t)P * a.I * 4,
-                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)
-      return err;
-    return hipSuccess;
-  }
+  if (rot_t1_fits(a, 0)) return launch_rot_t1(a, ws, s13, s2, shared, nullptr, nullptr, stream);
   hipLaunchKernelGGL(k_rot_route_quant, dim3((a.T + 3) / 4), dim3(512), 0, stream, a.x, a.logits,
                      a.T, a.H, a.E, a.k, a.topk_ids, a.topk_w, ws.qx, ws.sx);
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -2475,6 +2570,45 @@ hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const u
                                          hipMemcpyDeviceToDevice, stream)) != hipSuccess)
     return err;
   return hipSuccess;
+}
+
+// The routed layer with its shared expert.  Workspace: the routed layer's,
+// the shared expert's, the shared output [T, H] fp32 and one activation row.
+size_t moe_rot_shared_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t I, int k,
+                                      int64_t Is) {
+  return align_up(moe_workspace_bytes(T, H, E, I, k)) +
+         align_up(shared_expert_workspace_bytes(T, H, Is)) + align_up((size_t)(4 * T * H)) +
+         align_up((size_t)(4 * Is));
+}
+
+hipError_t launch_moe_rot_shared_forward(const MoeArgs& a, const uint16_t* s13,
+                                         const uint16_t* s2, const RotSharedW& sh,
+                                         hipStream_t stream) {
+  char* b = static_cast<char*>(a.ws);
+  const size_t o1 = align_up(moe_workspace_bytes(a.T, a.H, a.E, a.I, a.k));
+  const size_t o2 = o1 + align_up(shared_expert_workspace_bytes(a.T, a.H, sh.Is));
+  const size_t o3 = o2 + align_up((size_t)(4 * (int64_t)a.T * a.H));
+  float* y_sh = reinterpret_cast<float*>(b + o2);
+  float* act_sh = reinterpret_cast<float*>(b + o3);
+  if (rot_t1_fits(a, sh.Is)) {
+    const MoeWs ws = carve(a.ws, a.T, a.H, a.E, a.I, a.k);
+    return launch_rot_t1(a, ws, s13, s2, nullptr, &sh, act_sh, stream);
+  }
+  SharedArgs sa{};
+  sa.x = a.x;
+  sa.T = a.T;
+  sa.H = a.H;
+  sa.Is = sh.Is;
+  sa.wgu = sh.wgu;
+  sa.su8 = sh.su8;
+  sa.s2 = sh.sgu;
+  sa.wd = sh.wd;
+  sa.sd = sh.sd;
+  sa.y = y_sh;
+  sa.ws = b + o1;
+  hipError_t err = launch_shared_expert(sa, stream);
+  if (err != hipSuccess) return err;
+  return launch_moe_rot_forward(a, s13, s2, y_sh, stream);
 }
 
 // The shared expert: rotated codes of x, the g256 gate/up GEMM with the SiLU

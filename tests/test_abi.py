@@ -115,3 +115,23 @@ def test_stream_read_validation(L):
     assert f(A, 1 << 20, 1024, None, None) == INVALID
     assert f(A + 8, 1 << 20, 1024, A, None) == MISALIGNED
 
+
+def test_rot_layer_shared_validation(L):
+    f = L.moe_w8a8_rot_shared_forward_packed
+    ws = L.moe_w8a8_rot_shared_workspace_bytes(1, 256, 8, 128, 2, 128)
+    assert ws > L.moe_w8a8_workspace_bytes(1, 256, 8, 128, 2)
+    assert L.moe_w8a8_rot_shared_workspace_bytes(1, 256, 8, 128, 2, 0) == 0
+    args = lambda **kw: dict(dict(x=A, lg=A, T=1, H=256, E=8, I=128, k=2, Is=128, wsb=ws,
+                                  ws=A, su8=A), **kw)
+    def call(a):
+        return f(a["x"], a["lg"], a["T"], a["H"], a["E"], a["I"], a["k"], A, A, A, A, a["Is"], A,
+                 a["su8"], A, A, A, A, A, A, a["ws"], a["wsb"], None, None)
+    assert call(args(Is=0)) == INVALID
+    assert call(args(Is=100)) == SHAPE            # Is % 128
+    assert call(args(Is=4096)) == SHAPE           # Is > 2048
+    assert call(args(H=128)) == SHAPE             # H % 256
+    assert call(args(su8=None)) == INVALID
+    assert call(args(x=A + 2)) == MISALIGNED
+    assert call(args(wsb=ws - 1)) == WS_SMALL
+    assert call(args(T=0, x=None)) == OK
+

@@ -377,6 +377,52 @@ def test_rot_moe_and_shared_graph(orc, T):
                  check)
 
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_rot_layer_with_shared_graph(orc, T):
+    # the one-call layer: one token with the shared expert inside the two
+    # routed launches, two tokens composed
+    E, H, I, k, Is = 8, 256, 128, 4, 256
+    key = (78, T)
+    q13 = np.empty((E, 2 * I, H), np.int8)
+    s13 = np.empty((E, 2 * I, H // 128), np.uint16)
+    q2 = np.empty((E, H, I), np.int8)
+    s2 = np.empty((E, H, I // 128), np.uint16)
+    for e in range(E):
+        q13[e], s13[e] = orc.weight_prep_g128(synth.expert_weights(key, e, 2 * I, H, synth.T_W))
+        q2[e], s2[e] = orc.weight_prep_g128(synth.expert_weights(key, e, H, I, synth.T_W2))
+    S = (*orc.weight_prep_g256(synth.weights(key, 2 * Is, H)),
+         *orc.weight_prep_g128(synth.weights(key, H, Is, tensor_id=synth.T_W2)))
+    w13, w2 = mq.pack_moe_weights(dev(q13), dev(q2))
+    Wd = (w13, bf16_dev(s13), w2, bf16_dev(s2))
+    Sd = (mq.pack_weights(dev(S[0])), dev(S[1]), bf16_dev(S[2]), mq.pack_weights(dev(S[3])),
+          bf16_dev(S[4]))
+    sets_h = [(synth.activations((*key, i), T, H, 0, 1.0), synth.router_logits((*key, i), T, E))
+              for i in range(2)]
+    x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(mq.lib().moe_w8a8_rot_shared_workspace_bytes(T, H, E, I, k, Is),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        mq.moe_w8a8_rot_shared_forward(x, lg, *Wd, topk=k, shared_w=Sd, topk_ids=ids, topk_w=wt,
+                                       out=out, ws=ws)
+
+    def check(inp):
+        xh, lh = bf16_host(inp[0]), host(inp[1])
+        y_ref = orc.shared_expert(xh, *S)
+        ids_ref, w_ref = orc.route_topk(lh, k)
+        np.testing.assert_array_equal(host(ids), ids_ref)
+        want = orc.moe_rot_forward(xh, ids_ref, w_ref, q13, s13, q2, s2, shared=y_ref)
+        g = orc.bf16_to_f32(bf16_host(out)).astype(np.float64)
+        r = orc.bf16_to_f32(want).astype(np.float64)
+        assert np.all(np.abs(g - r) <= 1e-3 + 1e-2 * np.abs(r))
+
+    _graph_check(call, [x, lg], [(bf16_dev(a), dev(b)) for a, b in sets_h], [out, ids, wt], check)
+
+
 @pytest.mark.parametrize("M", [3, 300])
 def test_unpacked_linear_pack_and_noalloc_graph(orc, M):
     # linear_w8a8 (row-major weights), w8a8_pack_weights, the allocation-free

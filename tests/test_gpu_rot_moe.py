@@ -356,3 +356,63 @@ def test_shared_then_routed_full_size(orc, full_rot_weights, T):
                                   shared=y_ref)
     mism = assert_bf16_close(bf16_host(out)[sel], out_ref, f"shared + routed T={T}")
     say(f"shared + routed T={T}: bf16 mismatches {mism} of {out_ref.size}")
+
+
+# ------------------------------------------------ the layer with its shared --
+
+def _check_layer(orc, x, logits, k, W, Wd, S, Sd, label):
+    """The one-call layer: bit for bit the two-call composition on the GPU
+    (shared expert, then the routed layer with its output as the shared
+    term), and against the oracle's routed layer with the oracle's shared
+    expert as its shared term."""
+    out, ids, wt = mq.moe_w8a8_rot_shared_forward(bf16_dev(x), dev(logits), *Wd, topk=k,
+                                                  shared_w=Sd)
+    y = mq.shared_expert_w8a8_rot(bf16_dev(x), *Sd)
+    out2, ids2, wt2 = mq.moe_w8a8_rot_forward(bf16_dev(x), dev(logits), *Wd, topk=k, shared=y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(ids), host(ids2))
+    np.testing.assert_array_equal(host(wt), host(wt2))
+    np.testing.assert_array_equal(bf16_host(out), bf16_host(out2))
+    ids_ref, w_ref = orc.route_topk(logits, k)
+    np.testing.assert_array_equal(host(ids), ids_ref)
+    assert ulp_diff_f32(host(wt), w_ref).max() <= 1
+    y_ref = orc.shared_expert(x, *S)
+    out_ref = orc.moe_rot_forward(x, ids_ref, w_ref, *W, shared=y_ref)
+    mism = assert_bf16_close(bf16_host(out), out_ref, label)
+    say(f"{label}: bf16 mismatches {mism} of {out_ref.size}")
+
+
+# one token runs the shared expert inside the two routed launches (gate/up
+# tiles beside gemm1's, the down projection as one more pair of gemm2) when
+# k <= 15, I <= 1024, Is <= 1024 and k I/128 + Is/128 <= 64; else, and for
+# more tokens, the shared expert and the routed layer run one after the other
+@pytest.mark.parametrize("T,E,H,I,Is,k", [
+    (1, 8, 256, 128, 128, 2),
+    (1, 16, 512, 256, 384, 4),    # more shared gate/up tiles than routed ones
+    (1, 16, 512, 384, 128, 4),    # fewer
+    (1, 32, 256, 128, 128, 15),   # the most pairs the single-token form takes
+    (1, 32, 256, 128, 128, 16),   # one more: composed
+    (1, 8, 256, 128, 1152, 2),    # a shared row longer than 1024: composed
+    (3, 8, 256, 128, 128, 2),
+    (40, 16, 512, 256, 256, 4),
+])
+def test_rot_layer_with_shared(orc, T, E, H, I, Is, k):
+    W = _rot_weights(orc, (101, E, I), E, H, I)
+    S = _shared_weights(orc, (101, Is), H, Is)
+    x = synth.activations((101, T), T, H, 3, 10.0)
+    logits = synth.router_logits((101, T, E), T, E)
+    _check_layer(orc, x, logits, k, W, _dev_rot_weights(W), S, _dev_shared_weights(S),
+                 f"rot layer + shared T={T} E={E} I={I} Is={Is} k={k}")
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_rot_layer_with_shared_full_size(orc, full_rot_weights, T):
+    W, Wd = full_rot_weights
+    cfg = synth.moe(T)
+    E, H, I, k = cfg["E"], cfg["H"], cfg["I"], cfg["k"]
+    S = _shared_weights(orc, (102, 0), H, I)
+    x = synth.activations((102, T), T, H, 0, 1.0)
+    logits = synth.router_logits((102, T), T, E)
+    _check_layer(orc, x, logits, k, W, Wd, S, _dev_shared_weights(S),
+                 f"rot layer + shared full T={T}")
+
