@@ -147,10 +147,42 @@ constexpr int kSkinnyU = 8;
 // 16-channel tiles per CU (the down projection of the decode workload: one
 // token 14.1 -> 11.8 us, two 14.1 -> 13.4 us; with four workgroups a CU, as
 // for the gate_up projection, it is slower).
-template <int MMAX, int XH>
+// Eight consecutive values of a row: bf16 as one 16-byte load, fp32 as two.
+template <typename T>
+struct Row8;
+template <>
+struct Row8<uint16_t> {
+  v4u r;
+  __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const v4u*>(p); }
+  __device__ __forceinline__ void zero() { r = v4u{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ float at(int i) const {
+    const uint32_t w = r[i >> 1];
+    return bf16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xffffu));
+  }
+};
+template <>
+struct Row8<float> {
+  v4f a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const v4f*>(p);
+    b = *reinterpret_cast<const v4f*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() {
+    a = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    b = a;
+  }
+  __device__ __forceinline__ float at(int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
+
+// TIN: bf16 rows (the linear entry points) or fp32 rows (the MLP block's
+// activation, quantised as k_quant_rows<float>: IEEE quotient always).  With
+// q_out / s_out, workgroup 0 also writes the codes (row-major, row stride K)
+// and the scales.
+template <int MMAX, int XH, typename TIN>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void k_linear_skinny_fused(
-    const uint16_t* __restrict__ x, int64_t ldx, int M, int K, const int8_t* __restrict__ qw,
-    const float* __restrict__ sw, uint16_t* __restrict__ out, int64_t ldo) {
+    const TIN* __restrict__ x, int64_t ldx, int M, int K, const int8_t* __restrict__ qw,
+    const float* __restrict__ sw, uint16_t* __restrict__ out, int64_t ldo,
+    int8_t* __restrict__ q_out, float* __restrict__ s_out) {
   constexpr int WAVES = kSkinnyWaves, U = kSkinnyU, NT = WAVES * 64;
   __shared__ v4i red[WAVES][64];
   __shared__ float part[WAVES][MMAX];
@@ -166,13 +198,15 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_linear_skinny_fused(
   const int tot = M * nc8;
 
   // the rows: chunk c = tid + NT * i of the M x nc8 chunks
-  v4u xr[XH];
+  Row8<TIN> xr[XH];
 #pragma unroll
   for (int i = 0; i < XH; i++) {
     const int c = tid + NT * i;
     const int r = c / nc8, col = c - r * nc8;
-    xr[i] = c < tot ? *reinterpret_cast<const v4u*>(x + (int64_t)r * ldx + col * 8)
-                    : v4u{0u, 0u, 0u, 0u};
+    if (c < tot)
+      xr[i].load(x + (int64_t)r * ldx + col * 8);
+    else
+      xr[i].zero();
   }
   // the first weight batch
   const int8_t* wp = qw + tile * nchunk * 1024 + lane * 16;
@@ -192,12 +226,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_linear_skinny_fused(
 #pragma unroll
   for (int i = 0; i < XH; i++) {
     const int r = (tid + NT * i) / nc8;
-    const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
     float m8 = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 4; t++)
-      m8 = fmaxf(m8, fmaxf(fabsf(bf16_bits_to_f32(w4[t] & 0xffffu)),
-                           fabsf(bf16_bits_to_f32(w4[t] >> 16))));
+    for (int t = 0; t < 8; t++) m8 = fmaxf(m8, fabsf(xr[i].at(t)));
 #pragma unroll
     for (int rr = 0; rr < MMAX; rr++)
       if (rr == r) am[rr] = fmaxf(am[rr], m8);
@@ -217,6 +248,11 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_linear_skinny_fused(
     sc[r] = am[r] / 127.0f;
     rc[r] = 1.0f / sc[r];
   }
+  if (s_out && tile == 0 && tid < M) {
+#pragma unroll
+    for (int rr = 0; rr < MMAX; rr++)
+      if (rr == tid) s_out[rr] = am[rr] != 0.0f ? sc[rr] : 0.0f;
+  }
   // codes into LDS, row r at r * K
 #pragma unroll
   for (int i = 0; i < XH; i++) {
@@ -231,24 +267,24 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_linear_skinny_fused(
         r_ = rc[rr];
         a_ = am[rr];
       }
-    const bool recip = s_ >= 0x1p-100f;
-    const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+    // the reciprocal form is exact for bf16 rows only (k_quant_rows)
+    const bool recip = sizeof(TIN) == 2 && s_ >= 0x1p-100f;
     uint32_t pk[2] = {0u, 0u};
     if (a_ != 0.0f) {
 #pragma unroll
       for (int hh = 0; hh < 2; hh++) {
         int cd[4];
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
-          const float v0 = bf16_bits_to_f32(w4[2 * hh + t] & 0xffffu);
-          const float v1 = bf16_bits_to_f32(w4[2 * hh + t] >> 16);
-          cd[2 * t] = recip ? quant_code_recip(v0, s_, r_) : quant_code(v0, s_);
-          cd[2 * t + 1] = recip ? quant_code_recip(v1, s_, r_) : quant_code(v1, s_);
+        for (int t = 0; t < 4; t++) {
+          const float v = xr[i].at(4 * hh + t);
+          cd[t] = recip ? quant_code_recip(v, s_, r_) : quant_code(v, s_);
         }
         pk[hh] = pack4_i8(cd[0], cd[1], cd[2], cd[3]);
       }
     }
     *reinterpret_cast<uint2*>(q_lds + r * K + col * 8) = make_uint2(pk[0], pk[1]);
+    if (q_out && tile == 0)
+      *reinterpret_cast<uint2*>(q_out + (int64_t)r * K + col * 8) = make_uint2(pk[0], pk[1]);
   }
   __syncthreads();
 
@@ -295,27 +331,43 @@ bool linear_fused_fits(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 2 && K <= 16384 && N / 16 <= 2 * (int64_t)device_cus();
 }
 
-hipError_t launch_linear_skinny_fused(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
-                                      const int8_t* qw_packed, const float* sw, int64_t N,
-                                      uint16_t* y, int64_t ldy, hipStream_t stream) {
-  // 16-byte row chunks held a thread: ceil(M * K / 8 / 512), at most 4 for
-  // one row and 8 for two.  Two rows hold 5 up to K = 10240 (110 VGPRs: two
-  // workgroups a CU); holding 8 takes 150 VGPRs and one workgroup a CU.
+template <typename TIN>
+static hipError_t launch_fused_impl(const TIN* x, int64_t ldx, int64_t M, int64_t K,
+                                    const int8_t* qw_packed, const float* sw, int64_t N,
+                                    uint16_t* y, int64_t ldy, int8_t* q_out, float* s_out,
+                                    hipStream_t stream) {
+  // 8-value row chunks held a thread: ceil(M * K / 8 / 512), at most 4 for
+  // one row and 8 for two.  Two bf16 rows hold 5 up to K = 10240 (110
+  // VGPRs: two workgroups a CU); holding 8 takes 150 VGPRs and one
+  // workgroup a CU.
   const size_t lds = (size_t)(M * K);
   const int64_t need = (M * (K / 8) + kSkinnyWaves * 64 - 1) / (kSkinnyWaves * 64);
   const dim3 grid((unsigned)(N / 16)), block(kSkinnyWaves * 64);
   // (12 loads a wave for the down projection, as launch_skinny_impl: 12.38 ->
   // 12.29 us at one token, 13.67 -> 18.66 us at two; kept at 8)
   if (M == 1)
-    hipLaunchKernelGGL((k_linear_skinny_fused<1, 4>), grid, block, lds, stream, x, ldx, (int)M,
-                       (int)K, qw_packed, sw, y, ldy);
+    hipLaunchKernelGGL((k_linear_skinny_fused<1, 4, TIN>), grid, block, lds, stream, x, ldx,
+                       (int)M, (int)K, qw_packed, sw, y, ldy, q_out, s_out);
   else if (need <= 5)
-    hipLaunchKernelGGL((k_linear_skinny_fused<2, 5>), grid, block, lds, stream, x, ldx, (int)M,
-                       (int)K, qw_packed, sw, y, ldy);
+    hipLaunchKernelGGL((k_linear_skinny_fused<2, 5, TIN>), grid, block, lds, stream, x, ldx,
+                       (int)M, (int)K, qw_packed, sw, y, ldy, q_out, s_out);
   else
-    hipLaunchKernelGGL((k_linear_skinny_fused<2, 8>), grid, block, lds, stream, x, ldx, (int)M,
-                       (int)K, qw_packed, sw, y, ldy);
+    hipLaunchKernelGGL((k_linear_skinny_fused<2, 8, TIN>), grid, block, lds, stream, x, ldx,
+                       (int)M, (int)K, qw_packed, sw, y, ldy, q_out, s_out);
   return hipGetLastError();
+}
+
+hipError_t launch_linear_skinny_fused(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
+                                      const int8_t* qw_packed, const float* sw, int64_t N,
+                                      uint16_t* y, int64_t ldy, hipStream_t stream) {
+  return launch_fused_impl(x, ldx, M, K, qw_packed, sw, N, y, ldy, nullptr, nullptr, stream);
+}
+
+hipError_t launch_linear_skinny_fused_f32(const float* x, int64_t ldx, int64_t M, int64_t K,
+                                          const int8_t* qw_packed, const float* sw, int64_t N,
+                                          uint16_t* y, int64_t ldy, int8_t* q_out, float* s_out,
+                                          hipStream_t stream) {
+  return launch_fused_impl(x, ldx, M, K, qw_packed, sw, N, y, ldy, q_out, s_out, stream);
 }
 
 template <bool PACKED, int EPI>

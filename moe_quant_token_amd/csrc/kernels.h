@@ -50,6 +50,12 @@ bool linear_fused_fits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear_skinny_fused(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
                                       const int8_t* qw_packed, const float* sw, int64_t N,
                                       uint16_t* y, int64_t ldy, hipStream_t stream);
+// The same for fp32 rows (quantised as k_quant_rows<float>); q_out / s_out
+// (nullable) receive the codes (row-major, stride K) and the scales.
+hipError_t launch_linear_skinny_fused_f32(const float* x, int64_t ldx, int64_t M, int64_t K,
+                                          const int8_t* qw_packed, const float* sw, int64_t N,
+                                          uint16_t* y, int64_t ldy, int8_t* q_out, float* s_out,
+                                          hipStream_t stream);
 
 hipError_t launch_gemm_tile(const int8_t* qa, const float* sa, int64_t M, int64_t K,
                             int64_t lda, const int8_t* qw, const float* sw, int64_t N,

@@ -8,7 +8,8 @@
 // interleaved gate/up rows, per-token int8 requant, gemm2 -- applied to the
 // dense gate_up and down linears.
 //
-// Four launches on the caller's stream:
+// Four launches on the caller's stream (three for one token, whose requant
+// runs inside the down GEMM's launch as in the decode linear):
 //   1. per-token int8 codes of x (row-major for decode, tile layout for the
 //      tiled GEMM);
 //   2. the gate_up GEMM whose epilogue pairs the interleaved gate and up
@@ -76,12 +77,22 @@ hipError_t launch_mlp(const MlpArgs& a, hipStream_t stream) {
     if ((e = launch_gemm_skinny_silu(w.qx, w.sx, a.M, a.K, a.K, a.wgu, a.sgu, I2, w.act, a.I,
                                      stream)) != hipSuccess)
       return e;
-    if ((e = launch_quant_rows_f32(w.act, a.M, a.I, a.I, w.qa, a.I, w.sa, false, stream)) !=
-        hipSuccess)
-      return e;
-    if ((e = launch_gemm_skinny(w.qa, w.sa, a.M, a.I, a.I, a.wd, a.sd, a.N, a.I, true, a.y,
-                                a.ldy, stream)) != hipSuccess)
-      return e;
+    if (a.M == 1 && linear_fused_fits(a.M, a.N, a.I)) {
+      // one token: requant and down GEMM in one launch (its first workgroup
+      // also leaves the codes and scales in the workspace).  Measured on
+      // MI355X at K=5120, I=8704, N=5120: the block 33.0 -> 31.0 us; at two
+      // tokens (fp32 rows, 70 KiB a workgroup) 33.7 -> 34.9 us, so not there
+      if ((e = launch_linear_skinny_fused_f32(w.act, a.I, a.M, a.I, a.wd, a.sd, a.N, a.y, a.ldy,
+                                              w.qa, w.sa, stream)) != hipSuccess)
+        return e;
+    } else {
+      if ((e = launch_quant_rows_f32(w.act, a.M, a.I, a.I, w.qa, a.I, w.sa, false, stream)) !=
+          hipSuccess)
+        return e;
+      if ((e = launch_gemm_skinny(w.qa, w.sa, a.M, a.I, a.I, a.wd, a.sd, a.N, a.I, true, a.y,
+                                  a.ldy, stream)) != hipSuccess)
+        return e;
+    }
   } else {
     if ((e = launch_quant_rows_packed(a.x, a.M, a.K, a.ldx, w.qx, w.sx, stream)) != hipSuccess)
       return e;

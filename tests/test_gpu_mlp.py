@@ -67,11 +67,21 @@ def test_mlp_small(orc, M):
     key = (95, M)
     W = _weights(orc, key, K, I, N)
     x = synth.activations(key, M, K, 4, 20.0)
-    if M > 2:
-        x[1] = 0  # an all-zero token
+    if M >= 2:
+        x[M - 1] = 0  # an all-zero token
     y = _check(orc, x, W, _dev_weights(W), f"mlp small M={M}")
-    if M > 2:
-        assert not bf16_host(y)[1].any()
+    if M >= 2:
+        assert not bf16_host(y)[M - 1].any()
+
+
+def test_mlp_single_zero_token(orc):
+    # one token: the requant runs inside the down GEMM's launch; an all-zero
+    # token has a zero activation row (scale 0, codes 0) and a zero output
+    K, I, N = 512, 192, 128
+    W = _weights(orc, (95, 99), K, I, N)
+    x = np.zeros((1, K), np.uint16)
+    y = _check(orc, x, W, _dev_weights(W), "mlp zero token M=1")
+    assert not bf16_host(y).any()
 
 
 def test_mlp_strided_and_ragged(orc):
