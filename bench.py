@@ -344,9 +344,9 @@ def main():
         if st != 0:
             raise RuntimeError(f"linear_w8a8_packed failed: {st}")
 
-    def gemm_call(c):
+    def gemm_call(c, warm=False):
         sh = c["sh"]
-        qw, sw = weights(sh)
+        qw, sw = sh["copies"][0] if warm else weights(sh)
         st = L.gemm_w8a8_packed(c["q"].data_ptr(), c["s"].data_ptr(), c["M"], sh["K"], sh["K"],
                                 qw.data_ptr(), sw.data_ptr(), sh["N"], c["y"].data_ptr(),
                                 sh["N"], None, 0, stream)
@@ -612,6 +612,20 @@ def decode_cases(calls, linear_call, gemm_call, timer):
                 "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "alg_bytes": nbytes,
             }
+        if M == 1:
+            # warm: one weight copy over and over, so the weights sit in the
+            # 256 MB Infinity Cache (labelled; not an HBM figure)
+            fn = lambda i: gemm_call(c, warm=True)
+            for i in range(4):
+                fn(i)
+            _, each = timer.run(fn, it, groups=8)
+            med = pct(each, 50)
+            nbytes = linear_bytes(M, N, K, False)
+            res[f"decode_{sh['name']}_M{M}_gemm_warm"] = {
+                **timer.stats_us(each),
+                "gbs": round(nbytes / (med * 1e-3) / 1e9, 1),
+                "note": "one weight copy (Infinity Cache resident); not an HBM rate",
+            }
     return res
 
 
@@ -683,6 +697,27 @@ def prefill_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes):
             "linear_frac_mfma": round(ops / (t_l * 1e-3) / 1e12 / I8_PEAK_TOPS, 4),
             "weight_copies": ncopy,
         }
+        if N == 5120:
+            # the per-token quantiser alone on the 4096 x 5120 activations:
+            # cold (the rows rotate over copies beyond the Infinity Cache) and
+            # warm (one copy, as when the producing op just wrote them)
+            xcopies = [x] + [x.clone() for _ in range(math.ceil(2 * MALL_BYTES / (M * K * 2)))]
+            qq = torch.empty((M, K), dtype=torch.int8, device=dev)
+            ss = torch.empty((M,), dtype=torch.float32, device=dev)
+            for xc in xcopies:
+                mq.quant_per_token_i8(xc, qq, ss)
+            qbytes = M * K * 2 + M * K + 4 * M
+            for tag, fn in (("", lambda i: mq.quant_per_token_i8(xcopies[i % len(xcopies)], qq,
+                                                                  ss)),
+                            ("_warm", lambda i: mq.quant_per_token_i8(x, qq, ss))):
+                _, eq = timer.run(fn, 40, groups=8)
+                tq = pct(eq, 50)
+                res[f"quant_M{M}_K{K}{tag}"] = {
+                    **timer.stats_us(eq), "alg_bytes": qbytes,
+                    "gbs": round(qbytes / (tq * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(qbytes / (tq * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "input_copies": len(xcopies) if not tag else 1}
+            del xcopies, qq, ss
         del qw, sw, x, q, s, y, ws, ws_g, copies
         torch.cuda.empty_cache()
     return res
