@@ -37,12 +37,30 @@ __device__ __forceinline__ int quant_code(float x, float s) {
 // e = fma(-q0, s, x) (exact), q = fma(e, r, q0).  For bf16 x with
 // |x| <= amax and s = amax/127 >= 2^-100, rint(q) equals rint of the IEEE
 // quotient x/s: checked exhaustively over every such (x, amax) pair.  fp32
-// rows, and rows with a smaller scale, use the IEEE division.
+// rows, and rows with a smaller scale, use the IEEE division.  That quotient
+// is at most 127 + 2^-16 here, so the clamp never acts; adding 1.5 * 2^23
+// rounds q to an integer, ties to even (the sum's ulp is 1), and leaves it,
+// two's complement, in the low bits of the sum (the same check covers this).
 __device__ __forceinline__ int quant_code_recip(float x, float s, float r) {
   const float q0 = x * r;
   const float e = __builtin_fmaf(-q0, s, x);
   const float q = __builtin_fmaf(e, r, q0);
-  return (int)fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f);
+  return (int)(__float_as_uint(q + 0x1.8p23f) - 0x4B400000u);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Running maximum of |x| over two bf16 values a word, kept as bit patterns:
+// for finite bf16 the magnitude orders as the unsigned integer of the low 15
+// bits, so one packed u16 maximum covers two values.
+__device__ __forceinline__ uint32_t bf16x2_absmax(uint32_t m, uint32_t w) {
+  const u16x2 a = __builtin_bit_cast(u16x2, m);
+  const u16x2 b = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+__device__ __forceinline__ float bf16x2_absmax_value(uint32_t m) {
+  const uint32_t lo = m & 0xffffu, hi = m >> 16;
+  return bf16_bits_to_f32(lo > hi ? lo : hi);
 }
 
 // Wave-wide maximum through DPP row shifts and row broadcasts (no LDS

@@ -159,6 +159,12 @@ struct Row8<uint16_t> {
     const uint32_t w = r[i >> 1];
     return bf16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xffffu));
   }
+  __device__ __forceinline__ float absmax() const {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; i++) m = bf16x2_absmax(m, r[i]);
+    return bf16x2_absmax_value(m);
+  }
 };
 template <>
 struct Row8<float> {
@@ -172,6 +178,12 @@ struct Row8<float> {
     b = a;
   }
   __device__ __forceinline__ float at(int i) const { return i < 4 ? a[i] : b[i - 4]; }
+  __device__ __forceinline__ float absmax() const {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(at(i)));
+    return m;
+  }
 };
 
 // TIN: bf16 rows (the linear entry points) or fp32 rows (the MLP block's
@@ -226,9 +238,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_linear_skinny_fused(
 #pragma unroll
   for (int i = 0; i < XH; i++) {
     const int r = (tid + NT * i) / nc8;
-    float m8 = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 8; t++) m8 = fmaxf(m8, fabsf(xr[i].at(t)));
+    const float m8 = xr[i].absmax();
 #pragma unroll
     for (int rr = 0; rr < MMAX; rr++)
       if (rr == r) am[rr] = fmaxf(am[rr], m8);
@@ -270,17 +280,19 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void k_linear_skinny_fused(
     // the reciprocal form is exact for bf16 rows only (k_quant_rows)
     const bool recip = sizeof(TIN) == 2 && s_ >= 0x1p-100f;
     uint32_t pk[2] = {0u, 0u};
-    if (a_ != 0.0f) {
+    if (recip) {
 #pragma unroll
-      for (int hh = 0; hh < 2; hh++) {
-        int cd[4];
+      for (int hh = 0; hh < 2; hh++)
+        pk[hh] = pack4_i8(quant_code_recip(xr[i].at(4 * hh), s_, r_),
+                          quant_code_recip(xr[i].at(4 * hh + 1), s_, r_),
+                          quant_code_recip(xr[i].at(4 * hh + 2), s_, r_),
+                          quant_code_recip(xr[i].at(4 * hh + 3), s_, r_));
+    } else if (a_ != 0.0f) {
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-          const float v = xr[i].at(4 * hh + t);
-          cd[t] = recip ? quant_code_recip(v, s_, r_) : quant_code(v, s_);
-        }
-        pk[hh] = pack4_i8(cd[0], cd[1], cd[2], cd[3]);
-      }
+      for (int hh = 0; hh < 2; hh++)
+        pk[hh] = pack4_i8(quant_code(xr[i].at(4 * hh), s_), quant_code(xr[i].at(4 * hh + 1), s_),
+                          quant_code(xr[i].at(4 * hh + 2), s_),
+                          quant_code(xr[i].at(4 * hh + 3), s_));
     }
     *reinterpret_cast<uint2*>(q_lds + r * K + col * 8) = make_uint2(pk[0], pk[1]);
     if (q_out && tile == 0)

@@ -373,11 +373,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E,
 // (checked exhaustively over every such pair); smaller scales divide.
 __device__ __forceinline__ int code_bf16(uint32_t h, float sc, float rc) {
   const float x = bf16_bits_to_f32(h);
-  if (sc < 0x1p-100f) return quant_code(x, sc);
-  const float q0 = x * rc;
-  const float e = __builtin_fmaf(-q0, sc, x);
-  const float q = __builtin_fmaf(e, rc, q0);
-  return (int)fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f);
+  return sc < 0x1p-100f ? quant_code(x, sc) : quant_code_recip(x, sc, rc);
 }
 __device__ __forceinline__ uint32_t quant_pack4_bf16(uint32_t w0, uint32_t w1, float sc,
                                                      float rc) {

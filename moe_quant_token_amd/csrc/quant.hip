@@ -152,46 +152,47 @@ __global__ __launch_bounds__(256) void k_quant_rows_wave(const uint16_t* __restr
   const uint16_t* xr = x + row * ldx;
   const int nc = K >> 3;  // 8-value chunks
   v4u raw[NCH];
-  float amax = 0.0f;
+  uint32_t m2 = 0u;
 #pragma unroll
   for (int u = 0; u < NCH; u++) {
     const int c = lane + 64 * u;
     raw[u] = c < nc ? *reinterpret_cast<const v4u*>(xr + c * 8) : v4u{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[u][i] & 0xffffu)));
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[u][i] >> 16)));
-    }
+    for (int i = 0; i < 4; i++) m2 = bf16x2_absmax(m2, raw[u][i]);
   }
-  amax = wave_max(amax);
+  const float amax = wave_max(bf16x2_absmax_value(m2));
   const float sc = amax / 127.0f;
-  const bool recip = sc >= 0x1p-100f;
   const float rc = 1.0f / sc;
-  auto code = [&](uint32_t h) __attribute__((always_inline)) {
-    const float v = bf16_bits_to_f32(h);
-    return recip ? quant_code_recip(v, sc, rc) : quant_code(v, sc);
-  };
+  auto emit = [&](auto code) __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < NCH; u++) {
-    const int c = lane + 64 * u;
-    if (c >= nc) break;
-    uint32_t w[2] = {0u, 0u};
-    if (amax != 0.0f) {
+    for (int u = 0; u < NCH; u++) {
+      const int c = lane + 64 * u;
+      if (c >= nc) break;
+      uint32_t w[2];
 #pragma unroll
       for (int i = 0; i < 2; i++)
         w[i] = pack4_i8(code(raw[u][2 * i] & 0xffffu), code(raw[u][2 * i] >> 16),
                         code(raw[u][2 * i + 1] & 0xffffu), code(raw[u][2 * i + 1] >> 16));
+      int8_t* dst;
+      if (PACKED_OUT) {
+        const int c16 = c >> 1;  // 16-code slice: k bytes 16*c16 .. +15
+        dst = q + ((row >> 4) * (int64_t)(K >> 6) + (c16 >> 2)) * 1024 +
+              ((row & 15) + 16 * (c16 & 3)) * 16 + (c & 1) * 8;
+      } else {
+        dst = q + row * ldq + c * 8;
+      }
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
     }
-    int8_t* dst;
-    if (PACKED_OUT) {
-      const int c16 = c >> 1;  // 16-code slice: k bytes 16*c16 .. +15
-      dst = q + ((row >> 4) * (int64_t)(K >> 6) + (c16 >> 2)) * 1024 +
-            ((row & 15) + 16 * (c16 & 3)) * 16 + (c & 1) * 8;
-    } else {
-      dst = q + row * ldq + c * 8;
-    }
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-  }
+  };
+  // the scale test is wave-uniform: one branch for the whole row
+  if (sc >= 0x1p-100f)
+    emit([&](uint32_t h) __attribute__((always_inline)) {
+      return quant_code_recip(bf16_bits_to_f32(h), sc, rc);
+    });
+  else
+    emit([&](uint32_t h) __attribute__((always_inline)) {
+      return amax != 0.0f ? quant_code(bf16_bits_to_f32(h), sc) : 0;
+    });
   if (lane == 0) s[row] = amax != 0.0f ? sc : 0.0f;
 }
 
