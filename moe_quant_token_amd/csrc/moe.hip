@@ -1700,7 +1700,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
   constexpr int GW = (MAXG + WAVES - 1) / WAVES;  // groups a wave takes
   constexpr bool G256 = MODE == kRotG256Silu || MODE == kRotG256SiluX;
   constexpr bool ROT_IN = MODE == kRotActRot || MODE == kRotG256SiluX;  // rows rotated here
-  __shared__ v4i red[G256 ? 1 : NT][G256 ? 1 : MAXG][64];
+  // a group's int32 sums, element v of lane l at [v][l] (the fold reads one
+  // element of 64 consecutive lanes: no bank conflicts)
+  __shared__ int32_t red[G256 ? 1 : NT][G256 ? 1 : MAXG][4][64];
   __shared__ long long sred[G256 ? WAVES : 1][4][64];
   __shared__ int32_t m_lds[G256 ? 16 : 1][MAXG + 1];
   __shared__ float s_lds[NT * 16][MAXG + 1];
@@ -1756,13 +1758,24 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
     }
   }
 
+  // the first 16 threads hold their row's pair and token scale of the next
+  // block: those loads are in flight while the current block computes (rows
+  // past nrows are never read back: outputs use row min(r, nrows - 1))
+  int pid = 0;
+  float sxv = 0.0f;
+  if (threadIdx.x < 16 && rr.begin + (int)threadIdx.x < rr.end) {
+    pid = dense ? rr.begin + (int)threadIdx.x : sorted_pairs[rr.begin + threadIdx.x];
+    if (!ROT_IN) sxv = sx[pid / k];
+  }
   for (int pb = rr.begin; pb < rr.end; pb += 16) {
     const int nrows = min(16, rr.end - pb);
     __syncthreads();  // the previous block's LDS consumed
-    if (threadIdx.x < 16)
-      pair_lds[threadIdx.x] =
-          threadIdx.x < nrows ? (dense ? pb + (int)threadIdx.x : sorted_pairs[pb + threadIdx.x])
-                              : 0;
+    if (threadIdx.x < 16) {
+      pair_lds[threadIdx.x] = (int)threadIdx.x < nrows ? pid : 0;
+      if (!ROT_IN) sa_lds[threadIdx.x] = sxv;
+      const int nx = pb + 16 + (int)threadIdx.x;
+      if (nx < rr.end) pid = dense ? nx : sorted_pairs[nx];
+    }
     __syncthreads();
     if (ROT_IN) {
       for (int r = wv; r < nrows; r += WAVES) {
@@ -1791,9 +1804,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
         }
       }
     }
-    if (!ROT_IN && threadIdx.x < 16)
-      sa_lds[threadIdx.x] = sx[pair_lds[threadIdx.x < nrows ? threadIdx.x : 0] / k];
-    __syncthreads();
+    if (ROT_IN) __syncthreads();
 
     // this wave's groups: the activation slices once, every tile's MFMAs
     const bool a_ok = j < nrows;
@@ -1822,7 +1833,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
 #pragma unroll
             for (int v = 0; v < 4; v++) S[v] += (long long)acc[v] * M;
           } else {
-            red[t][gg][lane] = acc;
+#pragma unroll
+            for (int v = 0; v < 4; v++) red[t][gg][v][lane] = acc[v];
           }
         }
       }
@@ -1831,6 +1843,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
 #pragma unroll
       for (int v = 0; v < 4; v++) sred[wv][v][lane] = S[v];
     }
+    // the next block's token scales (its pairs have arrived by now)
+    if (!ROT_IN && threadIdx.x < 16 && pb + 16 + (int)threadIdx.x < rr.end) sxv = sx[pid / k];
     __syncthreads();
     // (tile, element) units over the waves: element v of every lane is row
     // 4 (lane / 16) + v, column 16 (tile0 + t) + lane % 16
@@ -1849,7 +1863,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
       } else {
         tt = 0.0;
         for (int gg = 0; gg < G; gg++)
-          tt = tt + (double)red[t][gg][lane][v] * (double)s_lds[t * 16 + j][gg];
+          tt = tt + (double)red[t][gg][v][lane] * (double)s_lds[t * 16 + j][gg];
         tt = tt * (double)sa_lds[rc];
       }
       tt = tt * 0.0078125;

@@ -235,10 +235,14 @@ def test_rot_moe_given_ids_and_skew(orc, T):
     assert_bf16_close(bf16_host(out), out_ref, "rot moe given ids")
 
 
-def test_rot_moe_wide_scale_range(orc):
+@pytest.mark.parametrize("T,I", [(1100, 256), (40, 256), (600, 768)])
+def test_rot_moe_wide_scale_range(orc, T, I):
     # some weight rows have one 128-group scaled down by 2^-28: the fold still
-    # matches the fp64 in-order sum of the definition
-    E, H, I, k, T = 4, 256, 256, 4, 1100
+    # matches the fp64 in-order sum of the definition (workgroups holding such
+    # a column fold in fp64, the others with integers); 40 tokens take the
+    # small-batch gemm2 that rotates the activations itself, 600 tokens with
+    # I = 768 the gemm2 of eight 128-groups
+    E, H, k = 4, 256, 4
     key = (97, 0)
     q13 = np.empty((E, 2 * I, H), np.int8)
     s13 = np.empty((E, 2 * I, H // 128), np.uint16)
