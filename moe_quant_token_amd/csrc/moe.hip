@@ -1886,6 +1886,126 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
   }
 }
 
+// Grouped g128 GEMM for large batches (gemm1 with the SiLU epilogue, or gemm2
+// on given rotated codes), one wave per 16-row weight tile holding all of K
+// of it in registers (NKMAX 1 KiB k steps), so the group sums never leave the
+// wave: each 128-group's two MFMA steps are folded into fp64 sums right away,
+// in group order, as defined.  Workgroup = four waves = four consecutive tiles
+// of one expert; the expert's pair rows come in blocks of 16, each block's
+// activation codes gathered straight into LDS (buffer loads to LDS, lane l =
+// row l % 16, 16-byte k slice l / 16: the MFMA operand layout) one block
+// ahead in two buffers, one barrier a block.  Every lane loads its row's pair
+// id two blocks ahead and its token scale one block ahead; a block starts
+// with a wait for every vector memory operation in flight (its copies, those
+// loads, the stores of the block before last), so nothing that block uses
+// waits again.
+template <int MODE, int NKMAX>
+__global__ __launch_bounds__(256, 2) void k_rot_gemm_kw(
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, int k,
+    const int8_t* __restrict__ W, const uint16_t* __restrict__ sW, int Nw, int K, int qx_rows,
+    const int32_t* __restrict__ expert_list, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ n_active, const int32_t* __restrict__ sorted_pairs,
+    float* __restrict__ out, int ldo) {
+  constexpr int GMAX = NKMAX / 2;
+  __shared__ __attribute__((aligned(1024))) int8_t a_lds[2][NKMAX * 1024];
+  RotRows rr;
+  if (!rot_rows(expert_list, seg_off, n_active, 0, 16, rr)) return;
+  const int nrows_all = rr.end - rr.begin;
+  if (nrows_all <= 0) return;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+  const int nk = K >> 6;
+  const int G = K >> 7;
+  const int tile = blockIdx.x * 4 + wv;
+  const int col = tile * 16 + j;
+
+  // the wave's tile, all of K, and the lane's column scales (indices clamped,
+  // no branch between the loads)
+  const int8_t* wb = W + ((int64_t)rr.e * (Nw >> 4) + tile) * nk * 1024 + lane * 16;
+  v4i bw[NKMAX];
+#pragma unroll
+  for (int c = 0; c < NKMAX; c++) bw[c] = ld_stream(wb + (int64_t)min(c, nk - 1) * 1024);
+  float sv[GMAX];
+  const uint16_t* sp = sW + ((int64_t)rr.e * Nw + col) * G;
+#pragma unroll
+  for (int gg = 0; gg < GMAX; gg++) sv[gg] = bf16_bits_to_f32(sp[min(gg, G - 1)]);
+
+  const int nblk = (nrows_all + 15) >> 4;
+  const __amdgpu_buffer_rsrc_t qrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)qx, 0, qx_rows * K, 0x00020000);
+  // block b's pair of row j (rows past the segment end repeat its last pair)
+  auto pair_of = [&](int b) __attribute__((always_inline)) {
+    return sorted_pairs[min(rr.begin + 16 * b + j, rr.end - 1)];
+  };
+  // block b's codes into buffer b & 1: wave w copies k steps w, w + 4, ...
+  auto copy = [&](int b, int p) __attribute__((always_inline)) {
+    int8_t* dst = a_lds[b & 1];
+    const int voff = (p / k) * K + 16 * g;
+    for (int c = wv; c < nk; c += 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qrs, (__attribute__((address_space(3))) void*)(dst + c * 1024), 16, voff + c * 64, 0,
+          0, 0);
+  };
+  auto store = [&](const float (&res)[4], int p_blk, int nrows) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int r = 4 * g + v;
+      const int p = __shfl(p_blk, r, 64);
+      if (r < nrows) {
+        if (MODE == kRotSilu) {
+          if ((j & 1) == 0) out[(int64_t)p * ldo + (col >> 1)] = res[v];
+        } else {
+          out[(int64_t)p * ldo + col] = res[v];
+        }
+      }
+    }
+  };
+  int p_cur = pair_of(0), p_prev = 0;
+  float s_cur = sx[p_cur / k];
+  copy(0, p_cur);
+  int p_nxt = pair_of(1);
+  float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int b = 0; b < nblk; b++) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    if (b > 0) store(res, p_prev, min(16, nrows_all - 16 * (b - 1)));
+    if (b + 1 < nblk) copy(b + 1, p_nxt);
+    const int p_nn = pair_of(b + 2);
+    const float s_nxt = sx[p_nxt / k];
+    // block b: every group's two k steps, then the fold, in group order
+    const int nrows = min(16, nrows_all - 16 * b);
+    const int8_t* ab = a_lds[b & 1] + lane * 16;
+    double tt[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int gg = 0; gg < GMAX; gg++) {
+      if (gg < G) {
+        v4i acc = {0, 0, 0, 0};
+        acc = mfma_16x16x64_i8(*reinterpret_cast<const v4i*>(ab + (2 * gg) * 1024), bw[2 * gg],
+                               acc);
+        acc = mfma_16x16x64_i8(*reinterpret_cast<const v4i*>(ab + (2 * gg + 1) * 1024),
+                               bw[2 * gg + 1], acc);
+#pragma unroll
+        for (int v = 0; v < 4; v++) tt[v] = tt[v] + (double)acc[v] * (double)sv[gg];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const float sa = __shfl(s_cur, min(4 * g + v, nrows - 1), 64);
+      double t = tt[v] * (double)sa;
+      t = t * 0.0078125;
+      const float hv = (float)t;
+      res[v] = MODE == kRotSilu ? rot_silu_pair(hv) : hv;
+    }
+    p_prev = p_cur;
+    p_cur = p_nxt;
+    s_cur = s_nxt;
+    p_nxt = p_nn;
+  }
+  store(res, p_prev, nrows_all - 16 * (nblk - 1));
+}
+
 // A single token in the Hadamard domain: two launches.  k_rot_t1_gemm1 fuses
 // the routing and the rotated quant of x into gemm1 (every workgroup repeats
 // them: wave 0 routes, wave 1 rotates and quantises the row into LDS; the
@@ -2527,6 +2647,37 @@ static hipError_t launch_rot_t1(const MoeArgs& a, const MoeWs& ws, const uint16_
   return hipSuccess;
 }
 
+// The K-per-wave grouped GEMM: K <= 2048 (a wave holds its tile's K in
+// registers), the activation buffer addressable with 32-bit offsets, and at
+// least 512 pairs (measured on MI355X, routed layer E=256 H=2048 I=512 k=8,
+// against the split-K kernels: 64 tokens 152 -> 146 us, 256 tokens 189 ->
+// 178 us, 2048 tokens 407 -> 372 us; from 4096 pairs only, 64 and 256 tokens
+// unchanged).
+constexpr int64_t kRotKwMinPairs = 512;
+static bool rot_kw_fits(int64_t P, int64_t rows, int64_t K) {
+  return P >= kRotKwMinPairs && K <= 2048 && rows * K < ((int64_t)1 << 31);
+}
+
+template <int MODE>
+static hipError_t launch_rot_kw(const int8_t* qx, const float* sx, int k, const int8_t* W,
+                                const uint16_t* sW, int64_t Nw, int64_t K, int64_t rows,
+                                const MoeWs& ws, unsigned slots, float* out, int64_t ldo,
+                                hipStream_t stream) {
+  const dim3 grid((unsigned)(Nw / 64), slots), block(256);
+#define W8A8_KW(n)                                                                              \
+  hipLaunchKernelGGL((k_rot_gemm_kw<MODE, n>), grid, block, 0, stream, qx, sx, k, W, sW,       \
+                     (int)Nw, (int)K, (int)rows, ws.expert_list, ws.seg_off, ws.n_active,     \
+                     ws.sorted_pairs, out, (int)ldo)
+  if (K <= 512)
+    W8A8_KW(8);
+  else if (K <= 1024)
+    W8A8_KW(16);
+  else
+    W8A8_KW(32);
+#undef W8A8_KW
+  return hipGetLastError();
+}
+
 hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const uint16_t* s2,
                                   const float* shared, hipStream_t stream) {
   const int64_t P = (int64_t)a.T * a.k;
@@ -2541,13 +2692,19 @@ hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const u
   if ((err = launch_rot_sort(a, ws, P, stream)) != hipSuccess) return err;
   // four (H <= 2048) or two 16-row weight tiles a workgroup: the activation
   // slices loaded once for all, more weight bytes in flight; LDS sized for H
-  auto g1 = a.H <= 2048 ? k_rot_gemm_splitk<kRotSilu, 8, 4, 16>
-                        : k_rot_gemm_splitk<kRotSilu, 8, 2, 32>;
-  const unsigned t1 = a.H <= 2048 ? I2 / 64 : I2 / 32;
-  hipLaunchKernelGGL(g1, dim3(t1, slots), dim3(512), 0, stream, ws.qx, ws.sx, nullptr, a.k,
-                     a.w13, s13, nullptr, I2, a.H, ws.expert_list, ws.seg_off, ws.n_active,
-                     ws.sorted_pairs, 0, ws.act, a.I, nullptr, nullptr);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (rot_kw_fits(P, a.T, a.H)) {
+    if ((err = launch_rot_kw<kRotSilu>(ws.qx, ws.sx, a.k, a.w13, s13, I2, a.H, a.T, ws, slots,
+                                       ws.act, a.I, stream)) != hipSuccess)
+      return err;
+  } else {
+    auto g1 = a.H <= 2048 ? k_rot_gemm_splitk<kRotSilu, 8, 4, 16>
+                          : k_rot_gemm_splitk<kRotSilu, 8, 2, 32>;
+    const unsigned t1 = a.H <= 2048 ? I2 / 64 : I2 / 32;
+    hipLaunchKernelGGL(g1, dim3(t1, slots), dim3(512), 0, stream, ws.qx, ws.sx, nullptr, a.k,
+                       a.w13, s13, nullptr, I2, a.H, ws.expert_list, ws.seg_off, ws.n_active,
+                       ws.sorted_pairs, 0, ws.act, a.I, nullptr, nullptr);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if (P <= kRotSplitMaxPairs) {
     hipLaunchKernelGGL((k_rot_gemm_splitk<kRotActRot, 4, 1, 16>), dim3(a.H / 16, slots),
                        dim3(256), 0, stream, nullptr, nullptr, ws.act, a.k, a.w2, s2, nullptr,
@@ -2557,14 +2714,20 @@ hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const u
     hipLaunchKernelGGL(k_rot_requant, dim3((unsigned)((P + 7) / 8)), dim3(512), 0, stream,
                        ws.act, P, a.I, ws.qa, ws.sa2);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    // four 16-row weight tiles a workgroup; LDS sized for I
-    auto g2 = a.I <= 512    ? k_rot_gemm_splitk<kRotCodes, 4, 4, 4>
-              : a.I <= 1024 ? k_rot_gemm_splitk<kRotCodes, 4, 4, 8>
-                            : k_rot_gemm_splitk<kRotCodes, 4, 4, 16>;
-    hipLaunchKernelGGL(g2, dim3(a.H / 64, slots), dim3(256), 0, stream, ws.qa, ws.sa2, nullptr,
-                       1, a.w2, s2, nullptr, a.H, a.I, ws.expert_list, ws.seg_off, ws.n_active,
-                       ws.sorted_pairs, 0, ws.y2, a.H, nullptr, nullptr);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (rot_kw_fits(P, P, a.I)) {
+      if ((err = launch_rot_kw<kRotCodes>(ws.qa, ws.sa2, 1, a.w2, s2, a.H, a.I, P, ws, slots,
+                                          ws.y2, a.H, stream)) != hipSuccess)
+        return err;
+    } else {
+      // four 16-row weight tiles a workgroup; LDS sized for I
+      auto g2 = a.I <= 512    ? k_rot_gemm_splitk<kRotCodes, 4, 4, 4>
+                : a.I <= 1024 ? k_rot_gemm_splitk<kRotCodes, 4, 4, 8>
+                              : k_rot_gemm_splitk<kRotCodes, 4, 4, 16>;
+      hipLaunchKernelGGL(g2, dim3(a.H / 64, slots), dim3(256), 0, stream, ws.qa, ws.sa2,
+                         nullptr, 1, a.w2, s2, nullptr, a.H, a.I, ws.expert_list, ws.seg_off,
+                         ws.n_active, ws.sorted_pairs, 0, ws.y2, a.H, nullptr, nullptr);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)(P * a.I),
                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)
       return err;
