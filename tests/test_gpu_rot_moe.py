@@ -202,6 +202,19 @@ def test_rot_moe_single_token_tied_logits(orc, pattern):
     _check_rot(orc, x, tie_logits(pattern, E), k, W, Wd, f"rot moe T=1 ties {pattern}")
 
 
+def test_rot_moe_wave_per_tile_shapes(orc):
+    # 640 pairs take the one-wave-per-tile grouped GEMMs: gemm1 with K = 1024
+    # (16 k steps a wave), gemm2 with K = 1536 (24 of 32 k steps, 12 groups),
+    # ragged 16-pair blocks in every expert
+    E, H, I, k, T = 16, 1024, 1536, 4, 160
+    W = _rot_weights(orc, (99, 0), E, H, I)
+    Wd = _dev_rot_weights(W)
+    x = synth.activations((99, T), T, H, 5, 10.0)
+    x[7] = 0
+    logits = synth.router_logits((99, T), T, E)
+    _check_rot(orc, x, logits, k, W, Wd, "rot moe wave-per-tile shapes")
+
+
 @pytest.mark.parametrize("T", [3, 100])
 def test_rot_moe_with_shared_term(orc, T):
     E, H, I, k = 16, 512, 256, 4
@@ -213,7 +226,7 @@ def test_rot_moe_with_shared_term(orc, T):
     _check_rot(orc, x, logits, k, W, Wd, f"rot moe + shared T={T}", shared=shared)
 
 
-@pytest.mark.parametrize("T", [1, 90])
+@pytest.mark.parametrize("T", [1, 90, 200])
 def test_rot_moe_given_ids_and_skew(orc, T):
     # every token picks expert 0 first: one long segment, the rest short
     E, H, I, k = 8, 256, 256, 3
