@@ -2582,8 +2582,12 @@ __global__ __launch_bounds__(256, 2) void k_rot_tile(const int8_t* __restrict__ 
 // kernel, which the shared expert's large batches use)
 constexpr int64_t kRotSplitMaxPairs = 256;
 
+// the one-workgroup sort up to 2048 pairs, as the routed int8 layer; beyond,
+// the two-launch chunked sort (measured on MI355X at 2048 tokens, 16384 pairs:
+// the Hadamard-domain routed layer 384 -> 374 us)
+constexpr int64_t kRotSortOneWgPairs = 2048;
 hipError_t launch_rot_sort(const MoeArgs& a, const MoeWs& ws, int64_t P, hipStream_t stream) {
-  if (P <= kMoeSortOneWg) {
+  if (P <= kRotSortOneWgPairs) {
     hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, stream, a.topk_ids, (int)P, a.E,
                        ws.expert_list, ws.seg_off, ws.n_active, ws.sorted_pairs, ws.amax);
     return hipGetLastError();
