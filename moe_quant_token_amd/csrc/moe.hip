@@ -1899,17 +1899,26 @@ __global__ __launch_bounds__(WAVES * 64) void k_rot_gemm_splitk(
 // with a wait for every vector memory operation in flight (its copies, those
 // loads, the stores of the block before last), so nothing that block uses
 // waits again.
-template <int MODE, int NKMAX>
+template <int MODE, int NKMAX, bool DENSE = false>
 __global__ __launch_bounds__(256, 2) void k_rot_gemm_kw(
     const int8_t* __restrict__ qx, const float* __restrict__ sx, int k,
-    const int8_t* __restrict__ W, const uint16_t* __restrict__ sW, int Nw, int K, int qx_rows,
+    const int8_t* __restrict__ W, const uint16_t* __restrict__ sW,
+    const uint8_t* __restrict__ su8, int Nw, int K, int qx_rows,
     const int32_t* __restrict__ expert_list, const int32_t* __restrict__ seg_off,
     const int32_t* __restrict__ n_active, const int32_t* __restrict__ sorted_pairs,
-    float* __restrict__ out, int ldo) {
+    int rows_per_y, float* __restrict__ out, int ldo) {
+  // g128 (kRotSilu, kRotCodes): the fold of the definition, fp64 in group
+  // order; kRotG256Silu (the shared expert's gate/up): each 256-group's exact
+  // int32 sum times its u8 scale into int64 sums, any order being exact
+  constexpr bool G256 = MODE == kRotG256Silu;
   constexpr int GMAX = NKMAX / 2;
   __shared__ __attribute__((aligned(1024))) int8_t a_lds[2][NKMAX * 1024];
   RotRows rr;
-  if (!rot_rows(expert_list, seg_off, n_active, 0, 16, rr)) return;
+  // DENSE: one plain matrix (expert_list null), rows_per_y token rows a
+  // workgroup row; else one expert's segment of sorted pairs
+  if (!rot_rows(DENSE ? nullptr : expert_list, seg_off, n_active, qx_rows,
+                DENSE ? rows_per_y : 16, rr))
+    return;
   const int nrows_all = rr.end - rr.begin;
   if (nrows_all <= 0) return;
   const int lane = threadIdx.x & 63;
@@ -1921,23 +1930,35 @@ __global__ __launch_bounds__(256, 2) void k_rot_gemm_kw(
   const int tile = blockIdx.x * 4 + wv;
   const int col = tile * 16 + j;
 
-  // the wave's tile, all of K, and the lane's column scales (indices clamped,
-  // no branch between the loads)
+  // the wave's tile, all of K (streamed past the caches when one call reads
+  // it once; a dense matrix is read again by every workgroup row), and the
+  // lane's column scales (indices clamped, no branch between the loads)
   const int8_t* wb = W + ((int64_t)rr.e * (Nw >> 4) + tile) * nk * 1024 + lane * 16;
   v4i bw[NKMAX];
 #pragma unroll
-  for (int c = 0; c < NKMAX; c++) bw[c] = ld_stream(wb + (int64_t)min(c, nk - 1) * 1024);
+  for (int c = 0; c < NKMAX; c++) {
+    const int8_t* pc = wb + (int64_t)min(c, nk - 1) * 1024;
+    bw[c] = DENSE ? *reinterpret_cast<const v4i*>(pc) : ld_stream(pc);
+  }
   float sv[GMAX];
-  const uint16_t* sp = sW + ((int64_t)rr.e * Nw + col) * G;
+  if constexpr (G256) {
+    const uint8_t* up = su8 + (int64_t)col * (K >> 8);
 #pragma unroll
-  for (int gg = 0; gg < GMAX; gg++) sv[gg] = bf16_bits_to_f32(sp[min(gg, G - 1)]);
+    for (int gg = 0; gg < GMAX; gg++) sv[gg] = (float)up[min(gg, (K >> 8) - 1)];
+  } else {
+    const uint16_t* sp = sW + ((int64_t)rr.e * Nw + col) * G;
+#pragma unroll
+    for (int gg = 0; gg < GMAX; gg++) sv[gg] = bf16_bits_to_f32(sp[min(gg, G - 1)]);
+  }
+  const float s2c = G256 ? bf16_bits_to_f32(sW[col]) : 0.0f;
 
   const int nblk = (nrows_all + 15) >> 4;
   const __amdgpu_buffer_rsrc_t qrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)qx, 0, qx_rows * K, 0x00020000);
   // block b's pair of row j (rows past the segment end repeat its last pair)
   auto pair_of = [&](int b) __attribute__((always_inline)) {
-    return sorted_pairs[min(rr.begin + 16 * b + j, rr.end - 1)];
+    const int r = min(rr.begin + 16 * b + j, rr.end - 1);
+    return DENSE ? r : sorted_pairs[r];
   };
   // block b's codes into buffer b & 1: wave w copies k steps w, w + 4, ...
   auto copy = [&](int b, int p) __attribute__((always_inline)) {
@@ -1954,7 +1975,7 @@ __global__ __launch_bounds__(256, 2) void k_rot_gemm_kw(
       const int r = 4 * g + v;
       const int p = __shfl(p_blk, r, 64);
       if (r < nrows) {
-        if (MODE == kRotSilu) {
+        if (MODE != kRotCodes) {
           if ((j & 1) == 0) out[(int64_t)p * ldo + (col >> 1)] = res[v];
         } else {
           out[(int64_t)p * ldo + col] = res[v];
@@ -1978,25 +1999,46 @@ __global__ __launch_bounds__(256, 2) void k_rot_gemm_kw(
     const int nrows = min(16, nrows_all - 16 * b);
     const int8_t* ab = a_lds[b & 1] + lane * 16;
     double tt[4] = {0.0, 0.0, 0.0, 0.0};
+    if constexpr (G256) {
+      long long S[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int gg = 0; gg < GMAX; gg++) {
-      if (gg < G) {
-        v4i acc = {0, 0, 0, 0};
-        acc = mfma_16x16x64_i8(*reinterpret_cast<const v4i*>(ab + (2 * gg) * 1024), bw[2 * gg],
-                               acc);
-        acc = mfma_16x16x64_i8(*reinterpret_cast<const v4i*>(ab + (2 * gg + 1) * 1024),
-                               bw[2 * gg + 1], acc);
+      for (int gq = 0; gq < GMAX / 2; gq++) {
+        if (4 * gq < nk) {
+          v4i acc = {0, 0, 0, 0};
 #pragma unroll
-        for (int v = 0; v < 4; v++) tt[v] = tt[v] + (double)acc[v] * (double)sv[gg];
+          for (int h = 0; h < 4; h++)
+            acc = mfma_16x16x64_i8(*reinterpret_cast<const v4i*>(ab + (4 * gq + h) * 1024),
+                                   bw[4 * gq + h], acc);
+          // |acc| <= 256 * 127^2, so acc * u8 < 2^31 is exact in int32
+          const int u8 = (int)sv[gq];
+#pragma unroll
+          for (int v = 0; v < 4; v++) S[v] += (long long)(acc[v] * u8);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 4; v++) tt[v] = (double)S[v];
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < GMAX; gg++) {
+        if (gg < G) {
+          v4i acc = {0, 0, 0, 0};
+          acc = mfma_16x16x64_i8(*reinterpret_cast<const v4i*>(ab + (2 * gg) * 1024),
+                                 bw[2 * gg], acc);
+          acc = mfma_16x16x64_i8(*reinterpret_cast<const v4i*>(ab + (2 * gg + 1) * 1024),
+                                 bw[2 * gg + 1], acc);
+#pragma unroll
+          for (int v = 0; v < 4; v++) tt[v] = tt[v] + (double)acc[v] * (double)sv[gg];
+        }
       }
     }
 #pragma unroll
     for (int v = 0; v < 4; v++) {
       const float sa = __shfl(s_cur, min(4 * g + v, nrows - 1), 64);
       double t = tt[v] * (double)sa;
+      if (G256) t = t * (double)s2c;
       t = t * 0.0078125;
       const float hv = (float)t;
-      res[v] = MODE == kRotSilu ? rot_silu_pair(hv) : hv;
+      res[v] = MODE == kRotCodes ? hv : rot_silu_pair(hv);
     }
     p_prev = p_cur;
     p_cur = p_nxt;
@@ -2662,16 +2704,20 @@ static bool rot_kw_fits(int64_t P, int64_t rows, int64_t K) {
   return P >= kRotKwMinPairs && K <= 2048 && rows * K < ((int64_t)1 << 31);
 }
 
-template <int MODE>
+template <int MODE, bool DENSE = false>
 static hipError_t launch_rot_kw(const int8_t* qx, const float* sx, int k, const int8_t* W,
-                                const uint16_t* sW, int64_t Nw, int64_t K, int64_t rows,
-                                const MoeWs& ws, unsigned slots, float* out, int64_t ldo,
-                                hipStream_t stream) {
-  const dim3 grid((unsigned)(Nw / 64), slots), block(256);
-#define W8A8_KW(n)                                                                              \
-  hipLaunchKernelGGL((k_rot_gemm_kw<MODE, n>), grid, block, 0, stream, qx, sx, k, W, sW,       \
-                     (int)Nw, (int)K, (int)rows, ws.expert_list, ws.seg_off, ws.n_active,     \
-                     ws.sorted_pairs, out, (int)ldo)
+                                const uint16_t* sW, const uint8_t* su8, int64_t Nw, int64_t K,
+                                int64_t rows, const MoeWs* ws, unsigned grid_y,
+                                int rows_per_y, float* out, int64_t ldo, hipStream_t stream) {
+  const dim3 grid((unsigned)(Nw / 64), grid_y), block(256);
+  const int32_t* el = ws ? ws->expert_list : nullptr;
+  const int32_t* so = ws ? ws->seg_off : nullptr;
+  const int32_t* na = ws ? ws->n_active : nullptr;
+  const int32_t* sp = ws ? ws->sorted_pairs : nullptr;
+#define W8A8_KW(n)                                                                          \
+  hipLaunchKernelGGL((k_rot_gemm_kw<MODE, n, DENSE>), grid, block, 0, stream, qx, sx, k, W, \
+                     sW, su8, (int)Nw, (int)K, (int)rows, el, so, na, sp, rows_per_y, out,  \
+                     (int)ldo)
   if (K <= 512)
     W8A8_KW(8);
   else if (K <= 1024)
@@ -2697,8 +2743,8 @@ hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const u
   // four (H <= 2048) or two 16-row weight tiles a workgroup: the activation
   // slices loaded once for all, more weight bytes in flight; LDS sized for H
   if (rot_kw_fits(P, a.T, a.H)) {
-    if ((err = launch_rot_kw<kRotSilu>(ws.qx, ws.sx, a.k, a.w13, s13, I2, a.H, a.T, ws, slots,
-                                       ws.act, a.I, stream)) != hipSuccess)
+    if ((err = launch_rot_kw<kRotSilu>(ws.qx, ws.sx, a.k, a.w13, s13, nullptr, I2, a.H, a.T,
+                                       &ws, slots, 0, ws.act, a.I, stream)) != hipSuccess)
       return err;
   } else {
     auto g1 = a.H <= 2048 ? k_rot_gemm_splitk<kRotSilu, 8, 4, 16>
@@ -2719,8 +2765,8 @@ hipError_t launch_moe_rot_forward(const MoeArgs& a, const uint16_t* s13, const u
                        ws.act, P, a.I, ws.qa, ws.sa2);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (rot_kw_fits(P, P, a.I)) {
-      if ((err = launch_rot_kw<kRotCodes>(ws.qa, ws.sa2, 1, a.w2, s2, a.H, a.I, P, ws, slots,
-                                          ws.y2, a.H, stream)) != hipSuccess)
+      if ((err = launch_rot_kw<kRotCodes>(ws.qa, ws.sa2, 1, a.w2, s2, nullptr, a.H, a.I, P,
+                                          &ws, slots, 0, ws.y2, a.H, stream)) != hipSuccess)
         return err;
     } else {
       // four 16-row weight tiles a workgroup; LDS sized for I
@@ -2861,15 +2907,34 @@ hipError_t launch_shared_expert(const SharedArgs& a, hipStream_t stream) {
                        nullptr, nullptr, nullptr, T, a.y, H, a.dbg_qa, a.dbg_sa);
   } else {
     const unsigned mbs = (unsigned)((a.T + 1023) / 1024 * 8);  // 128-row blocks, x 8 XCDs
-    hipLaunchKernelGGL(k_rot_tile<kRotG256Silu>, dim3(mbs * 2 * (2 * Is / 128)), dim3(256), 0,
-                       stream, ws.qx, ws.sx, a.wgu, a.s2, a.su8, 2 * Is, H, T, ws.act, Is);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // one wave per weight tile holding all of K where K fits (H, Is <= 2048),
+    // 32 token rows a workgroup row up to 1024 tokens, 64 beyond (measured on
+    // MI355X, H=2048, Is=512, against the tiled GEMMs: 128 tokens 34.5 ->
+    // 20.2 us, 512 tokens 36.2 -> 23.4 us, 2048 tokens 44.6 -> 43.9 us)
+    const bool kw = a.H <= 2048 && a.Is <= 2048 && a.T * a.H < ((int64_t)1 << 31);
+    const int kw_rows = a.T <= 1024 ? 32 : 64;
+    const unsigned ry = (unsigned)((a.T + kw_rows - 1) / kw_rows);
+    if (kw)
+      err = launch_rot_kw<kRotG256Silu, true>(ws.qx, ws.sx, 1, a.wgu, a.s2, a.su8, 2 * Is, H, T,
+                                              nullptr, ry, kw_rows, ws.act, Is, stream);
+    else {
+      hipLaunchKernelGGL(k_rot_tile<kRotG256Silu>, dim3(mbs * 2 * (2 * Is / 128)), dim3(256), 0,
+                         stream, ws.qx, ws.sx, a.wgu, a.s2, a.su8, 2 * Is, H, T, ws.act, Is);
+      err = hipGetLastError();
+    }
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k_rot_requant, dim3((unsigned)((a.T + 7) / 8)), dim3(512), 0, stream,
                        ws.act, a.T, Is, ws.qa, ws.sa);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_rot_tile<kRotCodes>, dim3(mbs * 2 * (H / 128)), dim3(256), 0, stream,
-                       ws.qa, ws.sa, a.wd, a.sd, nullptr, H, Is, T, a.y, H);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (kw)
+      err = launch_rot_kw<kRotCodes, true>(ws.qa, ws.sa, 1, a.wd, a.sd, nullptr, H, Is, T,
+                                           nullptr, ry, kw_rows, a.y, H, stream);
+    else {
+      hipLaunchKernelGGL(k_rot_tile<kRotCodes>, dim3(mbs * 2 * (H / 128)), dim3(256), 0, stream,
+                         ws.qa, ws.sa, a.wd, a.sd, nullptr, H, Is, T, a.y, H);
+      err = hipGetLastError();
+    }
+    if (err != hipSuccess) return err;
     if (a.dbg_qa && (err = hipMemcpyAsync(a.dbg_qa, ws.qa, (size_t)(a.T * a.Is),
                                           hipMemcpyDeviceToDevice, stream)) != hipSuccess)
       return err;

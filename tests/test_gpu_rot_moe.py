@@ -324,19 +324,22 @@ def _check_shared(orc, x, S, Sd, label):
     return y, y_ref
 
 
-def test_shared_expert_wide_scale_range(orc):
-    # the tiled GEMMs (more than 64 rows): down-weight rows with one 128-group
-    # scaled down by 2^-30 span more than the integer fold allows, so those
-    # waves fold in fp64 group by group while the others take the integer fold
-    H, Is, T = 512, 256, 200
+@pytest.mark.parametrize("H", [512, 4096])
+def test_shared_expert_wide_scale_range(orc, H):
+    # more than 64 rows (H = 512: the one-wave-per-tile GEMMs, which fold in
+    # fp64 in group order; H = 4096: the tiled GEMMs, where down-weight rows
+    # with one 128-group scaled down by 2^-30 span more than the integer fold
+    # allows, so those waves fold in fp64 group by group while the others take
+    # the integer fold)
+    Is, T = 256, 200
     wgu, su8, s2 = orc.weight_prep_g256(synth.weights((98, 5), 2 * Is, H, tensor_id=synth.T_W))
     Wd = synth.weights((98, 5), H, Is, tensor_id=synth.T_W2)
     Wd[:32, :128] *= np.float32(2.0 ** -30)
-    Wd[300:301, 128:] *= np.float32(2.0 ** -25)
+    Wd[H // 2:H // 2 + 1, 128:] *= np.float32(2.0 ** -25)
     wd, sd = orc.weight_prep_g128(Wd)
     S = (wgu, su8, s2, wd, sd)
     x = synth.activations((98, 6), T, H, 4, 10.0)
-    _check_shared(orc, x, S, _dev_shared_weights(S), "shared wide scale range")
+    _check_shared(orc, x, S, _dev_shared_weights(S), f"shared wide scale range H={H}")
 
 
 @pytest.mark.parametrize("T", [1, 7, 64, 65, 300])
