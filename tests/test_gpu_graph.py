@@ -331,7 +331,7 @@ def test_router_and_g128_prep_graph(orc):
 @pytest.mark.parametrize("T", [2, 40, 200])
 def test_rot_moe_and_shared_graph(orc, T):
     # split-K forms (2 and 40 tokens) and, at 200 tokens (800 pairs), the
-    # one-wave-per-tile grouped GEMMs and the tiled shared expert
+    # one-wave-per-tile GEMMs of the routed experts and of the shared expert
     E, H, I, k, Is = 8, 256, 128, 4, 128
     key = (77, T)
     q13 = np.empty((E, 2 * I, H), np.int8)
