@@ -120,11 +120,11 @@ def test_linear_g256_single_token(orc, K, N, zero):
 
 @pytest.mark.parametrize("M,K,N", [(33, 1024, 128), (64, 2048, 256), (100, 2048, 1152),
                                    (200, 1024, 384), (256, 2048, 8192), (129, 4096, 80),
-                                   (257, 2048, 96)])
+                                   (257, 2048, 96), (128, 2048, 1040), (320, 1024, 2048)])
 def test_linear_g256_mid_batches(orc, M, K, N):
-    # 33 to 257 rows through the fused entry (tile-layout codes, the g256 tile
+    # 33 to 320 rows through the fused entry (tile-layout codes, the g256 tile
     # kernel), ragged last row tile, K = 4096, a half-filled last 32-column
-    # block, an all-zero row
+    # block, a last 64-column tile with one 16-column tile, an all-zero row
     say(f"linear g256 mid batches M={M} K={K} N={N}")
     W = synth.weights((58, K, N), N, K)
     qw, su8, s2 = orc.weight_prep_g256(W)
