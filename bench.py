@@ -463,6 +463,8 @@ def main():
         cases.update(mlp_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes))
     if "kv" in groups:
         cases.update(kv_cases(torch, np, mq, synth, dev, timer, bf16_dev, hashes))
+    if cases and "hbm_stream" in out:
+        annotate_stream(cases, out["hbm_stream"]["stream_read"])
     if cases:
         out["cases"] = cases
     if timer.enqueue_bound:
@@ -528,6 +530,31 @@ def stream_ceiling(torch, timer, mq, shapes):
         med = pct(each, 50)
         probe[sh["name"]] = {"bytes": nbytes, "chunk": chunk, "median_us": round(med * 1e3, 2),
                              "gbs": round(nbytes / (med * 1e-3) / 1e9, 1)}
+    # reads the size of one-token launches: a single-token MoE gemm1 (8 experts'
+    # 1024 x 2048 codes, 32 KiB a workgroup) and gemm2 (8 x 2048 x 512, 8 KiB a
+    # workgroup), alone and as two launches back to back, the ceiling of a
+    # two-launch single-token layer; the first alone is also the size of the
+    # one-token Hadamard linear's weights (8192 x 2048)
+    small = {"t1_gemm1": (8 * 1024 * 2048, 16 * 2048), "t1_gemm2": (8 * 2048 * 512, 16 * 512)}
+    sviews = {}
+    for name, (nbytes, chk) in small.items():
+        nslice = big // nbytes
+        sviews[name] = ([buf[i * nbytes:(i + 1) * nbytes] for i in range(nslice)], chk)
+        vs = sviews[name][0]
+        _, each = timer.run(lambda i: mq.stream_read(vs[i % len(vs)], chk, sink), 48, groups=8)
+        med = pct(each, 50)
+        probe[name] = {"bytes": nbytes, "chunk": chk, "median_us": round(med * 1e3, 2),
+                       "gbs": round(nbytes / (med * 1e-3) / 1e9, 1)}
+    v1, c1 = sviews["t1_gemm1"]
+    v2, c2 = sviews["t1_gemm2"]
+
+    def pair(i):
+        mq.stream_read(v1[i % len(v1)], c1, sink)
+        mq.stream_read(v2[i % len(v2)], c2, sink)
+
+    _, each = timer.run(pair, 48, groups=8)
+    probe["t1_two_launches"] = {"bytes": small["t1_gemm1"][0] + small["t1_gemm2"][0],
+                                "median_us": round(pct(each, 50) * 1e3, 2)}
     chunk = 80 * 1024
     whole = big // chunk * chunk
     _, each = timer.run(lambda i: mq.stream_read(buf[:whole], chunk, sink), 10, groups=10)
@@ -538,6 +565,29 @@ def stream_ceiling(torch, timer, mq, shapes):
     del buf, sink
     torch.cuda.empty_cache()
     return res
+
+
+def annotate_stream(cases, probe):
+    """Beside each weight-streaming case, the time the streaming-read kernel
+    takes for the same weight bytes in the same number of launches (measured
+    in this run), and the case's time as a fraction of it: how close the
+    kernel comes to what a launch of that size can stream on this machine."""
+    def put(name, ref):
+        c = cases.get(name)
+        if c is None or ref not in probe:
+            return
+        t = c["median_us"] if "median_us" in c else None
+        if t:
+            c["stream_ceiling_us"] = probe[ref]["median_us"]
+            c["frac_stream"] = round(probe[ref]["median_us"] / t, 4)
+    for name in list(cases):
+        if name.startswith("decode_gate_up_") and not name.endswith("_warm"):
+            put(name, "gate_up")
+        elif name.startswith("decode_down_") and not name.endswith("_warm"):
+            put(name, "down")
+    put("moe_T1", "t1_two_launches")
+    put("rot_moe_T1_routed", "t1_two_launches")
+    put("fwht128_g256_M1_K2048_N8192", "t1_gemm1")
 
 
 def clock_probe(torch, clock, capture, seconds):
