@@ -440,7 +440,7 @@ def main():
     # ------------------------------------------------------------ what HBM delivers
     # torch's own copy and sum kernels over 1 GiB buffers, and the library's
     # streaming-read kernel over each decode shape's weight bytes: the rates
-    # this box delivers at this moment, beside which the roofline fractions
+    # this GPU delivers at this moment, beside which the roofline fractions
     # (against the published 8 TB/s) can be read
     if not args.probe_copy:
         out["hbm_stream"] = stream_ceiling(torch, timer, mq, shapes)
@@ -571,7 +571,7 @@ def annotate_stream(cases, probe):
     """Beside each weight-streaming case, the time the streaming-read kernel
     takes for the same weight bytes in the same number of launches (measured
     in this run), and the case's time as a fraction of it: how close the
-    kernel comes to what a launch of that size can stream on this machine."""
+    kernel comes to what a launch of that size can stream on this GPU."""
     def put(name, ref):
         c = cases.get(name)
         if c is None or ref not in probe:
