@@ -131,68 +131,89 @@ __global__ __launch_bounds__(TB * KS * 64) void k_router_mfma(
   }
 }
 
-// Larger batches: a wave takes 16 tokens x 16 EB experts (the token
-// fragment of each k step feeds EB MFMAs); workgroup = TB token blocks x KS
-// slices of H, the slices' partial sums added in slice order.  Each weight
+// Larger batches: workgroup = 16 TB tokens x 16 EB experts x KS slices of H,
+// the slices' partial sums added in slice order.  Wave (eh, ks) takes all TB
+// token blocks and the EB / EH expert blocks of half eh (each weight fragment
+// of a k step feeds TB MFMAs, each token fragment EB / EH), so the
+// workgroup loads every weight fragment once and every token fragment EH
+// times; each logit's sum (MFMA chain over its slice in k order, then the
+// slices in order) is the same whatever the split over waves.  Each weight
 // fragment is read by T / (16 TB) workgroups and each token fragment by
 // E / (16 EB), against E / 16 for the one-expert-block form.
-template <int TB, int KS, int EB>
-__global__ __launch_bounds__(TB * KS * 64) void k_router_mfma_wide(
+template <int TB, int KS, int EB, int EH>
+__global__ __launch_bounds__(EH * KS * 64) void k_router_mfma_wide(
     const uint16_t* __restrict__ x, int T, int H, int64_t ldx, const uint16_t* __restrict__ wg,
     float* __restrict__ logits, int64_t ldl) {
+  constexpr int EW = EB / EH;  // expert blocks a wave
+  static_assert(EB % EH == 0, "expert blocks must split over the waves");
   __shared__ v4f red[TB][KS][EB][64];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int tb = wv / KS, ks = wv - (wv / KS) * KS;
+  const int eh = wv / KS, ks = wv - (wv / KS) * KS;
   const int j = lane & 15;
   const int g = lane >> 4;
   const int e0 = blockIdx.x * 16 * EB;
-  const int t0 = (blockIdx.y * TB + tb) * 16;
-  const int ta = min(t0 + j, T - 1);  // rows past T read a valid row; not stored
+  const int tw0 = blockIdx.y * TB * 16;
   const int hs = H / KS;
-  const uint16_t* ap = x + (int64_t)ta * ldx + ks * hs + g * 8;
-  const uint16_t* bp = wg + (int64_t)(e0 + j) * H + ks * hs + g * 8;
-  v4f acc[EB];
+  const uint16_t* ap[TB];
 #pragma unroll
-  for (int b = 0; b < EB; b++) acc[b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  if (t0 < T) {
-    constexpr int U = 4;
-    for (int k0 = 0; k0 < hs; k0 += 32 * U) {  // hs is a multiple of 32 U (launcher)
-      v4u a[U], b[U][EB];
+  for (int tb = 0; tb < TB; tb++) {
+    const int ta = min(tw0 + 16 * tb + j, T - 1);  // rows past T read a valid row; not stored
+    ap[tb] = x + (int64_t)ta * ldx + ks * hs + g * 8;
+  }
+  const uint16_t* bp = wg + (int64_t)(e0 + 16 * EW * eh + j) * H + ks * hs + g * 8;
+  v4f acc[TB][EW];
 #pragma unroll
-      for (int u = 0; u < U; u++) {
-        a[u] = *reinterpret_cast<const v4u*>(ap + k0 + 32 * u);
+  for (int tb = 0; tb < TB; tb++)
 #pragma unroll
-        for (int e = 0; e < EB; e++)
-          b[u][e] = *reinterpret_cast<const v4u*>(bp + (int64_t)e * 16 * H + k0 + 32 * u);
-      }
+    for (int e = 0; e < EW; e++) acc[tb][e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int U = 4;
+  for (int k0 = 0; k0 < hs; k0 += 32 * U) {  // hs is a multiple of 32 U (launcher)
+    v4u a[U][TB], b[U][EW];
 #pragma unroll
-      for (int u = 0; u < U; u++)
+    for (int u = 0; u < U; u++) {
 #pragma unroll
-        for (int e = 0; e < EB; e++)
-          acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[u]),
-                                                           __builtin_bit_cast(v8bf, b[u][e]),
-                                                           acc[e], 0, 0, 0);
+      for (int tb = 0; tb < TB; tb++)
+        a[u][tb] = *reinterpret_cast<const v4u*>(ap[tb] + k0 + 32 * u);
+#pragma unroll
+      for (int e = 0; e < EW; e++)
+        b[u][e] = *reinterpret_cast<const v4u*>(bp + (int64_t)e * 16 * H + k0 + 32 * u);
     }
+#pragma unroll
+    for (int u = 0; u < U; u++)
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++)
+#pragma unroll
+        for (int e = 0; e < EW; e++)
+          acc[tb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(v8bf, a[u][tb]), __builtin_bit_cast(v8bf, b[u][e]), acc[tb][e],
+              0, 0, 0);
   }
 #pragma unroll
-  for (int e = 0; e < EB; e++) red[tb][ks][e][lane] = acc[e];
+  for (int tb = 0; tb < TB; tb++)
+#pragma unroll
+    for (int e = 0; e < EW; e++) red[tb][ks][EW * eh + e][lane] = acc[tb][e];
   __syncthreads();
-  if (ks != 0 || t0 >= T) return;
+  if (ks != 0) return;
 #pragma unroll
-  for (int e = 0; e < EB; e++) {
-    v4f sum = red[tb][0][e][lane];
-    for (int i = 1; i < KS; i++) {
-      const v4f p = red[tb][i][e][lane];
-      sum.x = sum.x + p.x;
-      sum.y = sum.y + p.y;
-      sum.z = sum.z + p.z;
-      sum.w = sum.w + p.w;
-    }
+  for (int tb = 0; tb < TB; tb++) {
+    const int t0 = tw0 + 16 * tb;
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-      const int t = t0 + 4 * g + v;
-      if (t < T) logits[(int64_t)t * ldl + e0 + 16 * e + j] = sum[v];
+    for (int e = 0; e < EW; e++) {
+      const int eb = EW * eh + e;
+      v4f sum = red[tb][0][eb][lane];
+      for (int i = 1; i < KS; i++) {
+        const v4f p = red[tb][i][eb][lane];
+        sum.x = sum.x + p.x;
+        sum.y = sum.y + p.y;
+        sum.z = sum.z + p.z;
+        sum.w = sum.w + p.w;
+      }
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int t = t0 + 4 * g + v;
+        if (t < T) logits[(int64_t)t * ldl + e0 + 16 * eb + j] = sum[v];
+      }
     }
   }
 }
@@ -207,9 +228,20 @@ hipError_t launch_router_gate_bf16(const uint16_t* x, int64_t T, int64_t H, int6
     hipLaunchKernelGGL((k_router_mfma<1, 8>), dim3((unsigned)(E / 16), (unsigned)((T + 15) / 16)),
                        dim3(512), 0, stream, x, (int)T, (int)H, ldx, wg, logits, ldl);
   } else if (E % 64 == 0 && H % 512 == 0) {
-    hipLaunchKernelGGL((k_router_mfma_wide<2, 4, 4>),
-                       dim3((unsigned)(E / 64), (unsigned)((T + 31) / 32)), dim3(512), 0, stream,
-                       x, (int)T, (int)H, ldx, wg, logits, ldl);
+    // the widest expert block that still gives every CU a workgroup (a
+    // workgroup's time is set by the bytes it reads: 32 tokens x 64 experts
+    // read 512 KiB at H = 2048, 32 x 16 read 192 KiB); the logits do not
+    // depend on the choice
+    const unsigned ty = (unsigned)((T + 31) / 32);
+    if ((E / 64) * ty >= 256)
+      hipLaunchKernelGGL((k_router_mfma_wide<2, 4, 4, 2>), dim3((unsigned)(E / 64), ty),
+                         dim3(512), 0, stream, x, (int)T, (int)H, ldx, wg, logits, ldl);
+    else if ((E / 32) * ty >= 256)
+      hipLaunchKernelGGL((k_router_mfma_wide<2, 4, 2, 2>), dim3((unsigned)(E / 32), ty),
+                         dim3(512), 0, stream, x, (int)T, (int)H, ldx, wg, logits, ldl);
+    else
+      hipLaunchKernelGGL((k_router_mfma_wide<2, 4, 1, 1>), dim3((unsigned)(E / 16), ty),
+                         dim3(256), 0, stream, x, (int)T, (int)H, ldx, wg, logits, ldl);
   } else if (H % 64 == 0) {
     hipLaunchKernelGGL((k_router_mfma<4, 2>), dim3((unsigned)(E / 16), (unsigned)((T + 63) / 64)),
                        dim3(512), 0, stream, x, (int)T, (int)H, ldx, wg, logits, ldl);

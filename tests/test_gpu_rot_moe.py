@@ -88,7 +88,7 @@ def test_weight_prep_g128(orc, N, K):
 # to 256), 16 x 64 tiles over 4 slices beyond (ragged last token block); the
 # 16 x 16 tiles over 2 slices where E is not a multiple of 64
 @pytest.mark.parametrize("T,E", [(1, 256), (3, 256), (16, 256), (17, 256), (100, 256),
-                                 (300, 256), (2048, 256), (300, 48)])
+                                 (300, 256), (1000, 256), (2048, 256), (300, 48)])
 def test_router_gate(orc, T, E):
     H = 2048
     x = synth.activations((91, T), T, H, 20, 10.0)
@@ -105,6 +105,19 @@ def test_router_gate(orc, T, E):
     err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
     assert (err <= bound).all(), f"router T={T} E={E}: max err / bound {(err / bound).max():.3f}"
     say(f"router T={T} E={E}: max err / bound {(err / bound).max():.4f}")
+
+
+def test_router_gate_wide_forms_agree():
+    # beyond 256 tokens the expert block per workgroup follows the batch size
+    # (64, 32 or 16 experts); a token's logits are the same sums either way
+    H, E = 2048, 256
+    x = synth.activations((92, 2048), 2048, H, 20, 10.0)
+    wg = bf16_dev(synth.to_bf16_bits(synth.weights((92, E), E, H)))
+    xd = bf16_dev(x)
+    full = host(mq.router_gate_bf16(xd, wg))
+    for T in (1000, 300):
+        part = host(mq.router_gate_bf16(xd[:T].contiguous(), wg))
+        np.testing.assert_array_equal(part, full[:T])
 
 
 @pytest.mark.parametrize("T", [5, 40])
